@@ -1,0 +1,242 @@
+/*
+ * medusa.h -- C ABI of libmedusa, the Medusa speculate-and-verify step on
+ * AMD MI355X (gfx950).
+ *
+ * One verify step is, in order (every call enqueues on one HIP stream):
+ *   medusa_heads               K Medusa heads: ResBlock, lm_head, top-k
+ *   medusa_build_tree          candidate tree from a medusa_choices spec
+ *   medusa_tree_attention      tree-masked attention over the KV prefix
+ *   (caller: base lm_head at the tree nodes -> logits)
+ *   medusa_evaluate_posterior  greedy / typical acceptance, best path
+ *   medusa_commit_kv           gather the accepted rows into contiguous slots
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronises, and keeps no state between
+ *    calls.  Outputs are valid once the stream reaches the call.
+ *  - `stream` is a hipStream_t (NULL = the default stream).
+ *  - Every call validates its arguments on the host BEFORE any HIP call and
+ *    returns a medusa_status synchronously; on a negative status nothing was
+ *    enqueued.  MEDUSA_ERR_HIP means a launch failed; medusa_last_error()
+ *    then holds the HIP message (per calling thread).
+ *  - Tensor pointers must be 16-byte aligned (MEDUSA_ERR_ALIGN).  Layouts
+ *    are dense row-major in the order given; no strides.
+ *  - Supported sizes: batch B <= 16, heads K <= 8, topk <= 64, tree nodes
+ *    T <= 256 (so at most 255 spec entries), head dim d in {64, 128}.
+ *  - bf16 tensors are raw bf16 bit patterns (uint16); f32 tensors are IEEE
+ *    float32.  Accumulation is always float32.
+ *
+ * Citations name the pages the operations come from:
+ *  [API] "Medusa API参考：核心函数与类详解" (jsqmd.com)
+ *  [NOTES] "Medusa — 让大模型自己同时猜好几个 token" (estelledc.github.io)
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MEDUSA_OK = 0,
+  MEDUSA_ERR_NULL = -1,      /* a required pointer is NULL                  */
+  MEDUSA_ERR_SHAPE = -2,     /* a size is outside the supported range       */
+  MEDUSA_ERR_DTYPE = -3,     /* unknown or unsupported dtype                */
+  MEDUSA_ERR_VALUE = -4,     /* a scalar argument is out of range           */
+  MEDUSA_ERR_WORKSPACE = -5, /* workspace smaller than the *_workspace size */
+  MEDUSA_ERR_HIP = -6,       /* a HIP launch failed (see medusa_last_error) */
+  MEDUSA_ERR_ALIGN = -7,     /* a tensor pointer is not 16-byte aligned     */
+  MEDUSA_ERR_ALIAS = -8      /* an output aliases an input it must not      */
+} medusa_status;
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
+
+/* Values of status[0] written on the device by medusa_build_tree.
+ * status[1] holds the offending spec entry (or the leaf count for
+ * MEDUSA_SPEC_TOO_MANY_PATHS), -1 when MEDUSA_SPEC_OK.  Entries are checked
+ * in this order: for each entry (in the given order) padding, then empty,
+ * then rank; then duplicates (the first entry repeating an earlier one);
+ * then missing prefixes (the first entry lacking a proper prefix); then the
+ * leaf count against p_max. */
+enum {
+  MEDUSA_SPEC_OK = 0,
+  MEDUSA_SPEC_PADDING = 1,        /* a -1 followed by a rank            */
+  MEDUSA_SPEC_EMPTY = 2,          /* an all -1 entry                    */
+  MEDUSA_SPEC_RANK = 3,           /* a rank outside [0, topk)           */
+  MEDUSA_SPEC_DUPLICATE = 4,      /* the same tuple twice               */
+  MEDUSA_SPEC_PREFIX = 5,         /* a proper prefix is not an entry    */
+  MEDUSA_SPEC_TOO_MANY_PATHS = 6  /* more leaves than p_max             */
+};
+
+/* ---------------------------------------------------------------------
+ * Medusa heads.  [API] MedusaModelABC (medusa_head: residual blocks and
+ * linear layers; MedusaConfig medusa_num_heads = 5, medusa_num_layers = 1);
+ * [NOTES] 是什么 / 核心要点 (K parallel heads on the last hidden state,
+ * each a one-layer MLP with a residual, head k proposing token t+k+1, the
+ * per-head top-k forming the candidate tree).
+ *
+ * For every sequence b and head j:
+ *   r[b][j]      = h[b] + SiLU(W1[j] h[b] + b1[j])           (float32)
+ *   logits[b][j] = Wlm[j] r[b][j]                             (no bias)
+ *   topk_ids[b][j][0..topk) = the topk largest logits, ordered by value
+ *   descending, equal values by lower token id first.
+ *
+ * Layouts: hidden [B][H]; w1 [K][H][H] (out x in: row i makes output i);
+ * b1 [K][H]; w_lm [K][V][H] (out x in); r [B][K][H] float32;
+ * topk_ids int32 and topk_logits float32 [B][K][topk]; logits float32
+ * [B][K][V].  `dtype` applies to hidden, w1, b1 and w_lm.  bf16 needs
+ * H % 8 == 0, f32 needs H % 4 == 0; 1 <= topk <= min(64, V).
+ *
+ * Workspace: medusa_heads_workspace() bytes of device memory.  Its first
+ * 256 bytes hold completion counters that MUST be zero before the first
+ * call; every call returns them to zero, so zero it once (hipMemset) and
+ * reuse it.  Calls that share a workspace must not run concurrently.
+ * ------------------------------------------------------------------- */
+size_t medusa_heads_workspace(int dtype, int B, int H, int V, int K, int topk);
+
+/* ResBlock of every head: writes r (float32 [B][K][H]). */
+int medusa_resblock(int dtype, int B, int H, int K,
+                    const void* hidden, const void* w1, const void* b1,
+                    float* r, void* stream);
+
+/* lm_head of every head on a float32 r [B][K][H], with fused top-k.
+ * logits_or_null: optional float32 [B][K][V] copy of every logit. */
+int medusa_lm_head_topk(int dtype, int B, int H, int V, int K, int topk,
+                        const float* r, const void* w_lm,
+                        int32_t* topk_ids, float* topk_logits, float* logits_or_null,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Both stages.  r_or_null: optional float32 [B][K][H] output of the
+ * ResBlocks (kept inside the workspace otherwise). */
+int medusa_heads(int dtype, int B, int H, int V, int K, int topk,
+                 const void* hidden, const void* w1, const void* b1, const void* w_lm,
+                 int32_t* topk_ids, float* topk_logits, float* logits_or_null,
+                 float* r_or_null, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Candidate tree.  [API] medusa_generate (medusa_choices),
+ * generate_candidates (tree_indices, retrieve_indices), tree_decoding
+ * (tree_candidates, medusa_position_ids); [NOTES] 核心要点 (prefix tree of
+ * the per-head top-k) and 实践案例 案例 3 (the worked mask: P, A, B, X, Y,
+ * X, Y with each continuation seeing only the prompt and its own branch).
+ *
+ * choices int32 [n_choices][K]: rank tuples (r1, ..., rd) padded with -1,
+ * in any order; tuple (r1..rd) is the r1-th token of head 1 followed by the
+ * r2-th token of head 2, etc.  T = n_choices + 1 nodes: node 0 is the root
+ * (the base model's next token, root_token[b]); the others are the tuples
+ * sorted by (length, lexicographic order).  One tree serves the whole
+ * batch; candidates and positions are per sequence.
+ *
+ * Outputs:
+ *   tree_candidates int32 [B][T]  token at each node
+ *   tree_indices    int32 [T]     0 for the root, else 1+(depth-1)*topk+rank:
+ *                                 index into [root, head-1 top-k, head-2 top-k, ...]
+ *   parent, depth   int32 [T]     parent[0] = -1
+ *   position_ids    int32 [B][T]  prefix_len[b] + depth
+ *   tree_mask       uint8 [T][T]  1 where node j is an ancestor of node i or i
+ *   retrieve        int32 [p_max][K+1]  leaf paths in ascending leaf order,
+ *                                 root first, -1 padded; rows >= num_paths are -1
+ *   num_paths       int32 [1]
+ *   status          int32 [2]     see MEDUSA_SPEC_*
+ * On a spec error the outputs describe the root alone (num_paths = 1,
+ * retrieve row 0 = (0, -1, ...), identity mask, every node the root token,
+ * depth 0), so later stages stay in bounds and accept nothing.
+ * ------------------------------------------------------------------- */
+int medusa_build_tree(int B, int K, int topk, int n_choices,
+                      const int32_t* choices, const int32_t* topk_ids,
+                      const int32_t* root_token, const int32_t* prefix_len,
+                      int32_t* tree_candidates, int32_t* tree_indices,
+                      int32_t* parent, int32_t* depth, int32_t* position_ids,
+                      uint8_t* tree_mask, int32_t* retrieve, int32_t* num_paths,
+                      int p_max, int32_t* status, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Tree attention.  [NOTES] 核心要点 (tree attention verifies every
+ * candidate in one forward) and 实践案例 案例 3 (ancestor-only mask);
+ * [API] tree_decoding (the tree runs against past_key_values).
+ *
+ * For sequence b, head h and tree node i (L = prefix_len[b]):
+ *   out[b][i][h] = softmax_m(scale * q[b][i][h] . K[m]) V[m]
+ * over the prefix slots m in [0, L) and the tree slots L + j with
+ * tree_mask[i][j] = 1.  The caller has written the tree's K/V at slots
+ * L .. L+T-1 and applied position encoding (positions prefix_len + depth)
+ * to q and the tree keys.  Slots past L+T are never read.
+ *
+ * Layouts: q, out [B][T][Hq][d]; k_cache, v_cache [B][Hq][max_slots][d]
+ * (one layer; pass a layer's base pointer for a multi-layer cache);
+ * tree_mask uint8 [T][T].  Requires L + T <= max_slots for every b (a larger
+ * L is clamped to max_slots - T).  scale is usually 1/sqrt(d).
+ * Workspace: medusa_tree_attention_workspace() bytes (no initialisation).
+ * ------------------------------------------------------------------- */
+size_t medusa_tree_attention_workspace(int dtype, int B, int T, int Hq, int d, int max_slots);
+
+int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int max_slots,
+                          const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* prefix_len, const uint8_t* tree_mask, float scale,
+                          void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Acceptance.  [API] evaluate_posterior (temperature, posterior_threshold
+ * = eps, posterior_alpha = delta; medusa_generate defaults 0.0, 0.09, 0.3);
+ * [NOTES] 核心要点 (typical acceptance) and 实践案例 案例 1 (keep the
+ * longest acceptable prefix from the root); 学到什么 (a verify step also
+ * yields the base model's next token).
+ *
+ * logits float32 [B][T][V]: base logits at every tree node.
+ * A candidate c with parent n is accepted when
+ *   temperature == 0: tree_candidates[b][c] == argmax logits[b][n]
+ *   temperature  > 0: p_n(x) > min(eps, delta * exp(-H(p_n))), where
+ *                     p_n = softmax(logits[b][n] / temperature), x is c's
+ *                     token and H the natural-log entropy.
+ * A path's length is its count of accepted nodes from the root's child on,
+ * stopping at the first reject or -1.  best_path = the lowest-index path of
+ * maximal length, accept_len its length, next_token = argmax of the logits
+ * at the path's last accepted node (ties: lowest token id).
+ * retrieve [p_max][D] and num_paths come from medusa_build_tree (D = K+1).
+ * Workspace: medusa_posterior_workspace() bytes (no initialisation).
+ * ------------------------------------------------------------------- */
+size_t medusa_posterior_workspace(int B, int T, int V);
+
+int medusa_evaluate_posterior(int B, int T, int V, int p_max, int D,
+                              const float* logits, const int32_t* tree_candidates,
+                              const int32_t* retrieve, const int32_t* num_paths,
+                              float temperature, float eps, float delta,
+                              int32_t* best_path, int32_t* accept_len, int32_t* next_token,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * KV commit.  [API] tree_decoding (tree K/V appended to past_key_values);
+ * [NOTES] 实践案例 案例 1 (only the accepted prefix is kept).
+ *
+ * For every layer, sequence b (L = prefix_len[b], path = retrieve[best_path[b]]),
+ * head and both caches, slot L + j receives the row that was at slot
+ * L + path[j] before the call, for j = 0 .. accept_len[b] (every source is
+ * read before any destination is written).  new_prefix_len[b] =
+ * L + accept_len[b] + 1.  Other slots are untouched.
+ *
+ * Layouts: k_cache, v_cache [n_layers][B][H][max_slots][d] (dtype sets the
+ * element size), updated in place; retrieve [p_max][D].  new_prefix_len must
+ * not alias prefix_len.  Rows whose source or destination would fall outside
+ * the cache are skipped.
+ * ------------------------------------------------------------------- */
+int medusa_commit_kv(int dtype, int B, int n_layers, int H, int d, int max_slots,
+                     void* k_cache, void* v_cache, const int32_t* prefix_len,
+                     const int32_t* retrieve, int p_max, int D,
+                     const int32_t* best_path, const int32_t* accept_len,
+                     int32_t* new_prefix_len, void* stream);
+
+/* Text for a medusa_status value. */
+const char* medusa_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* medusa_last_error(void);
+/* ABI version of this header (major * 100 + minor). */
+int medusa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_H */

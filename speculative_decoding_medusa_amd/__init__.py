@@ -1,0 +1,24 @@
+"""Medusa speculate-and-verify step on AMD MI355X (gfx950).
+
+The verify step runs in libmedusa.so, a C-ABI library of hand-written HIP
+kernels (``include/medusa.h``).  This package is its Python binding: the
+functions below carry the C entry points' names and only marshal torch
+tensors (device memory, the current stream) into those calls.
+
+Build the library in-tree with ``python -m speculative_decoding_medusa_amd.build``;
+importing the package without it raises ImportError.
+"""
+
+from ._lib import (  # noqa: F401
+    MEDUSA_BF16, MEDUSA_F32, SPEC_STATUS, EXPORTED, LIB_PATH, MedusaError, lib, workspace,
+    medusa_heads_workspace, medusa_resblock, medusa_lm_head_topk, medusa_heads, medusa_build_tree,
+    medusa_tree_attention_workspace, medusa_tree_attention, medusa_posterior_workspace,
+    medusa_evaluate_posterior, medusa_commit_kv,
+)
+
+__all__ = [
+    "MEDUSA_BF16", "MEDUSA_F32", "SPEC_STATUS", "MedusaError", "workspace",
+    "medusa_heads_workspace", "medusa_resblock", "medusa_lm_head_topk", "medusa_heads",
+    "medusa_build_tree", "medusa_tree_attention_workspace", "medusa_tree_attention",
+    "medusa_posterior_workspace", "medusa_evaluate_posterior", "medusa_commit_kv",
+]

@@ -1,0 +1,303 @@
+"""ctypes binding of libmedusa: argument marshalling only.
+
+Every function here has the name of the C entry point it calls, checks the
+tensors it is handed (device, dtype, contiguity, shape), allocates missing
+outputs and workspaces with torch, passes raw pointers and torch's current
+HIP stream, and raises MedusaError on a negative status.  All computation
+happens in the library's HIP kernels; there is no other code path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmedusa.so")
+
+MEDUSA_F32 = 0
+MEDUSA_BF16 = 1
+
+SPEC_STATUS = {0: "ok", 1: "padding", 2: "empty", 3: "rank", 4: "duplicate", 5: "prefix",
+               6: "too_many_paths"}
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, code, fn, msg):
+        super().__init__("%s failed with status %d: %s" % (fn, code, msg))
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libmedusa.so is not built (expected at %s); run "
+            "`python -m speculative_decoding_medusa_amd.build`" % LIB_PATH)
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "medusa_heads_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "medusa_resblock": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "medusa_lm_head_topk": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "medusa_heads": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "medusa_build_tree": (_i, [_i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp]),
+    "medusa_tree_attention_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "medusa_tree_attention": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _sz, _vp]),
+    "medusa_posterior_workspace": (_sz, [_i, _i, _i]),
+    "medusa_evaluate_posterior": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _f, _vp, _vp, _vp,
+                                       _vp, _sz, _vp]),
+    "medusa_commit_kv": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp]),
+    "medusa_status_string": (ctypes.c_char_p, [_i]),
+    "medusa_last_error": (ctypes.c_char_p, []),
+    "medusa_abi_version": (_i, []),
+}
+
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(rc, fn):
+    if rc != 0:
+        raise MedusaError(rc, fn, "%s (%s)" % (lib.medusa_status_string(rc).decode(),
+                                               lib.medusa_last_error().decode()))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MEDUSA_BF16
+    if t.dtype == torch.float32:
+        return MEDUSA_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_WS = {}
+
+
+def workspace(kind, device, nbytes):
+    """A cached zero-initialised workspace of at least ``nbytes`` bytes.
+
+    The heads workspace relies on its counters being zero before the first
+    call (each call leaves them zero), which torch.zeros provides.
+    """
+    key = (kind, torch.device(device).index)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def medusa_heads_workspace(dtype, B, H, V, K, topk):
+    return int(lib.medusa_heads_workspace(dtype, B, H, V, K, topk))
+
+
+def medusa_resblock(hidden, w1, b1, r=None):
+    dt = _dtype_code(hidden)
+    B, H = hidden.shape
+    K = w1.shape[0]
+    dev = hidden.device
+    if r is None:
+        r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+    rc = lib.medusa_resblock(dt, B, H, K, _ptr(hidden, "hidden"), _ptr(w1, "w1", hidden.dtype, (K, H, H)),
+                             _ptr(b1, "b1", hidden.dtype, (K, H)), _ptr(r, "r", torch.float32, (B, K, H)),
+                             _stream(dev))
+    _check(rc, "medusa_resblock")
+    return r
+
+
+def medusa_lm_head_topk(r, w_lm, topk, keep_logits=False, out=None, ws=None):
+    dt = _dtype_code(w_lm)
+    B, K, H = r.shape
+    V = w_lm.shape[1]
+    dev = r.device
+    out = out or {}
+    ids = out.get("topk_ids")
+    vals = out.get("topk_logits")
+    logits = out.get("logits")
+    if ids is None:
+        ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    if keep_logits and logits is None:
+        logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    need = medusa_heads_workspace(dt, B, H, V, K, topk)
+    if ws is None:
+        ws = workspace("heads", dev, need)
+    rc = lib.medusa_lm_head_topk(dt, B, H, V, K, topk, _ptr(r, "r", torch.float32),
+                                 _ptr(w_lm, "w_lm", None, (K, V, H)),
+                                 _ptr(ids, "topk_ids", torch.int32, (B, K, topk)),
+                                 _ptr(vals, "topk_logits", torch.float32, (B, K, topk)),
+                                 _ptr(logits, "logits", torch.float32, (B, K, V)),
+                                 _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_lm_head_topk")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits)
+
+
+def medusa_heads(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, ws=None):
+    dt = _dtype_code(hidden)
+    B, H = hidden.shape
+    K, V = w_lm.shape[0], w_lm.shape[1]
+    dev = hidden.device
+    ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    logits = torch.empty((B, K, V), dtype=torch.float32, device=dev) if keep_logits else None
+    r = torch.empty((B, K, H), dtype=torch.float32, device=dev) if keep_r else None
+    need = medusa_heads_workspace(dt, B, H, V, K, topk)
+    if ws is None:
+        ws = workspace("heads", dev, need)
+    rc = lib.medusa_heads(dt, B, H, V, K, topk, _ptr(hidden, "hidden"),
+                          _ptr(w1, "w1", hidden.dtype, (K, H, H)), _ptr(b1, "b1", hidden.dtype, (K, H)),
+                          _ptr(w_lm, "w_lm", hidden.dtype, (K, V, H)), _ptr(ids, "topk_ids"),
+                          _ptr(vals, "topk_logits"), _ptr(logits, "logits"), _ptr(r, "r"),
+                          _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_heads")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r)
+
+
+def medusa_build_tree(choices, topk_ids, root_token, prefix_len, p_max=None, out=None):
+    """choices int32 [N][K] (device), topk_ids int32 [B][K][topk], root_token / prefix_len int32 [B]."""
+    B, K, topk = topk_ids.shape
+    N = choices.shape[0]
+    T = N + 1
+    dev = topk_ids.device
+    if p_max is None:
+        p_max = T
+    o = out or {}
+
+    def get(name, shape, dtype=torch.int32):
+        t = o.get(name)
+        return t if t is not None else torch.empty(shape, dtype=dtype, device=dev)
+
+    res = dict(tree_candidates=get("tree_candidates", (B, T)), tree_indices=get("tree_indices", (T,)),
+               parent=get("parent", (T,)), depth=get("depth", (T,)),
+               position_ids=get("position_ids", (B, T)),
+               tree_mask=get("tree_mask", (T, T), torch.uint8),
+               retrieve=get("retrieve", (p_max, K + 1)), num_paths=get("num_paths", (1,)),
+               status=get("status", (2,)))
+    if N > 0:
+        cptr = _ptr(choices, "choices", torch.int32, (N, K))
+    else:
+        cptr = None
+    rc = lib.medusa_build_tree(B, K, topk, N, cptr, _ptr(topk_ids, "topk_ids", torch.int32),
+                               _ptr(root_token, "root_token", torch.int32, (B,)),
+                               _ptr(prefix_len, "prefix_len", torch.int32, (B,)),
+                               _ptr(res["tree_candidates"], "tree_candidates", torch.int32, (B, T)),
+                               _ptr(res["tree_indices"], "tree_indices", torch.int32, (T,)),
+                               _ptr(res["parent"], "parent", torch.int32, (T,)),
+                               _ptr(res["depth"], "depth", torch.int32, (T,)),
+                               _ptr(res["position_ids"], "position_ids", torch.int32, (B, T)),
+                               _ptr(res["tree_mask"], "tree_mask", torch.uint8, (T, T)),
+                               _ptr(res["retrieve"], "retrieve", torch.int32, (p_max, K + 1)),
+                               _ptr(res["num_paths"], "num_paths", torch.int32, (1,)), p_max,
+                               _ptr(res["status"], "status", torch.int32, (2,)), _stream(dev))
+    _check(rc, "medusa_build_tree")
+    return res
+
+
+def medusa_tree_attention_workspace(dtype, B, T, Hq, d, max_slots):
+    return int(lib.medusa_tree_attention_workspace(dtype, B, T, Hq, d, max_slots))
+
+
+def medusa_tree_attention(q, k_cache, v_cache, prefix_len, tree_mask, scale, out=None, ws=None):
+    """q [B][T][Hq][d]; k_cache, v_cache [B][Hq][max_slots][d] (one layer)."""
+    dt = _dtype_code(q)
+    B, T, Hq, d = q.shape
+    max_slots = k_cache.shape[2]
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    need = medusa_tree_attention_workspace(dt, B, T, Hq, d, max_slots)
+    if ws is None:
+        ws = workspace("attention", dev, need)
+    rc = lib.medusa_tree_attention(dt, B, T, Hq, d, max_slots, _ptr(q, "q"),
+                                   _ptr(k_cache, "k_cache", q.dtype, (B, Hq, max_slots, d)),
+                                   _ptr(v_cache, "v_cache", q.dtype, (B, Hq, max_slots, d)),
+                                   _ptr(prefix_len, "prefix_len", torch.int32, (B,)),
+                                   _ptr(tree_mask, "tree_mask", torch.uint8, (T, T)), float(scale),
+                                   _ptr(out, "out", q.dtype, (B, T, Hq, d)), _ptr(ws, "ws"),
+                                   ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_tree_attention")
+    return out
+
+
+def medusa_posterior_workspace(B, T, V):
+    return int(lib.medusa_posterior_workspace(B, T, V))
+
+
+def medusa_evaluate_posterior(logits, tree_candidates, retrieve, num_paths, temperature, eps, delta,
+                              out=None, ws=None):
+    B, T, V = logits.shape
+    p_max, D = retrieve.shape
+    dev = logits.device
+    o = out or {}
+    best = o.get("best_path")
+    acc = o.get("accept_len")
+    nxt = o.get("next_token")
+    if best is None:
+        best = torch.empty(B, dtype=torch.int32, device=dev)
+    if acc is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+    if nxt is None:
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    need = medusa_posterior_workspace(B, T, V)
+    if ws is None:
+        ws = workspace("posterior", dev, need)
+    rc = lib.medusa_evaluate_posterior(B, T, V, p_max, D, _ptr(logits, "logits", torch.float32),
+                                       _ptr(tree_candidates, "tree_candidates", torch.int32, (B, T)),
+                                       _ptr(retrieve, "retrieve", torch.int32),
+                                       _ptr(num_paths, "num_paths", torch.int32),
+                                       float(temperature), float(eps), float(delta),
+                                       _ptr(best, "best_path", torch.int32, (B,)),
+                                       _ptr(acc, "accept_len", torch.int32, (B,)),
+                                       _ptr(nxt, "next_token", torch.int32, (B,)), _ptr(ws, "ws"),
+                                       ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_evaluate_posterior")
+    return dict(best_path=best, accept_len=acc, next_token=nxt)
+
+
+def medusa_commit_kv(k_cache, v_cache, prefix_len, retrieve, best_path, accept_len, new_prefix_len=None):
+    """k_cache, v_cache [n_layers][B][H][max_slots][d], updated in place."""
+    dt = _dtype_code(k_cache)
+    nl, B, H, S, d = k_cache.shape
+    p_max, D = retrieve.shape
+    dev = k_cache.device
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = lib.medusa_commit_kv(dt, B, nl, H, d, S, _ptr(k_cache, "k_cache"),
+                              _ptr(v_cache, "v_cache", k_cache.dtype, tuple(k_cache.shape)),
+                              _ptr(prefix_len, "prefix_len", torch.int32, (B,)),
+                              _ptr(retrieve, "retrieve", torch.int32), p_max, D,
+                              _ptr(best_path, "best_path", torch.int32, (B,)),
+                              _ptr(accept_len, "accept_len", torch.int32, (B,)),
+                              _ptr(new_prefix_len, "new_prefix_len", torch.int32, (B,)), _stream(dev))
+    _check(rc, "medusa_commit_kv")
+    return new_prefix_len

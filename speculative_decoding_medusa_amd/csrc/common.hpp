@@ -1,0 +1,88 @@
+// Internal helpers shared by the libmedusa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "medusa.h"
+
+namespace medusa {
+
+constexpr int kWave = 64;
+constexpr int kMaxBatch = 16;
+constexpr int kMaxHeads = 8;
+constexpr int kMaxTopk = 64;
+constexpr int kMaxNodes = 256;
+
+// MFMA operand/accumulator vector types.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round a float32 to bf16 (nearest, ties to even).  Finite inputs only
+// matter here; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Total order used by every top-k and argmax here: larger value first,
+// equal values by smaller index.  NaN never wins.
+__device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+}  // namespace medusa
+
+// ---------------------------------------------------------------- host side
+namespace medusa_host {
+
+void set_error(const char* fmt, ...);
+int hip_check(const char* what);  // MEDUSA_OK or MEDUSA_ERR_HIP after a launch
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int dtype_size(int dtype) {
+  return dtype == MEDUSA_F32 ? 4 : (dtype == MEDUSA_BF16 ? 2 : 0);
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace medusa_host
+
+// Validation helpers: return the status from the enclosing entry point.
+#define MEDUSA_REQUIRE(cond, code, ...)            \
+  do {                                             \
+    if (!(cond)) {                                 \
+      medusa_host::set_error(__VA_ARGS__);         \
+      return (code);                               \
+    }                                              \
+  } while (0)
+
+#define MEDUSA_REQUIRE_PTR(p)                                                           \
+  do {                                                                                  \
+    MEDUSA_REQUIRE((p) != nullptr, MEDUSA_ERR_NULL, "%s: %s is NULL", __func__, #p);    \
+    MEDUSA_REQUIRE(medusa_host::aligned16(p), MEDUSA_ERR_ALIGN,                         \
+                   "%s: %s is not 16-byte aligned", __func__, #p);                      \
+  } while (0)

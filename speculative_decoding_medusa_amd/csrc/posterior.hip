@@ -1,0 +1,254 @@
+// Acceptance of the candidate tree on gfx950.
+//
+// Stage 1 (rows): grid (chunks, B*T).  Each workgroup reads one chunk of one
+// node's logits into registers once (16-byte loads), reduces max / argmax
+// (ties: lowest token id) and, for temperature > 0, the softmax statistics
+// S = sum exp(z - m) and A = sum (z - m) exp(z - m) of z = logits / temperature
+// relative to its own chunk maximum.  Wave shuffles, then LDS across waves.
+//
+// Stage 2 (decide): one workgroup per sequence merges the chunk statistics
+// per node (log-sum-exp rescaling), derives H = log S - A / S and the
+// threshold min(eps, delta * exp(-H)), walks every retrieve path with one
+// thread, and picks the lowest-index longest path with a block reduction.
+#include "common.hpp"
+
+namespace medusa {
+
+constexpr int kPostThreads = 256;
+constexpr int kPostVec = 4;         // float4 loads per thread per chunk
+constexpr int kPostChunk = kPostThreads * kPostVec * 4;
+
+struct RowStat {
+  float mx;     // max of the raw logits
+  int arg;      // first index of the max
+  float m;      // max of z (temperature > 0)
+  float S;      // sum exp(z - m)
+  float A;      // sum (z - m) exp(z - m)
+};
+
+__global__ __launch_bounds__(kPostThreads) void posterior_rows_kernel(
+    int T, int V, int nchunk, const float* __restrict__ logits, float temperature, RowStat* __restrict__ stats) {
+  const int chunk = blockIdx.x, row = blockIdx.y;   // row = b * T + node
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* x = logits + static_cast<size_t>(row) * V;
+  const int lo = chunk * kPostChunk;
+  const float NEG = -__builtin_huge_valf();
+  float v[kPostVec * 4];
+  const bool vec_ok = (V & 3) == 0;
+#pragma unroll
+  for (int r = 0; r < kPostVec; ++r) {
+    const int e = lo + (r * kPostThreads + tid) * 4;
+    if (vec_ok && e + 3 < V) {
+      const float4 f = *reinterpret_cast<const float4*>(x + e);
+      v[4 * r] = f.x; v[4 * r + 1] = f.y; v[4 * r + 2] = f.z; v[4 * r + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * r + c] = e + c < V ? x[e + c] : NEG;
+    }
+  }
+  // max / argmax over this thread's elements (ascending index order)
+  float mx = NEG;
+  int arg = 0x7fffffff;
+#pragma unroll
+  for (int r = 0; r < kPostVec; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lo + (r * kPostThreads + tid) * 4 + c;
+      if (e < V && beats(v[4 * r + c], e, mx, arg)) { mx = v[4 * r + c]; arg = e; }
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(mx, o);
+    const int oa = __shfl_xor(arg, o);
+    if (beats(om, oa, mx, arg)) { mx = om; arg = oa; }
+  }
+  __shared__ float smx[kPostThreads / kWave];
+  __shared__ int sarg[kPostThreads / kWave];
+  __shared__ float sS[kPostThreads / kWave], sA[kPostThreads / kWave];
+  if (lane == 0) { smx[wave] = mx; sarg[wave] = arg; }
+  __syncthreads();
+  mx = smx[0];
+  arg = sarg[0];
+  for (int w = 1; w < kPostThreads / kWave; ++w)
+    if (beats(smx[w], sarg[w], mx, arg)) { mx = smx[w]; arg = sarg[w]; }
+  RowStat out;
+  out.mx = mx;
+  out.arg = arg;
+  out.m = NEG;
+  out.S = 0.f;
+  out.A = 0.f;
+  if (temperature > 0.f) {
+    // division by a positive temperature is monotonic, so max z = max x / t
+    const float m = mx / temperature;
+    float S = 0.f, A = 0.f;
+#pragma unroll
+    for (int r = 0; r < kPostVec; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = lo + (r * kPostThreads + tid) * 4 + c;
+        if (e < V) {
+          const float dz = v[4 * r + c] / temperature - m;
+          const float p = expf(dz);
+          S += p;
+          A += dz * p;
+        }
+      }
+    S = wave_sum(S);
+    A = wave_sum(A);
+    if (lane == 0) { sS[wave] = S; sA[wave] = A; }
+    __syncthreads();
+    S = 0.f;
+    A = 0.f;
+    for (int w = 0; w < kPostThreads / kWave; ++w) { S += sS[w]; A += sA[w]; }
+    out.m = m;
+    out.S = S;
+    out.A = A;
+  }
+  if (tid == 0) stats[static_cast<size_t>(row) * nchunk + chunk] = out;
+}
+
+__global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
+    int T, int V, int nchunk, int p_max, int D, const float* __restrict__ logits,
+    const int32_t* __restrict__ tree_candidates, const int32_t* __restrict__ retrieve,
+    const int32_t* __restrict__ num_paths, float temperature, float eps, float delta,
+    const RowStat* __restrict__ stats, int32_t* __restrict__ best_path, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ next_token) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_arg[kMaxNodes];
+  __shared__ float s_m[kMaxNodes], s_S[kMaxNodes], s_thr[kMaxNodes];
+  __shared__ int s_len[kPostThreads / kWave], s_path[kPostThreads / kWave];
+  const bool typical = temperature > 0.f;
+
+  for (int node = tid; node < T; node += kPostThreads) {
+    const RowStat* st = stats + (static_cast<size_t>(b) * T + node) * nchunk;
+    float mx = -__builtin_huge_valf();
+    int arg = 0x7fffffff;
+    float m = -__builtin_huge_valf();
+    for (int c = 0; c < nchunk; ++c) {
+      if (beats(st[c].mx, st[c].arg, mx, arg)) { mx = st[c].mx; arg = st[c].arg; }
+      m = fmaxf(m, st[c].m);
+    }
+    s_arg[node] = arg;
+    if (typical) {
+      float S = 0.f, A = 0.f;
+      for (int c = 0; c < nchunk; ++c) {
+        const float w = expf(st[c].m - m);
+        S += st[c].S * w;
+        A += w * (st[c].A + (st[c].m - m) * st[c].S);
+      }
+      const float H = logf(S) - A / S;
+      s_m[node] = m;
+      s_S[node] = S;
+      s_thr[node] = fminf(eps, delta * expf(-H));
+    }
+  }
+  __syncthreads();
+
+  int P = *num_paths;
+  if (P > p_max) P = p_max;
+  if (P < 0) P = 0;
+  int best_len = -1, best_p = 0x7fffffff;
+  for (int p = tid; p < P; p += kPostThreads) {
+    const int32_t* path = retrieve + static_cast<size_t>(p) * D;
+    int ell = 0;
+    int prev = path[0];
+    if (prev >= 0 && prev < T) {
+      for (int j = 1; j < D; ++j) {
+        const int c = path[j];
+        if (c < 0 || c >= T) break;
+        const int tok = tree_candidates[static_cast<size_t>(b) * T + c];
+        bool acc;
+        if (tok < 0 || tok >= V) {
+          acc = false;
+        } else if (!typical) {
+          acc = tok == s_arg[prev];
+        } else {
+          const float z = logits[(static_cast<size_t>(b) * T + prev) * V + tok] / temperature;
+          const float pr = expf(z - s_m[prev]) / s_S[prev];
+          acc = pr > s_thr[prev];
+        }
+        if (!acc) break;
+        ++ell;
+        prev = c;
+      }
+    }
+    if (ell > best_len || (ell == best_len && p < best_p)) { best_len = ell; best_p = p; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int ol = __shfl_xor(best_len, o);
+    const int op = __shfl_xor(best_p, o);
+    if (ol > best_len || (ol == best_len && op < best_p)) { best_len = ol; best_p = op; }
+  }
+  if (lane == 0) { s_len[wave] = best_len; s_path[wave] = best_p; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kPostThreads / kWave; ++w)
+      if (s_len[w] > best_len || (s_len[w] == best_len && s_path[w] < best_p)) {
+        best_len = s_len[w];
+        best_p = s_path[w];
+      }
+    if (best_len < 0) { best_len = 0; best_p = 0; }   // no paths: the root alone
+    int last = 0;
+    if (P > 0) {
+      last = retrieve[static_cast<size_t>(best_p) * D + best_len];
+      if (last < 0 || last >= T) last = 0;
+    }
+    best_path[b] = best_p;
+    accept_len[b] = best_len;
+    next_token[b] = s_arg[last];
+  }
+}
+
+}  // namespace medusa
+
+namespace {
+using namespace medusa;
+int post_chunks(int V) { return (V + kPostChunk - 1) / kPostChunk; }
+size_t post_ws(int B, int T, int V) {
+  return medusa_host::round_up(static_cast<size_t>(B) * T * post_chunks(V) * sizeof(RowStat), 256);
+}
+}  // namespace
+
+extern "C" size_t medusa_posterior_workspace(int B, int T, int V) {
+  if (B < 1 || B > kMaxBatch || T < 1 || T > kMaxNodes || V < 1) return 0;
+  return post_ws(B, T, V);
+}
+
+extern "C" int medusa_evaluate_posterior(int B, int T, int V, int p_max, int D, const float* logits,
+                                         const int32_t* tree_candidates, const int32_t* retrieve,
+                                         const int32_t* num_paths, float temperature, float eps, float delta,
+                                         int32_t* best_path, int32_t* accept_len, int32_t* next_token,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  MEDUSA_REQUIRE(B >= 1 && B <= kMaxBatch, MEDUSA_ERR_SHAPE, "%s: B=%d", __func__, B);
+  MEDUSA_REQUIRE(T >= 1 && T <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: T=%d", __func__, T);
+  MEDUSA_REQUIRE(V >= 1 && V <= (1 << 24), MEDUSA_ERR_SHAPE, "%s: V=%d", __func__, V);
+  MEDUSA_REQUIRE(p_max >= 1 && p_max <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: p_max=%d", __func__, p_max);
+  MEDUSA_REQUIRE(D >= 1 && D <= kMaxHeads + 1, MEDUSA_ERR_SHAPE, "%s: D=%d", __func__, D);
+  MEDUSA_REQUIRE(temperature == temperature && temperature >= 0.f, MEDUSA_ERR_VALUE,
+                 "%s: temperature must be >= 0", __func__);
+  MEDUSA_REQUIRE(temperature == 0.f || (eps == eps && eps > 0.f && delta == delta && delta > 0.f),
+                 MEDUSA_ERR_VALUE, "%s: eps and delta must be positive", __func__);
+  MEDUSA_REQUIRE_PTR(logits);
+  MEDUSA_REQUIRE_PTR(tree_candidates);
+  MEDUSA_REQUIRE_PTR(retrieve);
+  MEDUSA_REQUIRE_PTR(num_paths);
+  MEDUSA_REQUIRE_PTR(best_path);
+  MEDUSA_REQUIRE_PTR(accept_len);
+  MEDUSA_REQUIRE_PTR(next_token);
+  MEDUSA_REQUIRE_PTR(ws);
+  MEDUSA_REQUIRE(ws_bytes >= post_ws(B, T, V), MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
+                 ws_bytes, post_ws(B, T, V));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nchunk = post_chunks(V);
+  RowStat* stats = static_cast<RowStat*>(ws);
+  hipLaunchKernelGGL(posterior_rows_kernel, dim3(nchunk, B * T), dim3(kPostThreads), 0, st, T, V, nchunk, logits,
+                     temperature, stats);
+  int rc = medusa_host::hip_check("medusa_evaluate_posterior rows launch");
+  if (rc != MEDUSA_OK) return rc;
+  hipLaunchKernelGGL(posterior_decide_kernel, dim3(B), dim3(kPostThreads), 0, st, T, V, nchunk, p_max, D, logits,
+                     tree_candidates, retrieve, num_paths, temperature, eps, delta, stats, best_path, accept_len,
+                     next_token);
+  return medusa_host::hip_check("medusa_evaluate_posterior decide launch");
+}

@@ -1,0 +1,145 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call (so these run
+without a GPU: every call here fails validation and enqueues nothing)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_medusa_amd as md
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "medusa.h")
+
+L = md.lib
+A = 0x10000          # a 16-byte aligned stand-in address (never dereferenced)
+MIS = 0x10004        # misaligned
+OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(medusa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_exports_agree():
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(md.EXPORTED) == names
+
+
+def test_version_and_strings():
+    assert L.medusa_abi_version() == 100
+    for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
+        assert L.medusa_status_string(code).decode() not in ("", "unknown status")
+    assert L.medusa_status_string(-99).decode() == "unknown status"
+
+
+def heads(dt=1, B=1, H=64, V=100, K=2, k=4, hidden=A, w1=A, b1=A, wlm=A, ids=A, vals=A, logits=None,
+          r=None, ws=A, wsb=1 << 30):
+    return L.medusa_heads(dt, B, H, V, K, k, hidden, w1, b1, wlm, ids, vals, logits, r, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE), (dict(B=0), SHAPE), (dict(B=17), SHAPE), (dict(K=0), SHAPE), (dict(K=9), SHAPE),
+    (dict(H=12), SHAPE), (dict(dt=0, H=6), SHAPE), (dict(k=0), SHAPE), (dict(k=65), SHAPE),
+    (dict(V=3, k=4), SHAPE), (dict(hidden=None), NULL), (dict(wlm=None), NULL), (dict(ws=None), NULL),
+    (dict(w1=MIS), ALIGN), (dict(logits=MIS), ALIGN), (dict(r=MIS), ALIGN), (dict(wsb=16), WS),
+])
+def test_heads_validation(kw, code):
+    assert heads(**kw) == code
+    assert L.medusa_last_error().decode() != ""
+
+
+def test_heads_workspace_sizes():
+    assert md.medusa_heads_workspace(1, 1, 4096, 32000, 5, 10) > 0
+    assert md.medusa_heads_workspace(1, 0, 4096, 32000, 5, 10) == 0
+    assert md.medusa_heads_workspace(9, 1, 4096, 32000, 5, 10) == 0
+    small = md.medusa_heads_workspace(1, 1, 4096, 32000, 5, 10)
+    big = md.medusa_heads_workspace(1, 8, 6656, 32000, 5, 10)
+    assert big > small
+
+
+def test_resblock_and_lm_validation():
+    assert L.medusa_resblock(1, 1, 12, 2, A, A, A, A, None) == SHAPE
+    assert L.medusa_resblock(1, 1, 64, 2, A, None, A, A, None) == NULL
+    assert L.medusa_lm_head_topk(1, 1, 64, 100, 2, 4, A, A, A, A, None, A, 8, None) == WS
+    assert L.medusa_lm_head_topk(1, 1, 64, 100, 2, 4, MIS, A, A, A, None, A, 1 << 30, None) == ALIGN
+
+
+def tree(B=1, K=2, k=2, N=6, ch=A, p_max=4, status=A, **kw):
+    ptrs = [kw.get(n, A) for n in ("ids", "root", "plen", "cand", "tidx", "par", "dep", "pos", "mask",
+                                   "ret", "np")]
+    return L.medusa_build_tree(B, K, k, N, ch, *ptrs, p_max, status, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(K=9), SHAPE), (dict(k=65), SHAPE), (dict(N=256), SHAPE), (dict(N=-1), SHAPE),
+    (dict(p_max=0), SHAPE), (dict(p_max=257), SHAPE), (dict(ch=None), NULL), (dict(status=None), NULL),
+    (dict(mask=MIS), ALIGN), (dict(ret=None), NULL),
+])
+def test_tree_validation(kw, code):
+    assert tree(**kw) == code
+
+
+def attn(dt=1, B=1, T=15, Hq=4, d=64, S=200, q=A, kc=A, vc=A, plen=A, mask=A, scale=0.125, out=A, ws=A,
+         wsb=1 << 30):
+    return L.medusa_tree_attention(dt, B, T, Hq, d, S, q, kc, vc, plen, mask, scale, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), DTYPE), (dict(d=96), SHAPE), (dict(T=0), SHAPE), (dict(T=257), SHAPE), (dict(S=10), SHAPE),
+    (dict(B=17), SHAPE), (dict(scale=0.0), VALUE), (dict(scale=-1.0), VALUE), (dict(scale=float("nan")), VALUE),
+    (dict(q=None), NULL), (dict(out=MIS), ALIGN), (dict(wsb=8), WS),
+])
+def test_attention_validation(kw, code):
+    assert attn(**kw) == code
+
+
+def test_attention_workspace_sizes():
+    assert md.medusa_tree_attention_workspace(1, 1, 64, 32, 128, 2112) > 0
+    assert md.medusa_tree_attention_workspace(1, 1, 64, 32, 96, 2112) == 0
+
+
+def post(B=1, T=15, V=1000, p_max=8, D=4, temp=0.7, eps=0.09, delta=0.3, logits=A, ws=A, wsb=1 << 30, **kw):
+    return L.medusa_evaluate_posterior(B, T, V, p_max, D, logits, kw.get("cand", A), kw.get("ret", A),
+                                       kw.get("np", A), temp, eps, delta, kw.get("best", A), kw.get("acc", A),
+                                       kw.get("nxt", A), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=257), SHAPE), (dict(V=0), SHAPE), (dict(D=10), SHAPE), (dict(p_max=0), SHAPE),
+    (dict(temp=-0.1), VALUE), (dict(temp=float("nan")), VALUE), (dict(eps=0.0), VALUE),
+    (dict(delta=-1.0), VALUE), (dict(logits=None), NULL), (dict(best=MIS), ALIGN), (dict(wsb=4), WS),
+])
+def test_posterior_validation(kw, code):
+    assert post(**kw) == code
+
+
+def test_posterior_greedy_ignores_eps_delta():
+    # with temperature 0, eps/delta are unused: validation passes them; the
+    # first failing check is then the deliberately missing logits pointer
+    assert post(temp=0.0, eps=0.0, delta=0.0, logits=None) == NULL
+
+
+def commit(dt=1, B=1, nl=2, H=4, d=128, S=100, kc=A, vc=A + 0x100000, plen=A, ret=A, p_max=4, D=4, best=A,
+           acc=A, newlen=A + 0x200):
+    return L.medusa_commit_kv(dt, B, nl, H, d, S, kc, vc, plen, ret, p_max, D, best, acc, newlen, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), DTYPE), (dict(d=96), SHAPE), (dict(D=10), SHAPE), (dict(nl=0), SHAPE),
+    (dict(newlen=A), ALIAS), (dict(vc=A), ALIAS), (dict(kc=None), NULL), (dict(best=MIS), ALIGN),
+])
+def test_commit_validation(kw, code):
+    assert commit(**kw) == code
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        md._lib._ptr(torch.zeros(4), "x")

@@ -1,0 +1,120 @@
+"""GPU parity of medusa_evaluate_posterior against the oracle: best path,
+accepted length and next token bit for bit, greedy and typical, on planted
+Vicuna-shaped logits, the tiny workload, closed-form distributions and edge
+shapes (a vocab that is not a multiple of 4, the root alone, 256 nodes)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_medusa_amd as md
+import synth
+from cases import posterior_case, to_dev, to_host, tree_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(logits, cand, retrieve, num_paths, temperature, eps, delta):
+    out = md.medusa_evaluate_posterior(to_dev(logits), to_dev(cand), to_dev(retrieve),
+                                       to_dev(np.array([num_paths], dtype=np.int32)), temperature, eps, delta)
+    torch.cuda.synchronize()
+    return {k: to_host(v) for k, v in out.items()}
+
+
+def _compare(got, ref):
+    assert got["best_path"].tolist() == ref["best_path"].tolist()
+    assert got["accept_len"].tolist() == ref["accept_len"].tolist()
+    assert got["next_token"].tolist() == ref["next_token"].tolist()
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+@pytest.mark.parametrize("seed", range(4))
+def test_posterior_vicuna7b_planted(gpu_device, temperature, seed):
+    w = synth.workload("vicuna-7b")
+    tc = tree_case(w, seed=seed)
+    pc = posterior_case(w, tc, temperature, seed=seed)
+    t = tc["ref"]
+    got = _gpu(pc["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], temperature, w["eps"], w["delta"])
+    print("plan", pc["plan"], "accept", pc["ref"]["accept_len"], flush=True)
+    _compare(got, pc["ref"])
+    # the planted path is accepted exactly up to its planted length
+    p, A = pc["plan"][0]
+    assert int(pc["ref"]["accept_len"][0]) >= A
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+def test_posterior_tiny(gpu_device, temperature):
+    w = synth.workload("tiny-f32")
+    tc = tree_case(w)
+    pc = posterior_case(w, tc, temperature)
+    t = tc["ref"]
+    got = _gpu(pc["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], temperature, w["eps"], w["delta"])
+    _compare(got, pc["ref"])
+
+
+@pytest.mark.slow
+def test_posterior_vicuna33b_batch8(gpu_device):
+    w = synth.workload("vicuna-33b-b8")
+    tc = tree_case(w, seed=1)
+    pc = posterior_case(w, tc, 0.7, seed=1)
+    t = tc["ref"]
+    got = _gpu(pc["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], 0.7, w["eps"], w["delta"])
+    _compare(got, pc["ref"])
+
+
+def _star_case(V, rows, children, temperature, eps=0.09, delta=0.3):
+    T = 1 + len(children)
+    cand = np.array([[0] + list(children)], dtype=np.int32)
+    retrieve = np.array([[0, 1 + c] for c in range(len(children))], dtype=np.int32)
+    logits = np.zeros((1, T, V), dtype=np.float32)
+    logits[0, 0] = rows
+    ref = oracle.evaluate_posterior(logits, cand, retrieve, len(children), temperature, eps, delta)
+    got = _gpu(logits, cand, retrieve, len(children), temperature, eps, delta)
+    _compare(got, ref)
+    return got
+
+
+def test_posterior_closed_forms(gpu_device):
+    V = 40
+    # 16 equal tokens: p = 1/16 accepted through the entropy branch; a 17th rejected
+    row = np.full(V, -300.0, dtype=np.float32)
+    row[:16] = 1.5
+    got = _star_case(V, row, [17, 9], 1.0)
+    assert got["accept_len"].tolist() == [1] and got["best_path"].tolist() == [1]
+    # two-point (0.05, 0.95): 0.05 rejected, 0.95 accepted
+    row = np.full(V, -500.0, dtype=np.float32)
+    row[0], row[1] = np.log(0.05), np.log(0.95)
+    got = _star_case(V, row, [0, 1], 1.0)
+    assert got["best_path"].tolist() == [1]
+    # dominant token, greedy and typical
+    row = np.zeros(V, dtype=np.float32)
+    row[4] = 60.0
+    for t in (0.0, 1.0):
+        got = _star_case(V, row, [5, 4, 6], t)
+        assert got["best_path"].tolist() == [1] and got["accept_len"].tolist() == [1]
+
+
+def test_posterior_odd_vocab_and_root_only(gpu_device):
+    rng = np.random.default_rng(0)
+    V = 1001
+    logits = rng.standard_normal((2, 1, V)).astype(np.float32) * 3
+    cand = np.array([[5], [6]], dtype=np.int32)
+    retrieve = np.array([[0, -1, -1]], dtype=np.int32)
+    for t in (0.0, 0.7):
+        ref = oracle.evaluate_posterior(logits, cand, retrieve, 1, t, 0.09, 0.3)
+        got = _gpu(logits, cand, retrieve, 1, t, 0.09, 0.3)
+        _compare(got, ref)
+        assert got["accept_len"].tolist() == [0, 0]
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+def test_posterior_256_nodes(gpu_device, temperature):
+    w = synth.workload("vicuna-7b", B=2, K=8, topk=64, V=3001, logit_std=2.0,
+                       depth_counts=(40, 60, 60, 40, 25, 15, 10, 5))
+    tc = tree_case(w, seed=5)
+    pc = posterior_case(w, tc, temperature, seed=5)
+    t = tc["ref"]
+    got = _gpu(pc["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], temperature, w["eps"],
+               w["delta"])
+    _compare(got, pc["ref"])
