@@ -1,0 +1,324 @@
+"""Benchmark: Medusa verify steps per second at the Vicuna-7B shape (batch 1).
+
+One step = every stage of the verify step on one HIP stream:
+  ResBlock (5 heads, H 4096)  ->  lm_head + top-10 (5 x 32000 x 4096 bf16)
+  -> candidate tree (64 nodes)  ->  tree attention (32 heads x 128, prefix
+  2048, one layer; the layer rotates over the 32-layer cache)
+  -> typical acceptance (T 0.7, eps 0.09, delta 0.3) over [64][32000] logits
+  -> KV commit across 32 layers x 32 heads.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  `roofline` covers the dominant kernel (lm_head +
+top-k): algorithmic bytes per launch over its mean duration, measured with
+HIP events on the stream it runs on.  `cpu_baseline` times the CPU oracle on
+one full step on this host.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Medusa verify steps/sec at Vicuna-7B shape (batch 1); achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Step:
+    """All buffers and pre-marshalled arguments of one verify step."""
+
+    def __init__(self, w, seed):
+        import numpy as np
+        import torch
+
+        import speculative_decoding_medusa_amd as md
+        import synth
+
+        self.md, self.torch = md, torch
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        self.w = w
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def d(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        B, H, V, K, k = w["B"], w["H"], w["V"], w["K"], w["topk"]
+        x = synth.heads_inputs(w, seed=seed)
+        self.hidden, self.w1, self.b1, self.w_lm = (d(x[n]) for n in ("hidden", "w1", "b1", "w_lm"))
+        del x
+        self.r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+        self.topk_ids = torch.empty((B, K, k), dtype=torch.int32, device=dev)
+        self.topk_vals = torch.empty((B, K, k), dtype=torch.float32, device=dev)
+        self.heads_ws = torch.zeros(md.medusa_heads_workspace(md.MEDUSA_BF16, B, H, V, K, k),
+                                    dtype=torch.uint8, device=dev)
+
+        choices = synth.random_tree_choices(w["depth_counts"], k, seed=seed, workload_id=w["wid"])
+        self.choices = d(synth.choices_array(choices, K))
+        self.N = len(choices)
+        self.T = T = self.N + 1
+        self.p_max = T
+        self.root = d(synth.root_token_input(w, seed=seed))
+        self.plen = d(synth.prefix_lengths(w, seed=seed))
+        self.tree = {n: torch.empty(s, dtype=dt, device=dev) for n, s, dt in [
+            ("tree_candidates", (B, T), torch.int32), ("tree_indices", (T,), torch.int32),
+            ("parent", (T,), torch.int32), ("depth", (T,), torch.int32),
+            ("position_ids", (B, T), torch.int32), ("tree_mask", (T, T), torch.uint8),
+            ("retrieve", (T, K + 1), torch.int32), ("num_paths", (1,), torch.int32),
+            ("status", (2,), torch.int32)]}
+
+        # one heads + tree pass to get this step's candidates (planted logits need them)
+        self.run_heads()
+        self.run_tree()
+        torch.cuda.synchronize()
+        assert self.tree["status"].cpu().tolist() == [0, -1]
+        cand = self.tree["tree_candidates"].cpu().numpy()
+        ret = self.tree["retrieve"].cpu().numpy()
+        npaths = int(self.tree["num_paths"].cpu()[0])
+        depth = self.tree["depth"].cpu().numpy()
+        self.num_paths_host = npaths
+
+        Hq, dh, S, nl = w["Hq"], w["d"], w["S_max"], w["n_layers"]
+        att = synth.attention_inputs(w, depth, synth.prefix_lengths(w, seed=seed), seed=seed)
+        self.q = d(att["q"])
+        del att
+        kc, vc = synth.kv_cache(dict(w, Hkv=Hq), seed=seed)
+        self.k_cache, self.v_cache = d(kc), d(vc)
+        del kc, vc
+        self.layer_elems = B * Hq * S * dh
+        self.att_out = torch.empty((B, T, Hq, dh), dtype=torch.bfloat16, device=dev)
+        self.att_ws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, B, T, Hq, dh, S),
+                                  dtype=torch.uint8, device=dev)
+
+        logits, plan = synth.posterior_logits(w, cand, ret, npaths, depth, seed=seed)
+        self.plan = plan
+        self.logits = d(logits)
+        del logits
+        self.post = {n: torch.empty(B, dtype=torch.int32, device=dev)
+                     for n in ("best_path", "accept_len", "next_token")}
+        self.post_ws = torch.zeros(md.medusa_posterior_workspace(B, T, V), dtype=torch.uint8, device=dev)
+        self.new_plen = torch.empty(B, dtype=torch.int32, device=dev)
+        self.scale = 1.0 / math.sqrt(dh)
+        self.layer = 0
+
+    # each stage calls the C entry point directly with pre-marshalled pointers
+    def run_resblock(self):
+        w, L = self.w, self.md.lib
+        rc = L.medusa_resblock(self.md.MEDUSA_BF16, w["B"], w["H"], w["K"], self.hidden.data_ptr(),
+                               self.w1.data_ptr(), self.b1.data_ptr(), self.r.data_ptr(), self.stream)
+        assert rc == 0, rc
+
+    def run_lm(self):
+        w, L = self.w, self.md.lib
+        rc = L.medusa_lm_head_topk(self.md.MEDUSA_BF16, w["B"], w["H"], w["V"], w["K"], w["topk"],
+                                   self.r.data_ptr(), self.w_lm.data_ptr(), self.topk_ids.data_ptr(),
+                                   self.topk_vals.data_ptr(), None, self.heads_ws.data_ptr(),
+                                   self.heads_ws.numel(), self.stream)
+        assert rc == 0, rc
+
+    def run_heads(self):
+        self.run_resblock()
+        self.run_lm()
+
+    def run_tree(self):
+        w, L, t = self.w, self.md.lib, self.tree
+        rc = L.medusa_build_tree(w["B"], w["K"], w["topk"], self.N, self.choices.data_ptr(),
+                                 self.topk_ids.data_ptr(), self.root.data_ptr(), self.plen.data_ptr(),
+                                 t["tree_candidates"].data_ptr(), t["tree_indices"].data_ptr(),
+                                 t["parent"].data_ptr(), t["depth"].data_ptr(), t["position_ids"].data_ptr(),
+                                 t["tree_mask"].data_ptr(), t["retrieve"].data_ptr(), t["num_paths"].data_ptr(),
+                                 self.p_max, t["status"].data_ptr(), self.stream)
+        assert rc == 0, rc
+
+    def run_attention(self):
+        w, L = self.w, self.md.lib
+        off = self.layer * self.layer_elems * 2
+        rc = L.medusa_tree_attention(self.md.MEDUSA_BF16, w["B"], self.T, w["Hq"], w["d"], w["S_max"],
+                                     self.q.data_ptr(), self.k_cache.data_ptr() + off,
+                                     self.v_cache.data_ptr() + off, self.plen.data_ptr(),
+                                     self.tree["tree_mask"].data_ptr(), self.scale, self.att_out.data_ptr(),
+                                     self.att_ws.data_ptr(), self.att_ws.numel(), self.stream)
+        assert rc == 0, rc
+        self.layer = (self.layer + 1) % w["n_layers"]
+
+    def run_posterior(self):
+        w, L, t, p = self.w, self.md.lib, self.tree, self.post
+        rc = L.medusa_evaluate_posterior(w["B"], self.T, w["V"], self.p_max, w["K"] + 1, self.logits.data_ptr(),
+                                         t["tree_candidates"].data_ptr(), t["retrieve"].data_ptr(),
+                                         t["num_paths"].data_ptr(), w["temperature"], w["eps"], w["delta"],
+                                         p["best_path"].data_ptr(), p["accept_len"].data_ptr(),
+                                         p["next_token"].data_ptr(), self.post_ws.data_ptr(),
+                                         self.post_ws.numel(), self.stream)
+        assert rc == 0, rc
+
+    def run_commit(self):
+        w, L, t, p = self.w, self.md.lib, self.tree, self.post
+        rc = L.medusa_commit_kv(self.md.MEDUSA_BF16, w["B"], w["n_layers"], w["Hq"], w["d"], w["S_max"],
+                                self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.plen.data_ptr(),
+                                t["retrieve"].data_ptr(), self.p_max, w["K"] + 1, p["best_path"].data_ptr(),
+                                p["accept_len"].data_ptr(), self.new_plen.data_ptr(), self.stream)
+        assert rc == 0, rc
+
+    STAGES = ("resblock", "lm_head_topk", "build_tree", "tree_attention", "posterior", "commit_kv")
+
+    def run(self, events=None):
+        fns = (self.run_resblock, self.run_lm, self.run_tree, self.run_attention, self.run_posterior,
+               self.run_commit)
+        for i, fn in enumerate(fns):
+            if events is not None:
+                events[i].record()
+            fn()
+        if events is not None:
+            events[len(fns)].record()
+
+
+def lm_bytes(w):
+    """Algorithmic bytes of one lm_head + top-k launch: every weight once,
+    r once, the top-k ids and logits written."""
+    B, H, V, K, k = w["B"], w["H"], w["V"], w["K"], w["topk"]
+    return K * V * H * 2 + B * K * H * 4 + B * K * k * 8
+
+
+def cpu_baseline(w, seed, repeats=3):
+    """The oracle on full steps of the same workload, on this host: the
+    median of ``repeats`` timed steps (inputs generated outside the timing)."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = synth.heads_inputs(w, seed=seed)
+    choices = synth.choices_array(
+        synth.random_tree_choices(w["depth_counts"], w["topk"], seed=seed, workload_id=w["wid"]), w["K"])
+    root = synth.root_token_input(w, seed=seed)
+    plen = synth.prefix_lengths(w, seed=seed)
+    kc, vc = synth.kv_cache(dict(w, Hkv=w["Hq"]), seed=seed)
+    att = logits = None
+    runs = []
+    for _ in range(repeats):
+        times = {}
+        t0 = time.perf_counter()
+        hd = oracle.heads(x["hidden"], x["w1"], x["b1"], x["w_lm"], w["topk"])
+        t1 = time.perf_counter()
+        tr = oracle.build_tree(choices, w["K"], w["topk"], hd["topk_ids"], root, plen)
+        t2 = time.perf_counter()
+        times["heads"], times["build_tree"] = t1 - t0, t2 - t1
+        if att is None:
+            att = synth.attention_inputs(w, tr["depth"], plen, seed=seed)
+            logits, _ = synth.posterior_logits(w, tr["tree_candidates"], tr["retrieve"], tr["num_paths"],
+                                               tr["depth"], seed=seed)
+        t2 = time.perf_counter()
+        oracle.tree_attention(att["q"], att["k_cache"], att["v_cache"], plen, tr["tree_mask"],
+                              1.0 / math.sqrt(w["d"]))
+        t3 = time.perf_counter()
+        post = oracle.evaluate_posterior(logits, tr["tree_candidates"], tr["retrieve"], tr["num_paths"],
+                                         w["temperature"], w["eps"], w["delta"])
+        t4 = time.perf_counter()
+        oracle.commit_kv(kc, vc, plen, tr["retrieve"], post["best_path"], post["accept_len"])
+        t5 = time.perf_counter()
+        times["tree_attention"], times["posterior"], times["commit_kv"] = t3 - t2, t4 - t3, t5 - t4
+        runs.append(times)
+    runs.sort(key=lambda t: sum(t.values()))
+    med = runs[len(runs) // 2]
+    total = sum(med.values())
+    return {"value": round(1.0 / total, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": "median of %d full verify steps at the same shapes (5 heads, 64-node tree, one "
+                      "attention layer at prefix 2048, typical posterior over 64x32000, 32-layer commit), "
+                      "fp64 NumPy" % repeats,
+            "seconds_per_step": round(total, 3), "stage_seconds": {k: round(v, 3) for k, v in med.items()}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs the verify step on one GPU only; --gpus %d is not supported "
+              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    w = synth.workload("vicuna-7b")
+    step = Step(w, args.seed)
+    nst = len(Step.STAGES)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step.run(ev[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)] for i in range(nst)]
+
+    def stats(xs):
+        xs = sorted(xs)
+        return {"mean_us": round(1000 * sum(xs) / len(xs), 2), "median_us": round(1000 * xs[len(xs) // 2], 2),
+                "p10_us": round(1000 * xs[len(xs) // 10], 2), "p90_us": round(1000 * xs[(9 * len(xs)) // 10], 2)}
+
+    stages = {name: stats(stage_ms[i]) for i, name in enumerate(Step.STAGES)}
+    lm_mean_s = sum(stage_ms[1]) / len(stage_ms[1]) / 1000.0
+    achieved = lm_bytes(w) / lm_mean_s / 1e9
+    acc = int(step.post["accept_len"].cpu()[0])
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "vicuna-7b verify step, batch 1", "B": w["B"], "H": w["H"], "V": w["V"],
+                   "K": w["K"], "topk": w["topk"], "T": step.T, "Hq": w["Hq"], "d": w["d"], "L": w["L"],
+                   "n_layers": w["n_layers"], "temperature": w["temperature"]},
+        "roofline": {"kernel": "lm_head_topk", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": lm_bytes(w),
+                     "mean_launch_us": round(lm_mean_s * 1e6, 2)},
+        "stages": stages,
+        "tokens_per_step": acc + 1,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.seed)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
