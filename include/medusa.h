@@ -82,7 +82,9 @@ enum {
  *   r[b][j]      = h[b] + SiLU(W1[j] h[b] + b1[j])           (float32)
  *   logits[b][j] = Wlm[j] r[b][j]                             (no bias)
  *   topk_ids[b][j][0..topk) = the topk largest logits, ordered by value
- *   descending, equal values by lower token id first.
+ *   descending, equal values (+0 and -0 included) by lower token id first.
+ *   A NaN logit is never selected; slots left without a candidate (only
+ *   possible with NaN logits) hold id -1 and value -inf.
  *
  * Layouts: hidden [B][H]; w1 [K][H][H] (out x in: row i makes output i);
  * b1 [K][H]; w_lm [K][V][H] (out x in); r [B][K][H] float32;
@@ -90,10 +92,12 @@ enum {
  * [B][K][V].  `dtype` applies to hidden, w1, b1 and w_lm.  bf16 needs
  * H % 8 == 0, f32 needs H % 4 == 0; 1 <= topk <= min(64, V).
  *
- * Workspace: medusa_heads_workspace() bytes of device memory.  Its first
- * 256 bytes hold completion counters that MUST be zero before the first
- * call; every call returns them to zero, so zero it once (hipMemset) and
- * reuse it.  Calls that share a workspace must not run concurrently.
+ * Workspace: medusa_heads_workspace() bytes of device memory, no
+ * initialisation needed (per-wave candidate lists and, in medusa_heads, r).
+ * medusa_lm_head_topk launches two kernels on `stream`: the weight stream,
+ * which leaves one sorted top-k list per wave in the workspace, then their
+ * merge (radix selection on unique value/id keys).  Calls that share a
+ * workspace must not run concurrently.
  * ------------------------------------------------------------------- */
 size_t medusa_heads_workspace(int dtype, int B, int H, int V, int K, int topk);
 

@@ -103,11 +103,7 @@ _WS = {}
 
 
 def workspace(kind, device, nbytes):
-    """A cached zero-initialised workspace of at least ``nbytes`` bytes.
-
-    The heads workspace relies on its counters being zero before the first
-    call (each call leaves them zero), which torch.zeros provides.
-    """
+    """A cached workspace of at least ``nbytes`` bytes (one per kind and device)."""
     key = (kind, torch.device(device).index)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:

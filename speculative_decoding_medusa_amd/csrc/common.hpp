@@ -53,6 +53,13 @@ __device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Pointers into LDS that stay LDS pointers (ds_read/ds_write) even when they
+// are volatile or pass through functions; a generic pointer would be lowered
+// to flat accesses, which count against the vector-memory counter.
+#define MEDUSA_LDS __attribute__((address_space(3)))
+typedef volatile MEDUSA_LDS float lds_vfloat;
+typedef volatile MEDUSA_LDS int lds_vint;
+
 }  // namespace medusa
 
 // ---------------------------------------------------------------- host side

@@ -15,10 +15,12 @@
 // products with the (exact) bf16 weights are summed in float32, which keeps
 // about 16 significant bits of r instead of 8.
 //
-// Top-k: wave 0 of each workgroup keeps a sorted list per sequence in LDS
-// and inserts the rare tile logits that beat its current k-th entry; the
-// workgroup then publishes its list and the last workgroup of each head
-// (completion counter) merges them.
+// Top-k: each wave (each workgroup in the split-K kernel) keeps sorted
+// lists per sequence in LDS and inserts the rare logits that beat its current
+// k-th entry; the lists are published to the workspace and a second, small
+// kernel merges them per (sequence, head).  Two launches rather than a
+// last-workgroup merge: on this chip a device-scope fence writes back and
+// invalidates the L2 of the issuing XCD, which every workgroup would pay.
 #include "common.hpp"
 
 namespace medusa {
@@ -26,12 +28,18 @@ namespace medusa {
 constexpr int kHeadsThreads = 256;
 constexpr int kHeadsWaves = kHeadsThreads / kWave;
 constexpr int kUnroll = 8;          // 32-wide K steps issued back to back per wave
-constexpr int kMergeCap = 1024;     // LDS survivors in the final merge
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+#ifndef MEDUSA_STREAM_NT
+#define MEDUSA_STREAM_NT 1
+#endif
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+#if MEDUSA_STREAM_NT
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -131,37 +139,41 @@ struct TopkLists {
   int count[kMaxBatch];
 };
 
-// Wave-uniform insertion of the candidates held by the lanes in `mask`.
-// The lists are shared by the lanes of wave 0 through LDS without a
-// barrier, so every access is volatile: each read is a real LDS read issued
-// after the wave's earlier writes (LDS operations of one wave complete in
-// order).
-__device__ void topk_insert(TopkLists& tl_, int b, int k, float v, int id, uint64_t mask, int lane) {
-  volatile TopkLists& tl = tl_;
+// Wave-uniform insertion of the candidates held by the lanes in `mask` into
+// one sorted list (values lv, ids li, length *cnt <= k).  A list is only
+// touched by one wave, through LDS and without a barrier, so every access is
+// volatile: each read is a real LDS read issued after the wave's earlier
+// writes (LDS operations of one wave complete in order).
+__device__ __forceinline__ void topk_insert_list(lds_vfloat* lv, lds_vint* li, lds_vint* cnt, int k, float v, int id,
+                                                 uint64_t mask, int lane) {
   while (mask) {
     const int src = __ffsll(static_cast<unsigned long long>(mask)) - 1;
     mask &= mask - 1;
     const float cv = __shfl(v, src);
     const int ci = __shfl(id, src);
-    const int c = tl.count[b];
-    if (c == k && !beats(cv, ci, tl.v[b][k - 1], tl.id[b][k - 1])) continue;
-    const float ev = lane < c ? tl.v[b][lane] : 0.f;
-    const int ei = lane < c ? tl.id[b][lane] : 0;
+    const int c = *cnt;
+    if (c == k && !beats(cv, ci, lv[k - 1], li[k - 1])) continue;
+    const float ev = lane < c ? lv[lane] : 0.f;
+    const int ei = lane < c ? li[lane] : 0;
     const int pos = __popcll(ballot(lane < c && beats(ev, ei, cv, ci)));
     const float pv = __shfl(ev, lane > 0 ? lane - 1 : 0);
     const int pi = __shfl(ei, lane > 0 ? lane - 1 : 0);
     const int nc = c + 1 < k ? c + 1 : k;
     if (lane < nc) {
       if (lane == pos) {
-        tl.v[b][lane] = cv;
-        tl.id[b][lane] = ci;
+        lv[lane] = cv;
+        li[lane] = ci;
       } else if (lane > pos) {
-        tl.v[b][lane] = pv;
-        tl.id[b][lane] = pi;
+        lv[lane] = pv;
+        li[lane] = pi;
       }
     }
-    tl.count[b] = nc;  // every lane stores the same value
+    *cnt = nc;  // every lane stores the same value
   }
+}
+
+__device__ __forceinline__ void topk_insert(TopkLists& tl, int b, int k, float v, int id, uint64_t mask, int lane) {
+  topk_insert_list((lds_vfloat*)tl.v[b], (lds_vint*)tl.id[b], (lds_vint*)&tl.count[b], k, v, id, mask, lane);
 }
 
 // Block-wide best (by `beats`) of one (value, id) per thread; all threads get it.
@@ -182,77 +194,188 @@ __device__ void block_best(float& v, int& id, float* sv, int* si) {
     if (beats(sv[w], si[w], v, id)) { v = sv[w]; id = si[w]; }
 }
 
-// The last workgroup of head j merges the G published lists of each sequence.
-__device__ void merge_head_lists(int B, int K, int V, int k, int G, int j,
-                                 const float* cand_v, const int* cand_i,
-                                 int32_t* topk_ids, float* topk_vals) {
-  __shared__ float mv[kMergeCap];
-  __shared__ int mi[kMergeCap];
-  __shared__ float redv[16];
-  __shared__ int redi[16];
-  __shared__ int mcount;
-  const int tid = threadIdx.x;
-  const float NEG = -__builtin_huge_valf();
-  for (int b = 0; b < B; ++b) {
-    const size_t base = (static_cast<size_t>(j) * B + b) * G * k;
-    // lower bound of the k-th best: the best of the per-list k-th entries
-    float tv = NEG;
-    int ti = 0x7fffffff;
-    bool have = false;
-    for (int w = tid; w < G; w += blockDim.x) {
-      const int e = cand_i[base + static_cast<size_t>(w) * k + (k - 1)];
-      if (e >= 0) {
-        const float ev = cand_v[base + static_cast<size_t>(w) * k + (k - 1)];
-        if (!have || beats(ev, e, tv, ti)) { tv = ev; ti = e; have = true; }
-      }
+// ------------------------------------------------------------- top-k merge
+// Final top-k of one (sequence b, head j) from the `lists` sorted lists of k
+// entries that the lm_head kernel published (a separate launch: the kernel
+// boundary makes every list visible to this workgroup whatever XCD wrote
+// it).  Selection runs on unique 64-bit keys whose unsigned order is the
+// order of `beats`: the high word is the value's bit pattern made monotonic
+// (+0 and -0 merged, as they compare equal), the low word the inverted
+// token id, so equal values rank the smaller id first.  Key 0 means "no
+// candidate" (an unused list slot; NaN is never a candidate).  The k-th
+// largest key is found by radix selection, 8 bits per pass from the top:
+// each pass histograms the keys that share the prefix chosen so far, one
+// wave scans the 256 bins from the top to pick the bucket holding the
+// still-needed rank, and selection stops as soon as the whole bucket is
+// needed.  The keys >= the selected prefix are then exactly the top k
+// (or every candidate, when there are fewer than k); each ranks itself
+// against the others.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeMaxKeys = 32;  // keys per thread: lists * k <= 32768
+
+__device__ __forceinline__ uint64_t merge_key(float v, int id) {
+  if (id < 0 || v != v) return 0;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t m = v == 0.f ? 0x80000000u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+  return (static_cast<uint64_t>(m) << 32) | static_cast<uint32_t>(~id);
+}
+
+__device__ __forceinline__ float merge_key_value(uint64_t x) {
+  const uint32_t m = static_cast<uint32_t>(x >> 32);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
+}
+
+template <int E>
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(int B, int K, int k, int lists,
+                                                                   const float* __restrict__ cand_v,
+                                                                   const int* __restrict__ cand_i,
+                                                                   int32_t* __restrict__ topk_ids,
+                                                                   float* __restrict__ topk_vals) {
+  const int b = blockIdx.x, j = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lists * k;
+  const size_t base = (static_cast<size_t>(j) * B + b) * n;
+  int32_t* oid = topk_ids + (static_cast<size_t>(b) * K + j) * k;
+  float* oval = topk_vals + (static_cast<size_t>(b) * K + j) * k;
+  __shared__ int hist[2][256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need, s_done, s_n;
+  __shared__ uint64_t s_keys[kMaxTopk];
+
+  // all loads first (clamped index, masked at use): one memory round trip
+  float v[E];
+  int id[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = min(i * kMergeThreads + tid, n - 1);
+    v[i] = cand_v[base + e];
+    id[i] = cand_i[base + e];
+  }
+  if (tid < 256) hist[0][tid] = 0;
+  if (tid == 0) {
+    s_prefix = 0;
+    s_need = k;
+    s_done = 0;
+    s_n = 0;
+  }
+  uint64_t key[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) key[i] = i * kMergeThreads + tid < n ? merge_key(v[i], id[i]) : 0;
+  __syncthreads();
+
+  for (int p = 0; p < 8; ++p) {
+    const int shift = 56 - 8 * p;
+    const uint64_t prefix = s_prefix;
+    int* h = hist[p & 1];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint64_t x = key[i];
+      const bool match = x != 0 && (p == 0 || (x >> (shift + 8)) == (prefix >> (shift + 8)));
+      if (match) atomicAdd(&h[static_cast<int>(x >> shift) & 255], 1);
     }
-    block_best(tv, ti, redv, redi);
-    const bool any_full = ti != 0x7fffffff;
-    if (tid == 0) mcount = 0;
     __syncthreads();
-    for (int e = tid; e < G * k; e += blockDim.x) {
-      const int id = cand_i[base + e];
-      if (id < 0) continue;
-      const float v = cand_v[base + e];
-      if (!any_full || !beats(tv, ti, v, id)) {
-        const int slot = atomicAdd(&mcount, 1);
-        if (slot < kMergeCap) { mv[slot] = v; mi[slot] = id; }
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (best first)
+      int c[4];
+      int sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = h[255 - 4 * lane - q];
+        sum += c[q];
       }
-    }
-    __syncthreads();
-    const int S = mcount;
-    int32_t* oid = topk_ids + (static_cast<size_t>(b) * K + j) * k;
-    float* oval = topk_vals + (static_cast<size_t>(b) * K + j) * k;
-    if (S <= kMergeCap) {
-      for (int s = tid; s < S; s += blockDim.x) {
-        int rank = 0;
-        for (int t = 0; t < S; ++t) rank += beats(mv[t], mi[t], mv[s], mi[s]) ? 1 : 0;
-        if (rank < k) { oid[rank] = mi[s]; oval[rank] = mv[s]; }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
       }
-      for (int s = S + tid; s < k; s += blockDim.x) { oid[s] = -1; oval[s] = NEG; }
-    } else {
-      // many exact ties: k rounds of "best entry ranked after the last pick"
-      float lv = __builtin_huge_valf();
-      int li = -1;
-      for (int round = 0; round < k; ++round) {
-        float bv = NEG;
-        int bi = 0x7fffffff;
-        bool found = false;
-        for (int e = tid; e < G * k; e += blockDim.x) {
-          const int id = cand_i[base + e];
-          if (id < 0) continue;
-          const float v = cand_v[base + e];
-          if ((round == 0 || beats(lv, li, v, id)) && (!found || beats(v, id, bv, bi))) {
-            bv = v; bi = id; found = true;
-          }
+      const int need = s_need;
+      const int total = __shfl(incl, kWave - 1);
+      if (total < need) {
+        // fewer candidates than k (first pass only): take them all
+        if (lane == 0) {
+          s_prefix = 1;
+          s_done = 1;
         }
-        block_best(bv, bi, redv, redi);
-        if (tid == 0) { oid[round] = bi == 0x7fffffff ? -1 : bi; oval[round] = bv; }
-        lv = bv;
-        li = bi;
+      } else if (incl - sum < need && need <= incl) {
+        int acc = incl - sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (acc < need && need <= acc + c[q]) {
+            const int rest = need - acc;
+            s_prefix = prefix | (static_cast<uint64_t>(255 - 4 * lane - q) << shift);
+            s_need = rest;
+            s_done = c[q] == rest ? 1 : 0;
+          }
+          acc += c[q];
+        }
       }
+    } else if (tid < 64 + 256) {
+      hist[(p + 1) & 1][tid - 64] = 0;
     }
     __syncthreads();
+    if (s_done) break;
+  }
+
+  const uint64_t thr = s_prefix;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    if (key[i] != 0 && key[i] >= thr) s_keys[atomicAdd(&s_n, 1)] = key[i];
+  }
+  __syncthreads();
+  const int S = s_n;  // <= k
+  if (tid < S) {
+    const uint64_t x = s_keys[tid];
+    int rank = 0;
+    for (int t = 0; t < S; ++t) rank += s_keys[t] > x ? 1 : 0;
+    oid[rank] = static_cast<int32_t>(~static_cast<uint32_t>(x));
+    oval[rank] = merge_key_value(x);
+  } else if (tid < k) {
+    oid[tid] = -1;
+    oval[tid] = -__builtin_huge_valf();
+  }
+}
+
+// Candidate sets beyond kMergeThreads * kMergeMaxKeys: k rounds of
+// block-wide "best entry ranked after the previous pick" over global memory.
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_rounds_kernel(int B, int K, int k, int lists,
+                                                                          const float* __restrict__ cand_v,
+                                                                          const int* __restrict__ cand_i,
+                                                                          int32_t* __restrict__ topk_ids,
+                                                                          float* __restrict__ topk_vals) {
+  const int b = blockIdx.x, j = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int n = lists * k;
+  const size_t base = (static_cast<size_t>(j) * B + b) * n;
+  int32_t* oid = topk_ids + (static_cast<size_t>(b) * K + j) * k;
+  float* oval = topk_vals + (static_cast<size_t>(b) * K + j) * k;
+  __shared__ float redv[kMergeThreads / kWave];
+  __shared__ int redi[kMergeThreads / kWave];
+  const float NEG = -__builtin_huge_valf();
+  const int NONE = 0x7fffffff;
+  float lv = __builtin_huge_valf();
+  int li = -1;
+  for (int round = 0; round < k; ++round) {
+    float bv = NEG;
+    int bi = NONE;
+    bool found = false;
+    for (int e = tid; e < n; e += kMergeThreads) {
+      const int id = cand_i[base + e];
+      const float v = cand_v[base + e];
+      if (id < 0 || v != v) continue;
+      if ((round == 0 || beats(lv, li, v, id)) && (!found || beats(v, id, bv, bi))) {
+        bv = v;
+        bi = id;
+        found = true;
+      }
+    }
+    block_best(bv, bi, redv, redi);
+    if (tid == 0) {
+      oid[round] = bi == NONE ? -1 : bi;
+      oval[round] = bi == NONE ? NEG : bv;
+    }
+    lv = bv;
+    li = bi;
   }
 }
 
@@ -265,7 +388,7 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
     int B, int H, int V, int K, int k, int rows_per_wg, int G,
     const float* __restrict__ r, const void* __restrict__ wlm_v,
     float* __restrict__ logits_out, int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals,
-    float* __restrict__ cand_v, int32_t* __restrict__ cand_i, unsigned* __restrict__ counters) {
+    float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
   constexpr int NP = kBF16 ? kHeadsWaves : 1;
   const int j = blockIdx.y, wg = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -276,7 +399,6 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
 
   __shared__ float red[2][NP][kMaxBatch][16];
   __shared__ TopkLists tl;
-  __shared__ unsigned s_ticket;
   if (threadIdx.x < kMaxBatch) tl.count[threadIdx.x] = 0;
   __syncthreads();
 
@@ -386,10 +508,10 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
         for (int w = 0; w < NP; ++w) v += red[buf][w][b][n];
         if (valid && logits_out != nullptr)
           logits_out[(static_cast<size_t>(b) * K + j) * V + row] = v;
-        volatile TopkLists& vtl = tl;
-        const int c = vtl.count[b];
-        const bool ok = valid && (v == v) &&
-                        (c < k || beats(v, row, vtl.v[b][k - 1], vtl.id[b][k - 1]));
+        lds_vfloat* lvb = (lds_vfloat*)tl.v[b];
+        lds_vint* lib = (lds_vint*)tl.id[b];
+        const int c = *(lds_vint*)&tl.count[b];
+        const bool ok = valid && (v == v) && (c < k || beats(v, row, lvb[k - 1], lib[k - 1]));
         const uint64_t m = ballot(ok);
         if (m) topk_insert(tl, b, k, v, row, m, lane);
       }
@@ -403,21 +525,408 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
     for (int b = 0; b < B; ++b) {
       const size_t base = ((static_cast<size_t>(j) * B + b) * G + wg) * k;
       if (lane < k) {
-        volatile TopkLists& vtl = tl;
-        const bool have = lane < vtl.count[b];
-        cand_v[base + lane] = have ? vtl.v[b][lane] : NEG;
-        cand_i[base + lane] = have ? vtl.id[b][lane] : -1;
+        const bool have = lane < *(lds_vint*)&tl.count[b];
+        cand_v[base + lane] = have ? ((lds_vfloat*)tl.v[b])[lane] : NEG;
+        cand_i[base + lane] = have ? ((lds_vint*)tl.id[b])[lane] : -1;
       }
     }
   }
-  __threadfence();
+}
+
+// ------------------------------------------------------------ K2, streamed
+// bf16 lm_head for 2*B*H*2 bytes of A planes that fit in LDS.
+//
+// The workgroup first splits r[b][j] into bf16 hi/lo planes in LDS (row
+// 2b = hi, 2b+1 = lo: exactly the MFMA A rows of lane m = l % 16).  Each wave
+// then owns `tpw` whole 16-row tiles of Wlm[j] and streams them alone: no
+// split-K, no barrier until the end.  Loads come in chunks of kChunkPairs
+// 64-wide K pairs (lane l reads 32 contiguous bytes of row l % 16, so a row
+// gets a full 128-byte line per pair) and are double-buffered in registers
+// across chunks and tiles; A operands come from LDS, whose counter is
+// separate from the vector-memory one, so consuming them never waits on the
+// weight stream.  After each tile the wave inserts its logits into its own
+// top-k lists and finally publishes them for the merge kernel.
+#ifndef MEDUSA_CHUNK_PAIRS
+#define MEDUSA_CHUNK_PAIRS 4
+#endif
+#ifndef MEDUSA_STREAM_ROTATE
+#define MEDUSA_STREAM_ROTATE 0
+#endif
+constexpr int kChunkPairs = MEDUSA_CHUNK_PAIRS;
+
+__device__ __forceinline__ int stream_chunk_pair0(int c, int cpt, int rot) {
+  int q = c - (c / cpt) * cpt + rot;
+  if (q >= cpt) q -= cpt;
+  return q * kChunkPairs;
+}
+
+__device__ __forceinline__ void stream_load_chunk(const uint16_t* __restrict__ wbase, int V, int H, int t0, int cpt,
+                                                  int rot, int n, int g, int c, u32x4 (&buf)[2 * kChunkPairs]) {
+  const int tq = c / cpt;
+  const int p0 = stream_chunk_pair0(c, cpt, rot);
+  const int row = (t0 + tq) * 16 + n;
+  const bool row_ok = row < V;
+  const uint16_t* wrow = wbase + static_cast<size_t>(row_ok ? row : V - 1) * H;
+  // Loads are unconditional, from clamped in-bounds addresses, and nothing
+  // consumes them here: with no branch or select behind them the compiler
+  // can count them and later wait only for the chunk being consumed, not for
+  // the prefetch issued after it.  Rows past V load row V-1 (their logits are
+  // discarded); the K tail is masked when the chunk is consumed.
+#pragma unroll
+  for (int u = 0; u < kChunkPairs; ++u) {
+    const int k0 = (p0 + u) * 64 + g * 16;
+    buf[2 * u] = ld16_stream(wrow + min(k0, H - 8));
+    buf[2 * u + 1] = ld16_stream(wrow + min(k0 + 8, H - 8));
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void stream_mfma_chunk(const uint16_t* __restrict__ A, int B, int H, int cpt, int rot, int n,
+                                                  int g, int c, const u32x4 (&buf)[2 * kChunkPairs], f32x4 (&acc)[MT]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int p0 = stream_chunk_pair0(c, cpt, rot);
+#pragma unroll
+  for (int u = 0; u < kChunkPairs; ++u) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int k0 = (p0 + u) * 64 + g * 16 + 8 * h2;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ar = t * 16 + n;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(ar < 2 * B ? ar : 0) * H +
+                                                         min(k0, H - 8));
+        const u32x4 a = (ar < 2 * B && k0 < H) ? x : zero;
+        const u32x4 w = k0 < H ? buf[2 * u + h2] : zero;
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(w), acc[t], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// End of a tile: lane (g, n) holds C[4g + i][n] of each M tile t, i.e. the
+// hi/lo halves of sequences 8t + 2g (i = 0, 1) and 8t + 2g + 1 (i = 2, 3) at
+// row `row`.  Writes the optional logits and offers them to the wave's lists.
+template <int MT>
+__device__ __forceinline__ void stream_tile_epilogue(int B, int K, int V, int k, int j, int row, int g, int lane,
+                                                     f32x4 (&acc)[MT], float* __restrict__ logits_out,
+                                                     lds_vfloat* my_v, lds_vint* my_i, lds_vint* my_c) {
+  const bool valid = row < V;
+  // the two sequences of each M tile, as plain scalars (no indexed array)
+  const float v00 = acc[0][0] + acc[0][1], v01 = acc[0][2] + acc[0][3];
+  const float v10 = MT > 1 ? acc[MT - 1][0] + acc[MT - 1][1] : 0.f;
+  const float v11 = MT > 1 ? acc[MT - 1][2] + acc[MT - 1][3] : 0.f;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (logits_out != nullptr && valid) {
+    const int b0 = 2 * g;
+    if (b0 < B) logits_out[(static_cast<size_t>(b0) * K + j) * V + row] = v00;
+    if (b0 + 1 < B) logits_out[(static_cast<size_t>(b0 + 1) * K + j) * V + row] = v01;
+    if (MT > 1 && b0 + 8 < B) logits_out[(static_cast<size_t>(b0 + 8) * K + j) * V + row] = v10;
+    if (MT > 1 && b0 + 9 < B) logits_out[(static_cast<size_t>(b0 + 9) * K + j) * V + row] = v11;
+  }
+  for (int b = 0; b < B; ++b) {
+    const bool odd = (b & 1) != 0;
+    const float v = b < 8 ? (odd ? v01 : v00) : (odd ? v11 : v10);
+    const int cnt = my_c[b];
+    const bool ok = valid && g == ((b & 7) >> 1) && (v == v) &&
+                    (cnt < k || beats(v, row, my_v[b * k + k - 1], my_i[b * k + k - 1]));
+    const uint64_t m = ballot(ok);
+    if (m) topk_insert_list(my_v + b * k, my_i + b * k, my_c + b, k, v, row, m, lane);
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kHeadsThreads) void lm_topk_stream_kernel(
+    int B, int H, int V, int K, int k, int tpw, int G, const float* __restrict__ r,
+    const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int j = blockIdx.y, wg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const float NEG = -__builtin_huge_valf();
+
+  uint16_t* A = reinterpret_cast<uint16_t*>(smem);                       // [2B][H]
+  const size_t a_bytes = (static_cast<size_t>(2 * B) * H * 2 + 15) / 16 * 16;
+  float* lv = reinterpret_cast<float*>(smem + a_bytes);                  // [4][B][k]
+  int* li = reinterpret_cast<int*>(lv + kHeadsWaves * B * k);            // [4][B][k]
+  int* lc = li + kHeadsWaves * B * k;                                    // [4][B]
+
+  // split r into hi/lo bf16 planes
+  const int h4 = H / 4;
+  for (int e4 = tid; e4 < B * h4; e4 += kHeadsThreads) {
+    const int b = e4 / h4, e = (e4 - b * h4) * 4;
+    const float4 x = *reinterpret_cast<const float4*>(r + (static_cast<size_t>(b) * K + j) * H + e);
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t hi = f32_to_bf16_bits(xs[c]);
+      const uint32_t lo = f32_to_bf16_bits(xs[c] - __uint_as_float(hi << 16));
+      A[static_cast<size_t>(2 * b) * H + e + c] = static_cast<uint16_t>(hi);
+      A[static_cast<size_t>(2 * b + 1) * H + e + c] = static_cast<uint16_t>(lo);
+    }
+  }
+  for (int e = tid; e < kHeadsWaves * B; e += kHeadsThreads) lc[e] = 0;
   __syncthreads();
-  if (threadIdx.x == 0) s_ticket = atomicAdd(&counters[j], 1u);
+
+  const int tiles = (V + 15) / 16;
+  const int t0 = (wg * kHeadsWaves + wave) * tpw;
+  const int t1 = min(t0 + tpw, tiles);
+  const int npairs = (H + 63) / 64;
+  const int cpt = (npairs + kChunkPairs - 1) / kChunkPairs;
+  const int nchunks = t1 > t0 ? (t1 - t0) * cpt : 0;
+  const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
+#if MEDUSA_STREAM_ROTATE
+  // waves start their rows at different K offsets, so concurrent requests
+  // spread over more HBM channels
+  const int rot = ((j * gridDim.x + wg) * kHeadsWaves + wave) % cpt;
+#else
+  const int rot = 0;
+#endif
+  lds_vfloat* my_v = (lds_vfloat*)(lv + wave * B * k);
+  lds_vint* my_i = (lds_vint*)(li + wave * B * k);
+  lds_vint* my_c = (lds_vint*)(lc + wave * B);
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Rotated double buffer (as in the row-diagonal kernel): both buffers are
+  // in flight before the loop, refills past the end reload the last chunk,
+  // so every MFMA waits only for the loads it consumes.
+  u32x4 wa[2 * kChunkPairs], wb[2 * kChunkPairs];
+#define MEDUSA_STREAM_STEP(cc, buf)                                                                       \
+  do {                                                                                                    \
+    stream_mfma_chunk<MT>(A, B, H, cpt, rot, n, g, (cc), buf, acc);                                       \
+    if ((cc) % cpt == cpt - 1)                                                                            \
+      stream_tile_epilogue<MT>(B, K, V, k, j, (t0 + (cc) / cpt) * 16 + n, g, lane, acc, logits_out, my_v, \
+                               my_i, my_c);                                                               \
+  } while (0)
+  if (nchunks > 0) {
+    const int lastc = nchunks - 1;
+    stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, 0, wa);
+    stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, min(1, lastc), wb);
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      stream_mfma_chunk<MT>(A, B, H, cpt, rot, n, g, c, wa, acc);
+      stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, min(c + 2, lastc), wa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c % cpt == cpt - 1)
+        stream_tile_epilogue<MT>(B, K, V, k, j, (t0 + c / cpt) * 16 + n, g, lane, acc, logits_out, my_v, my_i,
+                                 my_c);
+      stream_mfma_chunk<MT>(A, B, H, cpt, rot, n, g, c + 1, wb, acc);
+      stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, min(c + 3, lastc), wb);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((c + 1) % cpt == cpt - 1)
+        stream_tile_epilogue<MT>(B, K, V, k, j, (t0 + (c + 1) / cpt) * 16 + n, g, lane, acc, logits_out, my_v,
+                                 my_i, my_c);
+    }
+    if (c < nchunks) MEDUSA_STREAM_STEP(c, wa);
+  }
+#undef MEDUSA_STREAM_STEP
   __syncthreads();
-  if (s_ticket != static_cast<unsigned>(G - 1)) return;
-  __threadfence();
-  merge_head_lists(B, K, V, k, G, j, cand_v, cand_i, topk_ids, topk_vals);
-  if (threadIdx.x == 0) counters[j] = 0u;
+
+  // every wave publishes its own lists (list wg * 4 + wave of head j)
+  const int nlists = G * kHeadsWaves;
+  for (int b = 0; b < B; ++b) {
+    const size_t base = ((static_cast<size_t>(j) * B + b) * nlists + wg * kHeadsWaves + wave) * k;
+    if (lane < k) {
+      const bool have = lane < my_c[b];
+      cand_v[base + lane] = have ? my_v[b * k + lane] : NEG;
+      cand_i[base + lane] = have ? my_i[b * k + lane] : -1;
+    }
+  }
+}
+
+// ------------------------------------------------------- K2, row-diagonal
+// bf16 lm_head for B <= 2 and H <= 512 * 16, streaming whole weight rows.
+//
+// Lane l = 16g + n loads the 16 bytes of a row at element 512s + 8l, so one
+// wave instruction reads 1 KB of one row contiguously, in lane order, and a
+// row is NST = H/512 such loads.  The A operand holds r at the same
+// positions, so in C = A B the diagonal entry C[n][n] sums the products of
+// the four lanes with that n (the MFMA pairs A lane (g, m) with B lane
+// (g, n) over k): the trace of C accumulated over s is the row's logit.
+// Only the diagonal is used, but at two MFMAs (r's hi and lo bf16 halves)
+// per KB the matrix cores stay far below the time the KB takes to arrive.
+// Each wave streams its own contiguous block of rows (hundreds of KB), row
+// loads double-buffered in registers; r's split planes stay in registers for
+// the whole kernel.  Logits of 64 consecutive rows gather one per lane and
+// are offered to the wave's top-k lists together.
+__host__ __device__ constexpr int diag_nstmax(int nst) { return nst <= 4 ? 4 : (nst <= 8 ? 8 : (nst <= 13 ? 13 : 16)); }
+
+template <int NSTMAX>
+__device__ __forceinline__ void diag_load_row(const uint16_t* __restrict__ wrow, int H, int e0, u32x4 (&buf)[NSTMAX]) {
+#pragma unroll
+  for (int s = 0; s < NSTMAX; ++s) buf[s] = ld16_stream(wrow + min(512 * s + e0, H - 8));
+}
+
+// Sum of the 16 diagonal lanes (lanes 4q..4q+3 of each 16-lane row q hold
+// one value each, zero elsewhere): two DPP quad adds, then the four quad
+// sums read as scalars.  The result is wave-uniform.
+__device__ __forceinline__ float diag_sum(float d) {
+  int x = __float_as_int(d);
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, true));  // quad_perm(1,0,3,2)
+  x = __float_as_int(d);
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, true));  // quad_perm(2,3,0,1)
+  x = __float_as_int(d);
+  return (__int_as_float(__builtin_amdgcn_readlane(x, 0)) + __int_as_float(__builtin_amdgcn_readlane(x, 20))) +
+         (__int_as_float(__builtin_amdgcn_readlane(x, 40)) + __int_as_float(__builtin_amdgcn_readlane(x, 60)));
+}
+
+template <int NSTMAX, int NB>
+__device__ __forceinline__ void diag_row_logits(const u32x4 (&buf)[NSTMAX], const u32x4 (&ahi)[NB][NSTMAX],
+                                                const u32x4 (&alo)[NB][NSTMAX], int H, int e0, int n, int g,
+                                                float (&logit)[NB]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // hi and lo products accumulate separately: two independent MFMA chains
+  f32x4 acc_hi[NB], acc_lo[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    acc_hi[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc_lo[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < NSTMAX; ++s) {
+    const u32x4 w = 512 * s + e0 < H ? buf[s] : zero;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc_hi[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi[b][s]), as_bf16x8(w), acc_hi[b], 0, 0, 0);
+      acc_lo[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo[b][s]), as_bf16x8(w), acc_lo[b], 0, 0, 0);
+    }
+  }
+  // lane (g, n) holds C[4g + i][n]; the diagonal C[n][n] sits at g = n / 4, i = n % 4
+  const int i = n & 3;
+  const bool on_diag = g == (n >> 2);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const f32x4 a = acc_hi[b] + acc_lo[b];
+    const float d = i == 0 ? a[0] : (i == 1 ? a[1] : (i == 2 ? a[2] : a[3]));
+    logit[b] = diag_sum(on_diag ? d : 0.f);
+  }
+}
+
+template <int NSTMAX, int NB>
+__global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
+    int B, int H, int V, int K, int k, int rows_per_wave, int G, const float* __restrict__ r,
+    const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
+  __shared__ float s_lv[kHeadsWaves][2][kMaxTopk];
+  __shared__ int s_li[kHeadsWaves][2][kMaxTopk];
+  __shared__ int s_lc[kHeadsWaves][2];
+  const int j = blockIdx.y, wg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  // lane l owns elements [512s + 8l, +8): one wave instruction reads 1 KB in
+  // lane order (fully coalesced); any one-to-one assignment of 8-element
+  // pieces to lanes gives the same trace as long as A uses the same one
+  const int e0 = 8 * lane;
+  const float NEG = -__builtin_huge_valf();
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if (tid < kHeadsWaves * 2) s_lc[tid >> 1][tid & 1] = 0;
+
+  // r split into bf16 hi/lo at this lane's positions
+  u32x4 ahi[NB][NSTMAX], alo[NB][NSTMAX];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int s = 0; s < NSTMAX; ++s) {
+      const int k0 = 512 * s + e0;
+      ahi[b][s] = zero;
+      alo[b][s] = zero;
+      if (b < B && k0 < H) {
+        const float* x = r + (static_cast<size_t>(b) * K + j) * H + k0;
+        const float4 x0 = *reinterpret_cast<const float4*>(x);
+        const float4 x1 = *reinterpret_cast<const float4*>(x + 4);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t hb[8], lb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hb[e] = f32_to_bf16_bits(xs[e]);
+          lb[e] = f32_to_bf16_bits(xs[e] - __uint_as_float(hb[e] << 16));
+        }
+        ahi[b][s] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+        alo[b][s] = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+      }
+    }
+  }
+  __syncthreads();
+
+  const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
+  const int r1 = min(r0 + rows_per_wave, V);
+  const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
+  lds_vfloat* my_v = (lds_vfloat*)&s_lv[wave][0][0];
+  lds_vint* my_i = (lds_vint*)&s_li[wave][0][0];
+  lds_vint* my_c = (lds_vint*)&s_lc[wave][0];
+  float gath[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) gath[b] = NEG;
+
+  // gather row `row`'s logits into lane (row - r0) % 64; flush every 64 rows
+  auto offer = [&](int row, const float (&lg)[NB]) {
+    const int slot = (row - r0) & 63;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (lane == slot) gath[b] = lg[b];
+      if (logits_out != nullptr && lane == 0 && b < B) logits_out[(static_cast<size_t>(b) * K + j) * V + row] = lg[b];
+    }
+    if (slot == 63 || row == r1 - 1) {
+      const int myrow = row - slot + lane;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b >= B) continue;
+        const float v = gath[b];
+        const int cnt = my_c[b];
+        const bool ok = lane <= slot && (v == v) &&
+                        (cnt < k || beats(v, myrow, my_v[b * kMaxTopk + k - 1], my_i[b * kMaxTopk + k - 1]));
+        const uint64_t m = ballot(ok);
+        if (m) topk_insert_list(my_v + b * kMaxTopk, my_i + b * kMaxTopk, my_c + b, k, v, myrow, m, lane);
+        gath[b] = NEG;
+      }
+    }
+  };
+
+  if (r1 > r0) {
+    // Rotated double buffer: both buffers are in flight before the loop, so
+    // on every path into the loop header the older buffer's eight loads are
+    // exactly the ones to wait for.  Loads past the block reload its last row
+    // (an L2 hit) so that no load is conditional.  The scheduling barriers keep
+    // each refill after the MFMAs that free its registers and before the next
+    // buffer's MFMAs.
+    u32x4 wa[NSTMAX], wb[NSTMAX];
+    float lg[NB];
+    const int last = r1 - 1;
+    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(r0) * H, H, e0, wa);
+    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0 + 1, last)) * H, H, e0, wb);
+    int row = r0;
+    for (; row + 1 < r1; row += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      offer(row, lg);
+      diag_row_logits<NSTMAX, NB>(wb, ahi, alo, H, e0, n, g, lg);
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
+      __builtin_amdgcn_sched_barrier(0);
+      offer(row + 1, lg);
+    }
+    if (row < r1) {
+      diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
+      offer(row, lg);
+    }
+  }
+  __syncthreads();
+
+  // every wave publishes its own lists (list wg * 4 + wave of head j)
+  const int nlists = G * kHeadsWaves;
+  for (int b = 0; b < B; ++b) {
+    const size_t base = ((static_cast<size_t>(j) * B + b) * nlists + wg * kHeadsWaves + wave) * k;
+    if (lane < k) {
+      const bool have = lane < my_c[b];
+      cand_v[base + lane] = have ? my_v[b * kMaxTopk + lane] : NEG;
+      cand_i[base + lane] = have ? my_i[b * kMaxTopk + lane] : -1;
+    }
+  }
 }
 
 }  // namespace medusa
@@ -427,31 +936,89 @@ namespace {
 
 using namespace medusa;
 
-constexpr size_t kCounterBytes = 256;
+constexpr size_t kCounterBytes = 256;   // workspace header (alignment only)
 
 struct LmGrid {
-  int rows_per_wg;
-  int G;
+  bool diag;       // row-diagonal kernel (B <= 2)
+  int nst;         // 512-element steps per row
+  int rows_per_wave;
+  bool stream;     // streamed kernel (A planes in LDS) or the split-K kernel
+  int rows_per_wg; // split-K kernel
+  int tpw;         // streamed kernel: 16-row tiles per wave
+  int G;           // workgroups per head
+  int lists;       // published top-k lists per head (one per wave, or per workgroup for split-K)
+  size_t lds;      // dynamic LDS of the streamed kernel
 };
 
-// About four resident workgroups per CU over the whole grid; rows per
-// workgroup a multiple of the 16-row tile.
-LmGrid lm_grid(int V, int K) {
+constexpr size_t kStreamLdsMax = 64 * 1024;
+constexpr int kMaxWavesPerSimd = 8;
+
+size_t stream_lds(int B, int H, int topk) {
+  return (static_cast<size_t>(2 * B) * H * 2 + 15) / 16 * 16 +
+         static_cast<size_t>(kHeadsWaves) * B * topk * 8 + static_cast<size_t>(kHeadsWaves) * B * 4;
+}
+
+// Grid of the lm_head kernel for `wps` resident waves per SIMD: sized so that
+// every wave is resident at once (one round, no tail).  The launch passes the
+// kernel's actual occupancy; workspace sizes use kMaxWavesPerSimd, an upper
+// bound on G.
+LmGrid lm_grid(int dtype, int B, int H, int V, int K, int topk, int wps) {
+  LmGrid lg{};
+  lg.nst = (H + 511) / 512;
+  lg.diag = dtype == MEDUSA_BF16 && B <= 2 && lg.nst <= 16;
+  if (lg.diag) {
+    const long long waves = 256LL * 4 * wps;
+    long long wph = waves / K;
+    if (wph < 1) wph = 1;
+    long long rpw = (V + wph - 1) / wph;
+    const long long min_rpw = (V + kHeadsWaves * 1024LL - 1) / (kHeadsWaves * 1024LL);
+    if (rpw < min_rpw) rpw = min_rpw;
+    lg.rows_per_wave = static_cast<int>(rpw);
+    lg.G = static_cast<int>((V + kHeadsWaves * rpw - 1) / (kHeadsWaves * rpw));
+    lg.lists = lg.G * kHeadsWaves;
+    return lg;
+  }
+  lg.lds = stream_lds(B, H, topk);
+  lg.stream = dtype == MEDUSA_BF16 && lg.lds <= kStreamLdsMax;
+  if (lg.stream) {
+    const long long tiles = (V + 15) / 16;
+    const long long waves_target = 256LL * 4 * wps;
+    long long tpw = (tiles * K + waves_target - 1) / waves_target;
+    if (tpw < 1) tpw = 1;
+    const long long min_tpw = (tiles + kHeadsWaves * 1024LL - 1) / (kHeadsWaves * 1024LL);
+    if (tpw < min_tpw) tpw = min_tpw;
+    lg.tpw = static_cast<int>(tpw);
+    lg.G = static_cast<int>((tiles + kHeadsWaves * tpw - 1) / (kHeadsWaves * tpw));
+    lg.lists = lg.G * kHeadsWaves;
+    return lg;
+  }
+  // split-K kernel: about four resident workgroups per CU over the grid
   const int target = 1024;
   int g0 = (target + K - 1) / K;
   if (g0 < 1) g0 = 1;
   int rows = (V + g0 - 1) / g0;
   rows = (rows + 15) / 16 * 16;
   if (rows < 16) rows = 16;
-  LmGrid lg;
   lg.rows_per_wg = rows;
   lg.G = (V + rows - 1) / rows;
+  lg.lists = lg.G;
   return lg;
 }
 
-size_t cand_bytes(int B, int V, int K, int topk) {
-  const LmGrid lg = lm_grid(V, K);
-  return medusa_host::round_up(static_cast<size_t>(K) * B * lg.G * topk * 4, 256);
+// Resident workgroups (= waves per SIMD for 4-wave workgroups) of a kernel,
+// queried once per kernel and cached.
+template <typename F>
+int occupancy_wps(F kernel, size_t dyn_lds) {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kHeadsThreads, dyn_lds) != hipSuccess ||
+      blocks < 1)
+    blocks = 1;
+  return blocks > kMaxWavesPerSimd ? kMaxWavesPerSimd : blocks;
+}
+
+size_t cand_bytes(int dtype, int B, int H, int V, int K, int topk) {
+  const LmGrid lg = lm_grid(dtype, B, H, V, K, topk, kMaxWavesPerSimd);
+  return medusa_host::round_up(static_cast<size_t>(K) * B * lg.lists * topk * 4, 256);
 }
 
 size_t r_bytes(int B, int K, int H) {
@@ -490,34 +1057,88 @@ int launch_resblock(int dtype, int B, int H, int K, const void* hidden, const vo
 
 int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float* r, const void* w_lm,
                    int32_t* ids, float* vals, float* logits, void* ws, hipStream_t st) {
-  const LmGrid lg = lm_grid(V, K);
+  LmGrid lg = lm_grid(dtype, B, H, V, K, topk, kMaxWavesPerSimd);
   char* base = static_cast<char*>(ws);
-  unsigned* counters = reinterpret_cast<unsigned*>(base);
-  const size_t cb = cand_bytes(B, V, K, topk);
+  const size_t cb = cand_bytes(dtype, B, H, V, K, topk);
   float* cand_v = reinterpret_cast<float*>(base + kCounterBytes);
   int32_t* cand_i = reinterpret_cast<int32_t*>(base + kCounterBytes + cb);
-  dim3 grid(lg.G, K);
-  if (dtype == MEDUSA_BF16) {
+  if (lg.diag) {
+    const uint16_t* w = static_cast<const uint16_t*>(w_lm);
+#define MEDUSA_DIAG_LAUNCH(NS, NB)                                                                            \
+  do {                                                                                                        \
+    static const int wps = occupancy_wps(lm_topk_diag_kernel<NS, NB>, 0);                                     \
+    lg = lm_grid(dtype, B, H, V, K, topk, wps);                                                               \
+    hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, V, K,  \
+                       topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);      \
+  } while (0)
+    const int ns = diag_nstmax(lg.nst);
+    if (ns == 4) {
+      if (B == 1) MEDUSA_DIAG_LAUNCH(4, 1); else MEDUSA_DIAG_LAUNCH(4, 2);
+    } else if (ns == 8) {
+      if (B == 1) MEDUSA_DIAG_LAUNCH(8, 1); else MEDUSA_DIAG_LAUNCH(8, 2);
+    } else if (ns == 13) {
+      if (B == 1) MEDUSA_DIAG_LAUNCH(13, 1); else MEDUSA_DIAG_LAUNCH(13, 2);
+    } else {
+      if (B == 1) MEDUSA_DIAG_LAUNCH(16, 1); else MEDUSA_DIAG_LAUNCH(16, 2);
+    }
+#undef MEDUSA_DIAG_LAUNCH
+  } else if (lg.stream) {
+    const uint16_t* w = static_cast<const uint16_t*>(w_lm);
+    if (B <= 8) {
+      const int wps = occupancy_wps(lm_topk_stream_kernel<1>, lg.lds);
+      lg = lm_grid(dtype, B, H, V, K, topk, wps);
+      hipLaunchKernelGGL((lm_topk_stream_kernel<1>), dim3(lg.G, K), dim3(kHeadsThreads), lg.lds, st, B, H, V, K,
+                         topk, lg.tpw, lg.G, r, w, logits, ids, vals, cand_v, cand_i);
+    } else {
+      const int wps = occupancy_wps(lm_topk_stream_kernel<2>, lg.lds);
+      lg = lm_grid(dtype, B, H, V, K, topk, wps);
+      hipLaunchKernelGGL((lm_topk_stream_kernel<2>), dim3(lg.G, K), dim3(kHeadsThreads), lg.lds, st, B, H, V, K,
+                         topk, lg.tpw, lg.G, r, w, logits, ids, vals, cand_v, cand_i);
+    }
+  } else if (dtype == MEDUSA_BF16) {
+    dim3 grid(lg.G, K);
     if (B <= 8)
       hipLaunchKernelGGL((lm_topk_kernel<true, 1>), grid, dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
-                         lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i, counters);
+                         lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
     else
       hipLaunchKernelGGL((lm_topk_kernel<true, 2>), grid, dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
-                         lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i, counters);
+                         lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
   } else {
+    dim3 grid(lg.G, K);
     hipLaunchKernelGGL((lm_topk_kernel<false, 1>), grid, dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
-                       lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i, counters);
+                       lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
   }
-  return medusa_host::hip_check("medusa_lm_head_topk launch");
+  int rc = medusa_host::hip_check("medusa_lm_head_topk launch");
+  if (rc != MEDUSA_OK) return rc;
+  const int per = (lg.lists * topk + kMergeThreads - 1) / kMergeThreads;
+  const dim3 mg(B, K), mb(kMergeThreads);
+  if (per <= 1)
+    hipLaunchKernelGGL(topk_merge_kernel<1>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
+  else if (per <= 2)
+    hipLaunchKernelGGL(topk_merge_kernel<2>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
+  else if (per <= 4)
+    hipLaunchKernelGGL(topk_merge_kernel<4>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
+  else if (per <= 8)
+    hipLaunchKernelGGL(topk_merge_kernel<8>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
+  else if (per <= 16)
+    hipLaunchKernelGGL(topk_merge_kernel<16>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
+  else if (per <= kMergeMaxKeys)
+    hipLaunchKernelGGL(topk_merge_kernel<kMergeMaxKeys>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids,
+                       vals);
+  else
+    hipLaunchKernelGGL(topk_merge_rounds_kernel, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
+  return medusa_host::hip_check("medusa_lm_head_topk merge launch");
 }
 
-size_t lm_ws_bytes(int B, int V, int K, int topk) { return kCounterBytes + 2 * cand_bytes(B, V, K, topk); }
+size_t lm_ws_bytes(int dtype, int B, int H, int V, int K, int topk) {
+  return kCounterBytes + 2 * cand_bytes(dtype, B, H, V, K, topk);
+}
 
 }  // namespace
 
 extern "C" size_t medusa_heads_workspace(int dtype, int B, int H, int V, int K, int topk) {
   if (check_heads_shape("medusa_heads_workspace", dtype, B, H, V, K, topk) != MEDUSA_OK) return 0;
-  return lm_ws_bytes(B, V, K, topk) + r_bytes(B, K, H);
+  return lm_ws_bytes(dtype, B, H, V, K, topk) + r_bytes(B, K, H);
 }
 
 extern "C" int medusa_resblock(int dtype, int B, int H, int K, const void* hidden, const void* w1,
@@ -542,8 +1163,8 @@ extern "C" int medusa_lm_head_topk(int dtype, int B, int H, int V, int K, int to
   MEDUSA_REQUIRE_PTR(topk_logits);
   MEDUSA_REQUIRE_PTR(ws);
   if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
-  MEDUSA_REQUIRE(ws_bytes >= lm_ws_bytes(B, V, K, topk), MEDUSA_ERR_WORKSPACE,
-                 "%s: workspace %zu < %zu bytes", __func__, ws_bytes, lm_ws_bytes(B, V, K, topk));
+  MEDUSA_REQUIRE(ws_bytes >= lm_ws_bytes(dtype, B, H, V, K, topk), MEDUSA_ERR_WORKSPACE,
+                 "%s: workspace %zu < %zu bytes", __func__, ws_bytes, lm_ws_bytes(dtype, B, H, V, K, topk));
   return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws,
                         static_cast<hipStream_t>(stream));
 }
@@ -563,12 +1184,12 @@ extern "C" int medusa_heads(int dtype, int B, int H, int V, int K, int topk, con
   MEDUSA_REQUIRE_PTR(ws);
   if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
   if (r_or_null != nullptr) MEDUSA_REQUIRE_PTR(r_or_null);
-  const size_t need = lm_ws_bytes(B, V, K, topk) + r_bytes(B, K, H);
+  const size_t need = lm_ws_bytes(dtype, B, H, V, K, topk) + r_bytes(B, K, H);
   MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
                  ws_bytes, need);
   float* r = r_or_null != nullptr
                  ? r_or_null
-                 : reinterpret_cast<float*>(static_cast<char*>(ws) + lm_ws_bytes(B, V, K, topk));
+                 : reinterpret_cast<float*>(static_cast<char*>(ws) + lm_ws_bytes(dtype, B, H, V, K, topk));
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = launch_resblock(dtype, B, H, K, hidden, w1, b1, r, st);
   if (rc != MEDUSA_OK) return rc;
