@@ -1,29 +1,28 @@
 // Candidate tree from a medusa_choices spec, in one workgroup.
 //
-// Thread e owns spec entry e (and later node e).  The spec is validated in
-// the documented order with one atomicMin over (phase, entry, kind) keys, nodes
-// are ordered by counting the entries that sort before each one (length,
-// then lexicographic), parents are found by matching the tuple minus its
-// last rank, and every output is written from LDS.  Work is O(N^2 K) with
-// N <= 255: a few microseconds of integer work, bound by launch latency.
+// Thread e owns spec entry e.  Each valid tuple (r1..rl) is packed into one
+// 64-bit key: the length in bits 60..63, then r_m + 1 in 7-bit fields from
+// bit 60 downwards, zeros after the last rank.  Unsigned key order is then
+// the node order (length, then lexicographic), equal keys are equal tuples,
+// and a key of length m is a proper prefix of another exactly when it is
+// shorter and agrees on the top 4 + 7m bits below the length field.  One
+// pass of every entry over all keys yields its duplicate flag, which prefix
+// lengths are present, its node rank and its parent's entry.  The spec is
+// validated in the documented order with one atomicMin over (phase, entry,
+// kind) keys.  Work is O(N) per thread for N <= 255 entries.
 #include "common.hpp"
 
 namespace medusa {
 
 constexpr int kTreeThreads = 256;
 constexpr int kMaxDepth = kMaxHeads;
+constexpr int kRankBits = 7;
+constexpr uint64_t kRanksMask = (1ull << 60) - 1;
 
-__device__ __forceinline__ bool tuple_less(const int8_t* a, int la, const int8_t* b, int lb) {
-  if (la != lb) return la < lb;
-  for (int m = 0; m < la; ++m)
-    if (a[m] != b[m]) return a[m] < b[m];
-  return false;
-}
-
-__device__ __forceinline__ bool tuple_eq_prefix(const int8_t* a, const int8_t* b, int len) {
-  for (int m = 0; m < len; ++m)
-    if (a[m] != b[m]) return false;
-  return true;
+// bits of the first m ranks of a key (m <= 8)
+__device__ __forceinline__ uint64_t rank_field_mask(int m) {
+  const int sh = 60 - kRankBits * m;
+  return (kRanksMask >> sh) << sh;
 }
 
 __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
@@ -33,169 +32,245 @@ __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
     int32_t* __restrict__ tree_indices, int32_t* __restrict__ parent_out, int32_t* __restrict__ depth_out,
     int32_t* __restrict__ position_ids, uint8_t* __restrict__ tree_mask, int32_t* __restrict__ retrieve,
     int32_t* __restrict__ num_paths, int32_t* __restrict__ status) {
-  __shared__ int8_t tup[kMaxNodes][kMaxDepth];   // by entry
-  __shared__ int8_t len[kMaxNodes];
-  __shared__ int16_t node_entry[kMaxNodes];      // node -> entry (node 0 = root = -1)
-  __shared__ int16_t par[kMaxNodes];
+  __shared__ uint64_t skey[kMaxNodes];           // by entry
+  __shared__ int16_t node_of[kMaxNodes];         // entry -> node
+  __shared__ int16_t par[kMaxNodes];             // by node
   __shared__ int8_t dep[kMaxNodes];
   __shared__ uint8_t has_child[kMaxNodes];
-  __shared__ int16_t path_of[kMaxNodes];
+  __shared__ int16_t leaf_at[kMaxNodes];         // path -> leaf node
   __shared__ uint64_t anc[kMaxNodes][kMaxNodes / 64];
+  __shared__ int wave_leaves[kTreeThreads / kWave];
   __shared__ int err_key;
-  __shared__ int n_leaves;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int T = N + 1;
   const int D = K + 1;
-  if (tid == 0) { err_key = 0x7fffffff; n_leaves = 0; }
-  if (tid < kMaxNodes) has_child[tid] = 0;
-  __syncthreads();
+  const int NONE = 0x7fffffff;
 
-  // phase 0: per-entry format (padding, then empty, then rank)
+  // inputs first, all independent loads: the entry's row, the batch's root
+  // tokens and prefix lengths (clamped indices, masked at use)
+  int row[kMaxDepth];
+  const int e_row = min(tid, max(N - 1, 0));
+#pragma unroll
+  for (int m = 0; m < kMaxDepth; ++m) row[m] = N > 0 ? choices[static_cast<size_t>(e_row) * K + min(m, K - 1)] : -1;
+  int plen[kMaxBatch];
+  int root[kMaxBatch];
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) {
+    plen[b] = prefix_len[min(b, B - 1)];
+    root[b] = root_token[min(b, B - 1)];
+  }
+  if (tid == 0) err_key = NONE;
+  has_child[tid] = 0;
+
+  // phase 0: per-entry format (padding, then empty, then rank) and the key
+  const bool is_entry = tid < N;
+  int l = 0;
+  uint64_t key = 0;
   int my_err = 0;
-  if (tid < N) {
-    int row[kMaxDepth];
-    for (int m = 0; m < K; ++m) row[m] = choices[static_cast<size_t>(tid) * K + m];
-    int n = K;
-    while (n > 0 && row[n - 1] == -1) --n;
-    bool pad = false, rank = false;
-    for (int m = 0; m < n; ++m) {
-      if (row[m] == -1) pad = true;
-      else if (row[m] < 0 || row[m] >= topk) rank = true;
-    }
-    if (pad) my_err = MEDUSA_SPEC_PADDING;
-    else if (n == 0) my_err = MEDUSA_SPEC_EMPTY;
-    else if (rank) my_err = MEDUSA_SPEC_RANK;
-    for (int m = 0; m < kMaxDepth; ++m) tup[tid][m] = static_cast<int8_t>(m < n ? row[m] : -1);
-    len[tid] = static_cast<int8_t>(n);
-    if (my_err) atomicMin(&err_key, (0 << 24) | (tid << 8) | my_err);
-  }
-  __syncthreads();
-  if (err_key == 0x7fffffff && tid < N) {
-    // phase 1: duplicates (first entry equal to an earlier one)
-    const int l = len[tid];
-    for (int e = 0; e < tid; ++e) {
-      if (len[e] == l && tuple_eq_prefix(tup[e], tup[tid], l)) {
-        atomicMin(&err_key, (1 << 24) | (tid << 8) | MEDUSA_SPEC_DUPLICATE);
-        break;
+  {
+    int n = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxDepth; ++m)
+      if (m < K && row[m] != -1) n = m + 1;  // length after trimming trailing -1
+    bool pad = false, bad = false;
+#pragma unroll
+    for (int m = 0; m < kMaxDepth; ++m) {
+      if (m < n) {
+        if (row[m] == -1) pad = true;
+        else if (row[m] < 0 || row[m] >= topk) bad = true;
+        else key |= static_cast<uint64_t>(row[m] + 1) << (60 - kRankBits * (m + 1));
       }
     }
-    // phase 2: every proper prefix must be an entry
-    for (int m = 1; m < l; ++m) {
-      bool found = false;
-      for (int e = 0; e < N && !found; ++e) found = len[e] == m && tuple_eq_prefix(tup[e], tup[tid], m);
-      if (!found) {
-        atomicMin(&err_key, (2 << 24) | (tid << 8) | MEDUSA_SPEC_PREFIX);
-        break;
-      }
-    }
+    l = n;
+    key |= static_cast<uint64_t>(n) << 60;
+    my_err = pad ? MEDUSA_SPEC_PADDING : (n == 0 ? MEDUSA_SPEC_EMPTY : (bad ? MEDUSA_SPEC_RANK : 0));
   }
+  // the entry's candidate token for every sequence (in bounds even when invalid)
+  int tok[kMaxBatch];
+  {
+    const int dd = min(max(l, 1), K) - 1;
+    int last = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxDepth; ++m)
+      if (m == l - 1) last = row[m];
+    last = min(max(last, 0), topk - 1);
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b)
+      tok[b] = topk_ids[(static_cast<size_t>(min(b, B - 1)) * K + dd) * topk + last];
+  }
+  if (is_entry) skey[tid] = key;
   __syncthreads();
+  if (is_entry && my_err) atomicMin(&err_key, (0 << 24) | (tid << 8) | my_err);
 
-  bool ok = err_key == 0x7fffffff;
+  // one pass over every key: duplicates before me, present prefix lengths,
+  // my rank in node order, my parent's entry
+  bool dup = false;
+  uint32_t found = 0;
+  int rank = 0, pe = -1;
+  if (is_entry) {
+    int e = 0;
+    for (; e + 4 <= N; e += 4) {
+      uint64_t ke[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ke[q] = skey[e + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int le = static_cast<int>(ke[q] >> 60);
+        const bool pre = le >= 1 && le < l && ((ke[q] ^ key) & rank_field_mask(le)) == 0;
+        dup |= (e + q < tid) && ke[q] == key;
+        found |= pre ? (1u << le) : 0u;
+        pe = (pre && le == l - 1) ? e + q : pe;
+        rank += ke[q] < key ? 1 : 0;
+      }
+    }
+    for (; e < N; ++e) {
+      const uint64_t k1 = skey[e];
+      const int le = static_cast<int>(k1 >> 60);
+      const bool pre = le >= 1 && le < l && ((k1 ^ key) & rank_field_mask(le)) == 0;
+      dup |= (e < tid) && k1 == key;
+      found |= pre ? (1u << le) : 0u;
+      pe = (pre && le == l - 1) ? e : pe;
+      rank += k1 < key ? 1 : 0;
+    }
+    const uint32_t want = (1u << l) - 2u;  // lengths 1 .. l-1
+    if (dup) atomicMin(&err_key, (1 << 24) | (tid << 8) | MEDUSA_SPEC_DUPLICATE);
+    else if ((found & want) != want) atomicMin(&err_key, (2 << 24) | (tid << 8) | MEDUSA_SPEC_PREFIX);
+    node_of[tid] = static_cast<int16_t>(rank + 1);
+  }
+  __syncthreads();
+  bool ok = err_key == NONE;
+
+  // structure in LDS first; global outputs are written once, at the end,
+  // after the leaf count is checked against p_max
+  int last = 0;
+#pragma unroll
+  for (int m = 0; m < kMaxDepth; ++m)
+    if (m == l - 1) last = row[m];
+  const int node = rank + 1;
   if (ok) {
-    // node order: rank among entries by (length, lexicographic)
-    if (tid < N) {
-      int rank = 0;
-      for (int e = 0; e < N; ++e) rank += tuple_less(tup[e], len[e], tup[tid], len[tid]) ? 1 : 0;
-      node_entry[rank + 1] = static_cast<int16_t>(tid);
+    if (is_entry) {
+      const int pnode = l == 1 ? 0 : node_of[pe];
+      par[node] = static_cast<int16_t>(pnode);
+      dep[node] = static_cast<int8_t>(l);
+      has_child[pnode] = 1;
     }
-    if (tid == 0) { node_entry[0] = -1; par[0] = -1; dep[0] = 0; }
-    __syncthreads();
-    // parent of node i: the node whose tuple is node i's minus its last rank
-    if (tid >= 1 && tid < T) {
-      const int e = node_entry[tid];
-      const int l = len[e];
-      dep[tid] = static_cast<int8_t>(l);
-      int p = 0;
-      if (l > 1) {
-        for (int q = 1; q < T; ++q) {
-          const int f = node_entry[q];
-          if (len[f] == l - 1 && tuple_eq_prefix(tup[f], tup[e], l - 1)) { p = q; break; }
-        }
-      }
-      par[tid] = static_cast<int16_t>(p);
-      has_child[p] = 1;
-    }
-    __syncthreads();
-    // ancestor bitmasks (walk parents; depth <= K)
-    if (tid < T) {
-      uint64_t w[kMaxNodes / 64] = {0, 0, 0, 0};
-      int a = tid;
-      while (a >= 0) {
-        w[a >> 6] |= 1ull << (a & 63);
-        a = par[a];
-      }
-      for (int q = 0; q < kMaxNodes / 64; ++q) anc[tid][q] = w[q];
-    }
-    // leaf order: a leaf's path index is the number of leaves before it
-    if (tid < T && !has_child[tid]) {
-      int before = 0;
-      for (int q = 0; q < tid; ++q) before += has_child[q] ? 0 : 1;
-      path_of[tid] = static_cast<int16_t>(before);
-      atomicAdd(&n_leaves, 1);
-    }
-    __syncthreads();
-    if (n_leaves > p_max) {
-      if (tid == 0) err_key = (3 << 24) | ((n_leaves & 0xffff) << 8) | MEDUSA_SPEC_TOO_MANY_PATHS;
-      ok = false;
+    if (tid == 0) {
+      par[0] = -1;
+      dep[0] = 0;
     }
   }
   __syncthreads();
 
-  if (!ok) {
-    // the root alone: every later stage stays in bounds and accepts nothing
-    if (tid < T) {
-      par[tid] = -1;
-      dep[tid] = 0;
-      for (int q = 0; q < kMaxNodes / 64; ++q) anc[tid][q] = 0;
-      anc[tid][tid >> 6] = 1ull << (tid & 63);
-      has_child[tid] = 1;
-    }
-    __syncthreads();
-    if (tid == 0) { has_child[0] = 0; path_of[0] = 0; n_leaves = 1; }
-    __syncthreads();
-  }
-
-  // per-node outputs
-  if (tid < T) {
-    const int d = dep[tid];
-    int ti = 0;
-    if (ok && tid > 0) {
-      const int e = node_entry[tid];
-      ti = 1 + (d - 1) * topk + tup[e][d - 1];
-    }
-    tree_indices[tid] = ti;
-    parent_out[tid] = par[tid];
-    depth_out[tid] = d;
-    for (int b = 0; b < B; ++b) {
-      const int tok = ti == 0 ? root_token[b]
-                              : topk_ids[(static_cast<size_t>(b) * K + (d - 1)) * topk + (ti - 1 - (d - 1) * topk)];
-      tree_candidates[static_cast<size_t>(b) * T + tid] = tok;
-      position_ids[static_cast<size_t>(b) * T + tid] = prefix_len[b] + d;
-    }
-  }
-  // mask rows, written as bytes over the flat [T][T] array
-  for (int x = tid; x < T * T; x += kTreeThreads) {
-    const int i = x / T, jj = x - i * T;
-    tree_mask[x] = static_cast<uint8_t>((anc[i][jj >> 6] >> (jj & 63)) & 1ull);
-  }
-  // retrieve: rows >= num_paths are all -1
-  for (int x = tid; x < p_max * D; x += kTreeThreads) retrieve[x] = -1;
-  __syncthreads();
-  if (tid < T && !has_child[tid]) {
-    const int p = path_of[tid];
+  // ancestors (a walk of at most K parents) and leaf numbering by ballot;
+  // an invalid spec leaves the root alone (every later stage stays in
+  // bounds and accepts nothing)
+  const bool is_node = tid < T;
+  if (is_node) {
+    uint64_t w[kMaxNodes / 64] = {0, 0, 0, 0};
     int a = tid;
-    while (a >= 0) {
-      retrieve[static_cast<size_t>(p) * D + dep[a]] = a;
+    while (ok && a >= 0) {
+      w[a >> 6] |= 1ull << (a & 63);
       a = par[a];
     }
+    if (!ok) w[tid >> 6] = 1ull << (tid & 63);
+#pragma unroll
+    for (int q = 0; q < kMaxNodes / 64; ++q) anc[tid][q] = w[q];
+  }
+  const bool leaf = is_node && (ok ? !has_child[tid] : tid == 0);
+  const uint64_t lm = ballot(leaf);
+  if (lane == 0) wave_leaves[wave] = __popcll(lm);
+  __syncthreads();
+  int before = __popcll(lm & ((1ull << lane) - 1));
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kTreeThreads / kWave; ++w) {
+    before += w < wave ? wave_leaves[w] : 0;
+    total += wave_leaves[w];
+  }
+  if (ok && total > p_max) {
+    // too many paths: the root alone as well
+    ok = false;
+    if (tid == 0) err_key = (3 << 24) | ((total & 0xffff) << 8) | MEDUSA_SPEC_TOO_MANY_PATHS;
+    if (is_node) {
+#pragma unroll
+      for (int q = 0; q < kMaxNodes / 64; ++q) anc[tid][q] = q == (tid >> 6) ? 1ull << (tid & 63) : 0;
+    }
+    total = 1;
+    if (tid == 0) leaf_at[0] = 0;
+  } else if (leaf) {
+    leaf_at[before] = static_cast<int16_t>(tid);
+  }
+  if (!ok && is_node) {
+    par[tid] = -1;
+    dep[tid] = 0;
+  }
+  __syncthreads();
+
+  // per-node outputs: the entry's thread writes its node, thread 0 the root
+  // (or every thread its own node when only the root is kept)
+  if (ok && is_entry) {
+    tree_indices[node] = 1 + (l - 1) * topk + last;
+    parent_out[node] = par[node];
+    depth_out[node] = l;
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      if (b < B) {
+        tree_candidates[static_cast<size_t>(b) * T + node] = tok[b];
+        position_ids[static_cast<size_t>(b) * T + node] = plen[b] + l;
+      }
+    }
+  }
+  if ((ok && tid == 0) || (!ok && is_node)) {
+    tree_indices[tid] = 0;
+    parent_out[tid] = -1;
+    depth_out[tid] = 0;
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      if (b < B) {
+        tree_candidates[static_cast<size_t>(b) * T + tid] = root[b];
+        position_ids[static_cast<size_t>(b) * T + tid] = plen[b];
+      }
+    }
+  }
+  // mask rows over the flat [T][T] byte array, four bytes per store
+  const int nbytes = T * T;
+  uint32_t* mask_words = reinterpret_cast<uint32_t*>(tree_mask);
+  for (int w = tid; w * 4 < nbytes; w += kTreeThreads) {
+    uint32_t word = 0;
+    int i = (4 * w) / T, jj = 4 * w - i * T;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (4 * w + c < nbytes) word |= static_cast<uint32_t>((anc[i][jj >> 6] >> (jj & 63)) & 1ull) << (8 * c);
+      if (++jj == T) { jj = 0; ++i; }
+    }
+    if (4 * w + 4 <= nbytes) {
+      mask_words[w] = word;
+    } else {
+      for (int c = 0; 4 * w + c < nbytes; ++c) tree_mask[4 * w + c] = static_cast<uint8_t>(word >> (8 * c));
+    }
+  }
+  // retrieve[p][j]: the depth-j node on leaf p's path; -1 past the leaf
+  // and on rows >= num_paths
+  for (int x = tid; x < p_max * D; x += kTreeThreads) {
+    const int p = x / D, j = x - p * D;
+    int v = -1;
+    if (p < total) {
+      int a = leaf_at[p];
+      const int da = dep[a];
+      if (j <= da) {
+        for (int s2 = da; s2 > j; --s2) a = par[a];
+        v = a;
+      }
+    }
+    retrieve[x] = v;
   }
   if (tid == 0) {
-    *num_paths = n_leaves;
-    const int key = err_key;
-    status[0] = key == 0x7fffffff ? MEDUSA_SPEC_OK : (key & 0xff);
-    status[1] = key == 0x7fffffff ? -1 : ((key >> 8) & 0xffff);
+    *num_paths = total;
+    const int k2 = err_key;
+    status[0] = k2 == NONE ? MEDUSA_SPEC_OK : (k2 & 0xff);
+    status[1] = k2 == NONE ? -1 : ((k2 >> 8) & 0xffff);
   }
 }
 
