@@ -2,16 +2,21 @@
 // ancestor-only mask among the tree's own keys.
 //
 // bf16 path.  The key range [0, L+T) of each (sequence, head) is cut into
-// splits of kSplit keys (the last split takes the remainder), one workgroup
-// each, so a 32-head layer at L = 2048 fills the chip.  A workgroup holds up
-// to 64 queries (four waves of 16) and walks its split in 64-key chunks
-// staged through LDS: K row-major, V transposed (d-major) on the way in.
-// Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_16x16x32_bf16: a lane then holds four consecutive keys of one
-// query, which is exactly the B-operand layout P^T needs for O^T += V^T P^T,
-// so probabilities never leave registers.  Online softmax in base 2, fp32
-// accumulators.  Each split writes (O unnormalised, m, l) and a second
-// kernel merges the splits (log-sum-exp).
+// num_splits balanced splits, one workgroup each.  A workgroup holds up to
+// 64 queries (four waves of 16) and walks its split in 32-key chunks.  K and
+// V chunks go from HBM straight into an LDS ring of three stages with
+// 16-byte direct-to-LDS loads (two chunks in flight while one is used), so
+// the stream needs no registers and no LDS stores; rows are kept whole and
+// the 16-byte pieces within a row are XOR-swizzled by row so the MFMA
+// operand reads are free of bank conflicts.  Scores are computed
+// transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: a lane then holds
+// four consecutive keys of one query, which is the B-operand layout P^T
+// needs for O^T += V^T P^T, so probabilities never leave registers.  The
+// V^T operand is read from the row-major V chunk with the LDS transpose
+// read (ds_read_b64_tr_b16).  Online softmax in base 2, fp32 accumulators.
+// Each split writes (O unnormalised, m, l) and a second kernel merges the
+// splits (log-sum-exp).  Every global load is unconditional with a clamped
+// index (masked at use), so no load waits behind a branch.
 //
 // f32 path: one wave per (sequence, head, query), online softmax over
 // 64-key chunks on the VALU.
@@ -21,10 +26,12 @@ namespace medusa {
 
 constexpr int kAttnThreads = 256;
 constexpr int kQBlock = 64;        // queries per workgroup
-constexpr int kChunk = 64;         // keys per LDS chunk
-constexpr int kSplit = 256;        // keys per split
+constexpr int kChunk = 32;         // keys per LDS stage
+constexpr int kStages = 4;         // LDS ring depth: kStages - 1 chunks in flight
+constexpr int kSplit = 128;        // target keys per split
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Splits of a (sequence, head): about kSplit keys each, whole chunks.
 __host__ __device__ inline int num_splits(int total_keys) {
   const int s = total_keys / kSplit;
   return s < 1 ? 1 : s;
@@ -32,20 +39,215 @@ __host__ __device__ inline int num_splits(int total_keys) {
 
 __device__ __forceinline__ u32x4 ld16g(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define LDSB(x) ((MEDUSA_LDS uint8_t*)(x))
+
+// s_waitcnt: at most N vector-memory operations outstanding (N < 64) and
+// no LDS operation outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// 16-byte direct load from global memory into LDS: lane l's piece lands at
+// lds + 16*l.  Issued from inline assembly so that the compiler does not
+// track it: its own bookkeeping cannot tell the ring stages apart and would
+// wait for every chunk in flight before any LDS read.  The instruction
+// writes no register; completion is counted by vmcnt, and the kernel waits
+// for it explicitly (wait_vm) before the barrier that publishes a chunk.
+__device__ __forceinline__ void lds_dma16(const void* gptr, MEDUSA_LDS void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+}
+
+template <int D>
+struct AttnLayout {
+  static constexpr int PIECES = D / 8;                       // 16-byte pieces per row
+  static constexpr int ROWB = D * 2;                         // bytes per row
+  static constexpr int TILE = kChunk * ROWB;                 // bytes of K (or V) per chunk
+  static constexpr int LOADS = TILE / (kAttnThreads * 16);   // direct loads per thread per tensor
+  static constexpr int SH = D == 128 ? 0 : 1;                // rows sharing a bank base
+  // LDS slot of piece pc of row `row`
+  __device__ static int k_slot(int row, int pc) { return pc ^ ((row >> SH) & (PIECES - 1)); }
+  __device__ static int v_slot(int row, int pc) { return pc ^ (2 * ((row >> SH) & (PIECES / 2 - 1))); }
+};
+
+// Issue the direct loads of chunk [c0, c0 + kChunk) into one ring stage:
+// lane l of wave-instruction blk fills LDS slot blk*64 + l, i.e. (row,
+// slot), with the piece that slot holds under the swizzle (an involution).
+// Rows past k_hi repeat row k_hi - 1: finite data whose scores are masked.
+template <int D>
+__device__ __forceinline__ void attn_issue(const uint16_t* kbase, const uint16_t* vbase, int c0, int k_hi, int lane,
+                                           int wave, uint8_t* kst, uint8_t* vst) {
+  using Lay = AttnLayout<D>;
+#pragma unroll
+  for (int i = 0; i < Lay::LOADS; ++i) {
+    const int blk = i * (kAttnThreads / kWave) + wave;
+    const int sidx = blk * kWave + lane;
+    const int row = sidx / Lay::PIECES, slot = sidx % Lay::PIECES;
+    const size_t key = static_cast<size_t>(min(c0 + row, k_hi - 1));
+    lds_dma16(kbase + key * D + Lay::k_slot(row, slot) * 8, LDSB(kst) + blk * 1024);
+    lds_dma16(vbase + key * D + Lay::v_slot(row, slot) * 8, LDSB(vst) + blk * 1024);
+  }
+}
+
+// Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Allowed keys of one 32-key chunk for this lane's query, bit p = key c0 + p:
+// inside the split, and either in the prefix or an ancestor (or self) in
+// the tree.  mb: the query's ancestor words (LDS), bit j = tree key L + j.
+__device__ __forceinline__ uint32_t chunk_allowed(int c0, int k_hi, int L, const MEDUSA_LDS uint64_t* mb) {
+  const int nvalid = min(max(k_hi - c0, 0), 32);
+  uint32_t allow = nvalid == 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+  if (c0 + kChunk > L) {   // the chunk reaches the tree keys (uniform)
+    const int j0 = c0 - L;
+    uint32_t tree;
+    uint32_t prefix = 0;
+    if (j0 >= 0) {
+      const int w0 = j0 >> 6, sh = j0 & 63;
+      const uint64_t lo = mb[w0] >> sh;
+      const uint64_t hi = (sh != 0 && w0 < 3) ? (mb[w0 + 1] << (64 - sh)) : 0ull;
+      tree = static_cast<uint32_t>(lo | hi);
+    } else {
+      tree = static_cast<uint32_t>(mb[0] << (-j0));   // -j0 in (0, 32)
+      prefix = (1u << (-j0)) - 1u;
+    }
+    allow &= prefix | tree;
+  }
+  return allow;
+}
+
+// One chunk [c0, c0 + kChunk) from a ring stage: scores, online softmax, PV.
+// mrow: this lane's query row of ancestor words (LDS).  The running
+// reference m_run is raised only when some lane's chunk maximum exceeds it
+// by more than kLazy (log2 units): exponentials then stay below 2^kLazy,
+// and O and l, both taken against the same reference, stay exact.
+constexpr float kLazy = 8.f;
+template <int D>
+__device__ __forceinline__ void attn_chunk(const u32x4 (&qv)[D / 32], f32x4 (&o)[D / 16], float& m_run,
+                                           float& l_part, int c0, int k_hi, int L, int lane, float scale_log2,
+                                           const uint64_t* mrow, const uint8_t* kst, const uint8_t* vst) {
+  using Lay = AttnLayout<D>;
+  constexpr int DT = D / 16, DS = D / 32;
+  const int n = lane & 15, g = lane >> 4;
+  const MEDUSA_LDS uint8_t* Kc = (const MEDUSA_LDS uint8_t*)kst;
+  const MEDUSA_LDS uint8_t* Vc = (const MEDUSA_LDS uint8_t*)vst;
+  const uint32_t allow = chunk_allowed(c0, k_hi, L, (const MEDUSA_LDS uint64_t*)mrow);
+
+  // scores S^T[key = kt*16 + 4g + i][query n]
+  f32x4 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int row = kt * 16 + n;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const u32x4 a = *(const MEDUSA_LDS u32x4*)(Kc + row * Lay::ROWB + Lay::k_slot(row, ds * 4 + g) * 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, qv[ds]), acc, 0, 0, 0);
+    }
+    s[kt] = acc;
+  }
+  const float NEG = -__builtin_huge_valf();
+  float mloc = NEG;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = ((allow >> (kt * 16 + 4 * g + i)) & 1u) ? s[kt][i] * scale_log2 : NEG;
+      s[kt][i] = x;
+      mloc = fmaxf(mloc, x);
+    }
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  if (ballot(mloc > m_run + kLazy) != 0) {   // uniform: raise the reference
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = m_run == NEG ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      o[t][0] *= alpha;
+      o[t][1] *= alpha;
+      o[t][2] *= alpha;
+      o[t][3] *= alpha;
+    }
+    m_run = m_new;
+  }
+  const float ref = m_run == NEG ? 0.f : m_run;
+  float p[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[kt][i] = __builtin_amdgcn_exp2f(s[kt][i] - ref);
+      l_part += p[kt][i];
+    }
+  }
+  // O^T[d][q] += V^T[d][keys] P^T[keys][q]; the k-slots of group g are keys
+  // 4g + (0..3) and 16 + 4g + (0..3).  The transpose read gives lane m of a
+  // 16-lane group element m%4 of the 8 bytes addressed by lane 4c + m/4 of
+  // the group, as component c; so lane (c, qd) addresses row 16r + 4g + c,
+  // columns 16t + 4qd .. +3 of the row-major V chunk.
+  const u32x4 pv = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+  const int vrow = 4 * g + ((lane & 15) >> 2), qd = lane & 3;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    uint32_t w4[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 16 * r + vrow;
+      const int pc = 2 * t + (qd >> 1);
+      const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (MEDUSA_LDS v4s*)(Vc + row * Lay::ROWB + Lay::v_slot(row, pc) * 16 + (qd & 1) * 8));
+      const uint2 u = __builtin_bit_cast(uint2, x);
+      w4[2 * r] = u.x;
+      w4[2 * r + 1] = u.y;
+    }
+    const u32x4 av = {w4[0], w4[1], w4[2], w4[3]};
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                   __builtin_bit_cast(bf16x8, pv), o[t], 0, 0, 0);
+  }
+}
+
+// Wait until at most k (0 <= k <= K) chunks of PER loads each are still in
+// flight for this thread (and no LDS operation); s_waitcnt takes a constant.
+template <int PER, int K>
+__device__ __forceinline__ void wait_chunks(int k) {
+  if constexpr (K == 0) {
+    wait_vm<0>();
+  } else {
+    if (k >= K) wait_vm<PER * K>();
+    else wait_chunks<PER, K - 1>(k);
+  }
+}
+
+// Make chunk c visible to every wave: each thread waits for its own direct
+// loads of chunk c (later chunks stay in flight), then a bare barrier
+// publishes it -- a fenced barrier would also drain the chunks in flight.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
     int T, int Hq, int max_slots, int nsplit_max, int nqb,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ prefix_len, const uint8_t* __restrict__ tree_mask, float scale_log2,
     float* __restrict__ part_o, float2* __restrict__ part_ml) {
-  constexpr int KS = D + 8;            // K row stride in LDS (elements)
-  constexpr int VS = kChunk + 8;       // V^T row stride in LDS (elements)
-  constexpr int PIECES = D / 8;        // 16-byte pieces per row
-  constexpr int PER_THREAD = kChunk * PIECES / kAttnThreads;
-  constexpr int DT = D / 16;           // output d tiles
-  constexpr int DS = D / 32;           // K steps of the score MFMA
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kChunk * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  using Lay = AttnLayout<D>;
+  constexpr int DT = D / 16, DS = D / 32;
+  static_assert(Lay::LOADS * kAttnThreads * 16 == Lay::TILE, "chunk must split into whole loads");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][Lay::TILE];   // [stage][K, V]
   __shared__ uint64_t mbits[kQBlock][kMaxNodes / 64];
 
   const int split = blockIdx.x, h = blockIdx.y;
@@ -56,9 +258,12 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
   const int total = L + T;
   const int ns = num_splits(total);
   if (split >= ns) return;
-  const int k_lo = split * kSplit;
-  const int k_hi = split == ns - 1 ? total : k_lo + kSplit;
 
+  // whole chunks per split, spread evenly; only a head's last chunk is ragged
+  const int nc_all = (total + kChunk - 1) / kChunk;
+  const int c_base = nc_all / ns, c_rem = nc_all % ns;
+  const int k_lo = kChunk * (split * c_base + min(split, c_rem));
+  const int k_hi = min(total, k_lo + kChunk * (c_base + (split < c_rem ? 1 : 0)));
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -67,29 +272,79 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
   const size_t bh = static_cast<size_t>(b) * Hq + h;
   const uint16_t* kbase = kc + bh * max_slots * D;
   const uint16_t* vbase = vc + bh * max_slots * D;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-
-  // Q as the B operand of S^T: Q[qi][s*32 + 8g .. +8]
-  u32x4 qv[DS];
-  {
-    const uint16_t* qrow = q + ((static_cast<size_t>(b) * T + (q_ok ? qi : 0)) * Hq + h) * D;
+  // Q of the block's 64 queries goes through the same direct-load path into
+  // ring stage 2 (rows 0-31 in its K half, 32-63 in its V half, swizzled
+  // like K), ahead of chunks 0 and 1; stage 2 is first refilled after the
+  // barrier that ends the Q reads.  Rows past T repeat row T - 1.
+  constexpr int PER_CHUNK = 2 * Lay::LOADS;
+  const int nch = (k_hi - k_lo + kChunk - 1) / kChunk;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qv[s] = q_ok ? ld16g(qrow + s * 32 + g * 8) : zero;
+  for (int i = 0; i < 2 * Lay::LOADS; ++i) {
+    const int blk = i * (kAttnThreads / kWave) + wave;      // 1 KB blocks of the 64 x D tile
+    const int sidx = blk * kWave + lane;
+    const int row = sidx / Lay::PIECES, slot = sidx % Lay::PIECES;
+    const int qq = min(qb * kQBlock + row, T - 1);
+    const uint16_t* src = q + ((static_cast<size_t>(b) * T + qq) * Hq + h) * D + Lay::k_slot(row, slot) * 8;
+    const int half = blk * 1024 < Lay::TILE ? 0 : 1;
+    lds_dma16(src, LDSB(ring[kStages - 1][half]) + blk * 1024 - half * Lay::TILE);
   }
+  const int n0 = min(kStages - 1, nch);   // chunks issued ahead of the loop
+  for (int c = 0; c < n0; ++c)
+    attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, lane, wave, ring[c][0], ring[c][1]);
 
-  // ancestor bits of the block's queries (only splits that reach the tree)
+  // Ancestor words of the block's queries (only in a split that reaches the
+  // tree): word ww of query row r is a ballot over one coalesced 64-byte
+  // load of the mask row; each wave builds the rows of its own 16 queries.
+  // The bytes of word 0 are loaded here, but the ballots wait until the
+  // first chunk that reaches the tree: waiting for a load waits for every
+  // load issued before it, and by then only the split's last chunks are
+  // still in flight.
   const bool has_tree = k_hi > L;
+  uint8_t mbv[16];
   if (has_tree) {
-    const int ql = tid >> 2, w = tid & 3;
-    const int qq = qb * kQBlock + ql;
-    uint64_t word = 0;
-    if (qq < T) {
-      for (int jj = 0; jj < 64; ++jj) {
-        const int j = w * 64 + jj;
-        if (j < T && tree_mask[static_cast<size_t>(qq) * T + j]) word |= 1ull << jj;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = qb * kQBlock + wave * 16 + r;
+      mbv[r] = tree_mask[static_cast<size_t>(min(qq, T - 1)) * T + min(lane, T - 1)];
+    }
+  }
+  bool mask_ready = !has_tree;
+  auto build_mask = [&]() {
+    const int nw = (T + 63) >> 6;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = qb * kQBlock + wave * 16 + r;
+      const uint64_t word = ballot(qq < T && lane < T && mbv[r] != 0);
+      if (lane == 0) mbits[wave * 16 + r][0] = word;
+    }
+#pragma unroll 1
+    for (int ww = 1; ww < nw; ++ww) {   // trees of more than 64 nodes
+      const int j = ww * 64 + lane;
+      uint8_t mw[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = qb * kQBlock + wave * 16 + r;
+        mw[r] = tree_mask[static_cast<size_t>(min(qq, T - 1)) * T + min(j, T - 1)];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = qb * kQBlock + wave * 16 + r;
+        const uint64_t word = ballot(qq < T && j < T && mw[r] != 0);
+        if (lane == 0) mbits[wave * 16 + r][ww] = word;
       }
     }
-    mbits[ql][w] = word;
+  };
+  const uint64_t* mrow = mbits[wave * 16 + n];
+
+  // Q from LDS into registers once its loads (the oldest in flight) are in
+  wait_chunks<PER_CHUNK, kStages - 1>(n0);
+  ring_barrier();
+  u32x4 qv[DS];   // Q[qi][s*32 + 8g .. +8]: the B operand of S^T
+  {
+    const int row = wave * 16 + n;
+    const MEDUSA_LDS uint8_t* qt = LDSB(ring[kStages - 1][wave < 2 ? 0 : 1]) + (row & 31) * Lay::ROWB;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qv[s] = *(const MEDUSA_LDS u32x4*)(qt + Lay::k_slot(row, s * 4 + g) * 16);
   }
 
   float m_run = -__builtin_huge_valf();
@@ -98,116 +353,23 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 kreg[PER_THREAD], vreg[PER_THREAD];
-  auto fetch = [&](int c0) {
-#pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r) {
-      const int p = tid + r * kAttnThreads;
-      const int key = c0 + p / PIECES, pc = p % PIECES;
-      const bool ok = key < k_hi;
-      kreg[r] = ok ? ld16g(kbase + static_cast<size_t>(key) * D + pc * 8) : zero;
-      vreg[r] = ok ? ld16g(vbase + static_cast<size_t>(key) * D + pc * 8) : zero;
+  // chunk c sits in stage c % kStages; chunk c + kStages - 1 is issued into
+  // the stage chunk c - 1 used, once every wave is past it
+  for (int c = 0; c < nch; ++c) {
+    wait_chunks<PER_CHUNK, kStages - 2>(min(kStages - 2, nch - 1 - c));
+    ring_barrier();
+    const int cn = c + kStages - 1;
+    if (cn < nch) {
+      const int sn = cn % kStages;
+      attn_issue<D>(kbase, vbase, k_lo + cn * kChunk, k_hi, lane, wave, ring[sn][0], ring[sn][1]);
     }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r) {
-      const int p = tid + r * kAttnThreads;
-      const int key = p / PIECES, pc = p % PIECES;
-      *reinterpret_cast<u32x4*>(&Ks[key * KS + pc * 8]) = kreg[r];
-      const uint32_t w4[4] = {vreg[r][0], vreg[r][1], vreg[r][2], vreg[r][3]};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Vt[(pc * 8 + e) * VS + key] = static_cast<uint16_t>(w4[e >> 1] >> ((e & 1) * 16));
+    const int st = c % kStages;
+    if (!mask_ready && k_lo + (c + 1) * kChunk > L) {   // uniform: first chunk reaching the tree
+      build_mask();
+      mask_ready = true;
     }
-  };
-
-  const int nchunks = (k_hi - k_lo + kChunk - 1) / kChunk;
-  fetch(k_lo);
-  uint64_t my_bits[kMaxNodes / 64] = {0, 0, 0, 0};
-  for (int c = 0; c < nchunks; ++c) {
-    const int c0 = k_lo + c * kChunk;
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (c == 0 && has_tree) {
-#pragma unroll
-      for (int w = 0; w < kMaxNodes / 64; ++w) my_bits[w] = mbits[wave * 16 + n][w];
-    }
-    if (c + 1 < nchunks) fetch(c0 + kChunk);
-
-    // scores S^T[key = kt*16 + 4g + i][query n]
-    f32x4 s[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[(kt * 16 + n) * KS + st * 32 + g * 8]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                      __builtin_bit_cast(bf16x8, qv[st]), acc, 0, 0, 0);
-      }
-      s[kt] = acc;
-    }
-    float mloc = -__builtin_huge_valf();
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = c0 + kt * 16 + 4 * g + i;
-        float x = s[kt][i] * scale_log2;
-        bool allowed = key < k_hi;
-        if (key >= L) {
-          const int j = key - L;
-          allowed = allowed && ((my_bits[(j >> 6) & 3] >> (j & 63)) & 1ull);
-        }
-        x = allowed ? x : -__builtin_huge_valf();
-        s[kt][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float ref = m_new == -__builtin_huge_valf() ? 0.f : m_new;
-    const float alpha = exp2f(m_run - ref);
-    float psum = 0.f;
-    uint32_t pb[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f(s[kt][i] - ref);
-        psum += p[i];
-      }
-      pb[kt][0] = f32_to_bf16_bits(p[0]) | (f32_to_bf16_bits(p[1]) << 16);
-      pb[kt][1] = f32_to_bf16_bits(p[2]) | (f32_to_bf16_bits(p[3]) << 16);
-    }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      o[t][0] *= alpha;
-      o[t][1] *= alpha;
-      o[t][2] *= alpha;
-      o[t][3] *= alpha;
-    }
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]; K slots of group g are keys
-    // 32c + 4g + (0..3) and 32c + 16 + 4g + (0..3)
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const u32x4 pv = {pb[2 * c2][0], pb[2 * c2][1], pb[2 * c2 + 1][0], pb[2 * c2 + 1][1]};
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const uint16_t* vrow = &Vt[(t * 16 + n) * VS + 32 * c2 + 4 * g];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                       __builtin_bit_cast(bf16x8, pv), o[t], 0, 0, 0);
-      }
-    }
+    attn_chunk<D>(qv, o, m_run, l_part, k_lo + c * kChunk, k_hi, L, lane, scale_log2, mrow, ring[st][0],
+                  ring[st][1]);
   }
 
   float l = l_part + __shfl_xor(l_part, 16);
@@ -222,35 +384,53 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
   }
 }
 
-// Merge the splits of one (sequence, query, head): grid (T, Hq, B), D threads.
+// Merge the splits of one (sequence, query, head): grid (T, Hq, B), D
+// threads, thread = output column.  Splits are taken 16 at a time with all
+// their loads issued together, merged online against a running maximum.
 template <typename OutT>
 __global__ void tree_attn_combine_kernel(int T, int Hq, int D, int max_slots, int nsplit_max,
                                          const int32_t* __restrict__ prefix_len,
                                          const float* __restrict__ part_o, const float2* __restrict__ part_ml,
                                          OutT* __restrict__ out) {
+  constexpr int U = 16;
   const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int d = threadIdx.x;
   int L = prefix_len[b];
   if (L > max_slots - T) L = max_slots - T;
   if (L < 0) L = 0;
   const int ns = num_splits(L + T);
   const size_t bh = static_cast<size_t>(b) * Hq + h;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(bh * nsplit_max + s) * T + qi].x);
-  const float ref = M == -__builtin_huge_valf() ? 0.f : M;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const size_t row = (bh * nsplit_max + s) * T + qi;
-      const float2 ml = part_ml[row];
-      const float w = exp2f(ml.x - ref);
-      acc += w * part_o[row * D + d];
-      den += w * ml.y;
+  const float NEG = -__builtin_huge_valf();
+  float M = NEG, acc = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float2 ml[U];
+    float ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t row = (bh * nsplit_max + min(s0 + u, ns - 1)) * T + qi;
+      ml[u] = part_ml[row];
+      ov[u] = part_o[row * D + d];
     }
-    const float v = acc / den;
-    const size_t o = ((static_cast<size_t>(b) * T + qi) * Hq + h) * D + d;
-    if constexpr (sizeof(OutT) == 2) out[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-    else out[o] = v;
+    float bm = NEG;
+#pragma unroll
+    for (int u = 0; u < U; ++u) bm = fmaxf(bm, s0 + u < ns ? ml[u].x : NEG);
+    const float Mn = fmaxf(M, bm);
+    const float ref = Mn == NEG ? 0.f : Mn;
+    const float f = M == NEG ? 0.f : exp2f(M - ref);
+    acc *= f;
+    den *= f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = (s0 + u < ns && ml[u].x != NEG) ? exp2f(ml[u].x - ref) : 0.f;
+      acc += w * ov[u];
+      den += w * ml[u].y;
+    }
+    M = Mn;
   }
+  const float v = acc / den;
+  const size_t o = ((static_cast<size_t>(b) * T + qi) * Hq + h) * D + d;
+  if constexpr (sizeof(OutT) == 2) out[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  else out[o] = v;
 }
 
 // f32: one wave per (sequence, head, query); lanes over keys for scores,
