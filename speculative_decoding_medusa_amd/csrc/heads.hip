@@ -806,6 +806,108 @@ __device__ __forceinline__ void diag_row_logits(const u32x4 (&buf)[NSTMAX], cons
   }
 }
 
+// Dot products of one streamed row with a bf16 vector held in one plane
+// (exact): same lane layout and diagonal read-out as diag_row_logits.
+template <int NSTMAX, int NB>
+__device__ __forceinline__ void diag_row_dot(const u32x4 (&buf)[NSTMAX], const u32x4 (&a)[NB][NSTMAX], int H, int e0,
+                                             int n, int g, float (&dot)[NB]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSTMAX; ++s) {
+    const u32x4 w = 512 * s + e0 < H ? buf[s] : zero;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
+  }
+  const int i = n & 3;
+  const bool on_diag = g == (n >> 2);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float d = i == 0 ? acc[b][0] : (i == 1 ? acc[b][1] : (i == 2 ? acc[b][2] : acc[b][3]));
+    dot[b] = diag_sum(on_diag ? d : 0.f);
+  }
+}
+
+// ------------------------------------------------------- K1, row-diagonal
+// bf16 ResBlock for B <= 2 and H <= 512 * 16: each wave streams its own
+// contiguous block of W1[j] rows (double-buffered whole rows, 1 KB per wave
+// instruction) against h, gathers one row's dot product per lane, and every
+// 64 rows (and at the end) applies r = h + SiLU(dot + b1) to the gathered
+// rows in parallel, one coalesced store per sequence.
+template <int NSTMAX, int NB>
+__global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int H, int K, int rows_per_wave,
+                                                                      const uint16_t* __restrict__ hidden,
+                                                                      const uint16_t* __restrict__ w1,
+                                                                      const uint16_t* __restrict__ b1,
+                                                                      float* __restrict__ r) {
+  const int j = blockIdx.y, wg = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int e0 = 8 * lane;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 ah[NB][NSTMAX];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int s = 0; s < NSTMAX; ++s)
+      ah[b][s] = (b < B && 512 * s + e0 < H) ? ld16(hidden + static_cast<size_t>(b) * H + 512 * s + e0) : zero;
+
+  const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
+  const int r1 = min(r0 + rows_per_wave, H);
+  if (r1 <= r0) return;
+  const uint16_t* wbase = w1 + static_cast<size_t>(j) * H * H;
+  float gath[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) gath[b] = 0.f;
+
+  auto take = [&](int row, const float (&dot)[NB]) {
+    const int slot = (row - r0) & 63;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (lane == slot) gath[b] = dot[b];
+    if (slot == 63 || row == r1 - 1) {
+      const int myrow = row - slot + lane;
+      if (lane <= slot) {
+        const float bias = bf16_to_f32(b1[static_cast<size_t>(j) * H + myrow]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            const float u = gath[b] + bias;
+            const float h = bf16_to_f32(hidden[static_cast<size_t>(b) * H + myrow]);
+            r[(static_cast<size_t>(b) * K + j) * H + myrow] = h + u / (1.0f + expf(-u));
+          }
+        }
+      }
+    }
+  };
+
+  // rotated double buffer, as in the row-diagonal lm_head kernel
+  u32x4 wa[NSTMAX], wb[NSTMAX];
+  float dot[NB];
+  const int last = r1 - 1;
+  diag_load_row<NSTMAX>(wbase + static_cast<size_t>(r0) * H, H, e0, wa);
+  diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0 + 1, last)) * H, H, e0, wb);
+  int row = r0;
+  for (; row + 1 < r1; row += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    diag_row_dot<NSTMAX, NB>(wa, ah, H, e0, n, g, dot);
+    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    take(row, dot);
+    diag_row_dot<NSTMAX, NB>(wb, ah, H, e0, n, g, dot);
+    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    take(row + 1, dot);
+  }
+  if (row < r1) {
+    diag_row_dot<NSTMAX, NB>(wa, ah, H, e0, n, g, dot);
+    take(row, dot);
+  }
+}
+
 template <int NSTMAX, int NB>
 __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     int B, int H, int V, int K, int k, int rows_per_wave, int G, const float* __restrict__ r,
@@ -951,6 +1053,10 @@ struct LmGrid {
 };
 
 constexpr size_t kStreamLdsMax = 64 * 1024;
+// Resident waves per SIMD the row-diagonal lm_head grid is sized for: one
+// measured best at the Vicuna-7B shape (fewer, longer contiguous streams,
+// and fewer lists to merge).
+constexpr int kDiagWavesPerSimd = 1;
 constexpr int kMaxWavesPerSimd = 8;
 
 size_t stream_lds(int B, int H, int topk) {
@@ -1040,8 +1146,46 @@ int check_heads_shape(const char* fn, int dtype, int B, int H, int V, int K, int
   return MEDUSA_OK;
 }
 
+// Rows of W1 per wave for the row-diagonal ResBlock: `wps` waves per SIMD,
+// all resident at once, at least one row each.  One wave per SIMD measured
+// best at the Vicuna-7B shape: fewer, longer contiguous streams.
+constexpr int kResblockWavesPerSimd = 1;
+
+int resblock_rows_per_wave(int H, int K, int wps) {
+  const long long waves = 256LL * 4 * wps;
+  long long wph = waves / K;
+  if (wph < 1) wph = 1;
+  long long rpw = (H + wph - 1) / wph;
+  return static_cast<int>(rpw < 1 ? 1 : rpw);
+}
+
 int launch_resblock(int dtype, int B, int H, int K, const void* hidden, const void* w1, const void* b1,
                     float* r, hipStream_t st) {
+  const int nst = (H + 511) / 512;
+  if (dtype == MEDUSA_BF16 && B <= 2 && nst <= 16) {
+    const uint16_t* hh = static_cast<const uint16_t*>(hidden);
+    const uint16_t* ww = static_cast<const uint16_t*>(w1);
+    const uint16_t* bb = static_cast<const uint16_t*>(b1);
+#define MEDUSA_RES_LAUNCH(NS, NB)                                                                          \
+  do {                                                                                                     \
+    const int rpw = resblock_rows_per_wave(H, K, kResblockWavesPerSimd);                                   \
+    const int G = (H + kHeadsWaves * rpw - 1) / (kHeadsWaves * rpw);                                       \
+    hipLaunchKernelGGL((resblock_diag_kernel<NS, NB>), dim3(G, K), dim3(kHeadsThreads), 0, st, B, H, K, rpw, \
+                       hh, ww, bb, r);                                                                     \
+  } while (0)
+    const int ns = diag_nstmax(nst);
+    if (ns == 4) {
+      if (B == 1) MEDUSA_RES_LAUNCH(4, 1); else MEDUSA_RES_LAUNCH(4, 2);
+    } else if (ns == 8) {
+      if (B == 1) MEDUSA_RES_LAUNCH(8, 1); else MEDUSA_RES_LAUNCH(8, 2);
+    } else if (ns == 13) {
+      if (B == 1) MEDUSA_RES_LAUNCH(13, 1); else MEDUSA_RES_LAUNCH(13, 2);
+    } else {
+      if (B == 1) MEDUSA_RES_LAUNCH(16, 1); else MEDUSA_RES_LAUNCH(16, 2);
+    }
+#undef MEDUSA_RES_LAUNCH
+    return medusa_host::hip_check("medusa_resblock launch");
+  }
   dim3 grid((H + 15) / 16, K);
   if (dtype == MEDUSA_BF16) {
     hipLaunchKernelGGL(resblock_bf16_kernel, grid, dim3(kHeadsThreads), 0, st, B, H, K,
@@ -1066,8 +1210,7 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
     const uint16_t* w = static_cast<const uint16_t*>(w_lm);
 #define MEDUSA_DIAG_LAUNCH(NS, NB)                                                                            \
   do {                                                                                                        \
-    static const int wps = occupancy_wps(lm_topk_diag_kernel<NS, NB>, 0);                                     \
-    lg = lm_grid(dtype, B, H, V, K, topk, wps);                                                               \
+    lg = lm_grid(dtype, B, H, V, K, topk, kDiagWavesPerSimd);                                                 \
     hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, V, K,  \
                        topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);      \
   } while (0)

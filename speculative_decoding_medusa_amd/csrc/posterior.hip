@@ -107,6 +107,15 @@ __global__ __launch_bounds__(kPostThreads) void posterior_rows_kernel(
   if (tid == 0) stats[static_cast<size_t>(row) * nchunk + chunk] = out;
 }
 
+// Decide, in three phases of independent loads: (1) the sequence's
+// candidates and the retrieve paths into LDS, and every node's chunk
+// statistics (all chunks of a node loaded together) merged into its argmax
+// and threshold; (2) the accept flag of every (path, depth) pair at once --
+// the child's token against its parent's argmax, or its tempered
+// probability against the parent's threshold (one logit load); (3) each
+// path's run of leading accepted steps, and the lowest-index longest path.
+constexpr int kDecideUnroll = 8;   // chunk statistics loaded per batch
+
 __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
     int T, int V, int nchunk, int p_max, int D, const float* __restrict__ logits,
     const int32_t* __restrict__ tree_candidates, const int32_t* __restrict__ retrieve,
@@ -115,63 +124,116 @@ __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
     int32_t* __restrict__ next_token) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ int s_arg[kMaxNodes];
+  __shared__ int s_tok[kMaxNodes], s_arg[kMaxNodes];
   __shared__ float s_m[kMaxNodes], s_S[kMaxNodes], s_thr[kMaxNodes];
+  __shared__ int16_t s_ret[kMaxNodes * (kMaxHeads + 1)];
+  __shared__ uint8_t s_acc[kMaxNodes * (kMaxHeads + 1)];
   __shared__ int s_len[kPostThreads / kWave], s_path[kPostThreads / kWave];
   const bool typical = temperature > 0.f;
-
-  for (int node = tid; node < T; node += kPostThreads) {
-    const RowStat* st = stats + (static_cast<size_t>(b) * T + node) * nchunk;
-    float mx = -__builtin_huge_valf();
-    int arg = 0x7fffffff;
-    float m = -__builtin_huge_valf();
-    for (int c = 0; c < nchunk; ++c) {
-      if (beats(st[c].mx, st[c].arg, mx, arg)) { mx = st[c].mx; arg = st[c].arg; }
-      m = fmaxf(m, st[c].m);
-    }
-    s_arg[node] = arg;
-    if (typical) {
-      float S = 0.f, A = 0.f;
-      for (int c = 0; c < nchunk; ++c) {
-        const float w = expf(st[c].m - m);
-        S += st[c].S * w;
-        A += w * (st[c].A + (st[c].m - m) * st[c].S);
-      }
-      const float H = logf(S) - A / S;
-      s_m[node] = m;
-      s_S[node] = S;
-      s_thr[node] = fminf(eps, delta * expf(-H));
-    }
-  }
-  __syncthreads();
+  const float NEG = -__builtin_huge_valf();
 
   int P = *num_paths;
   if (P > p_max) P = p_max;
   if (P < 0) P = 0;
+  const int nret = P * D;
+  // (1a) candidates and paths (entries outside [0, T) end a path)
+  if (tid < T) s_tok[tid] = tree_candidates[static_cast<size_t>(b) * T + tid];
+  for (int x0 = 0; x0 < nret; x0 += kPostThreads * 4) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = retrieve[min(x0 + u * kPostThreads + tid, nret - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = x0 + u * kPostThreads + tid;
+      if (x < nret) s_ret[x] = static_cast<int16_t>(v[u] >= 0 && v[u] < T ? v[u] : -1);
+    }
+  }
+  // (1b) node statistics: chunks merged with log-sum-exp rescaling
+  if (tid < T) {
+    const RowStat* st = stats + (static_cast<size_t>(b) * T + tid) * nchunk;
+    float mx = NEG, m = NEG, S = 0.f, A = 0.f;
+    int arg = 0x7fffffff;
+    for (int c0 = 0; c0 < nchunk; c0 += kDecideUnroll) {
+      RowStat r[kDecideUnroll];
+#pragma unroll
+      for (int u = 0; u < kDecideUnroll; ++u) r[u] = st[min(c0 + u, nchunk - 1)];
+      float mb = m;
+#pragma unroll
+      for (int u = 0; u < kDecideUnroll; ++u) {
+        if (c0 + u < nchunk) {
+          if (beats(r[u].mx, r[u].arg, mx, arg)) { mx = r[u].mx; arg = r[u].arg; }
+          mb = fmaxf(mb, r[u].m);
+        }
+      }
+      if (typical) {
+        // rescale the running sums to the new maximum, then add this batch
+        if (m != NEG) {
+          const float w0 = expf(m - mb);
+          A = w0 * (A + (m - mb) * S);
+          S *= w0;
+        }
+#pragma unroll
+        for (int u = 0; u < kDecideUnroll; ++u) {
+          if (c0 + u < nchunk) {
+            const float w = expf(r[u].m - mb);
+            S += r[u].S * w;
+            A += w * (r[u].A + (r[u].m - mb) * r[u].S);
+          }
+        }
+      }
+      m = mb;
+    }
+    s_arg[tid] = arg;
+    if (typical) {
+      const float H = logf(S) - A / S;
+      s_m[tid] = m;
+      s_S[tid] = S;
+      s_thr[tid] = fminf(eps, delta * expf(-H));
+    }
+  }
+  __syncthreads();
+
+  // (2) accept flag of step j of path p: child c = ret[p][j], parent ret[p][j-1]
+  for (int x0 = 0; x0 < nret; x0 += kPostThreads * 4) {
+    float z[4];
+    int c[4], prev[4], tok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = min(x0 + u * kPostThreads + tid, nret - 1);
+      const int j = x % D;
+      c[u] = j > 0 ? s_ret[x] : -1;
+      prev[u] = j > 0 ? s_ret[x - 1] : -1;
+      tok[u] = c[u] >= 0 ? s_tok[c[u]] : -1;
+      const bool ok = prev[u] >= 0 && tok[u] >= 0 && tok[u] < V;
+      z[u] = 0.f;
+      if (typical)
+        z[u] = logits[(static_cast<size_t>(b) * T + (ok ? prev[u] : 0)) * V + (ok ? tok[u] : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = x0 + u * kPostThreads + tid;
+      if (x >= nret) continue;
+      const bool ok = c[u] >= 0 && prev[u] >= 0 && tok[u] >= 0 && tok[u] < V;
+      bool acc = false;
+      if (ok) {
+        if (!typical) {
+          acc = tok[u] == s_arg[prev[u]];
+        } else {
+          const float pr = expf(z[u] / temperature - s_m[prev[u]]) / s_S[prev[u]];
+          acc = pr > s_thr[prev[u]];
+        }
+      }
+      s_acc[x] = acc ? 1 : 0;
+    }
+  }
+  __syncthreads();
+
+  // (3) accepted length of every path; lowest-index longest path
   int best_len = -1, best_p = 0x7fffffff;
   for (int p = tid; p < P; p += kPostThreads) {
-    const int32_t* path = retrieve + static_cast<size_t>(p) * D;
     int ell = 0;
-    int prev = path[0];
-    if (prev >= 0 && prev < T) {
-      for (int j = 1; j < D; ++j) {
-        const int c = path[j];
-        if (c < 0 || c >= T) break;
-        const int tok = tree_candidates[static_cast<size_t>(b) * T + c];
-        bool acc;
-        if (tok < 0 || tok >= V) {
-          acc = false;
-        } else if (!typical) {
-          acc = tok == s_arg[prev];
-        } else {
-          const float z = logits[(static_cast<size_t>(b) * T + prev) * V + tok] / temperature;
-          const float pr = expf(z - s_m[prev]) / s_S[prev];
-          acc = pr > s_thr[prev];
-        }
-        if (!acc) break;
-        ++ell;
-        prev = c;
-      }
+    if (s_ret[p * D] >= 0) {
+      for (int j = 1; j < D && s_acc[p * D + j]; ++j) ++ell;
     }
     if (ell > best_len || (ell == best_len && p < best_p)) { best_len = ell; best_p = p; }
   }
@@ -192,8 +254,8 @@ __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
     if (best_len < 0) { best_len = 0; best_p = 0; }   // no paths: the root alone
     int last = 0;
     if (P > 0) {
-      last = retrieve[static_cast<size_t>(best_p) * D + best_len];
-      if (last < 0 || last >= T) last = 0;
+      last = s_ret[best_p * D + best_len];
+      if (last < 0) last = 0;
     }
     best_path[b] = best_p;
     accept_len[b] = best_len;
