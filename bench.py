@@ -38,7 +38,26 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """A plain copy of a known size, three times: what FETCH_SIZE / WRITE_SIZE
+    read for it calibrates the counters against the bytes really moved."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 3}))
 
 
 class Step:
@@ -198,6 +217,30 @@ class Step:
             events[len(fns)].record()
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lm_head_topk_vicuna7b_pmc_traffic.md")
+HEADS_SOURCE = os.path.join(ROOT, "speculative_decoding_medusa_amd", "csrc", "heads.hip")
+
+
+def measured_traffic():
+    """HBM bytes per lm_head + top-k call from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when that
+    summary is missing or was taken on a different heads.hip."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = open(HEADS_SOURCE, "rb").read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
+    if fields.get("heads_hip_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def lm_bytes(w):
     """Algorithmic bytes of one lm_head + top-k launch: every weight once,
     r once, the top-k ids and logits written."""
@@ -259,6 +302,9 @@ def cpu_baseline(w, seed, repeats=3):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print("bench.py: this build runs the verify step on one GPU only; --gpus %d is not supported "
               "(run with --gpus 1)" % args.gpus, file=sys.stderr)
@@ -328,7 +374,8 @@ def main():
                    "n_layers": w["n_layers"], "temperature": w["temperature"]},
         "roofline": {"kernel": "lm_head_topk", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": lm_bytes(w),
+                     "traffic": measured_traffic(), "traffic_unit": "bytes per call",
+                     "bytes_per_launch": lm_bytes(w),
                      "mean_launch_us": round(lm_mean_s * 1e6, 2)},
         "stages": stages,
         "stages_note": "per-stage means from a separate untimed pass of %d steps" % nb,
