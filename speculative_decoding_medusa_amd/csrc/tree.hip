@@ -41,6 +41,11 @@ __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
   __shared__ uint64_t anc[kMaxNodes][kMaxNodes / 64];
   __shared__ int wave_leaves[kTreeThreads / kWave];
   __shared__ int err_key;
+  __shared__ int s_ids[kMaxBatch * kMaxHeads * kMaxTopk];   // topk_ids [B][K][topk]
+  __shared__ int s_root[kMaxBatch], s_plen[kMaxBatch];
+  __shared__ uint32_t s_pfound[kTreeThreads];   // key-pass partials (bit 31: duplicate)
+  __shared__ int s_prank[kTreeThreads];
+  __shared__ int16_t s_ppe[kTreeThreads];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -48,18 +53,25 @@ __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
   const int D = K + 1;
   const int NONE = 0x7fffffff;
 
-  // inputs first, all independent loads: the entry's row, the batch's root
-  // tokens and prefix lengths (clamped indices, masked at use)
+  // Inputs first, all independent loads in one round trip: the entry's row,
+  // and into LDS the whole top-k table, the root tokens and the prefix
+  // lengths (clamped indices, masked at use); every later read is LDS.
   int row[kMaxDepth];
   const int e_row = min(tid, max(N - 1, 0));
 #pragma unroll
   for (int m = 0; m < kMaxDepth; ++m) row[m] = N > 0 ? choices[static_cast<size_t>(e_row) * K + min(m, K - 1)] : -1;
-  int plen[kMaxBatch];
-  int root[kMaxBatch];
+  const int n_ids = B * K * topk;
+  for (int x0 = 0; x0 < n_ids; x0 += kTreeThreads * 8) {
+    int v[8];
 #pragma unroll
-  for (int b = 0; b < kMaxBatch; ++b) {
-    plen[b] = prefix_len[min(b, B - 1)];
-    root[b] = root_token[min(b, B - 1)];
+    for (int u = 0; u < 8; ++u) v[u] = topk_ids[min(x0 + u * kTreeThreads + tid, n_ids - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (x0 + u * kTreeThreads + tid < n_ids) s_ids[x0 + u * kTreeThreads + tid] = v[u];
+  }
+  if (tid < B) {
+    s_root[tid] = root_token[tid];
+    s_plen[tid] = prefix_len[tid];
   }
   if (tid == 0) err_key = NONE;
   has_child[tid] = 0;
@@ -87,53 +99,67 @@ __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
     key |= static_cast<uint64_t>(n) << 60;
     my_err = pad ? MEDUSA_SPEC_PADDING : (n == 0 ? MEDUSA_SPEC_EMPTY : (bad ? MEDUSA_SPEC_RANK : 0));
   }
-  // the entry's candidate token for every sequence (in bounds even when invalid)
-  int tok[kMaxBatch];
-  {
-    const int dd = min(max(l, 1), K) - 1;
-    int last = 0;
-#pragma unroll
-    for (int m = 0; m < kMaxDepth; ++m)
-      if (m == l - 1) last = row[m];
-    last = min(max(last, 0), topk - 1);
-#pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b)
-      tok[b] = topk_ids[(static_cast<size_t>(min(b, B - 1)) * K + dd) * topk + last];
-  }
   if (is_entry) skey[tid] = key;
   __syncthreads();
   if (is_entry && my_err) atomicMin(&err_key, (0 << 24) | (tid << 8) | my_err);
 
-  // one pass over every key: duplicates before me, present prefix lengths,
-  // my rank in node order, my parent's entry
+  // One pass over every key, for entry q: duplicates before q, the prefix
+  // lengths present, q's rank in node order, q's parent's entry.  For small
+  // specs the keys are split over P threads per entry (thread t scans part
+  // t / EPP of the keys for entry t % EPP) and the partials are combined.
+  const int P = N <= 64 ? 4 : (N <= 128 ? 2 : 1);
+  const int EPP = kTreeThreads / P;
+  const int q_ent = tid % EPP, part = tid / EPP;
+  const int span = (N + P - 1) / P;
+  const int e_lo = part * span, e_hi = min(N, e_lo + span);
+  bool dup_p = false;
+  uint32_t found_p = 0;
+  int rank_p = 0, pe_p = -1;
+  if (q_ent < N) {
+    const uint64_t qk = skey[q_ent];
+    const int ql = static_cast<int>(qk >> 60);
+    int e = e_lo;
+    for (; e + 4 <= e_hi; e += 4) {
+      uint64_t ke[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ke[u] = skey[e + u];
+      // branch-free (bitwise & on the conditions, no short circuits)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int le = static_cast<int>(ke[u] >> 60);
+        const bool pre = (le >= 1) & (le < ql) & (((ke[u] ^ qk) & rank_field_mask(le)) == 0);
+        dup_p |= (e + u < q_ent) & (ke[u] == qk);
+        found_p |= static_cast<uint32_t>(pre) << le;
+        pe_p = (pre & (le == ql - 1)) ? e + u : pe_p;
+        rank_p += static_cast<int>(ke[u] < qk);
+      }
+    }
+    for (; e < e_hi; ++e) {
+      const uint64_t k1 = skey[e];
+      const int le = static_cast<int>(k1 >> 60);
+      const bool pre = (le >= 1) & (le < ql) & (((k1 ^ qk) & rank_field_mask(le)) == 0);
+      dup_p |= (e < q_ent) & (k1 == qk);
+      found_p |= static_cast<uint32_t>(pre) << le;
+      pe_p = (pre & (le == ql - 1)) ? e : pe_p;
+      rank_p += static_cast<int>(k1 < qk);
+    }
+  }
+  s_pfound[tid] = found_p | (static_cast<uint32_t>(dup_p) << 31);
+  s_prank[tid] = rank_p;
+  s_ppe[tid] = static_cast<int16_t>(pe_p);
+  __syncthreads();
   bool dup = false;
   uint32_t found = 0;
   int rank = 0, pe = -1;
   if (is_entry) {
-    int e = 0;
-    for (; e + 4 <= N; e += 4) {
-      uint64_t ke[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ke[q] = skey[e + q];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int le = static_cast<int>(ke[q] >> 60);
-        const bool pre = le >= 1 && le < l && ((ke[q] ^ key) & rank_field_mask(le)) == 0;
-        dup |= (e + q < tid) && ke[q] == key;
-        found |= pre ? (1u << le) : 0u;
-        pe = (pre && le == l - 1) ? e + q : pe;
-        rank += ke[q] < key ? 1 : 0;
-      }
+    for (int pp = 0; pp < P; ++pp) {
+      const int x = pp * EPP + tid;
+      found |= s_pfound[x];
+      rank += s_prank[x];
+      pe = max(pe, static_cast<int>(s_ppe[x]));
     }
-    for (; e < N; ++e) {
-      const uint64_t k1 = skey[e];
-      const int le = static_cast<int>(k1 >> 60);
-      const bool pre = le >= 1 && le < l && ((k1 ^ key) & rank_field_mask(le)) == 0;
-      dup |= (e < tid) && k1 == key;
-      found |= pre ? (1u << le) : 0u;
-      pe = (pre && le == l - 1) ? e : pe;
-      rank += k1 < key ? 1 : 0;
-    }
+    dup = (found >> 31) != 0;
+    found &= 0x7fffffffu;
     const uint32_t want = (1u << l) - 2u;  // lengths 1 .. l-1
     if (dup) atomicMin(&err_key, (1 << 24) | (tid << 8) | MEDUSA_SPEC_DUPLICATE);
     else if ((found & want) != want) atomicMin(&err_key, (2 << 24) | (tid << 8) | MEDUSA_SPEC_PREFIX);
@@ -214,24 +240,18 @@ __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
     tree_indices[node] = 1 + (l - 1) * topk + last;
     parent_out[node] = par[node];
     depth_out[node] = l;
-#pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b) {
-      if (b < B) {
-        tree_candidates[static_cast<size_t>(b) * T + node] = tok[b];
-        position_ids[static_cast<size_t>(b) * T + node] = plen[b] + l;
-      }
+    for (int b = 0; b < B; ++b) {
+      tree_candidates[static_cast<size_t>(b) * T + node] = s_ids[(b * K + (l - 1)) * topk + last];
+      position_ids[static_cast<size_t>(b) * T + node] = s_plen[b] + l;
     }
   }
   if ((ok && tid == 0) || (!ok && is_node)) {
     tree_indices[tid] = 0;
     parent_out[tid] = -1;
     depth_out[tid] = 0;
-#pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b) {
-      if (b < B) {
-        tree_candidates[static_cast<size_t>(b) * T + tid] = root[b];
-        position_ids[static_cast<size_t>(b) * T + tid] = plen[b];
-      }
+    for (int b = 0; b < B; ++b) {
+      tree_candidates[static_cast<size_t>(b) * T + tid] = s_root[b];
+      position_ids[static_cast<size_t>(b) * T + tid] = s_plen[b];
     }
   }
   // mask rows over the flat [T][T] byte array, four bytes per store
