@@ -136,27 +136,37 @@ __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
   if (P > p_max) P = p_max;
   if (P < 0) P = 0;
   const int nret = P * D;
-  // (1a) candidates and paths (entries outside [0, T) end a path)
-  if (tid < T) s_tok[tid] = tree_candidates[static_cast<size_t>(b) * T + tid];
-  for (int x0 = 0; x0 < nret; x0 += kPostThreads * 4) {
-    int v[4];
+  // (1) one round trip: this thread's candidate, its share of the paths and
+  // the first batch of its node's chunk statistics are all requested before
+  // anything waits (clamped indices, masked at use)
+  constexpr int RPER = (kMaxNodes * (kMaxHeads + 1) + kPostThreads - 1) / kPostThreads;
+  const int node = min(tid, T - 1);
+  const int tokv = tree_candidates[static_cast<size_t>(b) * T + node];
+  int retv[RPER];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = retrieve[min(x0 + u * kPostThreads + tid, nret - 1)];
+  for (int u = 0; u < RPER; ++u) retv[u] = retrieve[max(min(u * kPostThreads + tid, nret - 1), 0)];
+  const RowStat* st = stats + (static_cast<size_t>(b) * T + node) * nchunk;
+  RowStat r[kDecideUnroll];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = x0 + u * kPostThreads + tid;
-      if (x < nret) s_ret[x] = static_cast<int16_t>(v[u] >= 0 && v[u] < T ? v[u] : -1);
-    }
+  for (int u = 0; u < kDecideUnroll; ++u) r[u] = st[min(u, nchunk - 1)];
+
+  // candidates and paths into LDS (entries outside [0, T) end a path)
+  if (tid < T) s_tok[tid] = tokv;
+#pragma unroll
+  for (int u = 0; u < RPER; ++u) {
+    const int x = u * kPostThreads + tid;
+    if (x < nret) s_ret[x] = static_cast<int16_t>(retv[u] >= 0 && retv[u] < T ? retv[u] : -1);
   }
-  // (1b) node statistics: chunks merged with log-sum-exp rescaling
+  // node statistics: chunks merged with log-sum-exp rescaling, a batch of
+  // kDecideUnroll chunks at a time (one batch for V <= 32768)
   if (tid < T) {
-    const RowStat* st = stats + (static_cast<size_t>(b) * T + tid) * nchunk;
     float mx = NEG, m = NEG, S = 0.f, A = 0.f;
     int arg = 0x7fffffff;
     for (int c0 = 0; c0 < nchunk; c0 += kDecideUnroll) {
-      RowStat r[kDecideUnroll];
+      if (c0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kDecideUnroll; ++u) r[u] = st[min(c0 + u, nchunk - 1)];
+        for (int u = 0; u < kDecideUnroll; ++u) r[u] = st[min(c0 + u, nchunk - 1)];
+      }
       float mb = m;
 #pragma unroll
       for (int u = 0; u < kDecideUnroll; ++u) {
