@@ -76,12 +76,22 @@ def test_heads_vicuna7b(gpu_device):
     _check(case, _run(case, w, keep_logits=False), w)
 
 
-def test_heads_repeat_calls_keep_counters_clean(gpu_device):
-    # the completion counters must be back at zero after every call
+def test_heads_repeat_calls_are_stable(gpu_device):
+    # the same call three times on one cached workspace gives the same answer
     w = synth.workload("vicuna-7b", B=2, H=256, V=4000, K=3, topk=10)
     case = heads_case(w, seed=11)
     for _ in range(3):
         _check(case, _run(case, w, keep_logits=False), w, check_logits=False)
+
+
+@pytest.mark.parametrize("B,H,V,K,k", [
+    (1, 6656, 3001, 2, 10),    # 13 row steps of 512 (the 33B hidden size, batch 1)
+    (2, 8192, 2000, 1, 8),     # 16 row steps, two sequences per wave
+])
+def test_heads_bf16_wide_rows(gpu_device, B, H, V, K, k):
+    w = synth.workload("vicuna-7b", B=B, H=H, V=V, K=K, topk=k)
+    case = heads_case(w, seed=H + B)
+    _check(case, _run(case, w), w)
 
 
 @pytest.mark.slow
