@@ -248,9 +248,11 @@ def lm_bytes(w):
     return K * V * H * 2 + B * K * H * 4 + B * K * k * 8
 
 
-def cpu_baseline(w, seed, repeats=3):
-    """The oracle on full steps of the same workload, on this host: the
-    median of ``repeats`` timed steps (inputs generated outside the timing)."""
+def cpu_baseline(w, seed, min_steps=3, min_seconds=10.0, max_steps=30):
+    """The oracle on full steps of the same workload, on this host: whole
+    steps are timed until at least ``min_seconds`` of oracle work (and at
+    least ``min_steps`` steps) have run; the median step is reported.
+    Inputs are generated outside the timing."""
     import oracle
     import synth
 
@@ -267,7 +269,8 @@ def cpu_baseline(w, seed, repeats=3):
     kc, vc = synth.kv_cache(dict(w, Hkv=w["Hq"]), seed=seed)
     att = logits = None
     runs = []
-    for _ in range(repeats):
+    spent = 0.0
+    while len(runs) < max_steps and (len(runs) < min_steps or spent < min_seconds):
         times = {}
         t0 = time.perf_counter()
         hd = oracle.heads(x["hidden"], x["w1"], x["b1"], x["w_lm"], w["topk"])
@@ -290,13 +293,14 @@ def cpu_baseline(w, seed, repeats=3):
         t5 = time.perf_counter()
         times["tree_attention"], times["posterior"], times["commit_kv"] = t3 - t2, t4 - t3, t5 - t4
         runs.append(times)
+        spent += sum(times.values())
     runs.sort(key=lambda t: sum(t.values()))
     med = runs[len(runs) // 2]
     total = sum(med.values())
     return {"value": round(1.0 / total, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": "median of %d full verify steps at the same shapes (5 heads, 64-node tree, one "
-                      "attention layer at prefix 2048, typical posterior over 64x32000, 32-layer commit), "
-                      "fp64 NumPy" % repeats,
+            "sample": "median of %d full verify steps (%.1f s of oracle work) at the same shapes "
+                      "(5 heads, 64-node tree, one attention layer at prefix 2048, typical posterior over "
+                      "64x32000, 32-layer commit), fp64 NumPy" % (len(runs), spent),
             "seconds_per_step": round(total, 3), "stage_seconds": {k: round(v, 3) for k, v in med.items()}}
 
 

@@ -24,11 +24,11 @@
 
 namespace medusa {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 512;   // two groups of four waves
 constexpr int kQBlock = 64;        // queries per workgroup
 constexpr int kChunk = 32;         // keys per LDS stage
-constexpr int kStages = 4;         // LDS ring depth: kStages - 1 chunks in flight
-constexpr int kSplit = 128;        // target keys per split
+constexpr int kStages = 8;         // LDS ring depth: up to kStages - 2 chunks in flight
+constexpr int kSplit = 256;        // target keys per split
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Splits of a (sequence, head): about kSplit keys each, whole chunks.
@@ -65,29 +65,35 @@ struct AttnLayout {
   static constexpr int PIECES = D / 8;                       // 16-byte pieces per row
   static constexpr int ROWB = D * 2;                         // bytes per row
   static constexpr int TILE = kChunk * ROWB;                 // bytes of K (or V) per chunk
-  static constexpr int LOADS = TILE / (kAttnThreads * 16);   // direct loads per thread per tensor
+  static constexpr int PER = 2 * TILE / 16 / kAttnThreads;   // direct loads per thread per chunk (K and V)
   static constexpr int SH = D == 128 ? 0 : 1;                // rows sharing a bank base
   // LDS slot of piece pc of row `row`
   __device__ static int k_slot(int row, int pc) { return pc ^ ((row >> SH) & (PIECES - 1)); }
   __device__ static int v_slot(int row, int pc) { return pc ^ (2 * ((row >> SH) & (PIECES / 2 - 1))); }
 };
 
-// Issue the direct loads of chunk [c0, c0 + kChunk) into one ring stage:
-// lane l of wave-instruction blk fills LDS slot blk*64 + l, i.e. (row,
-// slot), with the piece that slot holds under the swizzle (an involution).
-// Rows past k_hi repeat row k_hi - 1: finite data whose scores are masked.
+// Issue the direct loads of chunk [c0, c0 + kChunk) into one ring stage.
+// The chunk's K and V tiles are 2 * TILE / 16 pieces of 16 bytes; piece x
+// (x = i * kAttnThreads + tid) is K piece x, or V piece x - TILE / 16.  A
+// wave instruction covers 64 consecutive pieces, one 1 KB block of K or of
+// V: lane l fills LDS slot blk * 64 + l, i.e. (row, slot), with the piece
+// that slot holds under the swizzle (an involution).  Rows past k_hi repeat
+// row k_hi - 1: finite data whose scores are masked.
 template <int D>
-__device__ __forceinline__ void attn_issue(const uint16_t* kbase, const uint16_t* vbase, int c0, int k_hi, int lane,
-                                           int wave, uint8_t* kst, uint8_t* vst) {
+__device__ __forceinline__ void attn_issue(const uint16_t* kbase, const uint16_t* vbase, int c0, int k_hi, int tid,
+                                           uint8_t* kst, uint8_t* vst) {
   using Lay = AttnLayout<D>;
+  constexpr int NP = Lay::TILE / 16;      // pieces per tensor
 #pragma unroll
-  for (int i = 0; i < Lay::LOADS; ++i) {
-    const int blk = i * (kAttnThreads / kWave) + wave;
-    const int sidx = blk * kWave + lane;
+  for (int i = 0; i < Lay::PER; ++i) {
+    const int x = i * kAttnThreads + tid;
+    const bool is_v = x >= NP;              // uniform per wave
+    const int sidx = is_v ? x - NP : x;
     const int row = sidx / Lay::PIECES, slot = sidx % Lay::PIECES;
     const size_t key = static_cast<size_t>(min(c0 + row, k_hi - 1));
-    lds_dma16(kbase + key * D + Lay::k_slot(row, slot) * 8, LDSB(kst) + blk * 1024);
-    lds_dma16(vbase + key * D + Lay::v_slot(row, slot) * 8, LDSB(vst) + blk * 1024);
+    const uint16_t* src = is_v ? vbase + key * D + Lay::v_slot(row, slot) * 8
+                               : kbase + key * D + Lay::k_slot(row, slot) * 8;
+    lds_dma16(src, LDSB(is_v ? vst : kst) + (sidx & ~63) * 16);
   }
 }
 
@@ -246,9 +252,11 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
     float* __restrict__ part_o, float2* __restrict__ part_ml) {
   using Lay = AttnLayout<D>;
   constexpr int DT = D / 16, DS = D / 32;
-  static_assert(Lay::LOADS * kAttnThreads * 16 == Lay::TILE, "chunk must split into whole loads");
+  constexpr int NW = kAttnThreads / kWave;           // waves: two groups of four
+  static_assert(Lay::PER * kAttnThreads * 16 == 2 * Lay::TILE, "chunk must split into whole loads");
+  static_assert(kStages >= 4 && kStages % 2 == 0, "chunks are consumed in pairs");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][Lay::TILE];   // [stage][K, V]
-  __shared__ uint64_t mbits[kQBlock][kMaxNodes / 64];
+  __shared__ uint64_t mbits[NW][16][kMaxNodes / 64];
 
   const int split = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z / nqb, qb = blockIdx.z - b * nqb;
@@ -266,45 +274,47 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
   const int k_hi = min(total, k_lo + kChunk * (c_base + (split < c_rem ? 1 : 0)));
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, wq = wave & 3;            // chunk group, query wave
   const int n = lane & 15, g = lane >> 4;
-  const int qi = qb * kQBlock + wave * 16 + n;     // this lane's query
+  const int qi = qb * kQBlock + wq * 16 + n;           // this lane's query
   const bool q_ok = qi < T;
   const size_t bh = static_cast<size_t>(b) * Hq + h;
   const uint16_t* kbase = kc + bh * max_slots * D;
   const uint16_t* vbase = vc + bh * max_slots * D;
-  // Q of the block's 64 queries goes through the same direct-load path into
-  // ring stage 2 (rows 0-31 in its K half, 32-63 in its V half, swizzled
-  // like K), ahead of chunks 0 and 1; stage 2 is first refilled after the
-  // barrier that ends the Q reads.  Rows past T repeat row T - 1.
-  constexpr int PER_CHUNK = 2 * Lay::LOADS;
+  constexpr int PER = Lay::PER;
   const int nch = (k_hi - k_lo + kChunk - 1) / kChunk;
+
+  // Q of the block's 64 queries goes through the same direct-load path into
+  // the last ring stage (rows 0-31 in its K half, 32-63 in its V half,
+  // swizzled like K), ahead of the first chunks; that stage is first
+  // refilled after the barrier that ends the Q reads.  Rows past T repeat
+  // row T - 1.
 #pragma unroll
-  for (int i = 0; i < 2 * Lay::LOADS; ++i) {
-    const int blk = i * (kAttnThreads / kWave) + wave;      // 1 KB blocks of the 64 x D tile
-    const int sidx = blk * kWave + lane;
-    const int row = sidx / Lay::PIECES, slot = sidx % Lay::PIECES;
+  for (int i = 0; i < PER; ++i) {
+    const int x = i * kAttnThreads + tid;                // piece of the 64 x D tile
+    const int row = x / Lay::PIECES, slot = x % Lay::PIECES;
     const int qq = min(qb * kQBlock + row, T - 1);
     const uint16_t* src = q + ((static_cast<size_t>(b) * T + qq) * Hq + h) * D + Lay::k_slot(row, slot) * 8;
-    const int half = blk * 1024 < Lay::TILE ? 0 : 1;
-    lds_dma16(src, LDSB(ring[kStages - 1][half]) + blk * 1024 - half * Lay::TILE);
+    const int half = x * 16 < Lay::TILE ? 0 : 1;
+    lds_dma16(src, LDSB(ring[kStages - 1][half]) + ((x & ~63) * 16 - half * Lay::TILE));
   }
-  const int n0 = min(kStages - 1, nch);   // chunks issued ahead of the loop
+  const int n0 = min(kStages - 2, nch);   // chunks issued ahead of the loop
   for (int c = 0; c < n0; ++c)
-    attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, lane, wave, ring[c][0], ring[c][1]);
+    attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, tid, ring[c][0], ring[c][1]);
 
-  // Ancestor words of the block's queries (only in a split that reaches the
+  // Ancestor words of the wave's queries (only in a split that reaches the
   // tree): word ww of query row r is a ballot over one coalesced 64-byte
-  // load of the mask row; each wave builds the rows of its own 16 queries.
+  // load of the mask row; every wave builds the rows of its own 16 queries.
   // The bytes of word 0 are loaded here, but the ballots wait until the
-  // first chunk that reaches the tree: waiting for a load waits for every
-  // load issued before it, and by then only the split's last chunks are
-  // still in flight.
+  // wave's first chunk that reaches the tree: waiting for a load waits for
+  // every load issued before it, and by then only the split's last chunks
+  // are still in flight.
   const bool has_tree = k_hi > L;
   uint8_t mbv[16];
   if (has_tree) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int qq = qb * kQBlock + wave * 16 + r;
+      const int qq = qb * kQBlock + wq * 16 + r;
       mbv[r] = tree_mask[static_cast<size_t>(min(qq, T - 1)) * T + min(lane, T - 1)];
     }
   }
@@ -313,9 +323,9 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
     const int nw = (T + 63) >> 6;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int qq = qb * kQBlock + wave * 16 + r;
+      const int qq = qb * kQBlock + wq * 16 + r;
       const uint64_t word = ballot(qq < T && lane < T && mbv[r] != 0);
-      if (lane == 0) mbits[wave * 16 + r][0] = word;
+      if (lane == 0) mbits[wave][r][0] = word;
     }
 #pragma unroll 1
     for (int ww = 1; ww < nw; ++ww) {   // trees of more than 64 nodes
@@ -323,26 +333,26 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
       uint8_t mw[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qq = qb * kQBlock + wave * 16 + r;
+        const int qq = qb * kQBlock + wq * 16 + r;
         mw[r] = tree_mask[static_cast<size_t>(min(qq, T - 1)) * T + min(j, T - 1)];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qq = qb * kQBlock + wave * 16 + r;
+        const int qq = qb * kQBlock + wq * 16 + r;
         const uint64_t word = ballot(qq < T && j < T && mw[r] != 0);
-        if (lane == 0) mbits[wave * 16 + r][ww] = word;
+        if (lane == 0) mbits[wave][r][ww] = word;
       }
     }
   };
-  const uint64_t* mrow = mbits[wave * 16 + n];
+  const uint64_t* mrow = mbits[wave][n];
 
   // Q from LDS into registers once its loads (the oldest in flight) are in
-  wait_chunks<PER_CHUNK, kStages - 1>(n0);
+  wait_chunks<PER, kStages - 2>(n0);
   ring_barrier();
   u32x4 qv[DS];   // Q[qi][s*32 + 8g .. +8]: the B operand of S^T
   {
-    const int row = wave * 16 + n;
-    const MEDUSA_LDS uint8_t* qt = LDSB(ring[kStages - 1][wave < 2 ? 0 : 1]) + (row & 31) * Lay::ROWB;
+    const int row = wq * 16 + n;
+    const MEDUSA_LDS uint8_t* qt = LDSB(ring[kStages - 1][row < 32 ? 0 : 1]) + (row & 31) * Lay::ROWB;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qv[s] = *(const MEDUSA_LDS u32x4*)(qt + Lay::k_slot(row, s * 4 + g) * 16);
   }
@@ -353,34 +363,75 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // chunk c sits in stage c % kStages; chunk c + kStages - 1 is issued into
-  // the stage chunk c - 1 used, once every wave is past it
-  for (int c = 0; c < nch; ++c) {
-    wait_chunks<PER_CHUNK, kStages - 2>(min(kStages - 2, nch - 1 - c));
+  // Chunks go in pairs: group 0 takes chunk c, group 1 chunk c + 1, each
+  // with its own online-softmax state.  Chunk c sits in stage c % kStages;
+  // after the barrier of pair c the stages of pair c - 2 are free and take
+  // chunks c + kStages - 2 and c + kStages - 1.
+  for (int c = 0; c < nch; c += 2) {
+    const int need_hi = min(c + 1, nch - 1);
+    const int issued_hi = min(c + kStages - 3, nch - 1);
+    wait_chunks<PER, kStages - 4>(issued_hi - need_hi);
     ring_barrier();
-    const int cn = c + kStages - 1;
-    if (cn < nch) {
-      const int sn = cn % kStages;
-      attn_issue<D>(kbase, vbase, k_lo + cn * kChunk, k_hi, lane, wave, ring[sn][0], ring[sn][1]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cn = c + kStages - 2 + u;
+      if (cn < nch) {
+        const int sn = cn % kStages;
+        attn_issue<D>(kbase, vbase, k_lo + cn * kChunk, k_hi, tid, ring[sn][0], ring[sn][1]);
+      }
     }
-    const int st = c % kStages;
-    if (!mask_ready && k_lo + (c + 1) * kChunk > L) {   // uniform: first chunk reaching the tree
-      build_mask();
-      mask_ready = true;
+    const int cc = c + grp;
+    if (cc < nch) {
+      if (!mask_ready && k_lo + (cc + 1) * kChunk > L) {   // uniform: the wave's first chunk reaching the tree
+        build_mask();
+        mask_ready = true;
+      }
+      const int st = cc % kStages;
+      attn_chunk<D>(qv, o, m_run, l_part, k_lo + cc * kChunk, k_hi, L, lane, scale_log2, mrow, ring[st][0],
+                    ring[st][1]);
     }
-    attn_chunk<D>(qv, o, m_run, l_part, k_lo + c * kChunk, k_hi, L, lane, scale_log2, mrow, ring[st][0],
-                  ring[st][1]);
   }
 
-  float l = l_part + __shfl_xor(l_part, 16);
-  l += __shfl_xor(l, 32);
-  if (q_ok) {
-    const size_t row = (bh * nsplit_max + split) * T + qi;
-    float* orow = part_o + row * D;
+  // Group 1 hands its state to group 0 through LDS (the ring is free: every
+  // direct load has landed and every chunk has been read), then group 0
+  // merges the two -- each taken against its own reference -- and writes
+  // the split's partial.
+  constexpr int NF = 4 * DT + 2;                       // floats per lane: O, m, l
+  float* xfer = reinterpret_cast<float*>(&ring[0][0][0]);
+  ring_barrier();
+  if (grp == 1) {
 #pragma unroll
     for (int t = 0; t < DT; ++t)
-      *reinterpret_cast<float4*>(orow + t * 16 + 4 * g) = float4{o[t][0], o[t][1], o[t][2], o[t][3]};
-    if (g == 0) part_ml[row] = float2{m_run, l};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xfer[(wq * NF + 4 * t + i) * kWave + lane] = o[t][i];
+    xfer[(wq * NF + 4 * DT) * kWave + lane] = m_run;
+    xfer[(wq * NF + 4 * DT + 1) * kWave + lane] = l_part;
+  }
+  ring_barrier();
+  if (grp == 0) {
+    const float NEG = -__builtin_huge_valf();
+    const float m1 = xfer[(wq * NF + 4 * DT) * kWave + lane];
+    const float l1 = xfer[(wq * NF + 4 * DT + 1) * kWave + lane];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = m_run == NEG ? 0.f : exp2f(m_run - M);
+    const float a1 = m1 == NEG ? 0.f : exp2f(m1 - M);
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * a0 + xfer[(wq * NF + 4 * t + i) * kWave + lane] * a1;
+    l_part = l_part * a0 + l1 * a1;
+    m_run = M;
+
+    float l = l_part + __shfl_xor(l_part, 16);
+    l += __shfl_xor(l, 32);
+    if (q_ok) {
+      const size_t row = (bh * nsplit_max + split) * T + qi;
+      float* orow = part_o + row * D;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        *reinterpret_cast<float4*>(orow + t * 16 + 4 * g) = float4{o[t][0], o[t][1], o[t][2], o[t][3]};
+      if (g == 0) part_ml[row] = float2{m_run, l};
+    }
   }
 }
 
