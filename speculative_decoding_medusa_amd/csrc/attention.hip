@@ -2,21 +2,23 @@
 // ancestor-only mask among the tree's own keys.
 //
 // bf16 path.  The key range [0, L+T) of each (sequence, head) is cut into
-// num_splits balanced splits, one workgroup each.  A workgroup holds up to
-// 64 queries (four waves of 16) and walks its split in 32-key chunks.  K and
-// V chunks go from HBM straight into an LDS ring of three stages with
-// 16-byte direct-to-LDS loads (two chunks in flight while one is used), so
-// the stream needs no registers and no LDS stores; rows are kept whole and
-// the 16-byte pieces within a row are XOR-swizzled by row so the MFMA
-// operand reads are free of bank conflicts.  Scores are computed
-// transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: a lane then holds
-// four consecutive keys of one query, which is the B-operand layout P^T
-// needs for O^T += V^T P^T, so probabilities never leave registers.  The
-// V^T operand is read from the row-major V chunk with the LDS transpose
-// read (ds_read_b64_tr_b16).  Online softmax in base 2, fp32 accumulators.
-// Each split writes (O unnormalised, m, l) and a second kernel merges the
-// splits (log-sum-exp).  Every global load is unconditional with a clamped
-// index (masked at use), so no load waits behind a branch.
+// num_splits splits of whole 32-key chunks, one workgroup each.  A workgroup
+// holds up to 64 queries in two groups of four waves (16 queries a wave);
+// the groups take alternate chunks of the split.  K and V chunks go from HBM
+// straight into an eight-stage LDS ring with 16-byte direct-to-LDS loads (up
+// to six chunks in flight), so the stream needs no registers and no LDS
+// stores; rows are kept whole and the 16-byte pieces within a row are
+// XOR-swizzled by row so the MFMA operand reads are free of bank conflicts.
+// Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_16x16x32_bf16: a lane then holds four consecutive keys of one
+// query, which is the B-operand layout P^T needs for O^T += V^T P^T, so
+// probabilities never leave registers.  The V^T operand is read from the
+// row-major V chunk with the LDS transpose read (ds_read_b64_tr_b16).
+// Online softmax in base 2, fp32 accumulators.  The second group hands its
+// (O, m, l) to the first through LDS; each split writes (O unnormalised, m,
+// l) and a second kernel merges the splits (log-sum-exp).  Every global load
+// is unconditional with a clamped index (masked at use), so no load waits
+// behind a branch.
 //
 // f32 path: one wave per (sequence, head, query), online softmax over
 // 64-key chunks on the VALU.
@@ -95,14 +97,6 @@ __device__ __forceinline__ void attn_issue(const uint16_t* kbase, const uint16_t
                                : kbase + key * D + Lay::k_slot(row, slot) * 8;
     lds_dma16(src, LDSB(is_v ? vst : kst) + (sidx & ~63) * 16);
   }
-}
-
-// Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Allowed keys of one 32-key chunk for this lane's query, bit p = key c0 + p:
@@ -435,32 +429,41 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
   }
 }
 
-// Merge the splits of one (sequence, query, head): grid (T, Hq, B), D
-// threads, thread = output column.  Splits are taken 16 at a time with all
-// their loads issued together, merged online against a running maximum.
-template <typename OutT>
-__global__ void tree_attn_combine_kernel(int T, int Hq, int D, int max_slots, int nsplit_max,
-                                         const int32_t* __restrict__ prefix_len,
-                                         const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-                                         OutT* __restrict__ out) {
-  constexpr int U = 16;
-  const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int d = threadIdx.x;
+// Merge the splits of each (sequence, head, query) by log-sum-exp.  D/4
+// threads per query, four output columns each (16-byte partial loads); a
+// 256-thread workgroup takes 1024/D consecutive queries of one (sequence,
+// head), so its loads of one split are one contiguous run.  Splits are taken
+// eight at a time with all their loads issued together, merged online
+// against a running maximum.
+template <typename OutT, int D>
+__global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, int Hq, int max_slots, int nsplit_max,
+                                                              const int32_t* __restrict__ prefix_len,
+                                                              const float* __restrict__ part_o,
+                                                              const float2* __restrict__ part_ml,
+                                                              OutT* __restrict__ out) {
+  constexpr int TPQ = D / 4, QPW = 256 / TPQ, U = 8;
+  const int t = threadIdx.x % TPQ;
+  const long long Q = static_cast<long long>(blockIdx.x) * QPW + threadIdx.x / TPQ;
+  if (Q >= static_cast<long long>(B) * Hq * T) return;
+  const int qi = static_cast<int>(Q % T);
+  const int h = static_cast<int>((Q / T) % Hq);
+  const int b = static_cast<int>(Q / (static_cast<long long>(T) * Hq));
   int L = prefix_len[b];
   if (L > max_slots - T) L = max_slots - T;
   if (L < 0) L = 0;
   const int ns = num_splits(L + T);
   const size_t bh = static_cast<size_t>(b) * Hq + h;
   const float NEG = -__builtin_huge_valf();
-  float M = NEG, acc = 0.f, den = 0.f;
+  float M = NEG, den = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < ns; s0 += U) {
     float2 ml[U];
-    float ov[U];
+    float4 ov[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const size_t row = (bh * nsplit_max + min(s0 + u, ns - 1)) * T + qi;
       ml[u] = part_ml[row];
-      ov[u] = part_o[row * D + d];
+      ov[u] = *reinterpret_cast<const float4*>(part_o + row * D + 4 * t);
     }
     float bm = NEG;
 #pragma unroll
@@ -468,20 +471,29 @@ __global__ void tree_attn_combine_kernel(int T, int Hq, int D, int max_slots, in
     const float Mn = fmaxf(M, bm);
     const float ref = Mn == NEG ? 0.f : Mn;
     const float f = M == NEG ? 0.f : exp2f(M - ref);
-    acc *= f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] *= f;
     den *= f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float w = (s0 + u < ns && ml[u].x != NEG) ? exp2f(ml[u].x - ref) : 0.f;
-      acc += w * ov[u];
+      acc[0] += w * ov[u].x;
+      acc[1] += w * ov[u].y;
+      acc[2] += w * ov[u].z;
+      acc[3] += w * ov[u].w;
       den += w * ml[u].y;
     }
     M = Mn;
   }
-  const float v = acc / den;
-  const size_t o = ((static_cast<size_t>(b) * T + qi) * Hq + h) * D + d;
-  if constexpr (sizeof(OutT) == 2) out[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-  else out[o] = v;
+  const size_t o = ((static_cast<size_t>(b) * T + qi) * Hq + h) * D + 4 * t;
+  if constexpr (sizeof(OutT) == 2) {
+    uint2 w;
+    w.x = f32_to_bf16_bits(acc[0] / den) | (f32_to_bf16_bits(acc[1] / den) << 16);
+    w.y = f32_to_bf16_bits(acc[2] / den) | (f32_to_bf16_bits(acc[3] / den) << 16);
+    *reinterpret_cast<uint2*>(out + o) = w;
+  } else {
+    *reinterpret_cast<float4*>(out + o) = float4{acc[0] / den, acc[1] / den, acc[2] / den, acc[3] / den};
+  }
 }
 
 // f32: one wave per (sequence, head, query); lanes over keys for scores,
@@ -614,7 +626,13 @@ extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int
                        static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml);
   rc = medusa_host::hip_check("medusa_tree_attention launch");
   if (rc != MEDUSA_OK) return rc;
-  hipLaunchKernelGGL(tree_attn_combine_kernel<uint16_t>, dim3(T, Hq, B), dim3(d), 0, st, T, Hq, d, max_slots,
-                     nsm, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
+  const long long nq = static_cast<long long>(B) * Hq * T;
+  const unsigned cgrid = static_cast<unsigned>((nq * (d / 4) + 255) / 256);
+  if (d == 128)
+    hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 128>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
+                       nsm, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 64>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
+                       nsm, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
   return medusa_host::hip_check("medusa_tree_attention combine launch");
 }

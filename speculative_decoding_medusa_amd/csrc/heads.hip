@@ -724,8 +724,6 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_stream_kernel(
     if (c < nchunks) MEDUSA_STREAM_STEP(c, wa);
   }
 #undef MEDUSA_STREAM_STEP
-  __syncthreads();
-
   // every wave publishes its own lists (list wg * 4 + wave of head j)
   const int nlists = G * kHeadsWaves;
   for (int b = 0; b < B; ++b) {
@@ -925,41 +923,64 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   const int e0 = 8 * lane;
   const float NEG = -__builtin_huge_valf();
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  if (tid < kHeadsWaves * 2) s_lc[tid >> 1][tid & 1] = 0;
-
-  // r split into bf16 hi/lo at this lane's positions
-  u32x4 ahi[NB][NSTMAX], alo[NB][NSTMAX];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int s = 0; s < NSTMAX; ++s) {
-      const int k0 = 512 * s + e0;
-      ahi[b][s] = zero;
-      alo[b][s] = zero;
-      if (b < B && k0 < H) {
-        const float* x = r + (static_cast<size_t>(b) * K + j) * H + k0;
-        const float4 x0 = *reinterpret_cast<const float4*>(x);
-        const float4 x1 = *reinterpret_cast<const float4*>(x + 4);
-        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint32_t hb[8], lb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hb[e] = f32_to_bf16_bits(xs[e]);
-          lb[e] = f32_to_bf16_bits(xs[e] - __uint_as_float(hb[e] << 16));
-        }
-        ahi[b][s] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-        alo[b][s] = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
-      }
-    }
-  }
-  __syncthreads();
-
-  const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
-  const int r1 = min(r0 + rows_per_wave, V);
-  const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
   lds_vfloat* my_v = (lds_vfloat*)&s_lv[wave][0][0];
   lds_vint* my_i = (lds_vint*)&s_li[wave][0][0];
   lds_vint* my_c = (lds_vint*)&s_lc[wave][0];
+  if (lane < 2) my_c[lane] = 0;   // a wave's lists are its own: no barrier
+
+  const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
+  const int r1 = min(r0 + rows_per_wave, V);
+  const int last = r1 - 1;   // r1 >= 1; an empty block (r0 > last) still loads row `last`
+  const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
+
+  // Prologue in one memory round trip: a round of r loads (clamped, with no
+  // branch, so all are in flight together), the block's first two weight
+  // rows, then r's split into exact bf16 hi/lo planes at this lane's
+  // positions while the rows arrive.  Larger r (two sequences, wide rows)
+  // takes further rounds of eight 32-byte pieces.
+  constexpr int P = NB * NSTMAX;
+  constexpr int GR = P < 8 ? P : 8;
+  u32x4 ahi[NB][NSTMAX], alo[NB][NSTMAX];
+  u32x4 wa[NSTMAX], wb[NSTMAX];
+#pragma unroll
+  for (int p0 = 0; p0 < P; p0 += GR) {
+    float4 x[GR][2];
+#pragma unroll
+    for (int q = 0; q < GR; ++q) {
+      const int p = p0 + q;
+      if (p < P) {
+        const int b = p / NSTMAX, s = p % NSTMAX;
+        const float* src = r + (static_cast<size_t>(min(b, B - 1)) * K + j) * H + min(512 * s + e0, H - 8);
+        x[q][0] = *reinterpret_cast<const float4*>(src);
+        x[q][1] = *reinterpret_cast<const float4*>(src + 4);
+      }
+    }
+    if (p0 == 0) {
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0, last)) * H, H, e0, wa);
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0 + 1, last)) * H, H, e0, wb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < GR; ++q) {
+      const int p = p0 + q;
+      if (p < P) {
+        const int b = p / NSTMAX, s = p % NSTMAX;
+        const bool valid = b < B && 512 * s + e0 < H;
+        const float xs[8] = {x[q][0].x, x[q][0].y, x[q][0].z, x[q][0].w,
+                             x[q][1].x, x[q][1].y, x[q][1].z, x[q][1].w};
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hw[e] = pack_bf16x2(xs[2 * e], xs[2 * e + 1]);
+          lw[e] = pack_bf16x2(xs[2 * e] - __uint_as_float(hw[e] << 16),
+                              xs[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
+        }
+        ahi[b][s] = valid ? u32x4{hw[0], hw[1], hw[2], hw[3]} : zero;
+        alo[b][s] = valid ? u32x4{lw[0], lw[1], lw[2], lw[3]} : zero;
+      }
+    }
+  }
+
   float gath[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) gath[b] = NEG;
@@ -988,37 +1009,31 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     }
   };
 
-  if (r1 > r0) {
-    // Rotated double buffer: both buffers are in flight before the loop, so
-    // on every path into the loop header the older buffer's eight loads are
-    // exactly the ones to wait for.  Loads past the block reload its last row
-    // (an L2 hit) so that no load is conditional.  The scheduling barriers keep
-    // each refill after the MFMAs that free its registers and before the next
-    // buffer's MFMAs.
-    u32x4 wa[NSTMAX], wb[NSTMAX];
-    float lg[NB];
-    const int last = r1 - 1;
-    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(r0) * H, H, e0, wa);
-    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0 + 1, last)) * H, H, e0, wb);
-    int row = r0;
-    for (; row + 1 < r1; row += 2) {
-      __builtin_amdgcn_sched_barrier(0);
-      diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
-      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
-      __builtin_amdgcn_sched_barrier(0);
-      offer(row, lg);
-      diag_row_logits<NSTMAX, NB>(wb, ahi, alo, H, e0, n, g, lg);
-      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
-      __builtin_amdgcn_sched_barrier(0);
-      offer(row + 1, lg);
-    }
-    if (row < r1) {
-      diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
-      offer(row, lg);
-    }
+  // Rotated double buffer: both buffers are in flight before the loop, so on
+  // every path into the loop header the older buffer's eight loads are exactly
+  // the ones to wait for.  Loads past the block reload its last row (an L2
+  // hit) so that no load is conditional.  The scheduling barriers keep each
+  // refill after the MFMAs that free its registers and before the next
+  // buffer's MFMAs.  An empty block runs neither the loop nor the tail; with
+  // no branch around both, the prologue's loads cannot be sunk below its
+  // conversions.
+  float lg[NB];
+  int row = r0;
+  for (; row + 1 < r1; row += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
+    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    offer(row, lg);
+    diag_row_logits<NSTMAX, NB>(wb, ahi, alo, H, e0, n, g, lg);
+    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    offer(row + 1, lg);
   }
-  __syncthreads();
-
+  if (row < r1) {
+    diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
+    offer(row, lg);
+  }
   // every wave publishes its own lists (list wg * 4 + wave of head j)
   const int nlists = G * kHeadsWaves;
   for (int b = 0; b < B; ++b) {
