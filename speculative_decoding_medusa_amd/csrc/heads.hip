@@ -176,6 +176,35 @@ __device__ __forceinline__ void topk_insert(TopkLists& tl, int b, int k, float v
   topk_insert_list((lds_vfloat*)tl.v[b], (lds_vint*)tl.id[b], (lds_vint*)&tl.count[b], k, v, id, mask, lane);
 }
 
+// The same insertion into a sorted list held in registers: lane t < cnt
+// holds the list's t-th entry (cnt wave-uniform, k <= 64).  Each candidate
+// and a full list's last entry are read out as scalars, so a candidate costs
+// a few ALU operations and no memory access; one that beats entries moves
+// them down one lane.
+__device__ __forceinline__ void topk_reg_insert(float& lv, int& li, int& cnt, int k, float v, int id,
+                                                uint64_t mask, int lane) {
+  while (mask) {
+    const int src = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+    mask &= mask - 1;
+    const float cv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+    const int ci = __builtin_amdgcn_readlane(id, src);
+    if (cnt == k && !beats(cv, ci, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), k - 1)),
+                           __builtin_amdgcn_readlane(li, k - 1)))
+      continue;
+    const int pos = __popcll(ballot(lane < cnt && beats(lv, li, cv, ci)));
+    const float pv = __shfl(lv, lane > 0 ? lane - 1 : 0);
+    const int pi = __shfl(li, lane > 0 ? lane - 1 : 0);
+    if (lane == pos) {
+      lv = cv;
+      li = ci;
+    } else if (lane > pos) {
+      lv = pv;
+      li = pi;
+    }
+    cnt = cnt + 1 < k ? cnt + 1 : k;
+  }
+}
+
 // Block-wide best (by `beats`) of one (value, id) per thread; all threads get it.
 __device__ void block_best(float& v, int& id, float* sv, int* si) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -756,77 +785,74 @@ __host__ __device__ constexpr int diag_nstmax(int nst) { return nst <= 4 ? 4 : (
 template <int NSTMAX>
 __device__ __forceinline__ void diag_load_row(const uint16_t* __restrict__ wrow, int H, int e0, u32x4 (&buf)[NSTMAX]) {
 #pragma unroll
-  for (int s = 0; s < NSTMAX; ++s) buf[s] = ld16_stream(wrow + min(512 * s + e0, H - 8));
+  for (int s = 0; s < NSTMAX; ++s) buf[s] = ld16_stream(wrow + static_cast<uint32_t>(min(512 * s + e0, H - 8)));
 }
 
-// Sum of the 16 diagonal lanes (lanes 4q..4q+3 of each 16-lane row q hold
-// one value each, zero elsewhere): two DPP quad adds, then the four quad
-// sums read as scalars.  The result is wave-uniform.
-__device__ __forceinline__ float diag_sum(float d) {
-  int x = __float_as_int(d);
-  d += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, true));  // quad_perm(1,0,3,2)
-  x = __float_as_int(d);
-  d += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, true));  // quad_perm(2,3,0,1)
-  x = __float_as_int(d);
+// Trace of a 16x16 MFMA result.  Lane (g, n) holds C[4g + i][n] in a[i], so
+// C[n][n] is component n % 4 of lane 16 (n / 4) + n: the diagonal fills the
+// four whole quads of lanes 0-3, 20-23, 40-43 and 60-63, quad lane i holding
+// it in a[i].  Each quad's first lane gathers its neighbours' components with
+// DPP quad broadcasts; the four quad sums are read as scalars.  The result
+// is wave-uniform.
+__device__ __forceinline__ float diag_trace(const f32x4& a) {
+  float d = a[0];
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a[1]), 0x55, 0xf, 0xf, true));  // quad_perm(1,1,1,1)
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a[2]), 0xAA, 0xf, 0xf, true));  // quad_perm(2,2,2,2)
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a[3]), 0xFF, 0xf, 0xf, true));  // quad_perm(3,3,3,3)
+  const int x = __float_as_int(d);
   return (__int_as_float(__builtin_amdgcn_readlane(x, 0)) + __int_as_float(__builtin_amdgcn_readlane(x, 20))) +
          (__int_as_float(__builtin_amdgcn_readlane(x, 40)) + __int_as_float(__builtin_amdgcn_readlane(x, 60)));
 }
 
-template <int NSTMAX, int NB>
+// Logits of one streamed row against r's hi and lo bf16 planes: both planes
+// accumulate into one chain (the matrix core pipelines a dependent
+// accumulator), then one trace.  FULL: H is exactly NSTMAX * 512, so no
+// piece lies past the row and no select is needed; otherwise such pieces
+// (clamped reloads of the row's last 16 bytes) are replaced by zeros.
+template <int NSTMAX, int NB, bool FULL>
 __device__ __forceinline__ void diag_row_logits(const u32x4 (&buf)[NSTMAX], const u32x4 (&ahi)[NB][NSTMAX],
-                                                const u32x4 (&alo)[NB][NSTMAX], int H, int e0, int n, int g,
+                                                const u32x4 (&alo)[NB][NSTMAX], int H, int e0,
                                                 float (&logit)[NB]) {
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  // hi and lo products accumulate separately: two independent MFMA chains
-  f32x4 acc_hi[NB], acc_lo[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    acc_hi[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_lo[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int s = 0; s < NSTMAX; ++s) {
-    const u32x4 w = 512 * s + e0 < H ? buf[s] : zero;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      acc_hi[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi[b][s]), as_bf16x8(w), acc_hi[b], 0, 0, 0);
-      acc_lo[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo[b][s]), as_bf16x8(w), acc_lo[b], 0, 0, 0);
-    }
-  }
-  // lane (g, n) holds C[4g + i][n]; the diagonal C[n][n] sits at g = n / 4, i = n % 4
-  const int i = n & 3;
-  const bool on_diag = g == (n >> 2);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const f32x4 a = acc_hi[b] + acc_lo[b];
-    const float d = i == 0 ? a[0] : (i == 1 ? a[1] : (i == 2 ? a[2] : a[3]));
-    logit[b] = diag_sum(on_diag ? d : 0.f);
-  }
-}
-
-// Dot products of one streamed row with a bf16 vector held in one plane
-// (exact): same lane layout and diagonal read-out as diag_row_logits.
-template <int NSTMAX, int NB>
-__device__ __forceinline__ void diag_row_dot(const u32x4 (&buf)[NSTMAX], const u32x4 (&a)[NB][NSTMAX], int H, int e0,
-                                             int n, int g, float (&dot)[NB]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NSTMAX; ++s) {
-    const u32x4 w = 512 * s + e0 < H ? buf[s] : zero;
+    const u32x4 w = (FULL || 512 * s + e0 < H) ? buf[s] : zero;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) logit[b] = diag_trace(acc[b]);
+}
+
+// Dot products of one streamed row with a bf16 vector held in one plane
+// (exact): same lane layout and trace as diag_row_logits.
+template <int NSTMAX, int NB, bool FULL>
+__device__ __forceinline__ void diag_row_dot(const u32x4 (&buf)[NSTMAX], const u32x4 (&a)[NB][NSTMAX], int H, int e0,
+                                             float (&dot)[NB]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSTMAX; ++s) {
+    const u32x4 w = (FULL || 512 * s + e0 < H) ? buf[s] : zero;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
   }
-  const int i = n & 3;
-  const bool on_diag = g == (n >> 2);
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const float d = i == 0 ? acc[b][0] : (i == 1 ? acc[b][1] : (i == 2 ? acc[b][2] : acc[b][3]));
-    dot[b] = diag_sum(on_diag ? d : 0.f);
-  }
+  for (int b = 0; b < NB; ++b) dot[b] = diag_trace(acc[b]);
+}
+
+// Put a wave-uniform value into lane `slot` (uniform) of v.
+__device__ __forceinline__ float put_lane(float v, float x, int slot) {
+  return static_cast<int>(threadIdx.x & 63) == slot ? x : v;
 }
 
 // ------------------------------------------------------- K1, row-diagonal
@@ -835,15 +861,15 @@ __device__ __forceinline__ void diag_row_dot(const u32x4 (&buf)[NSTMAX], const u
 // instruction) against h, gathers one row's dot product per lane, and every
 // 64 rows (and at the end) applies r = h + SiLU(dot + b1) to the gathered
 // rows in parallel, one coalesced store per sequence.
-template <int NSTMAX, int NB>
+template <int NSTMAX, int NB, bool FULL>
 __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int H, int K, int rows_per_wave,
                                                                       const uint16_t* __restrict__ hidden,
                                                                       const uint16_t* __restrict__ w1,
                                                                       const uint16_t* __restrict__ b1,
                                                                       float* __restrict__ r) {
   const int j = blockIdx.y, wg = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  // the wave index made uniform: rows, addresses and gather slots in scalars
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e0 = 8 * lane;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   u32x4 ah[NB][NSTMAX];
@@ -864,8 +890,7 @@ __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int
   auto take = [&](int row, const float (&dot)[NB]) {
     const int slot = (row - r0) & 63;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      if (lane == slot) gath[b] = dot[b];
+    for (int b = 0; b < NB; ++b) gath[b] = put_lane(gath[b], dot[b], slot);
     if (slot == 63 || row == r1 - 1) {
       const int myrow = row - slot + lane;
       if (lane <= slot) {
@@ -891,43 +916,35 @@ __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int
   int row = r0;
   for (; row + 1 < r1; row += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_dot<NSTMAX, NB>(wa, ah, H, e0, n, g, dot);
+    diag_row_dot<NSTMAX, NB, FULL>(wa, ah, H, e0, dot);
     diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
     __builtin_amdgcn_sched_barrier(0);
     take(row, dot);
-    diag_row_dot<NSTMAX, NB>(wb, ah, H, e0, n, g, dot);
+    diag_row_dot<NSTMAX, NB, FULL>(wb, ah, H, e0, dot);
     diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
     __builtin_amdgcn_sched_barrier(0);
     take(row + 1, dot);
   }
   if (row < r1) {
-    diag_row_dot<NSTMAX, NB>(wa, ah, H, e0, n, g, dot);
+    diag_row_dot<NSTMAX, NB, FULL>(wa, ah, H, e0, dot);
     take(row, dot);
   }
 }
 
-template <int NSTMAX, int NB>
+template <int NSTMAX, int NB, bool FULL>
 __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     int B, int H, int V, int K, int k, int rows_per_wave, int G, const float* __restrict__ r,
     const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
-  __shared__ float s_lv[kHeadsWaves][2][kMaxTopk];
-  __shared__ int s_li[kHeadsWaves][2][kMaxTopk];
-  __shared__ int s_lc[kHeadsWaves][2];
   const int j = blockIdx.y, wg = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  // the wave index made uniform: rows, addresses and gather slots in scalars
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // lane l owns elements [512s + 8l, +8): one wave instruction reads 1 KB in
   // lane order (fully coalesced); any one-to-one assignment of 8-element
   // pieces to lanes gives the same trace as long as A uses the same one
   const int e0 = 8 * lane;
   const float NEG = -__builtin_huge_valf();
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  lds_vfloat* my_v = (lds_vfloat*)&s_lv[wave][0][0];
-  lds_vint* my_i = (lds_vint*)&s_li[wave][0][0];
-  lds_vint* my_c = (lds_vint*)&s_lc[wave][0];
-  if (lane < 2) my_c[lane] = 0;   // a wave's lists are its own: no barrier
-
   const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
   const int r1 = min(r0 + rows_per_wave, V);
   const int last = r1 - 1;   // r1 >= 1; an empty block (r0 > last) still loads row `last`
@@ -981,16 +998,24 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     }
   }
 
-  float gath[NB];
+  // per sequence: gathered logits, and the wave's sorted top-k list in
+  // registers (lane t holds entry t)
+  float gath[NB], lv[NB];
+  int li[NB], cnt[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) gath[b] = NEG;
+  for (int b = 0; b < NB; ++b) {
+    gath[b] = NEG;
+    lv[b] = NEG;
+    li[b] = -1;
+    cnt[b] = 0;
+  }
 
   // gather row `row`'s logits into lane (row - r0) % 64; flush every 64 rows
   auto offer = [&](int row, const float (&lg)[NB]) {
     const int slot = (row - r0) & 63;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (lane == slot) gath[b] = lg[b];
+      gath[b] = put_lane(gath[b], lg[b], slot);
       if (logits_out != nullptr && lane == 0 && b < B) logits_out[(static_cast<size_t>(b) * K + j) * V + row] = lg[b];
     }
     if (slot == 63 || row == r1 - 1) {
@@ -999,11 +1024,12 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
       for (int b = 0; b < NB; ++b) {
         if (b >= B) continue;
         const float v = gath[b];
-        const int cnt = my_c[b];
-        const bool ok = lane <= slot && (v == v) &&
-                        (cnt < k || beats(v, myrow, my_v[b * kMaxTopk + k - 1], my_i[b * kMaxTopk + k - 1]));
+        bool ok = lane <= slot && (v == v);
+        if (cnt[b] == k)
+          ok = ok && beats(v, myrow, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[b]), k - 1)),
+                           __builtin_amdgcn_readlane(li[b], k - 1));
         const uint64_t m = ballot(ok);
-        if (m) topk_insert_list(my_v + b * kMaxTopk, my_i + b * kMaxTopk, my_c + b, k, v, myrow, m, lane);
+        if (m) topk_reg_insert(lv[b], li[b], cnt[b], k, v, myrow, m, lane);
         gath[b] = NEG;
       }
     }
@@ -1021,27 +1047,29 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   int row = r0;
   for (; row + 1 < r1; row += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
+    diag_row_logits<NSTMAX, NB, FULL>(wa, ahi, alo, H, e0, lg);
     diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
     __builtin_amdgcn_sched_barrier(0);
     offer(row, lg);
-    diag_row_logits<NSTMAX, NB>(wb, ahi, alo, H, e0, n, g, lg);
+    diag_row_logits<NSTMAX, NB, FULL>(wb, ahi, alo, H, e0, lg);
     diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
     __builtin_amdgcn_sched_barrier(0);
     offer(row + 1, lg);
   }
   if (row < r1) {
-    diag_row_logits<NSTMAX, NB>(wa, ahi, alo, H, e0, n, g, lg);
+    diag_row_logits<NSTMAX, NB, FULL>(wa, ahi, alo, H, e0, lg);
     offer(row, lg);
   }
   // every wave publishes its own lists (list wg * 4 + wave of head j)
   const int nlists = G * kHeadsWaves;
-  for (int b = 0; b < B; ++b) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= B) continue;
     const size_t base = ((static_cast<size_t>(j) * B + b) * nlists + wg * kHeadsWaves + wave) * k;
     if (lane < k) {
-      const bool have = lane < my_c[b];
-      cand_v[base + lane] = have ? my_v[b * kMaxTopk + lane] : NEG;
-      cand_i[base + lane] = have ? my_i[b * kMaxTopk + lane] : -1;
+      const bool have = lane < cnt[b];
+      cand_v[base + lane] = have ? lv[b] : NEG;
+      cand_i[base + lane] = have ? li[b] : -1;
     }
   }
 }
@@ -1185,8 +1213,12 @@ int launch_resblock(int dtype, int B, int H, int K, const void* hidden, const vo
   do {                                                                                                     \
     const int rpw = resblock_rows_per_wave(H, K, kResblockWavesPerSimd);                                   \
     const int G = (H + kHeadsWaves * rpw - 1) / (kHeadsWaves * rpw);                                       \
-    hipLaunchKernelGGL((resblock_diag_kernel<NS, NB>), dim3(G, K), dim3(kHeadsThreads), 0, st, B, H, K, rpw, \
-                       hh, ww, bb, r);                                                                     \
+    if (H == (NS) * 512)                                                                                   \
+      hipLaunchKernelGGL((resblock_diag_kernel<NS, NB, true>), dim3(G, K), dim3(kHeadsThreads), 0, st, B, H, \
+                         K, rpw, hh, ww, bb, r);                                                             \
+    else                                                                                                   \
+      hipLaunchKernelGGL((resblock_diag_kernel<NS, NB, false>), dim3(G, K), dim3(kHeadsThreads), 0, st, B, \
+                         H, K, rpw, hh, ww, bb, r);                                                          \
   } while (0)
     const int ns = diag_nstmax(nst);
     if (ns == 4) {
@@ -1226,8 +1258,12 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
 #define MEDUSA_DIAG_LAUNCH(NS, NB)                                                                            \
   do {                                                                                                        \
     lg = lm_grid(dtype, B, H, V, K, topk, kDiagWavesPerSimd);                                                 \
-    hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, V, K,  \
-                       topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);      \
+    if (H == (NS) * 512)                                                                                      \
+      hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, true>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H,  \
+                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);          \
+    else                                                                                                      \
+      hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, false>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, \
+                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);          \
   } while (0)
     const int ns = diag_nstmax(lg.nst);
     if (ns == 4) {
