@@ -806,13 +806,17 @@ __device__ __forceinline__ float diag_trace(const f32x4& a) {
 
 // Logits of one streamed row against r's hi and lo bf16 planes: both planes
 // accumulate into one chain (the matrix core pipelines a dependent
-// accumulator), then one trace.  FULL: H is exactly NSTMAX * 512, so no
-// piece lies past the row and no select is needed; otherwise such pieces
-// (clamped reloads of the row's last 16 bytes) are replaced by zeros.
-template <int NSTMAX, int NB, bool FULL>
-__device__ __forceinline__ void diag_row_logits(const u32x4 (&buf)[NSTMAX], const u32x4 (&ahi)[NB][NSTMAX],
+// accumulator), then one trace.  With REFILL, each 16-byte piece of the
+// buffer is reloaded from `next` as soon as its two MFMAs have read it, so a
+// wave keeps close to two rows of loads in flight through the chain instead
+// of one (the scheduling barriers pin that order).  FULL: H is exactly
+// NSTMAX * 512, so no piece lies past the row and no select is needed;
+// otherwise such pieces (clamped reloads of the row's last 16 bytes) are
+// replaced by zeros.
+template <int NSTMAX, int NB, bool FULL, bool REFILL>
+__device__ __forceinline__ void diag_row_logits(u32x4 (&buf)[NSTMAX], const u32x4 (&ahi)[NB][NSTMAX],
                                                 const u32x4 (&alo)[NB][NSTMAX], int H, int e0,
-                                                float (&logit)[NB]) {
+                                                const uint16_t* __restrict__ next, float (&logit)[NB]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc[NB];
 #pragma unroll
@@ -825,16 +829,20 @@ __device__ __forceinline__ void diag_row_logits(const u32x4 (&buf)[NSTMAX], cons
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
     }
+    if (REFILL) {
+      buf[s] = ld16_stream(next + static_cast<uint32_t>(min(512 * s + e0, H - 8)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) logit[b] = diag_trace(acc[b]);
 }
 
 // Dot products of one streamed row with a bf16 vector held in one plane
-// (exact): same lane layout and trace as diag_row_logits.
-template <int NSTMAX, int NB, bool FULL>
-__device__ __forceinline__ void diag_row_dot(const u32x4 (&buf)[NSTMAX], const u32x4 (&a)[NB][NSTMAX], int H, int e0,
-                                             float (&dot)[NB]) {
+// (exact): same lane layout, trace and piecewise refill as diag_row_logits.
+template <int NSTMAX, int NB, bool FULL, bool REFILL>
+__device__ __forceinline__ void diag_row_dot(u32x4 (&buf)[NSTMAX], const u32x4 (&a)[NB][NSTMAX], int H, int e0,
+                                             const uint16_t* __restrict__ next, float (&dot)[NB]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc[NB];
 #pragma unroll
@@ -845,6 +853,10 @@ __device__ __forceinline__ void diag_row_dot(const u32x4 (&buf)[NSTMAX], const u
 #pragma unroll
     for (int b = 0; b < NB; ++b)
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[b][s]), as_bf16x8(w), acc[b], 0, 0, 0);
+    if (REFILL) {
+      buf[s] = ld16_stream(next + static_cast<uint32_t>(min(512 * s + e0, H - 8)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) dot[b] = diag_trace(acc[b]);
@@ -916,17 +928,14 @@ __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int
   int row = r0;
   for (; row + 1 < r1; row += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_dot<NSTMAX, NB, FULL>(wa, ah, H, e0, dot);
-    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
-    __builtin_amdgcn_sched_barrier(0);
+    diag_row_dot<NSTMAX, NB, FULL, true>(wa, ah, H, e0, wbase + static_cast<size_t>(min(row + 2, last)) * H, dot);
     take(row, dot);
-    diag_row_dot<NSTMAX, NB, FULL>(wb, ah, H, e0, dot);
-    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
     __builtin_amdgcn_sched_barrier(0);
+    diag_row_dot<NSTMAX, NB, FULL, true>(wb, ah, H, e0, wbase + static_cast<size_t>(min(row + 3, last)) * H, dot);
     take(row + 1, dot);
   }
   if (row < r1) {
-    diag_row_dot<NSTMAX, NB, FULL>(wa, ah, H, e0, dot);
+    diag_row_dot<NSTMAX, NB, FULL, false>(wa, ah, H, e0, wbase, dot);
     take(row, dot);
   }
 }
@@ -1035,29 +1044,27 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     }
   };
 
-  // Rotated double buffer: both buffers are in flight before the loop, so on
-  // every path into the loop header the older buffer's eight loads are exactly
-  // the ones to wait for.  Loads past the block reload its last row (an L2
-  // hit) so that no load is conditional.  The scheduling barriers keep each
-  // refill after the MFMAs that free its registers and before the next
-  // buffer's MFMAs.  An empty block runs neither the loop nor the tail; with
-  // no branch around both, the prologue's loads cannot be sunk below its
-  // conversions.
+  // Rotated double buffer: both buffers are in flight before the loop, and
+  // each piece is refilled with the row two ahead as soon as its MFMAs have
+  // read it, so every MFMA waits only for the piece it consumes, with about
+  // two rows of loads still in flight.  Loads past the block reload its last
+  // row (an L2 hit) so that no load is conditional.  An empty block runs
+  // neither the loop nor the tail; with no branch around both, the
+  // prologue's loads cannot be sunk below its conversions.
   float lg[NB];
   int row = r0;
   for (; row + 1 < r1; row += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_logits<NSTMAX, NB, FULL>(wa, ahi, alo, H, e0, lg);
-    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 2, last)) * H, H, e0, wa);
-    __builtin_amdgcn_sched_barrier(0);
+    diag_row_logits<NSTMAX, NB, FULL, true>(wa, ahi, alo, H, e0, wbase + static_cast<size_t>(min(row + 2, last)) * H,
+                                            lg);
     offer(row, lg);
-    diag_row_logits<NSTMAX, NB, FULL>(wb, ahi, alo, H, e0, lg);
-    diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(row + 3, last)) * H, H, e0, wb);
     __builtin_amdgcn_sched_barrier(0);
+    diag_row_logits<NSTMAX, NB, FULL, true>(wb, ahi, alo, H, e0, wbase + static_cast<size_t>(min(row + 3, last)) * H,
+                                            lg);
     offer(row + 1, lg);
   }
   if (row < r1) {
-    diag_row_logits<NSTMAX, NB, FULL>(wa, ahi, alo, H, e0, lg);
+    diag_row_logits<NSTMAX, NB, FULL, false>(wa, ahi, alo, H, e0, wbase, lg);
     offer(row, lg);
   }
   // every wave publishes its own lists (list wg * 4 + wave of head j)
