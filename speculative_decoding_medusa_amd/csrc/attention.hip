@@ -434,7 +434,10 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
 // 256-thread workgroup takes 1024/D consecutive queries of one (sequence,
 // head), so its loads of one split are one contiguous run.  Splits are taken
 // eight at a time with all their loads issued together, merged online
-// against a running maximum.
+// against a running maximum.  The first eight are addressed within the
+// workspace's nsplit_max splits, so their loads go out with the prefix
+// length's in one round trip; splits at or past the sequence's own count
+// (never written by this call) are dropped by selects, never multiplied.
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, int Hq, int max_slots, int nsplit_max,
                                                               const int32_t* __restrict__ prefix_len,
@@ -443,28 +446,33 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
                                                               OutT* __restrict__ out) {
   constexpr int TPQ = D / 4, QPW = 256 / TPQ, U = 8;
   const int t = threadIdx.x % TPQ;
-  const long long Q = static_cast<long long>(blockIdx.x) * QPW + threadIdx.x / TPQ;
-  if (Q >= static_cast<long long>(B) * Hq * T) return;
-  const int qi = static_cast<int>(Q % T);
-  const int h = static_cast<int>((Q / T) % Hq);
-  const int b = static_cast<int>(Q / (static_cast<long long>(T) * Hq));
-  int L = prefix_len[b];
-  if (L > max_slots - T) L = max_slots - T;
-  if (L < 0) L = 0;
-  const int ns = num_splits(L + T);
+  // B * Hq * T * D / 4 stays below 2^31 (B <= 16, Hq <= 1024, T <= 256)
+  const unsigned Q = blockIdx.x * QPW + threadIdx.x / TPQ;
+  if (Q >= static_cast<unsigned>(B * Hq * T)) return;
+  const int qi = static_cast<int>(Q % static_cast<unsigned>(T));
+  const int h = static_cast<int>((Q / static_cast<unsigned>(T)) % static_cast<unsigned>(Hq));
+  const int b = static_cast<int>(Q / static_cast<unsigned>(T * Hq));
   const size_t bh = static_cast<size_t>(b) * Hq + h;
   const float NEG = -__builtin_huge_valf();
   float M = NEG, den = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += U) {
-    float2 ml[U];
-    float4 ov[U];
+  float2 ml[U];
+  float4 ov[U];
+  auto load = [&](int s0, int smax) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t row = (bh * nsplit_max + min(s0 + u, ns - 1)) * T + qi;
+      const size_t row = (bh * nsplit_max + min(s0 + u, smax - 1)) * T + qi;
       ml[u] = part_ml[row];
       ov[u] = *reinterpret_cast<const float4*>(part_o + row * D + 4 * t);
     }
+  };
+  load(0, nsplit_max);
+  int L = prefix_len[b];
+  if (L > max_slots - T) L = max_slots - T;
+  if (L < 0) L = 0;
+  const int ns = num_splits(L + T);
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    if (s0 > 0) load(s0, ns);
     float bm = NEG;
 #pragma unroll
     for (int u = 0; u < U; ++u) bm = fmaxf(bm, s0 + u < ns ? ml[u].x : NEG);
@@ -476,12 +484,14 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
     den *= f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = (s0 + u < ns && ml[u].x != NEG) ? exp2f(ml[u].x - ref) : 0.f;
-      acc[0] += w * ov[u].x;
-      acc[1] += w * ov[u].y;
-      acc[2] += w * ov[u].z;
-      acc[3] += w * ov[u].w;
-      den += w * ml[u].y;
+      if (s0 + u < ns && ml[u].x != NEG) {
+        const float w = exp2f(ml[u].x - ref);
+        acc[0] += w * ov[u].x;
+        acc[1] += w * ov[u].y;
+        acc[2] += w * ov[u].z;
+        acc[3] += w * ov[u].w;
+        den += w * ml[u].y;
+      }
     }
     M = Mn;
   }
@@ -626,8 +636,7 @@ extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int
                        static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml);
   rc = medusa_host::hip_check("medusa_tree_attention launch");
   if (rc != MEDUSA_OK) return rc;
-  const long long nq = static_cast<long long>(B) * Hq * T;
-  const unsigned cgrid = static_cast<unsigned>((nq * (d / 4) + 255) / 256);
+  const unsigned cgrid = static_cast<unsigned>((B * Hq * T * (d / 4) + 255) / 256);
   if (d == 128)
     hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 128>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
                        nsm, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
