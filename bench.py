@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)")
     return ap.parse_args()
@@ -304,6 +305,39 @@ def cpu_baseline(w, seed, min_steps=3, min_seconds=10.0, max_steps=30):
             "seconds_per_step": round(total, 3), "stage_seconds": {k: round(v, 3) for k, v in med.items()}}
 
 
+def graph_timing(step, steps):
+    """The same verify step replayed from HIP graphs: one graph per attention
+    layer (a step reads the rotating layer's cache slice), captured on a side
+    stream of default priority, then exactly `steps` replays in layer order,
+    bracketed by events on the stream they run on."""
+    import torch
+    n = step.w["n_layers"]
+    saved_stream, saved_layer = step.stream, step.layer
+    side = torch.cuda.Stream()
+    graphs = []
+    torch.cuda.synchronize()
+    for layer in range(n):
+        g = torch.cuda.CUDAGraph()
+        step.layer = layer
+        with torch.cuda.graph(g, stream=side):
+            step.stream = torch.cuda.current_stream().cuda_stream
+            step.run()
+        graphs.append(g)
+    step.stream, step.layer = saved_stream, saved_layer
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % n].replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return {"value": round(1000.0 / ms, 2), "unit": "steps/s", "ms_per_step": round(ms, 4), "graphs": n,
+            "note": "the whole step replayed from HIP graphs (one per attention layer), %d steps" % steps}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -385,6 +419,8 @@ def main():
         "stages_note": "per-stage means from a separate untimed pass of %d steps" % nb,
         "tokens_per_step": acc + 1,
     }
+    if not args.no_graph:
+        result["graph"] = graph_timing(step, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)
     print(json.dumps(result))
