@@ -92,12 +92,16 @@ enum {
  * [B][K][V].  `dtype` applies to hidden, w1, b1 and w_lm.  bf16 needs
  * H % 8 == 0, f32 needs H % 4 == 0; 1 <= topk <= min(64, V).
  *
- * Workspace: medusa_heads_workspace() bytes of device memory, no
- * initialisation needed (per-wave candidate lists and, in medusa_heads, r).
- * medusa_lm_head_topk launches two kernels on `stream`: the weight stream,
- * which leaves one sorted top-k list per wave in the workspace, then their
- * merge (radix selection on unique value/id keys).  Calls that share a
- * workspace must not run concurrently.
+ * Workspace: medusa_heads_workspace() bytes of device memory (per-wave
+ * candidate lists, one arrival count per head and, in medusa_heads, r).
+ * Its first 256 bytes must be zero before the first call that uses it
+ * (allocate it zeroed once); every call leaves them zero again.  The rest
+ * needs no initialisation.  medusa_lm_head_topk streams the weights in one
+ * kernel on `stream`; each wave leaves a sorted top-k list, and the merge
+ * of a head's lists (radix selection on unique value/id keys) runs in the
+ * last workgroup of that head to finish when they fit its 2048-key budget,
+ * in a second kernel otherwise.  Calls that share a workspace must not run
+ * concurrently.
  * ------------------------------------------------------------------- */
 size_t medusa_heads_workspace(int dtype, int B, int H, int V, int K, int topk);
 

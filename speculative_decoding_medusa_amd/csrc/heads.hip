@@ -241,6 +241,7 @@ __device__ void block_best(float& v, int& id, float* sv, int* si) {
 // against the others.
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeMaxKeys = 32;  // keys per thread: lists * k <= 32768
+constexpr int kFusedMergeKeys = 8;  // in-kernel merge: lists * k <= 256 * 8
 
 __device__ __forceinline__ uint64_t merge_key(float v, int id) {
   if (id < 0 || v != v) return 0;
@@ -254,48 +255,53 @@ __device__ __forceinline__ float merge_key_value(uint64_t x) {
   return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
 }
 
-template <int E>
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(int B, int K, int k, int lists,
-                                                                   const float* __restrict__ cand_v,
-                                                                   const int* __restrict__ cand_i,
-                                                                   int32_t* __restrict__ topk_ids,
-                                                                   float* __restrict__ topk_vals) {
-  const int b = blockIdx.x, j = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lists * k;
-  const size_t base = (static_cast<size_t>(j) * B + b) * n;
-  int32_t* oid = topk_ids + (static_cast<size_t>(b) * K + j) * k;
-  float* oval = topk_vals + (static_cast<size_t>(b) * K + j) * k;
-  __shared__ int hist[2][256];
-  __shared__ uint64_t s_prefix;
-  __shared__ int s_need, s_done, s_n;
-  __shared__ uint64_t s_keys[kMaxTopk];
+// Shared state of one radix selection.
+struct MergeSmem {
+  int hist[2][256];
+  uint64_t prefix;
+  int need, done, nsel;
+  uint64_t keys[kMaxTopk];
+};
 
-  // all loads first (clamped index, masked at use): one memory round trip
+// Top-k of the n candidates (cv, ci) by radix selection with NT threads
+// (E keys each, n <= NT * E); writes k entries of oid / oval (-1 / -inf
+// past the candidates).  Every thread of the workgroup calls it.
+template <int NT, int E, bool COHERENT>
+__device__ __forceinline__ void radix_topk(const float* __restrict__ cv, const int* __restrict__ ci, int n, int k,
+                                           int32_t* __restrict__ oid, float* __restrict__ oval, MergeSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // all loads first (clamped index, masked at use): one memory round trip;
+  // COHERENT: lists written by other workgroups of the running kernel, read
+  // with device-scope loads
   float v[E];
   int id[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const int e = min(i * kMergeThreads + tid, n - 1);
-    v[i] = cand_v[base + e];
-    id[i] = cand_i[base + e];
+    const int e = min(i * NT + tid, n - 1);
+    if (COHERENT) {
+      v[i] = __hip_atomic_load(cv + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      id[i] = __hip_atomic_load(ci + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      v[i] = cv[e];
+      id[i] = ci[e];
+    }
   }
-  if (tid < 256) hist[0][tid] = 0;
+  for (int x = tid; x < 256; x += NT) sm.hist[0][x] = 0;
   if (tid == 0) {
-    s_prefix = 0;
-    s_need = k;
-    s_done = 0;
-    s_n = 0;
+    sm.prefix = 0;
+    sm.need = k;
+    sm.done = 0;
+    sm.nsel = 0;
   }
   uint64_t key[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i) key[i] = i * kMergeThreads + tid < n ? merge_key(v[i], id[i]) : 0;
+  for (int i = 0; i < E; ++i) key[i] = i * NT + tid < n ? merge_key(v[i], id[i]) : 0;
   __syncthreads();
 
   for (int p = 0; p < 8; ++p) {
     const int shift = 56 - 8 * p;
-    const uint64_t prefix = s_prefix;
-    int* h = hist[p & 1];
+    const uint64_t prefix = sm.prefix;
+    int* h = sm.hist[p & 1];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint64_t x = key[i];
@@ -318,13 +324,13 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(int B, int K,
         const int t = __shfl_up(incl, o);
         if (lane >= o) incl += t;
       }
-      const int need = s_need;
+      const int need = sm.need;
       const int total = __shfl(incl, kWave - 1);
       if (total < need) {
         // fewer candidates than k (first pass only): take them all
         if (lane == 0) {
-          s_prefix = 1;
-          s_done = 1;
+          sm.prefix = 1;
+          sm.done = 1;
         }
       } else if (incl - sum < need && need <= incl) {
         int acc = incl - sum;
@@ -332,37 +338,52 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(int B, int K,
         for (int q = 0; q < 4; ++q) {
           if (acc < need && need <= acc + c[q]) {
             const int rest = need - acc;
-            s_prefix = prefix | (static_cast<uint64_t>(255 - 4 * lane - q) << shift);
-            s_need = rest;
-            s_done = c[q] == rest ? 1 : 0;
+            sm.prefix = prefix | (static_cast<uint64_t>(255 - 4 * lane - q) << shift);
+            sm.need = rest;
+            sm.done = c[q] == rest ? 1 : 0;
           }
           acc += c[q];
         }
       }
-    } else if (tid < 64 + 256) {
-      hist[(p + 1) & 1][tid - 64] = 0;
+    } else {
+      for (int x = tid - kWave; x < 256; x += NT - kWave) sm.hist[(p + 1) & 1][x] = 0;
     }
     __syncthreads();
-    if (s_done) break;
+    if (sm.done) break;
   }
 
-  const uint64_t thr = s_prefix;
+  const uint64_t thr = sm.prefix;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    if (key[i] != 0 && key[i] >= thr) s_keys[atomicAdd(&s_n, 1)] = key[i];
+    if (key[i] != 0 && key[i] >= thr) sm.keys[atomicAdd(&sm.nsel, 1)] = key[i];
   }
   __syncthreads();
-  const int S = s_n;  // <= k
+  const int S = sm.nsel;  // <= k
   if (tid < S) {
-    const uint64_t x = s_keys[tid];
+    const uint64_t x = sm.keys[tid];
     int rank = 0;
-    for (int t = 0; t < S; ++t) rank += s_keys[t] > x ? 1 : 0;
+    for (int t = 0; t < S; ++t) rank += sm.keys[t] > x ? 1 : 0;
     oid[rank] = static_cast<int32_t>(~static_cast<uint32_t>(x));
     oval[rank] = merge_key_value(x);
   } else if (tid < k) {
     oid[tid] = -1;
     oval[tid] = -__builtin_huge_valf();
   }
+}
+
+template <int E>
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(int B, int K, int k, int lists,
+                                                                   const float* __restrict__ cand_v,
+                                                                   const int* __restrict__ cand_i,
+                                                                   int32_t* __restrict__ topk_ids,
+                                                                   float* __restrict__ topk_vals) {
+  const int b = blockIdx.x, j = blockIdx.y;
+  const int n = lists * k;
+  const size_t base = (static_cast<size_t>(j) * B + b) * n;
+  __shared__ MergeSmem sm;
+  radix_topk<kMergeThreads, E, false>(cand_v + base, cand_i + base, n, k,
+                                      topk_ids + (static_cast<size_t>(b) * K + j) * k,
+                               topk_vals + (static_cast<size_t>(b) * K + j) * k, sm);
 }
 
 // Candidate sets beyond kMergeThreads * kMergeMaxKeys: k rounds of
@@ -944,7 +965,8 @@ template <int NSTMAX, int NB, bool FULL>
 __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     int B, int H, int V, int K, int k, int rows_per_wave, int G, const float* __restrict__ r,
     const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
+    float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i,
+    int* __restrict__ counters, int fuse) {
   const int j = blockIdx.y, wg = blockIdx.x;
   // the wave index made uniform: rows, addresses and gather slots in scalars
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1075,10 +1097,40 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     const size_t base = ((static_cast<size_t>(j) * B + b) * nlists + wg * kHeadsWaves + wave) * k;
     if (lane < k) {
       const bool have = lane < cnt[b];
-      cand_v[base + lane] = have ? lv[b] : NEG;
-      cand_i[base + lane] = have ? li[b] : -1;
+      const float pv = have ? lv[b] : NEG;
+      const int pi = have ? li[b] : -1;
+      if (fuse) {
+        __hip_atomic_store(cand_v + base + lane, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(cand_i + base + lane, pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        cand_v[base + lane] = pv;
+        cand_i[base + lane] = pi;
+      }
     }
   }
+  if (!fuse) return;
+  // The last workgroup of head j to finish merges the head's lists.  Lists
+  // are written and read with device-scope (write-through) accesses, so no
+  // cache-wide writeback or invalidation is needed: each wave waits for its
+  // stores to complete before the workgroup's arrival is counted, and the
+  // count is reset for the next call.
+  __shared__ MergeSmem sm;
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1 ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  const int n = nlists * k;
+  for (int b = 0; b < B; ++b) {
+    const size_t base = (static_cast<size_t>(j) * B + b) * n;
+    radix_topk<kHeadsThreads, kFusedMergeKeys, true>(cand_v + base, cand_i + base, n, k,
+                                                     topk_ids + (static_cast<size_t>(b) * K + j) * k,
+                                                     topk_vals + (static_cast<size_t>(b) * K + j) * k, sm);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace medusa
@@ -1088,7 +1140,9 @@ namespace {
 
 using namespace medusa;
 
-constexpr size_t kCounterBytes = 256;   // workspace header (alignment only)
+// Workspace header: one arrival count per head for the in-kernel merge
+// (zero before the first call; every call leaves it zero).
+constexpr size_t kCounterBytes = 256;
 
 struct LmGrid {
   bool diag;       // row-diagonal kernel (B <= 2)
@@ -1258,19 +1312,24 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
   LmGrid lg = lm_grid(dtype, B, H, V, K, topk, kMaxWavesPerSimd);
   char* base = static_cast<char*>(ws);
   const size_t cb = cand_bytes(dtype, B, H, V, K, topk);
+  int* counters = reinterpret_cast<int*>(base);
   float* cand_v = reinterpret_cast<float*>(base + kCounterBytes);
   int32_t* cand_i = reinterpret_cast<int32_t*>(base + kCounterBytes + cb);
+  bool fused = false;
   if (lg.diag) {
     const uint16_t* w = static_cast<const uint16_t*>(w_lm);
 #define MEDUSA_DIAG_LAUNCH(NS, NB)                                                                            \
   do {                                                                                                        \
     lg = lm_grid(dtype, B, H, V, K, topk, kDiagWavesPerSimd);                                                 \
+    fused = lg.lists * topk <= kHeadsThreads * kFusedMergeKeys;                                               \
     if (H == (NS) * 512)                                                                                      \
       hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, true>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H,  \
-                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);          \
+                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i,           \
+                         counters, fused ? 1 : 0);                                                              \
     else                                                                                                      \
       hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, false>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, \
-                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i);          \
+                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i,           \
+                         counters, fused ? 1 : 0);                                                              \
   } while (0)
     const int ns = diag_nstmax(lg.nst);
     if (ns == 4) {
@@ -1310,7 +1369,7 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
                        lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
   }
   int rc = medusa_host::hip_check("medusa_lm_head_topk launch");
-  if (rc != MEDUSA_OK) return rc;
+  if (rc != MEDUSA_OK || fused) return rc;
   const int per = (lg.lists * topk + kMergeThreads - 1) / kMergeThreads;
   const dim3 mg(B, K), mb(kMergeThreads);
   if (per <= 1)

@@ -84,6 +84,19 @@ def test_heads_repeat_calls_are_stable(gpu_device):
         _check(case, _run(case, w, keep_logits=False), w, check_logits=False)
 
 
+def test_heads_back_to_back_inputs_share_workspace(gpu_device):
+    # different inputs in turn (A, B, A, B) through one cached workspace:
+    # the in-kernel merge (taken here: 5 heads of 50 workgroups x 4 lists x
+    # 10 = 2000 candidates) must read the lists of the running call, never a
+    # previous call's, and leave its arrival counts ready for the next
+    w = synth.workload("vicuna-7b", B=1, H=512, V=6000, K=5, topk=10)
+    a = heads_case(w, seed=21)
+    b = heads_case(w, seed=22)
+    assert not np.array_equal(a["topk_ids"], b["topk_ids"])
+    for case in (a, b, a, b):
+        _check(case, _run(case, w, keep_logits=False, split=True), w, check_logits=False)
+
+
 @pytest.mark.parametrize("B,H,V,K,k", [
     (1, 6656, 3001, 2, 10),    # 13 row steps of 512 (the 33B hidden size, batch 1)
     (2, 8192, 2000, 1, 8),     # 16 row steps, two sequences per wave
