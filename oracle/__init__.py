@@ -8,6 +8,8 @@ computes, written from the pages' descriptions of Medusa:
   attention.py  tree-masked attention over a KV prefix
   posterior.py  greedy / typical acceptance and the longest accepted prefix
   commit.py     gathering the accepted path's K/V into contiguous slots
+  base_head.py  the base model's lm_head over the tree nodes, and the
+                acceptance test on its logits
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package.  It shares no code with the GPU library and imports neither it
@@ -30,9 +32,10 @@ from .tree import SpecError, parse_choices, build_tree
 from .attention import tree_attention
 from .posterior import node_statistics, evaluate_posterior
 from .commit import commit_kv
+from .base_head import base_logits, base_posterior
 
 __all__ = [
     "as_f64", "resblock", "lm_head_logits", "topk_by_value", "heads",
     "SpecError", "parse_choices", "build_tree", "tree_attention",
-    "node_statistics", "evaluate_posterior", "commit_kv",
+    "node_statistics", "evaluate_posterior", "commit_kv", "base_logits", "base_posterior",
 ]
