@@ -6,7 +6,7 @@
  *   medusa_heads               K Medusa heads: ResBlock, lm_head, top-k
  *   medusa_build_tree          candidate tree from a medusa_choices spec
  *   medusa_tree_attention      tree-masked attention over the KV prefix
- *   (caller: base lm_head at the tree nodes -> logits)
+ *   medusa_base_lm_head        base lm_head at the tree nodes -> logits
  *   medusa_evaluate_posterior  greedy / typical acceptance, best path
  *   medusa_commit_kv           gather the accepted rows into contiguous slots
  *
@@ -235,6 +235,37 @@ int medusa_commit_kv(int dtype, int B, int n_layers, int H, int d, int max_slots
                      const int32_t* retrieve, int p_max, int D,
                      const int32_t* best_path, const int32_t* accept_len,
                      int32_t* new_prefix_len, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Base lm_head over the tree nodes.  [API] tree_decoding (the base model's
+ * logits at every tree node) and evaluate_posterior (which takes them).
+ * The step that produces medusa_evaluate_posterior's `logits`.
+ *
+ * logits[m][v] = sum_k hidden[m][k] * W[v][k] for every m < M and v < V:
+ * float32 accumulation of the bf16 products, no bias.  Rows m are the B*T
+ * final hidden states of the tree nodes in node order.
+ *
+ * Layouts: hidden bf16 [M][H]; logits float32 [M][V].  W is bf16, out x in
+ * (row v makes logit v), given either row-major [V][H] (w_packed = 0) or in
+ * the packed layout written by medusa_base_lm_head_pack (w_packed = 1),
+ * which streams faster.  dtype must be MEDUSA_BF16.  1 <= M <= 4096,
+ * 8 <= H <= 65536 with H % 8 == 0, 1 <= V <= 2^24.  No workspace; one
+ * kernel on `stream`.
+ *
+ * Packed layout (medusa_base_lm_head_packed_bytes(H, V) bytes): for tile
+ * t = v / 16, k step s = k / 32 and lane l = 16 g + n, the 16 bytes
+ * W[16 t + n][32 s + 8 g .. 32 s + 8 g + 7] sit at byte offset
+ * (((t / 2) * ceil(H / 32) + s) * 2 + t % 2) * 1024 + l * 16, with the
+ * tile count padded to an even number; entries past V or H are zero.
+ * The weights are static, so a caller packs them once.
+ * medusa_base_lm_head_packed_bytes returns 0 for invalid sizes.
+ * ------------------------------------------------------------------- */
+size_t medusa_base_lm_head_packed_bytes(int H, int V);
+
+int medusa_base_lm_head_pack(int dtype, int H, int V, const void* w_base, void* w_packed, void* stream);
+
+int medusa_base_lm_head(int dtype, int M, int H, int V, const void* hidden, const void* w_base,
+                        int w_packed, float* logits, void* stream);
 
 /* Text for a medusa_status value. */
 const char* medusa_status_string(int status);

@@ -5,7 +5,7 @@ kernels (``include/medusa.h``).  This package is its Python binding: the
 functions below carry the C entry points' names and only marshal torch
 tensors (device memory, the current stream) into those calls.
 
-Build the library in-tree with ``python -m speculative_decoding_medusa_amd.build``;
+Build the library in-tree with ``python speculative_decoding_medusa_amd/build.py``;
 importing the package without it raises ImportError.
 """
 
@@ -13,12 +13,13 @@ from ._lib import (  # noqa: F401
     MEDUSA_BF16, MEDUSA_F32, SPEC_STATUS, EXPORTED, LIB_PATH, MedusaError, lib, workspace,
     medusa_heads_workspace, medusa_resblock, medusa_lm_head_topk, medusa_heads, medusa_build_tree,
     medusa_tree_attention_workspace, medusa_tree_attention, medusa_posterior_workspace,
-    medusa_evaluate_posterior, medusa_commit_kv,
+    medusa_evaluate_posterior, medusa_commit_kv, medusa_base_lm_head, medusa_base_lm_head_pack,
 )
 
 __all__ = [
     "MEDUSA_BF16", "MEDUSA_F32", "SPEC_STATUS", "MedusaError", "workspace",
     "medusa_heads_workspace", "medusa_resblock", "medusa_lm_head_topk", "medusa_heads",
     "medusa_build_tree", "medusa_tree_attention_workspace", "medusa_tree_attention",
-    "medusa_posterior_workspace", "medusa_evaluate_posterior", "medusa_commit_kv",
+    "medusa_posterior_workspace", "medusa_evaluate_posterior", "medusa_commit_kv", "medusa_base_lm_head",
+    "medusa_base_lm_head_pack",
 ]

@@ -32,7 +32,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             "libmedusa.so is not built (expected at %s); run "
-            "`python -m speculative_decoding_medusa_amd.build`" % LIB_PATH)
+            "`python speculative_decoding_medusa_amd/build.py`" % LIB_PATH)
     return ctypes.CDLL(LIB_PATH)
 
 
@@ -52,6 +52,9 @@ _SIGS = {
     "medusa_evaluate_posterior": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _f, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
     "medusa_commit_kv": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp]),
+    "medusa_base_lm_head_packed_bytes": (_sz, [_i, _i]),
+    "medusa_base_lm_head_pack": (_i, [_i, _i, _i, _vp, _vp, _vp]),
+    "medusa_base_lm_head": (_i, [_i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
     "medusa_status_string": (ctypes.c_char_p, [_i]),
     "medusa_last_error": (ctypes.c_char_p, []),
     "medusa_abi_version": (_i, []),
@@ -297,3 +300,46 @@ def medusa_commit_kv(k_cache, v_cache, prefix_len, retrieve, best_path, accept_l
                               _ptr(new_prefix_len, "new_prefix_len", torch.int32, (B,)), _stream(dev))
     _check(rc, "medusa_commit_kv")
     return new_prefix_len
+
+
+def medusa_base_lm_head_pack(w_base):
+    """bf16 [V][H] row-major base lm_head -> its packed layout (uint8 tensor)."""
+    V, H = w_base.shape
+    nbytes = int(lib.medusa_base_lm_head_packed_bytes(H, V))
+    if nbytes == 0:
+        raise MedusaError(MEDUSA_ERR_SHAPE, "medusa_base_lm_head_pack: bad shape (%d, %d)" % (V, H))
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=w_base.device)
+    rc = lib.medusa_base_lm_head_pack(_dtype_code(w_base), H, V, _ptr(w_base, "w_base"), _ptr(packed, "w_packed"),
+                                      _stream(w_base.device))
+    _check(rc, "medusa_base_lm_head_pack")
+    return packed
+
+
+def medusa_base_lm_head(hidden, w_base, logits=None, V=None):
+    """hidden bf16 [M][H] (or [B][T][H]) -> logits float32 [M][V] (or [B][T][V]).
+
+    w_base: bf16 [V][H] row-major, or the uint8 tensor from
+    medusa_base_lm_head_pack (then V must be given)."""
+    shape = hidden.shape
+    H = shape[-1]
+    M = 1
+    for x in shape[:-1]:
+        M *= x
+    packed = w_base.dtype == torch.uint8
+    if packed:
+        if V is None:
+            raise ValueError("V is required with packed weights")
+        if w_base.numel() != int(lib.medusa_base_lm_head_packed_bytes(H, V)):
+            raise ValueError("packed weights have %d bytes, expected %d for H=%d V=%d"
+                             % (w_base.numel(), lib.medusa_base_lm_head_packed_bytes(H, V), H, V))
+        wptr = _ptr(w_base, "w_base")
+    else:
+        V = w_base.shape[0]
+        wptr = _ptr(w_base, "w_base", hidden.dtype, (V, H))
+    dev = hidden.device
+    if logits is None:
+        logits = torch.empty(tuple(shape[:-1]) + (V,), dtype=torch.float32, device=dev)
+    rc = lib.medusa_base_lm_head(_dtype_code(hidden), M, H, V, _ptr(hidden, "hidden"), wptr, 1 if packed else 0,
+                                 _ptr(logits, "logits", torch.float32, tuple(shape[:-1]) + (V,)), _stream(dev))
+    _check(rc, "medusa_base_lm_head")
+    return logits

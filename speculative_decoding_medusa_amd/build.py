@@ -1,6 +1,9 @@
 """Build libmedusa.so for gfx950 in-tree with hipcc.
 
-    python -m speculative_decoding_medusa_amd.build
+    python speculative_decoding_medusa_amd/build.py
+
+(run as a script, not as a module of the package: importing the package
+loads the library this script rebuilds)
 
 Every call recompiles every source (objects go to ``_build/`` at the repo
 root) and links ``speculative_decoding_medusa_amd/libmedusa.so``.
@@ -18,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmedusa.so")
 
-SOURCES = ["abi.cpp", "heads.hip", "tree.hip", "attention.hip", "posterior.hip", "commit.hip"]
+SOURCES = ["abi.cpp", "heads.hip", "tree.hip", "attention.hip", "posterior.hip", "commit.hip", "base_head.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,263 @@
+// The base model's lm_head over the tree nodes on gfx950:
+// logits[m][v] = sum_k hidden[m][k] * W[v][k], float32 accumulation, no bias.
+//
+// A skinny GEMM: M = B*T rows of final hidden states (tens of rows), V weight
+// rows of H elements (32000 x 4096 bf16 = 262 MB), so every weight is
+// streamed from HBM exactly once and the whole grid is resident at once.
+// Workgroup = (a block of 128 vocab rows, an M tile of 64 hidden rows): four
+// waves, each owning two 16-row weight tiles, walk K in chunks of 256.
+//
+//  * The M tile's chunk of hidden states (64 x 256 bf16, 32 KB) is staged in
+//    LDS, double-buffered and shared by the four waves; its 16-byte pieces
+//    are XOR-swizzled by row so the MFMA operand reads are conflict-free.
+//  * Weight tiles go straight from HBM into registers, double-buffered
+//    across chunks, each 16-byte piece refilled as soon as its MFMAs have
+//    read it.  From the packed layout (medusa_base_lm_head_pack: pairs of
+//    16-row tiles, 32-element k steps, the pair's two tiles, lanes) one wave
+//    instruction reads 1 KB contiguously and a wave's two tiles stream as
+//    one run; from the row-major layout it reads 64 bytes of each of 16 rows.
+//  * v_mfma_f32_16x16x32_bf16 with A = 16 hidden rows, B = 16 weight rows:
+//    lane (g, n) of a tile holds logits[4g + i][n] in component i.
+//  * Chunks are published with an LDS-only wait and a bare barrier, so the
+//    weight loads in flight are never drained at a chunk boundary.
+#include "common.hpp"
+
+namespace medusa {
+
+constexpr int kBhThreads = 256;
+constexpr int kBhWaves = 4;
+constexpr int kBhTiles = 2;                           // 16-row weight tiles per wave
+constexpr int kBhVBlock = kBhWaves * kBhTiles * 16;   // vocab rows per workgroup
+constexpr int kBhMTile = 64;                          // hidden rows per workgroup
+constexpr int kBhKC = 256;                            // K elements per chunk
+constexpr int kBhSteps = kBhKC / 32;                  // MFMA k-steps per chunk
+constexpr int kBhPieces = kBhKC / 8;                  // 16-byte pieces of a row chunk
+constexpr int kBhStage = kBhMTile * kBhPieces / kBhThreads;   // pieces staged per thread
+
+// Packed weights: tile vt (rows 16 vt ..), k step ks (elements 32 ks ..),
+// lane l = 16 g + n -> the 16 bytes W[16 vt + n][32 ks + 8 g .. + 8], zero
+// past V or H.  Order: tile pair vt / 2, k step, tile vt % 2, lane -- 1 KB
+// per (tile, step), so the two tiles a wave owns form one contiguous run.
+// The tile count is padded to an even number.
+__host__ __device__ inline int bh_ksteps(int H) { return (H + 31) / 32; }
+__host__ __device__ inline int bh_vtiles(int V) { return ((V + 31) / 32) * 2; }
+__host__ __device__ inline size_t bh_block(int vt, int ks, int ks_n) {
+  return (static_cast<size_t>(vt / 2) * ks_n + ks) * 2 + (vt & 1);
+}
+
+// 16-byte slot of piece p of hidden row r in a chunk buffer.
+__device__ __forceinline__ int bh_slot(int r, int p) { return r * kBhPieces + (p ^ (r & 7)); }
+
+// Every LDS operation of this thread complete (vector memory left in flight).
+__device__ __forceinline__ void bh_wait_lds() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ void bh_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ u32x4 bh_ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 bh_ld16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <bool PACKED>
+__global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, int V,
+                                                                  const uint16_t* __restrict__ hidden,
+                                                                  const uint16_t* __restrict__ w,
+                                                                  float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) u32x4 sa[2][kBhMTile * kBhPieces];
+  const int m0 = blockIdx.y * kBhMTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nch = (H + kBhKC - 1) / kBhKC;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  // this lane's weight row in each tile (rows past V reload row V-1 or the
+  // last packed tile, and are not written)
+  const int ks_n = bh_ksteps(H), vt_n = bh_vtiles(V);
+  int vrow[kBhTiles];
+  const uint16_t* wr[kBhTiles];
+#pragma unroll
+  for (int t = 0; t < kBhTiles; ++t) {
+    const int vt = blockIdx.x * (kBhVBlock / 16) + wave * kBhTiles + t;
+    vrow[t] = vt * 16 + n;
+    if (PACKED)
+      wr[t] = w + (bh_block(min(vt, vt_n - 1), 0, ks_n) * 64 + lane) * 8;
+    else
+      wr[t] = w + static_cast<size_t>(min(vrow[t], V - 1)) * H;
+  }
+  // the 16 bytes of weight piece (chunk c, step s) of tile t for this lane
+  auto wpiece = [&](int t, int c, int s) -> u32x4 {
+    if (PACKED) return bh_ld16_stream(wr[t] + static_cast<size_t>(min(c * kBhSteps + s, ks_n - 1)) * 1024);
+    return bh_ld16_stream(wr[t] + static_cast<uint32_t>(min(c * kBhKC + 32 * s + 8 * g, H - 8)));
+  };
+
+  // staging of the hidden chunk: thread tid moves pieces tid + 256 q
+  auto load_a = [&](int c, u32x4 (&ra)[kBhStage]) {
+#pragma unroll
+    for (int q = 0; q < kBhStage; ++q) {
+      const int x = q * kBhThreads + tid;
+      const int r = x / kBhPieces, p = x % kBhPieces;
+      ra[q] = bh_ld16(hidden + static_cast<size_t>(min(m0 + r, M - 1)) * H + min(c * kBhKC + 8 * p, H - 8));
+    }
+  };
+  auto store_a = [&](int buf, int c, const u32x4 (&ra)[kBhStage]) {
+#pragma unroll
+    for (int q = 0; q < kBhStage; ++q) {
+      const int x = q * kBhThreads + tid;
+      const int r = x / kBhPieces, p = x % kBhPieces;
+      const bool ok = m0 + r < M && c * kBhKC + 8 * p < H;
+      sa[buf][bh_slot(r, p)] = ok ? ra[q] : zero;
+    }
+  };
+  // weight pieces of chunk c: step s, lane group g -> k = 256 c + 32 s + 8 g,
+  // issued in step order so step s waits only for its own two pieces
+  auto load_w = [&](int c, u32x4 (&bw)[kBhTiles][kBhSteps]) {
+#pragma unroll
+    for (int s = 0; s < kBhSteps; ++s)
+#pragma unroll
+      for (int t = 0; t < kBhTiles; ++t) bw[t][s] = wpiece(t, c, s);
+  };
+
+  f32x4 acc[kBhTiles][4];
+#pragma unroll
+  for (int t = 0; t < kBhTiles; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // chunk c from LDS buffer buf and weight buffer bw; each piece of bw is
+  // refilled with chunk cn right after its MFMAs (cn < 0: no refill)
+  auto compute = [&](int buf, int c, u32x4 (&bw)[kBhTiles][kBhSteps], int cn) {
+#pragma unroll
+    for (int s = 0; s < kBhSteps; ++s) {
+      u32x4 a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = sa[buf][bh_slot(mt * 16 + n, 4 * s + g)];
+      const bool kin = c * kBhKC + 32 * s + 8 * g < H;   // K tail: the hidden side is zero too
+#pragma unroll
+      for (int t = 0; t < kBhTiles; ++t) {
+        const u32x4 b = kin ? bw[t][s] : zero;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[mt]), as_bf16x8(b), acc[t][mt], 0, 0, 0);
+      }
+      if (cn >= 0) {
+#pragma unroll
+        for (int t = 0; t < kBhTiles; ++t) bw[t][s] = wpiece(t, cn, s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Issue order keeps every wait on the oldest loads: hidden chunk 0, weight
+  // chunks 0 and 1, hidden chunk 1; then per chunk: compute (refilling the
+  // weights two chunks ahead piece by piece), stage the next hidden chunk,
+  // prefetch the one after.  An LDS buffer is rewritten only after the
+  // barrier that follows its last reads.
+  u32x4 ra[kBhStage];
+  u32x4 wa[kBhTiles][kBhSteps], wb[kBhTiles][kBhSteps];
+  const int lastc = nch - 1;
+  load_a(0, ra);
+  load_w(0, wa);
+  load_w(min(1, lastc), wb);
+  store_a(0, 0, ra);
+  load_a(min(1, lastc), ra);
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    bh_wait_lds();
+    bh_barrier();
+    compute(0, c, wa, min(c + 2, lastc));
+    store_a(1, c + 1, ra);
+    load_a(min(c + 2, lastc), ra);
+    bh_wait_lds();
+    bh_barrier();
+    compute(1, c + 1, wb, min(c + 3, lastc));
+    store_a(0, c + 2, ra);
+    load_a(min(c + 3, lastc), ra);
+  }
+  if (c < nch) {
+    bh_wait_lds();
+    bh_barrier();
+    compute(0, c, wa, -1);
+  }
+
+  // logits[m][v]: lane (g, n) of tile (t, mt) holds rows mt*16 + 4g + i
+#pragma unroll
+  for (int t = 0; t < kBhTiles; ++t) {
+    if (vrow[t] >= V) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + mt * 16 + 4 * g + i;
+        if (m < M) logits[static_cast<size_t>(m) * V + vrow[t]] = acc[t][mt][i];
+      }
+  }
+}
+
+// Row-major weights [V][H] -> the packed layout, one 16-byte piece per
+// thread (zeros past V or H).
+__global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, const uint16_t* __restrict__ w,
+                                                               uint16_t* __restrict__ wp, long long npieces) {
+  const long long x = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (x >= npieces) return;
+  const int ks_n = bh_ksteps(H);
+  const int l = static_cast<int>(x & 63);
+  const long long blk = x >> 6;                 // ((pair * ks_n + ks) * 2 + half)
+  const int half = static_cast<int>(blk & 1);
+  const int ks = static_cast<int>((blk >> 1) % ks_n);
+  const int vt = static_cast<int>((blk >> 1) / ks_n) * 2 + half;
+  const int row = vt * 16 + (l & 15), k = ks * 32 + 8 * (l >> 4);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < V && k < H) v = *reinterpret_cast<const u32x4*>(w + static_cast<size_t>(row) * H + k);
+  *reinterpret_cast<u32x4*>(wp + x * 8) = v;
+}
+
+}  // namespace medusa
+
+extern "C" size_t medusa_base_lm_head_packed_bytes(int H, int V) {
+  using namespace medusa;
+  if (H < 8 || H > (1 << 16) || H % 8 != 0 || V < 1 || V > (1 << 24)) return 0;
+  return static_cast<size_t>(bh_vtiles(V)) * bh_ksteps(H) * 1024;
+}
+
+extern "C" int medusa_base_lm_head_pack(int dtype, int H, int V, const void* w_base, void* w_packed, void* stream) {
+  using namespace medusa;
+  MEDUSA_REQUIRE(dtype == MEDUSA_BF16, MEDUSA_ERR_DTYPE, "%s: dtype %d (bf16 only)", __func__, dtype);
+  MEDUSA_REQUIRE(H >= 8 && H <= (1 << 16) && H % 8 == 0, MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE(V >= 1 && V <= (1 << 24), MEDUSA_ERR_SHAPE, "%s: V=%d", __func__, V);
+  MEDUSA_REQUIRE_PTR(w_base);
+  MEDUSA_REQUIRE_PTR(w_packed);
+  MEDUSA_REQUIRE(w_packed != w_base, MEDUSA_ERR_ALIAS, "%s: w_packed must not alias w_base", __func__);
+  const long long npieces = static_cast<long long>(bh_vtiles(V)) * bh_ksteps(H) * 64;
+  hipLaunchKernelGGL(base_lm_head_pack_kernel, dim3(static_cast<unsigned>((npieces + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), H, V, static_cast<const uint16_t*>(w_base),
+                     static_cast<uint16_t*>(w_packed), npieces);
+  return medusa_host::hip_check("medusa_base_lm_head_pack launch");
+}
+
+extern "C" int medusa_base_lm_head(int dtype, int M, int H, int V, const void* hidden, const void* w_base,
+                                   int w_packed, float* logits, void* stream) {
+  using namespace medusa;
+  MEDUSA_REQUIRE(dtype == MEDUSA_BF16, MEDUSA_ERR_DTYPE, "%s: dtype %d (bf16 only)", __func__, dtype);
+  MEDUSA_REQUIRE(M >= 1 && M <= kMaxBatch * kMaxNodes, MEDUSA_ERR_SHAPE, "%s: M=%d", __func__, M);
+  MEDUSA_REQUIRE(H >= 8 && H <= (1 << 16) && H % 8 == 0, MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE(V >= 1 && V <= (1 << 24), MEDUSA_ERR_SHAPE, "%s: V=%d", __func__, V);
+  MEDUSA_REQUIRE_PTR(hidden);
+  MEDUSA_REQUIRE_PTR(w_base);
+  MEDUSA_REQUIRE_PTR(logits);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + kBhMTile - 1) / kBhMTile);
+  if (w_packed)
+    hipLaunchKernelGGL(base_lm_head_kernel<true>, grid, dim3(kBhThreads), 0, st, M, H, V,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits);
+  else
+    hipLaunchKernelGGL(base_lm_head_kernel<false>, grid, dim3(kBhThreads), 0, st, M, H, V,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits);
+  return medusa_host::hip_check("medusa_base_lm_head launch");
+}

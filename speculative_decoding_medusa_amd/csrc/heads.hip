@@ -42,7 +42,6 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 #endif
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ------------------------------------------------------------------ K1 bf16
 // Grid (ceil(H/16), K).  r[b][j][i] = h[b][i] + SiLU(W1[j][i] . h[b] + b1[j][i]).

@@ -183,3 +183,12 @@ def kv_cache(w, seed=0, n_layers=None, rows=None):
         x[:, :, :, :R] = normal_f32(seed, w["wid"], name, (), nl * B * H * R * d).reshape(nl, B, H, R, d)
         out[name] = _encode(x, w["dtype"])
     return out["cache_k"], out["cache_v"]
+
+
+def base_head_inputs(M, H, V, seed=0, workload_id=9):
+    """The base model's final hidden states at M tree nodes, N(0, 1), and its
+    lm_head, N(0, 0.02^2), as bf16 bits: hidden [M][H], w_base [V][H]
+    (out x in, no bias)."""
+    h = normal_f32(seed, workload_id, "h_tree", (M, H), M * H)
+    w = normal_f32(seed, workload_id, "w_base", (V, H), V * H, std=0.02)
+    return dict(hidden=bf16_bits(h).reshape(M, H), w_base=bf16_bits(w).reshape(V, H))

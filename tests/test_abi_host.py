@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 100
+    assert L.medusa_abi_version() == 101
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -137,6 +137,34 @@ def commit(dt=1, B=1, nl=2, H=4, d=128, S=100, kc=A, vc=A + 0x100000, plen=A, re
 ])
 def test_commit_validation(kw, code):
     assert commit(**kw) == code
+
+
+def base(dt=1, M=64, H=4096, V=32000, hidden=A, w=A, logits=A, packed=0):
+    return L.medusa_base_lm_head(dt, M, H, V, hidden, w, packed, logits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), DTYPE), (dict(dt=5), DTYPE), (dict(M=0), SHAPE), (dict(M=4097), SHAPE), (dict(H=0), SHAPE),
+    (dict(H=12), SHAPE), (dict(H=1 << 17), SHAPE), (dict(V=0), SHAPE), (dict(hidden=None), NULL),
+    (dict(w=None), NULL), (dict(logits=None), NULL), (dict(hidden=MIS), ALIGN), (dict(logits=MIS), ALIGN),
+])
+def test_base_lm_head_validation(kw, code):
+    assert base(**kw) == code
+    assert L.medusa_last_error().decode() != ""
+
+
+def test_base_lm_head_pack_validation_and_sizes():
+    # one KB per (16-row tile, 32-element k step), partial tiles and steps padded
+    assert L.medusa_base_lm_head_packed_bytes(4096, 32000) == 2000 * 128 * 1024
+    assert L.medusa_base_lm_head_packed_bytes(40, 17) == 2 * 2 * 1024
+    assert L.medusa_base_lm_head_packed_bytes(40, 33) == 4 * 2 * 1024   # three tiles padded to four
+    assert L.medusa_base_lm_head_packed_bytes(12, 17) == 0
+    assert L.medusa_base_lm_head_packed_bytes(4096, 0) == 0
+    assert L.medusa_base_lm_head_pack(0, 64, 100, A, A + 4096, None) == DTYPE
+    assert L.medusa_base_lm_head_pack(1, 60, 100, A, A + 4096, None) == SHAPE
+    assert L.medusa_base_lm_head_pack(1, 64, 100, None, A, None) == NULL
+    assert L.medusa_base_lm_head_pack(1, 64, 100, A, MIS, None) == ALIGN
+    assert L.medusa_base_lm_head_pack(1, 64, 100, A, A, None) == ALIAS
 
 
 def test_binding_rejects_cpu_tensors():

@@ -1,0 +1,102 @@
+"""GPU parity of the base lm_head over the tree nodes against the oracle.
+
+logits = hidden . W^T with bf16 inputs: every product is exact in float32,
+so the kernel's float32 sums stay within 1e-4 max relative error of the
+fp64 oracle (tighter than the 2e-2 bf16 bar).  Both weight layouts: row-
+major and packed (the packed bytes themselves are checked bit for bit
+against the layout the header documents, restated here with NumPy).
+Sizes: ragged M (partial M tiles), ragged V (partial vocab blocks and
+tiles), H below and past the 256-element K chunk with a tail and a partial
+32-element k step, the smallest shape, and the Vicuna-7B tree (64 nodes,
+H 4096, V 32000).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_medusa_amd as md
+import synth
+from cases import rel_err, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, H, V, seed):
+    x = synth.base_head_inputs(M, H, V, seed=seed)
+    return x["hidden"], x["w_base"]
+
+
+def _packed_reference(w):
+    """The documented packed layout of bf16 bits w [V][H]: for tile t, k step
+    s and lane l = 16 g + n, 8 elements W[16 t + n][32 s + 8 g ..] (zero past
+    V or H, tile count padded to even), ordered tile pair, step, tile within
+    the pair, lane."""
+    V, H = w.shape
+    Vt, S = (V + 31) // 32 * 2, (H + 31) // 32
+    pad = np.zeros((Vt * 16, S * 32), dtype=np.uint16)
+    pad[:V, :H] = w
+    t = pad.reshape(Vt // 2, 2, 16, S, 4, 8)          # [pair][q][n][s][g][e]
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 4, 2, 5)).reshape(-1)   # [pair][s][q][g][n][e]
+
+
+@pytest.mark.parametrize("V,H", [(1, 8), (17, 40), (300, 72), (1000, 264)])
+def test_base_lm_head_pack_layout(gpu_device, V, H):
+    _, w = _inputs(1, H, V, seed=V * H)
+    got = md.medusa_base_lm_head_pack(to_dev(w))
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _packed_reference(w))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("M,H,V", [
+    (1, 8, 1),          # smallest shape
+    (5, 72, 300),       # one partial K chunk, partial vocab block, partial M tile
+    (64, 520, 1000),    # K tail past two chunks, ragged V
+    (130, 264, 777),    # three M tiles
+    (16, 4096, 2051),   # full-width rows, ragged V
+    (7, 40, 33),        # partial 32-element k step, partial 16-row tile
+])
+def test_base_lm_head_matches_oracle(gpu_device, M, H, V, packed):
+    h, w = _inputs(M, H, V, seed=M + H + V)
+    print("case", M, H, V, packed, flush=True)
+    wd = to_dev(w)
+    if packed:
+        wd = md.medusa_base_lm_head_pack(wd)
+    got = md.medusa_base_lm_head(to_dev(h), wd, V=V)
+    torch.cuda.synchronize()
+    ref = oracle.base_logits(h, w)
+    assert rel_err(to_host(got), ref) < 1e-4
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_base_lm_head_vicuna7b_tree(gpu_device, packed):
+    # the 64 tree nodes of one sequence against the 32000 x 4096 lm_head,
+    # through the [B][T][H] form of the binding
+    M, H, V = 64, 4096, 32000
+    h, w = _inputs(M, H, V, seed=0)
+    wd = to_dev(w)
+    if packed:
+        wd = md.medusa_base_lm_head_pack(wd)
+    got = md.medusa_base_lm_head(to_dev(h).view(1, M, H), wd, V=V)
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (1, M, V)
+    ref = oracle.base_logits(h, w)
+    assert rel_err(to_host(got).reshape(M, V), ref) < 1e-4
+
+
+def test_base_lm_head_writes_only_its_rows(gpu_device):
+    # an output larger than M x V keeps its tail: rows past M are never written
+    M, H, V = 3, 64, 200
+    h, w = _inputs(M, H, V, seed=9)
+    big = torch.full((M + 2, V), 7.0, dtype=torch.float32, device=gpu_device)
+    hd, wd = to_dev(h), to_dev(w)   # held until the kernel has run
+    rc = md.lib.medusa_base_lm_head(md.MEDUSA_BF16, M, H, V, hd.data_ptr(), wd.data_ptr(), 0, big.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    out = big.cpu().numpy()
+    assert rel_err(out[:M], oracle.base_logits(h, w)) < 1e-4
+    assert np.all(out[M:] == 7.0)
