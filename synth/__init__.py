@@ -17,7 +17,7 @@ from .rng import stream, normal_f32, bf16_bits, bf16_to_f32, f32_round
 from .shapes import WORKLOADS, workload
 from .trees import (full_tree_choices, random_tree_choices, worked_example_choices,
                     chain_choices, choices_array)
-from .gen import (base_head_inputs, heads_inputs, topk_ids_input, root_token_input, attention_inputs,
+from .gen import (base_head_inputs, base_posterior_inputs, heads_inputs, topk_ids_input, root_token_input, attention_inputs,
                   posterior_logits, kv_cache, rope_rotate, prefix_lengths)
 
 __all__ = [
@@ -25,6 +25,6 @@ __all__ = [
     "WORKLOADS", "workload",
     "full_tree_choices", "random_tree_choices", "worked_example_choices", "chain_choices",
     "choices_array",
-    "base_head_inputs", "heads_inputs", "topk_ids_input", "root_token_input", "attention_inputs",
+    "base_head_inputs", "base_posterior_inputs", "heads_inputs", "topk_ids_input", "root_token_input", "attention_inputs",
     "posterior_logits", "kv_cache", "rope_rotate", "prefix_lengths",
 ]

@@ -192,3 +192,39 @@ def base_head_inputs(M, H, V, seed=0, workload_id=9):
     h = normal_f32(seed, workload_id, "h_tree", (M, H), M * H)
     w = normal_f32(seed, workload_id, "w_base", (V, H), V * H, std=0.02)
     return dict(hidden=bf16_bits(h).reshape(M, H), w_base=bf16_bits(w).reshape(V, H))
+
+
+def base_posterior_inputs(w, tree_candidates, retrieve, num_paths, seed=0, scale=7.0, plant=True):
+    """Final hidden states at the tree nodes and a base lm_head, with one
+    planted path per sequence (bf16 bits): hidden [B][T][H] ~ N(0, 1),
+    w_base [V][H] ~ N(0, 0.02^2).
+
+    As in ``posterior_logits``, a deepest path is chosen uniformly and
+    A ~ Binomial(depth, 1/2) drawn; for j < A, ``scale`` times the lm_head row
+    of the path's (j+1)-th token is added to the hidden state of its j-th
+    node, which lifts that token's logit there far above the row's others
+    (by about scale * |w_row|^2).  Returns dict(hidden, w_base, plan).
+    """
+    B, H, V, wid = w["B"], w["H"], w["V"], w["wid"]
+    cand = np.asarray(tree_candidates)
+    T = int(cand.shape[1])
+    wb = normal_f32(seed, wid, "w_base", (), V * H, std=0.02).reshape(V, H)
+    h = normal_f32(seed, wid, "h_tree", (), B * T * H).reshape(B, T, H)
+    plan = []
+    for b in range(B):
+        if not plant:
+            plan.append(None)
+            continue
+        g = stream(seed, wid, "plant", b)
+        P = int(num_paths)
+        ret = np.asarray(retrieve)[:P]
+        lens = np.array([int(np.sum(r >= 0)) - 1 for r in ret])
+        deepest = np.flatnonzero(lens == lens.max())
+        p = int(deepest[int(g.integers(len(deepest)))])
+        A = int(g.binomial(int(lens[p]), 0.5))
+        for j in range(A):
+            node = int(ret[p, j])
+            tok = int(cand[b][int(ret[p, j + 1])])
+            h[b, node] += np.float32(scale) * wb[tok]
+        plan.append((p, A))
+    return dict(hidden=bf16_bits(h).reshape(B, T, H), w_base=bf16_bits(wb).reshape(V, H), plan=plan)

@@ -100,3 +100,55 @@ def test_base_lm_head_writes_only_its_rows(gpu_device):
     out = big.cpu().numpy()
     assert rel_err(out[:M], oracle.base_logits(h, w)) < 1e-4
     assert np.all(out[M:] == 7.0)
+
+
+_CASES = {}
+
+
+def _base_posterior_case(w, temperature, seed=0, max_retries=20):
+    """Tree, planted hidden states and the oracle's verdict; redrawn until
+    the decisions clear float error (as for the posterior on given logits).
+    Cached per (temperature, seed)."""
+    key = (temperature, seed)
+    if key in _CASES:
+        return _CASES[key]
+    from cases import non_planted_children_clear, posterior_margins_ok, tree_case
+    tcase = tree_case(w, seed=seed)
+    ref = tcase["ref"]
+    for retry in range(max_retries):
+        x = synth.base_posterior_inputs(w, ref["tree_candidates"], ref["retrieve"], ref["num_paths"],
+                                        seed=seed + 1000 * retry, scale=20.0)
+        B, T, H = x["hidden"].shape
+        z = oracle.base_logits(x["hidden"].reshape(B * T, H), x["w_base"]).reshape(B, T, -1).astype(np.float32)
+        if not non_planted_children_clear(z, ref, x["plan"]):
+            continue
+        if not posterior_margins_ok(z, ref, temperature, w["eps"], w["delta"]):
+            continue
+        exp = oracle.base_posterior(x["hidden"], x["w_base"], ref["tree_candidates"], ref["retrieve"],
+                                    ref["num_paths"], temperature, w["eps"], w["delta"])
+        _CASES[key] = (tcase, x, exp, retry)
+        return _CASES[key]
+    raise RuntimeError("no margin after %d redraws" % max_retries)
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+def test_base_lm_head_then_posterior_matches_oracle(gpu_device, temperature):
+    # the base logits of the 64-node tree (H 1024, V 8000, packed weights;
+    # the full 4096 x 32000 GEMM has its own parity test) feed the acceptance
+    # test; best path, accepted length and next token equal the oracle's on
+    # the same planted inputs
+    w = synth.workload("vicuna-7b", H=1024, V=8000)
+    tcase, x, exp, retry = _base_posterior_case(w, temperature)
+    print("retry", retry, "plan", x["plan"], "expected", exp["accept_len"], flush=True)
+    ref = tcase["ref"]
+    B, T, H = x["hidden"].shape
+    V = x["w_base"].shape[0]
+    wp = md.medusa_base_lm_head_pack(to_dev(x["w_base"]))
+    logits = md.medusa_base_lm_head(to_dev(x["hidden"]), wp, V=V)
+    got = md.medusa_evaluate_posterior(logits, to_dev(ref["tree_candidates"]), to_dev(ref["retrieve"]),
+                                       to_dev(np.array([ref["num_paths"]], dtype=np.int32)), temperature,
+                                       w["eps"], w["delta"])
+    torch.cuda.synchronize()
+    for key in ("best_path", "accept_len", "next_token"):
+        assert np.array_equal(got[key].cpu().numpy(), exp[key]), key
+    assert int(exp["accept_len"][0]) == x["plan"][0][1]
