@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-base-head", action="store_true",
+                    help="skip the base lm_head timing (the step before the acceptance test)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)")
     return ap.parse_args()
@@ -338,6 +340,43 @@ def graph_timing(step, steps):
             "note": "the whole step replayed from HIP graphs (one per attention layer), %d steps" % steps}
 
 
+def base_head_timing(w, seed, steps):
+    """The base model's lm_head over the 64 tree nodes (packed bf16 weights,
+    H x V of the workload): the step that produces the acceptance test's
+    logits, outside the verify step's own metric.  Two weight copies (the
+    second the negated first) alternate so the stream never sits in the last-
+    level cache; `steps` calls timed with events on the stream they run on."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    import synth
+    dev = torch.device("cuda:0")
+    T, H, V = 64, w["H"], w["V"]
+    x = synth.base_head_inputs(T, H, V, seed=seed)
+    hidden = torch.from_numpy(x["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+    wb = torch.from_numpy(x["w_base"].view(np.int16)).to(dev).view(torch.bfloat16)
+    packs = [md.medusa_base_lm_head_pack(wb), md.medusa_base_lm_head_pack(wb.neg())]
+    del wb
+    out = torch.empty((T, V), dtype=torch.float32, device=dev)
+    for i in range(4):
+        md.medusa_base_lm_head(hidden, packs[i % 2], out, V=V)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        md.medusa_base_lm_head(hidden, packs[i % 2], out, V=V)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1000.0 / steps
+    nbytes = V * H * 2 + T * H * 2 + T * V * 4
+    gbs = nbytes / us / 1e3
+    return {"kernel": "base_lm_head", "M": T, "H": H, "V": V, "layout": "packed", "mean_launch_us": round(us, 2),
+            "bound": "hbm", "bytes_per_launch": nbytes, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_tflops": round(2.0 * T * H * V / us / 1e6, 1)}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -421,6 +460,8 @@ def main():
     }
     if not args.no_graph:
         result["graph"] = graph_timing(step, args.steps)
+    if not args.no_base_head:
+        result["base_lm_head"] = base_head_timing(w, args.seed, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)
     print(json.dumps(result))
