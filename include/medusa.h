@@ -7,6 +7,7 @@
  *   medusa_build_tree          candidate tree from a medusa_choices spec
  *   medusa_tree_attention      tree-masked attention over the KV prefix
  *   medusa_base_lm_head        base lm_head at the tree nodes -> logits
+ *                              (or medusa_base_posterior: both fused)
  *   medusa_evaluate_posterior  greedy / typical acceptance, best path
  *   medusa_commit_kv           gather the accepted rows into contiguous slots
  *
@@ -266,6 +267,34 @@ int medusa_base_lm_head_pack(int dtype, int H, int V, const void* w_base, void* 
 
 int medusa_base_lm_head(int dtype, int M, int H, int V, const void* hidden, const void* w_base,
                         int w_packed, float* logits, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Base lm_head fused with the acceptance test.  [API] tree_decoding
+ * (base logits at every tree node) and evaluate_posterior.
+ *
+ * The result of medusa_base_lm_head followed by medusa_evaluate_posterior
+ * (same arguments and readings; logits = hidden . W^T of the B*T node
+ * rows), without the logits ever reaching memory: each block of 128
+ * vocabulary entries leaves, per node, its maximum, first argmax and
+ * (temperature > 0) the softmax sums of logits / temperature, plus the
+ * logits of the tree candidates whose tokens it holds; a merge and the
+ * path decision follow.  Three kernels on `stream`.
+ *
+ * hidden bf16 [B][T][H] (node order); W bf16 row-major or packed as in
+ * medusa_base_lm_head (w_packed); tree_candidates [B][T], retrieve
+ * [p_max][D], num_paths, temperature, eps, delta and the outputs as in
+ * medusa_evaluate_posterior.  V <= 131072.  Workspace:
+ * medusa_base_posterior_workspace() bytes (no initialisation; 0 for
+ * invalid sizes).
+ * ------------------------------------------------------------------- */
+size_t medusa_base_posterior_workspace(int B, int T, int H, int V);
+
+int medusa_base_posterior(int B, int T, int H, int V, int p_max, int D,
+                          const void* hidden, const void* w_base, int w_packed,
+                          const int32_t* tree_candidates, const int32_t* retrieve,
+                          const int32_t* num_paths, float temperature, float eps, float delta,
+                          int32_t* best_path, int32_t* accept_len, int32_t* next_token,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Text for a medusa_status value. */
 const char* medusa_status_string(int status);

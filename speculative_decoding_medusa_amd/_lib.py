@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmedusa.so")
 
 MEDUSA_F32 = 0
 MEDUSA_BF16 = 1
+_ERR_SHAPE = -2   # MEDUSA_ERR_SHAPE
 
 SPEC_STATUS = {0: "ok", 1: "padding", 2: "empty", 3: "rank", 4: "duplicate", 5: "prefix",
                6: "too_many_paths"}
@@ -55,6 +56,9 @@ _SIGS = {
     "medusa_base_lm_head_packed_bytes": (_sz, [_i, _i]),
     "medusa_base_lm_head_pack": (_i, [_i, _i, _i, _vp, _vp, _vp]),
     "medusa_base_lm_head": (_i, [_i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
+    "medusa_base_posterior_workspace": (_sz, [_i, _i, _i, _i]),
+    "medusa_base_posterior": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _f, _f, _f, _vp, _vp, _vp,
+                                   _vp, _sz, _vp]),
     "medusa_status_string": (ctypes.c_char_p, [_i]),
     "medusa_last_error": (ctypes.c_char_p, []),
     "medusa_abi_version": (_i, []),
@@ -307,7 +311,7 @@ def medusa_base_lm_head_pack(w_base):
     V, H = w_base.shape
     nbytes = int(lib.medusa_base_lm_head_packed_bytes(H, V))
     if nbytes == 0:
-        raise MedusaError(MEDUSA_ERR_SHAPE, "medusa_base_lm_head_pack: bad shape (%d, %d)" % (V, H))
+        raise MedusaError(_ERR_SHAPE, "medusa_base_lm_head_pack", "unsupported shape V=%d H=%d" % (V, H))
     packed = torch.empty(nbytes, dtype=torch.uint8, device=w_base.device)
     rc = lib.medusa_base_lm_head_pack(_dtype_code(w_base), H, V, _ptr(w_base, "w_base"), _ptr(packed, "w_packed"),
                                       _stream(w_base.device))
@@ -343,3 +347,44 @@ def medusa_base_lm_head(hidden, w_base, logits=None, V=None):
                                  _ptr(logits, "logits", torch.float32, tuple(shape[:-1]) + (V,)), _stream(dev))
     _check(rc, "medusa_base_lm_head")
     return logits
+
+
+def medusa_base_posterior(hidden, w_base, tree_candidates, retrieve, num_paths, temperature, eps, delta,
+                          V=None, out=None, ws=None):
+    """The acceptance test on the base logits of every tree node, fused:
+    hidden bf16 [B][T][H]; w_base bf16 [V][H] or packed (uint8, V given)."""
+    B, T, H = hidden.shape
+    packed = w_base.dtype == torch.uint8
+    if packed:
+        if V is None:
+            raise ValueError("V is required with packed weights")
+        wptr = _ptr(w_base, "w_base")
+    else:
+        V = w_base.shape[0]
+        wptr = _ptr(w_base, "w_base", hidden.dtype, (V, H))
+    p_max, D = retrieve.shape
+    dev = hidden.device
+    o = out or {}
+    best = o.get("best_path")
+    acc = o.get("accept_len")
+    nxt = o.get("next_token")
+    if best is None:
+        best = torch.empty(B, dtype=torch.int32, device=dev)
+    if acc is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+    if nxt is None:
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    need = int(lib.medusa_base_posterior_workspace(B, T, H, V))
+    if need == 0:
+        raise MedusaError(_ERR_SHAPE, "medusa_base_posterior", "unsupported shape B=%d T=%d H=%d V=%d" % (B, T, H, V))
+    if ws is None:
+        ws = workspace("base_posterior", dev, need)
+    rc = lib.medusa_base_posterior(B, T, H, V, p_max, D, _ptr(hidden, "hidden"), wptr, 1 if packed else 0,
+                                   _ptr(tree_candidates, "tree_candidates", torch.int32, (B, T)),
+                                   _ptr(retrieve, "retrieve", torch.int32), _ptr(num_paths, "num_paths", torch.int32),
+                                   float(temperature), float(eps), float(delta),
+                                   _ptr(best, "best_path", torch.int32, (B,)), _ptr(acc, "accept_len", torch.int32, (B,)),
+                                   _ptr(nxt, "next_token", torch.int32, (B,)), _ptr(ws, "ws"),
+                                   ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_base_posterior")
+    return dict(best_path=best, accept_len=acc, next_token=nxt)

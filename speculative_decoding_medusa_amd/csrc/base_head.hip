@@ -64,11 +64,22 @@ __device__ __forceinline__ u32x4 bh_ld16_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <bool PACKED>
+// Fused-epilogue arguments (STATS): instead of the logits, each workgroup
+// writes per-row statistics over its 128 vocabulary entries and the logits
+// of the tree candidates whose tokens fall among them.
+struct BhStatsArgs {
+  int T;                        // nodes per sequence (rows m = b * T + node)
+  float temperature;            // > 0: softmax statistics of logits / temperature
+  const int32_t* candidates;    // [B][T] token of every node
+  RowStat* parts;               // [M][gridDim.x]
+  float* child_z;               // [B][T][T]: child_z[b][n][c] = logit of c's token at node n
+};
+
+template <bool PACKED, bool STATS>
 __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, int V,
                                                                   const uint16_t* __restrict__ hidden,
                                                                   const uint16_t* __restrict__ w,
-                                                                  float* __restrict__ logits) {
+                                                                  float* __restrict__ logits, BhStatsArgs sa_args) {
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][kBhMTile * kBhPieces];
   const int m0 = blockIdx.y * kBhMTile;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -186,17 +197,114 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
     compute(0, c, wa, -1);
   }
 
-  // logits[m][v]: lane (g, n) of tile (t, mt) holds rows mt*16 + 4g + i
+  if (!STATS) {
+    // logits[m][v]: lane (g, n) of tile (t, mt) holds rows mt*16 + 4g + i
 #pragma unroll
-  for (int t = 0; t < kBhTiles; ++t) {
-    if (vrow[t] >= V) continue;
+    for (int t = 0; t < kBhTiles; ++t) {
+      if (vrow[t] >= V) continue;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + mt * 16 + 4 * g + i;
+          if (m < M) logits[static_cast<size_t>(m) * V + vrow[t]] = acc[t][mt][i];
+        }
+    }
+    return;
+  }
+
+  // ---- fused epilogue: the workgroup's 64 x 128 logits go to LDS (over the
+  // hidden-state buffers, once every wave is past its last chunk)
+  bh_wait_lds();
+  bh_barrier();
+  constexpr int LD = kBhVBlock + 1;   // padded row
+  float* lg = reinterpret_cast<float*>(&sa[0][0]);
+  static_assert(kBhMTile * LD * 4 <= 2 * kBhMTile * kBhPieces * 16, "logit tile fits the LDS buffers");
+#pragma unroll
+  for (int t = 0; t < kBhTiles; ++t)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + mt * 16 + 4 * g + i;
-        if (m < M) logits[static_cast<size_t>(m) * V + vrow[t]] = acc[t][mt][i];
+      for (int i = 0; i < 4; ++i) lg[(mt * 16 + 4 * g + i) * LD + (wave * kBhTiles + t) * 16 + n] = acc[t][mt][i];
+  // tree candidates whose token lies in this block: (sequence, node, column);
+  // a 64-row tile spans at most 63 / T + 2 sequences, so at most 2 * kMaxNodes
+  // (sequence, node) pairs are checked
+  __shared__ int s_hits[2 * kMaxNodes];
+  __shared__ int s_nhit;
+  const int v0 = blockIdx.x * kBhVBlock;
+  const int Tn = sa_args.T;
+  const int b_lo = m0 / Tn, b_hi = min(m0 + kBhMTile, M) - 1;
+  const int npair = (b_hi / Tn - b_lo + 1) * Tn;
+  if (tid == 0) s_nhit = 0;
+  bh_wait_lds();
+  bh_barrier();
+  for (int x = tid; x < npair; x += kBhThreads) {
+    const int b = b_lo + x / Tn, c = x % Tn;
+    const int tok = sa_args.candidates[static_cast<size_t>(b) * Tn + c];
+    if (tok >= v0 && tok < v0 + kBhVBlock && tok < V) {
+      const int slot = atomicAdd(&s_nhit, 1);
+      if (slot < 2 * kMaxNodes) s_hits[slot] = ((x / Tn) << 24) | (c << 8) | (tok - v0);
+    }
+  }
+  bh_wait_lds();
+  bh_barrier();
+
+  // four threads per row, 32 columns each: max / argmax, then (temperature
+  // > 0) S and A against the quarter's own maximum; quarters merged by
+  // shuffles
+  const int r = tid >> 2, q = tid & 3;
+  const float NEG = -__builtin_huge_valf();
+  RowStat st = {NEG, 0x7fffffff, NEG, 0.f, 0.f};
+  const float* lr = lg + r * LD + q * 32;
+#pragma unroll 8
+  for (int j = 0; j < 32; ++j) {
+    const int v = v0 + q * 32 + j;
+    const float z = lr[j];
+    if (v < V && beats(z, v, st.mx, st.arg)) {
+      st.mx = z;
+      st.arg = v;
+    }
+  }
+  const float temp = sa_args.temperature;
+  const bool typical = temp > 0.f;
+  if (typical && st.mx != NEG && st.mx == st.mx) {
+    const float mq = st.mx / temp;   // positive temperature: max z = max logit / t
+    float S = 0.f, A = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      if (v0 + q * 32 + j < V) {
+        const float dz = lr[j] / temp - mq;
+        const float p = expf(dz);
+        S += p;
+        A += dz * p;
       }
+    }
+    st.m = mq;
+    st.S = S;
+    st.A = A;
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    RowStat y;
+    y.mx = __shfl_xor(st.mx, o);
+    y.arg = __shfl_xor(st.arg, o);
+    y.m = __shfl_xor(st.m, o);
+    y.S = __shfl_xor(st.S, o);
+    y.A = __shfl_xor(st.A, o);
+    rowstat_merge(st, y, typical);
+  }
+  if (q == 0 && m0 + r < M) sa_args.parts[static_cast<size_t>(m0 + r) * gridDim.x + blockIdx.x] = st;
+
+  // the candidates' logits at every node of their sequence in this tile
+  const int nhit = min(s_nhit, 2 * kMaxNodes);
+  for (int e = 0; e < nhit; ++e) {
+    const int code = s_hits[e];
+    const int b = b_lo + (code >> 24), c = (code >> 8) & 0xffff, col = code & 0xff;
+    if (tid < kBhMTile) {
+      const int m = m0 + tid;
+      if (m < M && m / Tn == b)
+        sa_args.child_z[(static_cast<size_t>(b) * Tn + m % Tn) * Tn + c] = lg[tid * LD + col];
+    }
   }
 }
 
@@ -253,11 +361,86 @@ extern "C" int medusa_base_lm_head(int dtype, int M, int H, int V, const void* h
   MEDUSA_REQUIRE_PTR(logits);
   hipStream_t st = static_cast<hipStream_t>(stream);
   dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + kBhMTile - 1) / kBhMTile);
+  const BhStatsArgs none = {1, 0.f, nullptr, nullptr, nullptr};
   if (w_packed)
-    hipLaunchKernelGGL(base_lm_head_kernel<true>, grid, dim3(kBhThreads), 0, st, M, H, V,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits);
+    hipLaunchKernelGGL((base_lm_head_kernel<true, false>), grid, dim3(kBhThreads), 0, st, M, H, V,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits, none);
   else
-    hipLaunchKernelGGL(base_lm_head_kernel<false>, grid, dim3(kBhThreads), 0, st, M, H, V,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits);
+    hipLaunchKernelGGL((base_lm_head_kernel<false, false>), grid, dim3(kBhThreads), 0, st, M, H, V,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits, none);
   return medusa_host::hip_check("medusa_base_lm_head launch");
+}
+
+namespace {
+size_t bp_parts_bytes(int B, int T, int V) {
+  return medusa_host::round_up(static_cast<size_t>(B) * T * ((V + medusa::kBhVBlock - 1) / medusa::kBhVBlock) *
+                                   sizeof(medusa::RowStat), 256);
+}
+size_t bp_merged_bytes(int B, int T) {
+  return medusa_host::round_up(static_cast<size_t>(B) * T * sizeof(medusa::RowStat), 256);
+}
+size_t bp_childz_bytes(int B, int T) {
+  return medusa_host::round_up(static_cast<size_t>(B) * T * T * sizeof(float), 256);
+}
+constexpr int kBpMaxParts = 1024;   // vocabulary blocks the merge takes: V <= 131072
+}  // namespace
+
+extern "C" size_t medusa_base_posterior_workspace(int B, int T, int H, int V) {
+  using namespace medusa;
+  if (B < 1 || B > kMaxBatch || T < 1 || T > kMaxNodes || H < 8 || H > (1 << 16) || H % 8 != 0 || V < 1 ||
+      (V + kBhVBlock - 1) / kBhVBlock > kBpMaxParts)
+    return 0;
+  return bp_parts_bytes(B, T, V) + bp_merged_bytes(B, T) + bp_childz_bytes(B, T);
+}
+
+extern "C" int medusa_base_posterior(int B, int T, int H, int V, int p_max, int D, const void* hidden,
+                                     const void* w_base, int w_packed, const int32_t* tree_candidates,
+                                     const int32_t* retrieve, const int32_t* num_paths, float temperature,
+                                     float eps, float delta, int32_t* best_path, int32_t* accept_len,
+                                     int32_t* next_token, void* ws, size_t ws_bytes, void* stream) {
+  using namespace medusa;
+  MEDUSA_REQUIRE(B >= 1 && B <= kMaxBatch, MEDUSA_ERR_SHAPE, "%s: B=%d", __func__, B);
+  MEDUSA_REQUIRE(T >= 1 && T <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: T=%d", __func__, T);
+  MEDUSA_REQUIRE(H >= 8 && H <= (1 << 16) && H % 8 == 0, MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE(V >= 1 && (V + kBhVBlock - 1) / kBhVBlock <= kBpMaxParts, MEDUSA_ERR_SHAPE,
+                 "%s: V=%d (at most %d)", __func__, V, kBpMaxParts * kBhVBlock);
+  MEDUSA_REQUIRE(p_max >= 1 && p_max <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: p_max=%d", __func__, p_max);
+  MEDUSA_REQUIRE(D >= 1 && D <= kMaxHeads + 1, MEDUSA_ERR_SHAPE, "%s: D=%d", __func__, D);
+  MEDUSA_REQUIRE(temperature == temperature && temperature >= 0.f, MEDUSA_ERR_VALUE,
+                 "%s: temperature must be >= 0", __func__);
+  MEDUSA_REQUIRE(temperature == 0.f || (eps == eps && eps > 0.f && delta == delta && delta > 0.f),
+                 MEDUSA_ERR_VALUE, "%s: eps and delta must be positive", __func__);
+  MEDUSA_REQUIRE_PTR(hidden);
+  MEDUSA_REQUIRE_PTR(w_base);
+  MEDUSA_REQUIRE_PTR(tree_candidates);
+  MEDUSA_REQUIRE_PTR(retrieve);
+  MEDUSA_REQUIRE_PTR(num_paths);
+  MEDUSA_REQUIRE_PTR(best_path);
+  MEDUSA_REQUIRE_PTR(accept_len);
+  MEDUSA_REQUIRE_PTR(next_token);
+  MEDUSA_REQUIRE_PTR(ws);
+  const size_t need = medusa_base_posterior_workspace(B, T, H, V);
+  MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                 need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  RowStat* parts = reinterpret_cast<RowStat*>(base);
+  RowStat* merged = reinterpret_cast<RowStat*>(base + bp_parts_bytes(B, T, V));
+  float* child_z = reinterpret_cast<float*>(base + bp_parts_bytes(B, T, V) + bp_merged_bytes(B, T));
+  const int M = B * T;
+  dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + kBhMTile - 1) / kBhMTile);
+  const BhStatsArgs args = {T, temperature, tree_candidates, parts, child_z};
+  if (w_packed)
+    hipLaunchKernelGGL((base_lm_head_kernel<true, true>), grid, dim3(kBhThreads), 0, st, M, H, V,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base),
+                       static_cast<float*>(nullptr), args);
+  else
+    hipLaunchKernelGGL((base_lm_head_kernel<false, true>), grid, dim3(kBhThreads), 0, st, M, H, V,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base),
+                       static_cast<float*>(nullptr), args);
+  int rc = medusa_host::hip_check("medusa_base_posterior launch");
+  if (rc != MEDUSA_OK) return rc;
+  return medusa_host::posterior_from_parts(B, T, V, p_max, D, static_cast<int>(grid.x), parts, merged, child_z,
+                                           tree_candidates, retrieve, num_paths, temperature, eps, delta,
+                                           best_path, accept_len, next_token, st);
 }

@@ -64,6 +64,41 @@ __device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Statistics of one node's logits over a set of vocabulary entries: the raw
+// maximum and its first index and, for a positive temperature t, with
+// z = logit / t: m = max z, S = sum exp(z - m), A = sum (z - m) exp(z - m).
+// An empty set has mx = m = -inf, S = A = 0.
+struct RowStat {
+  float mx;     // max of the raw logits
+  int arg;      // first index of the max
+  float m;      // max of z (temperature > 0)
+  float S;      // sum exp(z - m)
+  float A;      // sum (z - m) exp(z - m)
+};
+
+// a <- statistics of the union of two disjoint sets (log-sum-exp rescaling;
+// an empty side contributes nothing).
+__device__ __forceinline__ void rowstat_merge(RowStat& a, const RowStat& b, bool typical) {
+  if (beats(b.mx, b.arg, a.mx, a.arg)) {
+    a.mx = b.mx;
+    a.arg = b.arg;
+  }
+  if (!typical) return;
+  const float NEG = -__builtin_huge_valf();
+  if (b.m == NEG) return;
+  if (a.m == NEG) {
+    a.m = b.m;
+    a.S = b.S;
+    a.A = b.A;
+    return;
+  }
+  const float m = fmaxf(a.m, b.m);
+  const float wa = expf(a.m - m), wb = expf(b.m - m);
+  a.A = wa * (a.A + (a.m - m) * a.S) + wb * (b.A + (b.m - m) * b.S);
+  a.S = wa * a.S + wb * b.S;
+  a.m = m;
+}
+
 // Pointers into LDS that stay LDS pointers (ds_read/ds_write) even when they
 // are volatile or pass through functions; a generic pointer would be lowered
 // to flat accesses, which count against the vector-memory counter.
@@ -78,6 +113,14 @@ namespace medusa_host {
 
 void set_error(const char* fmt, ...);
 int hip_check(const char* what);  // MEDUSA_OK or MEDUSA_ERR_HIP after a launch
+
+// Acceptance test from per-(node, vocabulary block) statistics and the
+// children's logits (posterior.hip; used by the fused base lm_head).
+int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, const medusa::RowStat* parts,
+                         medusa::RowStat* merged, const float* child_z, const int32_t* tree_candidates,
+                         const int32_t* retrieve, const int32_t* num_paths, float temperature, float eps,
+                         float delta, int32_t* best_path, int32_t* accept_len, int32_t* next_token,
+                         hipStream_t st);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -18,14 +18,6 @@ constexpr int kPostThreads = 256;
 constexpr int kPostVec = 4;         // float4 loads per thread per chunk
 constexpr int kPostChunk = kPostThreads * kPostVec * 4;
 
-struct RowStat {
-  float mx;     // max of the raw logits
-  int arg;      // first index of the max
-  float m;      // max of z (temperature > 0)
-  float S;      // sum exp(z - m)
-  float A;      // sum (z - m) exp(z - m)
-};
-
 __global__ __launch_bounds__(kPostThreads) void posterior_rows_kernel(
     int T, int V, int nchunk, const float* __restrict__ logits, float temperature, RowStat* __restrict__ stats) {
   const int chunk = blockIdx.x, row = blockIdx.y;   // row = b * T + node
@@ -116,12 +108,15 @@ __global__ __launch_bounds__(kPostThreads) void posterior_rows_kernel(
 // path's run of leading accepted steps, and the lowest-index longest path.
 constexpr int kDecideUnroll = 8;   // chunk statistics loaded per batch
 
+//
+// child_z (optional, [B][T][T]): child_z[b][n][c] = the logit of node c's
+// token at node n, supplied by the fused base lm_head instead of `logits`.
 __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
     int T, int V, int nchunk, int p_max, int D, const float* __restrict__ logits,
     const int32_t* __restrict__ tree_candidates, const int32_t* __restrict__ retrieve,
     const int32_t* __restrict__ num_paths, float temperature, float eps, float delta,
     const RowStat* __restrict__ stats, int32_t* __restrict__ best_path, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ next_token) {
+    int32_t* __restrict__ next_token, const float* __restrict__ child_z) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int s_tok[kMaxNodes], s_arg[kMaxNodes];
@@ -216,8 +211,12 @@ __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
       tok[u] = c[u] >= 0 ? s_tok[c[u]] : -1;
       const bool ok = prev[u] >= 0 && tok[u] >= 0 && tok[u] < V;
       z[u] = 0.f;
-      if (typical)
-        z[u] = logits[(static_cast<size_t>(b) * T + (ok ? prev[u] : 0)) * V + (ok ? tok[u] : 0)];
+      if (typical) {
+        if (child_z != nullptr)
+          z[u] = child_z[(static_cast<size_t>(b) * T + (ok ? prev[u] : 0)) * T + (ok ? c[u] : 0)];
+        else
+          z[u] = logits[(static_cast<size_t>(b) * T + (ok ? prev[u] : 0)) * V + (ok ? tok[u] : 0)];
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -321,6 +320,70 @@ extern "C" int medusa_evaluate_posterior(int B, int T, int V, int p_max, int D, 
   if (rc != MEDUSA_OK) return rc;
   hipLaunchKernelGGL(posterior_decide_kernel, dim3(B), dim3(kPostThreads), 0, st, T, V, nchunk, p_max, D, logits,
                      tree_candidates, retrieve, num_paths, temperature, eps, delta, stats, best_path, accept_len,
-                     next_token);
+                     next_token, static_cast<const float*>(nullptr));
   return medusa_host::hip_check("medusa_evaluate_posterior decide launch");
 }
+
+namespace medusa {
+
+// Per-row statistics from `nparts` partial ones (disjoint vocabulary
+// blocks): one workgroup per row, every part requested in one round trip,
+// merged in registers, across the wave by shuffles, then across waves.
+constexpr int kMergeParts = 4;   // parts per thread: nparts <= 1024
+
+__global__ __launch_bounds__(kPostThreads) void posterior_merge_kernel(int nparts, int typical,
+                                                                     const RowStat* __restrict__ parts,
+                                                                     RowStat* __restrict__ out) {
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const RowStat* pr = parts + static_cast<size_t>(row) * nparts;
+  const float NEG = -__builtin_huge_valf();
+  RowStat x[kMergeParts];
+#pragma unroll
+  for (int u = 0; u < kMergeParts; ++u) x[u] = pr[min(u * kPostThreads + tid, nparts - 1)];
+  RowStat acc = {NEG, 0x7fffffff, NEG, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kMergeParts; ++u)
+    if (u * kPostThreads + tid < nparts) rowstat_merge(acc, x[u], typical != 0);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    RowStat y;
+    y.mx = __shfl_xor(acc.mx, o);
+    y.arg = __shfl_xor(acc.arg, o);
+    y.m = __shfl_xor(acc.m, o);
+    y.S = __shfl_xor(acc.S, o);
+    y.A = __shfl_xor(acc.A, o);
+    rowstat_merge(acc, y, typical != 0);
+  }
+  __shared__ RowStat s_part[kPostThreads / kWave];
+  if (lane == 0) s_part[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kPostThreads / kWave; ++w) rowstat_merge(acc, s_part[w], typical != 0);
+    out[row] = acc;
+  }
+}
+
+}  // namespace medusa
+
+namespace medusa_host {
+
+// Acceptance from per-(row, part) statistics and the children's logits
+// (rows = B * T nodes): merge kernel, then the decide kernel on one
+// statistic per row.  `merged` holds B * T statistics.
+int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, const medusa::RowStat* parts,
+                         medusa::RowStat* merged, const float* child_z, const int32_t* tree_candidates,
+                         const int32_t* retrieve, const int32_t* num_paths, float temperature, float eps,
+                         float delta, int32_t* best_path, int32_t* accept_len, int32_t* next_token,
+                         hipStream_t st) {
+  using namespace medusa;
+  hipLaunchKernelGGL(posterior_merge_kernel, dim3(B * T), dim3(kPostThreads), 0, st, nparts,
+                     temperature > 0.f ? 1 : 0, parts, merged);
+  int rc = hip_check("posterior merge launch");
+  if (rc != MEDUSA_OK) return rc;
+  hipLaunchKernelGGL(posterior_decide_kernel, dim3(B), dim3(kPostThreads), 0, st, T, V, 1, p_max, D,
+                     static_cast<const float*>(nullptr), tree_candidates, retrieve, num_paths, temperature, eps,
+                     delta, merged, best_path, accept_len, next_token, child_z);
+  return hip_check("posterior decide launch");
+}
+
+}  // namespace medusa_host

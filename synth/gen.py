@@ -194,10 +194,12 @@ def base_head_inputs(M, H, V, seed=0, workload_id=9):
     return dict(hidden=bf16_bits(h).reshape(M, H), w_base=bf16_bits(w).reshape(V, H))
 
 
-def base_posterior_inputs(w, tree_candidates, retrieve, num_paths, seed=0, scale=7.0, plant=True):
+def base_posterior_inputs(w, tree_candidates, retrieve, num_paths, seed=0, scale=7.0, plant=True, h_std=1.0):
     """Final hidden states at the tree nodes and a base lm_head, with one
-    planted path per sequence (bf16 bits): hidden [B][T][H] ~ N(0, 1),
-    w_base [V][H] ~ N(0, 0.02^2).
+    planted path per sequence (bf16 bits): hidden [B][T][H] ~ N(0, h_std^2),
+    w_base [V][H] ~ N(0, 0.02^2), so a node's logits have standard deviation
+    about 0.02 h_std sqrt(H) (h_std sets how peaked each node's distribution
+    is, and with it the typical-acceptance thresholds).
 
     As in ``posterior_logits``, a deepest path is chosen uniformly and
     A ~ Binomial(depth, 1/2) drawn; for j < A, ``scale`` times the lm_head row
@@ -209,7 +211,7 @@ def base_posterior_inputs(w, tree_candidates, retrieve, num_paths, seed=0, scale
     cand = np.asarray(tree_candidates)
     T = int(cand.shape[1])
     wb = normal_f32(seed, wid, "w_base", (), V * H, std=0.02).reshape(V, H)
-    h = normal_f32(seed, wid, "h_tree", (), B * T * H).reshape(B, T, H)
+    h = normal_f32(seed, wid, "h_tree", (), B * T * H, std=h_std).reshape(B, T, H)
     plan = []
     for b in range(B):
         if not plant:

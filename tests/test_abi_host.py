@@ -167,6 +167,30 @@ def test_base_lm_head_pack_validation_and_sizes():
     assert L.medusa_base_lm_head_pack(1, 64, 100, A, A, None) == ALIAS
 
 
+def bpost(B=1, T=64, H=4096, V=32000, p_max=64, D=6, hidden=A, w=A, packed=1, cand=A, ret=A, npaths=A,
+          temp=0.7, eps=0.09, delta=0.3, best=A, acc=A, nxt=A, ws=A, wsb=1 << 30):
+    return L.medusa_base_posterior(B, T, H, V, p_max, D, hidden, w, packed, cand, ret, npaths, temp, eps, delta,
+                                   best, acc, nxt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(T=257), SHAPE), (dict(H=12), SHAPE), (dict(V=131073), SHAPE), (dict(D=10), SHAPE),
+    (dict(p_max=0), SHAPE), (dict(temp=-1.0), VALUE), (dict(eps=0.0), VALUE), (dict(hidden=None), NULL),
+    (dict(cand=None), NULL), (dict(ws=None), NULL), (dict(w=MIS), ALIGN), (dict(wsb=16), WS),
+])
+def test_base_posterior_validation(kw, code):
+    assert bpost(**kw) == code
+    assert L.medusa_last_error().decode() != ""
+
+
+def test_base_posterior_workspace_sizes():
+    assert L.medusa_base_posterior_workspace(1, 64, 4096, 32000) > 0
+    assert L.medusa_base_posterior_workspace(1, 64, 4096, 131072) > 0
+    assert L.medusa_base_posterior_workspace(1, 64, 4096, 131073) == 0
+    assert L.medusa_base_posterior_workspace(0, 64, 4096, 32000) == 0
+    assert L.medusa_base_posterior_workspace(1, 64, 12, 32000) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -9,6 +9,15 @@ Sizes: ragged M (partial M tiles), ragged V (partial vocab blocks and
 tiles), H below and past the 256-element K chunk with a tail and a partial
 32-element k step, the smallest shape, and the Vicuna-7B tree (64 nodes,
 H 4096, V 32000).
+
+The fused form (medusa_base_posterior: per-row statistics and the
+children's logits in the GEMM epilogue, the logits never written) returns
+best path, accepted length and next token equal to the oracle's acceptance
+test on the same planted inputs: greedy and typical, both weight layouts,
+one sequence and several whose 64-row tiles straddle sequence boundaries.
+Greedy decisions follow from the raw logits alone, which the fused and the
+unfused forms compute with the same MFMA accumulation, so on unplanted
+inputs the two agree exactly as well.
 """
 
 import numpy as np
@@ -105,11 +114,11 @@ def test_base_lm_head_writes_only_its_rows(gpu_device):
 _CASES = {}
 
 
-def _base_posterior_case(w, temperature, seed=0, max_retries=20):
+def _base_posterior_case(w, temperature, seed=0, max_retries=20, scale=20.0, h_std=1.0):
     """Tree, planted hidden states and the oracle's verdict; redrawn until
     the decisions clear float error (as for the posterior on given logits).
-    Cached per (temperature, seed)."""
-    key = (temperature, seed)
+    Cached per (shape, temperature, seed, generator settings)."""
+    key = (w["B"], w["H"], w["V"], w["K"], w["topk"], w["tree"], temperature, seed, scale, h_std)
     if key in _CASES:
         return _CASES[key]
     from cases import non_planted_children_clear, posterior_margins_ok, tree_case
@@ -117,7 +126,7 @@ def _base_posterior_case(w, temperature, seed=0, max_retries=20):
     ref = tcase["ref"]
     for retry in range(max_retries):
         x = synth.base_posterior_inputs(w, ref["tree_candidates"], ref["retrieve"], ref["num_paths"],
-                                        seed=seed + 1000 * retry, scale=20.0)
+                                        seed=seed + 1000 * retry, scale=scale, h_std=h_std)
         B, T, H = x["hidden"].shape
         z = oracle.base_logits(x["hidden"].reshape(B * T, H), x["w_base"]).reshape(B, T, -1).astype(np.float32)
         if not non_planted_children_clear(z, ref, x["plan"]):
@@ -152,3 +161,73 @@ def test_base_lm_head_then_posterior_matches_oracle(gpu_device, temperature):
     for key in ("best_path", "accept_len", "next_token"):
         assert np.array_equal(got[key].cpu().numpy(), exp[key]), key
     assert int(exp["accept_len"][0]) == x["plan"][0][1]
+
+
+def _fused(x, ref, w, temperature, packed):
+    V = x["w_base"].shape[0]
+    wd = to_dev(x["w_base"])
+    if packed:
+        wd = md.medusa_base_lm_head_pack(wd)
+    args = (to_dev(x["hidden"]), wd, to_dev(ref["tree_candidates"]), to_dev(ref["retrieve"]),
+            to_dev(np.array([ref["num_paths"]], dtype=np.int32)))
+    got = md.medusa_base_posterior(*args, temperature, w["eps"], w["delta"], V=V)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in got.items()}
+
+
+# (workload overrides, generator settings)
+_FUSED_SHAPES = {
+    # the 64-node Vicuna-7B tree, one sequence (H, V cut for the oracle)
+    "vicuna7b-tree": (dict(H=1024, V=8000), dict()),
+    # 5 sequences of 15 nodes: M = 75, the first 64-row tile holds five
+    # sequences, the second a partial one; ragged V (last block 57 wide)
+    "b5-full15": (dict(B=5, K=3, topk=2, tree="full", H=512, V=3001), dict()),
+    # 3 sequences of the 64-node tree: tiles aligned with sequences; H with a
+    # partial K chunk
+    "b3-tree": (dict(B=3, H=520, V=4100), dict()),
+    # peaked nodes (logit std about 3): low entropy, so typical acceptance
+    # thresholds sit among the children's probabilities and decide
+    "b4-tree-peaked": (dict(B=4, H=512, V=3001), dict(h_std=6.0, scale=80.0)),
+}
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+@pytest.mark.parametrize("shape", sorted(_FUSED_SHAPES))
+def test_base_posterior_fused_matches_oracle(gpu_device, shape, temperature, packed):
+    over, gen = _FUSED_SHAPES[shape]
+    w = synth.workload("vicuna-7b", **over)
+    tcase, x, exp, retry = _base_posterior_case(w, temperature, **gen)
+    print("case", shape, temperature, packed, "retry", retry, "plan", x["plan"], "expected", exp["accept_len"],
+          flush=True)
+    got = _fused(x, tcase["ref"], w, temperature, packed)
+    for key in ("best_path", "accept_len", "next_token"):
+        assert np.array_equal(got[key], exp[key]), key
+    if temperature == 0.0:
+        assert [int(a) for a in exp["accept_len"]] == [p[1] for p in x["plan"]]
+
+
+@pytest.mark.parametrize("shape", sorted(_FUSED_SHAPES))
+def test_base_posterior_fused_equals_unfused_greedy(gpu_device, shape):
+    # unplanted hidden states: arbitrary argmaxes, decided on logits both
+    # forms compute identically
+    over, gen = _FUSED_SHAPES[shape]
+    w = synth.workload("vicuna-7b", **over)
+    ref = tree_case_ref(w)
+    x = synth.base_posterior_inputs(w, ref["tree_candidates"], ref["retrieve"], ref["num_paths"], seed=77,
+                                    plant=False, h_std=gen.get("h_std", 1.0))
+    V = x["w_base"].shape[0]
+    got = _fused(x, ref, w, 0.0, True)
+    wp = md.medusa_base_lm_head_pack(to_dev(x["w_base"]))
+    logits = md.medusa_base_lm_head(to_dev(x["hidden"]), wp, V=V)
+    un = md.medusa_evaluate_posterior(logits, to_dev(ref["tree_candidates"]), to_dev(ref["retrieve"]),
+                                      to_dev(np.array([ref["num_paths"]], dtype=np.int32)), 0.0, w["eps"],
+                                      w["delta"])
+    torch.cuda.synchronize()
+    for key in ("best_path", "accept_len", "next_token"):
+        assert np.array_equal(got[key], un[key].cpu().numpy()), key
+
+
+def tree_case_ref(w, seed=0):
+    from cases import tree_case
+    return tree_case(w, seed=seed)["ref"]
