@@ -9,6 +9,7 @@ One step = every stage of the verify step on one HIP stream:
 Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --tree-sweep [--steps K]     # step cost vs heads K and tree size T
 
 Prints one JSON line.  `roofline` covers the dominant kernel (lm_head +
 top-k): algorithmic bytes per launch over its mean duration, measured with
@@ -43,6 +44,9 @@ def parse():
                     help="skip the base lm_head timing (the step before the acceptance test)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)")
+    ap.add_argument("--tree-sweep", action="store_true",
+                    help="run only the tree-shape sweep: step cost and expected tokens per step against the "
+                         "number of heads K and tree nodes T (one JSON line)")
     return ap.parse_args()
 
 
@@ -340,41 +344,198 @@ def graph_timing(step, steps):
             "note": "the whole step replayed from HIP graphs (one per attention layer), %d steps" % steps}
 
 
-def base_head_timing(w, seed, steps):
+def base_head_timing(step, seed, steps):
     """The base model's lm_head over the 64 tree nodes (packed bf16 weights,
     H x V of the workload): the step that produces the acceptance test's
     logits, outside the verify step's own metric.  Two weight copies (the
     second the negated first) alternate so the stream never sits in the last-
-    level cache; `steps` calls timed with events on the stream they run on."""
+    level cache; `steps` calls timed with events on the stream they run on.
+    Also timed: the acceptance test on those logits, unfused (lm_head, then
+    medusa_evaluate_posterior) and fused (medusa_base_posterior: row
+    statistics in the lm_head's epilogue, the logits never written)."""
     import numpy as np
     import torch
 
     import speculative_decoding_medusa_amd as md
     import synth
+    w = step.w
     dev = torch.device("cuda:0")
-    T, H, V = 64, w["H"], w["V"]
+    T, H, V = step.T, w["H"], w["V"]
     x = synth.base_head_inputs(T, H, V, seed=seed)
     hidden = torch.from_numpy(x["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
     wb = torch.from_numpy(x["w_base"].view(np.int16)).to(dev).view(torch.bfloat16)
     packs = [md.medusa_base_lm_head_pack(wb), md.medusa_base_lm_head_pack(wb.neg())]
     del wb
-    out = torch.empty((T, V), dtype=torch.float32, device=dev)
-    for i in range(4):
-        md.medusa_base_lm_head(hidden, packs[i % 2], out, V=V)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        md.medusa_base_lm_head(hidden, packs[i % 2], out, V=V)
-    end.record()
-    torch.cuda.synchronize()
-    us = start.elapsed_time(end) * 1000.0 / steps
+    out = torch.empty((1, T, V), dtype=torch.float32, device=dev)
+    h3 = hidden.view(1, T, H)
+    tr = step.tree
+    post = {n: torch.empty(1, dtype=torch.int32, device=dev) for n in ("best_path", "accept_len", "next_token")}
+    ws_p = torch.zeros(md.medusa_posterior_workspace(1, T, V), dtype=torch.uint8, device=dev)
+    ws_f = torch.zeros(md.medusa_base_posterior_workspace(1, T, H, V), dtype=torch.uint8, device=dev)
+    temp, eps, delta = w["temperature"], w["eps"], w["delta"]
+
+    def gemm(i):
+        md.medusa_base_lm_head(h3, packs[i % 2], out, V=V)
+
+    def unfused(i):
+        md.medusa_base_lm_head(h3, packs[i % 2], out, V=V)
+        md.medusa_evaluate_posterior(out, tr["tree_candidates"], tr["retrieve"], tr["num_paths"], temp, eps, delta,
+                                     out=post, ws=ws_p)
+
+    def fused(i):
+        md.medusa_base_posterior(h3, packs[i % 2], tr["tree_candidates"], tr["retrieve"], tr["num_paths"], temp,
+                                 eps, delta, V=V, out=post, ws=ws_f)
+
+    def timed(fn):
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) * 1000.0 / steps
+
+    us = timed(gemm)
+    us_unfused = timed(unfused)
+    us_fused = timed(fused)
     nbytes = V * H * 2 + T * H * 2 + T * V * 4
     gbs = nbytes / us / 1e3
     return {"kernel": "base_lm_head", "M": T, "H": H, "V": V, "layout": "packed", "mean_launch_us": round(us, 2),
             "bound": "hbm", "bytes_per_launch": nbytes, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "mfma_tflops": round(2.0 * T * H * V / us / 1e6, 1)}
+            "mfma_tflops": round(2.0 * T * H * V / us / 1e6, 1),
+            "with_acceptance_us": {"unfused": round(us_unfused, 2), "fused": round(us_fused, 2),
+                                   "temperature": temp}}
+
+
+SWEEP_K = (3, 4, 5, 8)
+SWEEP_T = (16, 32, 64, 128)
+
+
+def tree_sweep(args):
+    """Cost of one verify step against the tree's shape (Vicuna-7B sizes,
+    batch 1): for each number of heads K and tree size T, the T - 1 rank
+    tuples with the highest acceptance probability under the synthetic
+    acceptance model (synth.geometric_acceptance) form the tree; a step
+    (K heads, tree, one attention layer at prefix L, acceptance on T x V
+    logits, commit over every layer) is captured in a HIP graph and its
+    replays timed with events on the capture stream, and the heads alone
+    likewise.  Reported beside it: the model's expected tokens per step
+    (accepted length + the bonus token) and their ratio to the step time.
+    Weights and activations are random on the device (timing does not
+    depend on their values)."""
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    import synth
+
+    w = synth.workload("vicuna-7b")
+    dev = torch.device("cuda:0")
+    B, H, V, k = 1, w["H"], w["V"], w["topk"]
+    Hq, dh, L, nl = w["Hq"], w["d"], w["L"], w["n_layers"]
+    Kmax, Tmax = max(SWEEP_K), max(SWEEP_T)
+    S = L + Tmax + 8
+    bf = torch.bfloat16
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(bf)
+
+    hidden = rnd((B, H), 1.0)
+    w1, b1 = rnd((Kmax, H, H), 0.02), rnd((Kmax, H), 0.02)
+    w_lm = torch.empty((Kmax, V, H), dtype=bf, device=dev)
+    for h in range(Kmax):
+        w_lm[h] = rnd((V, H), 0.02)
+    kc = torch.empty((nl, B, Hq, S, dh), dtype=bf, device=dev)
+    vc = torch.empty_like(kc)
+    for layer in range(nl):
+        kc[layer] = rnd((B, Hq, S, dh), 1.0)
+        vc[layer] = rnd((B, Hq, S, dh), 1.0)
+    plen = torch.full((B,), L, dtype=torch.int32, device=dev)
+    root = torch.full((B,), 7, dtype=torch.int32, device=dev)
+    i32 = torch.int32
+
+    def time_graph(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) * 1000.0 / args.steps
+
+    rows = []
+    for K in SWEEP_K:
+        acc_model = synth.geometric_acceptance(K, k)
+        r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+        heads = dict(topk_ids=torch.empty((B, K, k), dtype=i32, device=dev),
+                     topk_logits=torch.empty((B, K, k), dtype=torch.float32, device=dev))
+        ws_h = torch.zeros(md.medusa_heads_workspace(md.MEDUSA_BF16, B, H, V, K, k), dtype=torch.uint8,
+                           device=dev)
+        w1k, b1k, wlk = w1[:K], b1[:K], w_lm[:K]
+
+        def run_heads():
+            md.medusa_resblock(hidden, w1k, b1k, r=r)
+            md.medusa_lm_head_topk(r, wlk, k, out=heads, ws=ws_h)
+
+        heads_us = time_graph(run_heads)
+        for T in SWEEP_T:
+            choices = synth.best_tree_choices(acc_model, T - 1)
+            expect = synth.expected_accept_length(acc_model, choices)
+            ch = torch.from_numpy(synth.choices_array(choices, K)).to(dev)
+            tree = dict(tree_candidates=torch.empty((B, T), dtype=i32, device=dev),
+                        tree_indices=torch.empty(T, dtype=i32, device=dev),
+                        parent=torch.empty(T, dtype=i32, device=dev), depth=torch.empty(T, dtype=i32, device=dev),
+                        position_ids=torch.empty((B, T), dtype=i32, device=dev),
+                        tree_mask=torch.empty((T, T), dtype=torch.uint8, device=dev),
+                        retrieve=torch.empty((T, K + 1), dtype=i32, device=dev),
+                        num_paths=torch.empty(1, dtype=i32, device=dev), status=torch.empty(2, dtype=i32, device=dev))
+            q = rnd((B, T, Hq, dh), 1.0)
+            att = torch.empty_like(q)
+            ws_a = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, B, T, Hq, dh, S),
+                               dtype=torch.uint8, device=dev)
+            logits = torch.randn((B, T, V), generator=gen, device=dev) * w["logit_std"]
+            post = {n: torch.empty(B, dtype=i32, device=dev) for n in ("best_path", "accept_len", "next_token")}
+            ws_p = torch.zeros(md.medusa_posterior_workspace(B, T, V), dtype=torch.uint8, device=dev)
+            new_plen = torch.empty(B, dtype=i32, device=dev)
+
+            def run_step():
+                run_heads()
+                md.medusa_build_tree(ch, heads["topk_ids"], root, plen, p_max=T, out=tree)
+                md.medusa_tree_attention(q, kc[0], vc[0], plen, tree["tree_mask"], dh ** -0.5, out=att, ws=ws_a)
+                md.medusa_evaluate_posterior(logits, tree["tree_candidates"], tree["retrieve"], tree["num_paths"],
+                                             w["temperature"], w["eps"], w["delta"], out=post, ws=ws_p)
+                md.medusa_commit_kv(kc, vc, plen, tree["retrieve"], post["best_path"], post["accept_len"],
+                                    new_prefix_len=new_plen)
+
+            us = time_graph(run_step)
+            status = tree["status"].cpu().tolist()
+            if status != [0, -1]:
+                raise RuntimeError("tree build failed for K=%d T=%d: %s" % (K, T, status))
+            tps = 1.0 + expect
+            rows.append({"K": K, "topk": k, "T": T, "depth": max(len(t) for t in choices),
+                         "us_per_step": round(us, 2), "heads_us": round(heads_us, 2),
+                         "rest_us": round(us - heads_us, 2), "expected_tokens_per_step": round(tps, 4),
+                         "tokens_per_ms": round(tps / us * 1000.0, 3)})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"tree_sweep": rows, "workload": "vicuna-7b verify step, batch 1 (H %d, V %d, L %d, "
+                      "%d layers, one attention layer per step)" % (H, V, L, nl),
+                      "acceptance_model": "p[d][i] = q1 gamma^d (1 - rho) rho^i, q1 0.85, gamma 0.9, rho 0.5",
+                      "steps": args.steps, "timing": "HIP graph replays, events on the capture stream"}))
 
 
 def main():
@@ -386,6 +547,9 @@ def main():
         print("bench.py: this build runs the verify step on one GPU only; --gpus %d is not supported "
               "(run with --gpus 1)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.tree_sweep:
+        tree_sweep(args)
+        return
 
     import torch
 
@@ -461,7 +625,7 @@ def main():
     if not args.no_graph:
         result["graph"] = graph_timing(step, args.steps)
     if not args.no_base_head:
-        result["base_lm_head"] = base_head_timing(w, args.seed, args.steps)
+        result["base_lm_head"] = base_head_timing(step, args.seed, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)
     print(json.dumps(result))

@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     medusa_heads_workspace, medusa_resblock, medusa_lm_head_topk, medusa_heads, medusa_build_tree,
     medusa_tree_attention_workspace, medusa_tree_attention, medusa_posterior_workspace,
     medusa_evaluate_posterior, medusa_commit_kv, medusa_base_lm_head, medusa_base_lm_head_pack,
-    medusa_base_posterior,
+    medusa_base_posterior_workspace, medusa_base_posterior,
 )
 
 __all__ = [
@@ -22,5 +22,5 @@ __all__ = [
     "medusa_heads_workspace", "medusa_resblock", "medusa_lm_head_topk", "medusa_heads",
     "medusa_build_tree", "medusa_tree_attention_workspace", "medusa_tree_attention",
     "medusa_posterior_workspace", "medusa_evaluate_posterior", "medusa_commit_kv", "medusa_base_lm_head",
-    "medusa_base_lm_head_pack", "medusa_base_posterior",
+    "medusa_base_lm_head_pack", "medusa_base_posterior_workspace", "medusa_base_posterior",
 ]

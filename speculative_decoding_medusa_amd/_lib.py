@@ -349,6 +349,10 @@ def medusa_base_lm_head(hidden, w_base, logits=None, V=None):
     return logits
 
 
+def medusa_base_posterior_workspace(B, T, H, V):
+    return int(lib.medusa_base_posterior_workspace(B, T, H, V))
+
+
 def medusa_base_posterior(hidden, w_base, tree_candidates, retrieve, num_paths, temperature, eps, delta,
                           V=None, out=None, ws=None):
     """The acceptance test on the base logits of every tree node, fused:
@@ -374,7 +378,7 @@ def medusa_base_posterior(hidden, w_base, tree_candidates, retrieve, num_paths, 
         acc = torch.empty(B, dtype=torch.int32, device=dev)
     if nxt is None:
         nxt = torch.empty(B, dtype=torch.int32, device=dev)
-    need = int(lib.medusa_base_posterior_workspace(B, T, H, V))
+    need = medusa_base_posterior_workspace(B, T, H, V)
     if need == 0:
         raise MedusaError(_ERR_SHAPE, "medusa_base_posterior", "unsupported shape B=%d T=%d H=%d V=%d" % (B, T, H, V))
     if ws is None:

@@ -135,6 +135,21 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
       for (int t = 0; t < kBhTiles; ++t) bw[t][s] = wpiece(t, c, s);
   };
 
+  // STATS: the tokens of the (sequence, node) pairs this M tile covers,
+  // requested now so the epilogue does not wait on them.  A 64-row tile
+  // spans at most ceil(63 / T) + 1 sequences: at most 2 * kMaxNodes pairs,
+  // two per thread (clamped addresses, masked at use).
+  const int Tn = STATS ? sa_args.T : 1;
+  const int b_lo = m0 / Tn;
+  const int npair = STATS ? ((min(m0 + kBhMTile, M) - 1) / Tn - b_lo + 1) * Tn : 0;
+  int ctok[2] = {-1, -1};
+  static_assert(2 * kBhThreads >= 2 * kMaxNodes, "two candidate tokens per thread cover a tile's pairs");
+  if constexpr (STATS) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      ctok[u] = sa_args.candidates[static_cast<size_t>(b_lo) * Tn + min(u * kBhThreads + tid, npair - 1)];
+  }
+
   f32x4 acc[kBhTiles][4];
 #pragma unroll
   for (int t = 0; t < kBhTiles; ++t)
@@ -232,18 +247,15 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
   __shared__ int s_hits[2 * kMaxNodes];
   __shared__ int s_nhit;
   const int v0 = blockIdx.x * kBhVBlock;
-  const int Tn = sa_args.T;
-  const int b_lo = m0 / Tn, b_hi = min(m0 + kBhMTile, M) - 1;
-  const int npair = (b_hi / Tn - b_lo + 1) * Tn;
   if (tid == 0) s_nhit = 0;
   bh_wait_lds();
   bh_barrier();
-  for (int x = tid; x < npair; x += kBhThreads) {
-    const int b = b_lo + x / Tn, c = x % Tn;
-    const int tok = sa_args.candidates[static_cast<size_t>(b) * Tn + c];
-    if (tok >= v0 && tok < v0 + kBhVBlock && tok < V) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = u * kBhThreads + tid, tok = ctok[u];
+    if (x < npair && tok >= v0 && tok < v0 + kBhVBlock && tok < V) {
       const int slot = atomicAdd(&s_nhit, 1);
-      if (slot < 2 * kMaxNodes) s_hits[slot] = ((x / Tn) << 24) | (c << 8) | (tok - v0);
+      if (slot < 2 * kMaxNodes) s_hits[slot] = ((x / Tn) << 24) | ((x % Tn) << 8) | (tok - v0);
     }
   }
   bh_wait_lds();

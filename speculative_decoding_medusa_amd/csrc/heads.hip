@@ -1175,11 +1175,12 @@ LmGrid lm_grid(int dtype, int B, int H, int V, int K, int topk, int wps) {
   LmGrid lg{};
   lg.nst = (H + 511) / 512;
   lg.diag = dtype == MEDUSA_BF16 && B <= 2 && lg.nst <= 16;
+  // workgroups per head: the K heads share 256 CUs x wps resident
+  // workgroups, rounded down so the whole grid is one round
+  long long wgh = 256LL * wps / K;
+  if (wgh < 1) wgh = 1;
   if (lg.diag) {
-    const long long waves = 256LL * 4 * wps;
-    long long wph = waves / K;
-    if (wph < 1) wph = 1;
-    long long rpw = (V + wph - 1) / wph;
+    long long rpw = (V + kHeadsWaves * wgh - 1) / (kHeadsWaves * wgh);
     const long long min_rpw = (V + kHeadsWaves * 1024LL - 1) / (kHeadsWaves * 1024LL);
     if (rpw < min_rpw) rpw = min_rpw;
     lg.rows_per_wave = static_cast<int>(rpw);
@@ -1191,8 +1192,7 @@ LmGrid lm_grid(int dtype, int B, int H, int V, int K, int topk, int wps) {
   lg.stream = dtype == MEDUSA_BF16 && lg.lds <= kStreamLdsMax;
   if (lg.stream) {
     const long long tiles = (V + 15) / 16;
-    const long long waves_target = 256LL * 4 * wps;
-    long long tpw = (tiles * K + waves_target - 1) / waves_target;
+    long long tpw = (tiles + kHeadsWaves * wgh - 1) / (kHeadsWaves * wgh);
     if (tpw < 1) tpw = 1;
     const long long min_tpw = (tiles + kHeadsWaves * 1024LL - 1) / (kHeadsWaves * 1024LL);
     if (tpw < min_tpw) tpw = min_tpw;
@@ -1255,10 +1255,9 @@ int check_heads_shape(const char* fn, int dtype, int B, int H, int V, int K, int
 constexpr int kResblockWavesPerSimd = 1;
 
 int resblock_rows_per_wave(int H, int K, int wps) {
-  const long long waves = 256LL * 4 * wps;
-  long long wph = waves / K;
-  if (wph < 1) wph = 1;
-  long long rpw = (H + wph - 1) / wph;
+  long long wgh = 256LL * wps / K;   // workgroups per head, one round over 256 CUs
+  if (wgh < 1) wgh = 1;
+  long long rpw = (H + kHeadsWaves * wgh - 1) / (kHeadsWaves * wgh);
   return static_cast<int>(rpw < 1 ? 1 : rpw);
 }
 

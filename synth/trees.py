@@ -73,3 +73,58 @@ def choices_array(choices, K):
             raise ValueError("tuple longer than K")
         arr[i, :len(t)] = t
     return arr
+
+
+# ------------------------------------------------------- tree-shape sweeps
+# A synthetic acceptance model for choosing and scoring trees of a given
+# size.  It is a workload model, not part of the verify step: it says how
+# likely each head rank is to be the base model's next token.
+
+def geometric_acceptance(K, topk, q1=0.85, gamma=0.9, rho=0.5):
+    """p [K][topk]: p[d][i] = chance that rank i of head d+1 is the base
+    model's token at that depth, given every earlier depth was right.
+    Head d+1 holds q1 * gamma^d of that chance over its ranks, split
+    geometrically with ratio rho: p[d][i] = q1 gamma^d (1 - rho) rho^i."""
+    d = np.arange(K, dtype=np.float64)[:, None]
+    i = np.arange(topk, dtype=np.float64)[None, :]
+    return q1 * gamma ** d * (1.0 - rho) * rho ** i
+
+
+def path_probability(p, t):
+    """Chance that the whole rank tuple t is right: the product of its edges."""
+    out = 1.0
+    for depth, r in enumerate(t):
+        out *= float(p[depth][r])
+    return out
+
+
+def best_tree_choices(p, n):
+    """The n rank tuples of highest path probability (ties: the smaller
+    tuple first), in that order.  Probabilities fall along both child and
+    next-sibling edges (every p <= 1 and p[d] non-increasing in rank), so a
+    best-first walk over those edges meets tuples in non-increasing order
+    and the chosen set contains every chosen tuple's ancestors."""
+    import heapq
+    K, topk = len(p), len(p[0])
+    heap = [(-path_probability(p, (0,)), (0,))]
+    out = []
+    while heap and len(out) < n:
+        _, t = heapq.heappop(heap)
+        out.append(t)
+        if len(t) < K:
+            c = t + (0,)
+            heapq.heappush(heap, (-path_probability(p, c), c))
+        if t[-1] + 1 < topk:
+            s = t[:-1] + (t[-1] + 1,)
+            heapq.heappush(heap, (-path_probability(p, s), s))
+    if len(out) < n:
+        raise ValueError("only %d tuples exist for K=%d, topk=%d" % (len(out), K, topk))
+    return out
+
+
+def expected_accept_length(p, choices):
+    """Expected accepted length of a step on this tree: a step accepts
+    exactly the tree nodes on the base model's own continuation (one token
+    is right at each depth), so the mean is the sum of the nodes' path
+    probabilities."""
+    return float(sum(path_probability(p, t) for t in choices))
