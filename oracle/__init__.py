@@ -7,6 +7,8 @@ computes, written from the pages' descriptions of Medusa:
   tree.py       the candidate tree from a ``medusa_choices`` spec
   attention.py  tree-masked attention over a KV prefix
   posterior.py  greedy / typical acceptance and the longest accepted prefix
+  nucleus.py    nucleus (top-p) acceptance: a sample per node, children
+                accepted when they equal their parent's sample
   commit.py     gathering the accepted path's K/V into contiguous slots
   base_head.py  the base model's lm_head over the tree nodes, and the
                 acceptance test on its logits
@@ -33,9 +35,11 @@ from .attention import tree_attention
 from .posterior import node_statistics, evaluate_posterior
 from .commit import commit_kv
 from .base_head import base_logits, base_posterior
+from .nucleus import nucleus, nucleus_sample, evaluate_posterior_nucleus
 
 __all__ = [
     "as_f64", "resblock", "lm_head_logits", "topk_by_value", "heads",
     "SpecError", "parse_choices", "build_tree", "tree_attention",
     "node_statistics", "evaluate_posterior", "commit_kv", "base_logits", "base_posterior",
+    "nucleus", "nucleus_sample", "evaluate_posterior_nucleus",
 ]
