@@ -9,6 +9,7 @@
  *   medusa_base_lm_head        base lm_head at the tree nodes -> logits
  *                              (or medusa_base_posterior: both fused)
  *   medusa_evaluate_posterior  greedy / typical acceptance, best path
+ *                              (or medusa_evaluate_posterior_nucleus: top-p)
  *   medusa_commit_kv           gather the accepted rows into contiguous slots
  *
  * Conventions shared by every call
@@ -215,6 +216,38 @@ int medusa_evaluate_posterior(int B, int T, int V, int p_max, int D,
                               float temperature, float eps, float delta,
                               int32_t* best_path, int32_t* accept_len, int32_t* next_token,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Nucleus (top-p) acceptance.  [API] medusa_generate, generate_candidates
+ * and evaluate_posterior take top_p (default 0.8) beside the sampling
+ * mode; the pages define nothing further, and this call takes the plain
+ * reading:
+ *   p_n = softmax(logits[b][n] / temperature) (temperature > 0);
+ *   the nucleus of node n is the shortest prefix of the vocabulary ordered
+ *   by p_n descending (ties: lower token id first) whose mass reaches top_p;
+ *   s_n = the token drawn from the nucleus with uniforms[b][n]: walking the
+ *   nucleus in token-id order, the first token whose running mass exceeds
+ *   u * (nucleus mass), u clamped to [0, 1] (if rounding leaves none, the
+ *   nucleus's highest id).
+ * A candidate c with parent n is accepted when tree_candidates[b][c] ==
+ * s_n; best_path and accept_len as in medusa_evaluate_posterior, and
+ * next_token = s at the path's last accepted node.  Each accepted token is
+ * a draw from the base model's nucleus, so the tokens a step emits follow
+ * nucleus sampling of the base model.
+ *
+ * logits float32 [B][T][V] (finite), V <= 262144; uniforms float32 [B][T]
+ * (the caller's random numbers, one per node); samples int32 [B][T] (may be
+ * NULL): every node's draw.  0 < top_p <= 1.  Workspace:
+ * medusa_posterior_nucleus_workspace() bytes (no initialisation).
+ * ------------------------------------------------------------------- */
+size_t medusa_posterior_nucleus_workspace(int B, int T);
+
+int medusa_evaluate_posterior_nucleus(int B, int T, int V, int p_max, int D,
+                                      const float* logits, const int32_t* tree_candidates,
+                                      const int32_t* retrieve, const int32_t* num_paths,
+                                      float temperature, float top_p, const float* uniforms,
+                                      int32_t* best_path, int32_t* accept_len, int32_t* next_token,
+                                      int32_t* samples, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
  * KV commit.  [API] tree_decoding (tree K/V appended to past_key_values);

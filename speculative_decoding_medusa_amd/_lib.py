@@ -59,6 +59,9 @@ _SIGS = {
     "medusa_base_posterior_workspace": (_sz, [_i, _i, _i, _i]),
     "medusa_base_posterior": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _f, _f, _f, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "medusa_posterior_nucleus_workspace": (_sz, [_i, _i]),
+    "medusa_evaluate_posterior_nucleus": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, _sz, _vp]),
     "medusa_status_string": (ctypes.c_char_p, [_i]),
     "medusa_last_error": (ctypes.c_char_p, []),
     "medusa_abi_version": (_i, []),
@@ -285,6 +288,42 @@ def medusa_evaluate_posterior(logits, tree_candidates, retrieve, num_paths, temp
                                        ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_evaluate_posterior")
     return dict(best_path=best, accept_len=acc, next_token=nxt)
+
+
+def medusa_posterior_nucleus_workspace(B, T):
+    return int(lib.medusa_posterior_nucleus_workspace(B, T))
+
+
+def medusa_evaluate_posterior_nucleus(logits, tree_candidates, retrieve, num_paths, temperature, top_p, uniforms,
+                                      out=None, ws=None, keep_samples=False):
+    """Nucleus (top-p) acceptance: logits float32 [B][T][V], uniforms
+    float32 [B][T] (one random number per node)."""
+    B, T, V = logits.shape
+    p_max, D = retrieve.shape
+    dev = logits.device
+    o = out or {}
+    res = {}
+    for name in ("best_path", "accept_len", "next_token"):
+        t = o.get(name)
+        res[name] = t if t is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    samples = o.get("samples")
+    if samples is None and keep_samples:
+        samples = torch.empty((B, T), dtype=torch.int32, device=dev)
+    need = medusa_posterior_nucleus_workspace(B, T)
+    if ws is None:
+        ws = workspace("posterior_nucleus", dev, need)
+    rc = lib.medusa_evaluate_posterior_nucleus(
+        B, T, V, p_max, D, _ptr(logits, "logits", torch.float32),
+        _ptr(tree_candidates, "tree_candidates", torch.int32, (B, T)), _ptr(retrieve, "retrieve", torch.int32),
+        _ptr(num_paths, "num_paths", torch.int32), float(temperature), float(top_p),
+        _ptr(uniforms, "uniforms", torch.float32, (B, T)), _ptr(res["best_path"], "best_path", torch.int32, (B,)),
+        _ptr(res["accept_len"], "accept_len", torch.int32, (B,)),
+        _ptr(res["next_token"], "next_token", torch.int32, (B,)),
+        _ptr(samples, "samples", torch.int32, (B, T)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(dev))
+    _check(rc, "medusa_evaluate_posterior_nucleus")
+    res["samples"] = samples
+    return res
 
 
 def medusa_commit_kv(k_cache, v_cache, prefix_len, retrieve, best_path, accept_len, new_prefix_len=None):

@@ -122,6 +122,11 @@ int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, cons
                          float delta, int32_t* best_path, int32_t* accept_len, int32_t* next_token,
                          hipStream_t st);
 
+// Acceptance from one drawn token per node (posterior.hip; nucleus mode).
+int decide_on_draws(int B, int T, int V, int p_max, int D, const medusa::RowStat* draws,
+                    const int32_t* tree_candidates, const int32_t* retrieve, const int32_t* num_paths,
+                    int32_t* best_path, int32_t* accept_len, int32_t* next_token, hipStream_t st);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline int dtype_size(int dtype) {

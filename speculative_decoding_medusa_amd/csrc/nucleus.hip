@@ -1,0 +1,582 @@
+// Nucleus (top-p) acceptance on gfx950.
+//
+// Per tree node: p = softmax(logits / temperature); the nucleus is the
+// shortest prefix of the vocabulary ordered by p descending (ties by token
+// id) whose mass reaches top_p; one token is drawn from it by inverse CDF
+// in token-id order with the caller's uniform.  A child is then accepted
+// exactly when its token equals its parent's draw, and the step's next
+// token is the draw at the last accepted node -- the greedy decision with
+// the draw in place of the argmax, so the decide kernel of the posterior
+// runs unchanged on the draws.
+//
+// One workgroup per node; each thread holds a contiguous chunk of the row
+// in registers (loaded once when the row fits 256 x 128 tokens) and every
+// walk runs over the chunks:
+//   0. the row maximum (masses are exp((x - max) / temperature), held as
+//      fixed-point integers so every sum is exact and order-independent);
+//   1-3. radix select by MASS on the order key of x: 11, 11, then 10 bits;
+//      each walk adds the masses of the keys that share the digits chosen
+//      so far into per-wave LDS histograms (the whole mass S on the first
+//      walk), and one wave then picks the highest bucket at which the mass
+//      from the top reaches what is still needed.  The result is the
+//      boundary key kappa: every key above it is in the nucleus, and the
+//      first c tokens (by id) with key kappa complete it;
+//   4. the nucleus mass Z, and target = floor(u * Z);
+//   5. a workgroup scan of the chunks' nucleus masses in id order: the one
+//      thread whose interval holds the target walks its chunk to the token.
+#include "common.hpp"
+
+namespace medusa {
+
+constexpr int kNucThreads = 256;
+constexpr int kNucWaves = kNucThreads / kWave;
+constexpr int kNucBuckets = 2048;           // 11-bit digits
+constexpr int kNucMaxV = 1 << 18;           // fixed-point sums stay below 2^58
+static_assert(kNucWaves == 4, "the block reductions below combine four waves");
+
+// Masses are exp((x - max) / temperature) in (0, 1], held as fixed-point
+// integers with 40 fraction bits: every sum below is exact and independent
+// of the order of the additions (at most 2^18 tokens: sums < 2^58).
+typedef unsigned long long u64;
+
+// Order key of a float: larger value, larger key (both zeros map to +0).
+__device__ __forceinline__ uint32_t nuc_key(float x) {
+  const uint32_t b = x == 0.f ? 0u : __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float nuc_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ u64 wave_sum_u64(u64 v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive scan across the wave's lanes in lane order.
+template <typename X>
+__device__ __forceinline__ X wave_incl_scan(X v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const X y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Bucket choice for one digit (called by one whole wave): among buckets
+// [0, nb) of `h` (masses), the highest d with h[d] > 0 whose mass from the
+// top through d reaches `need`; if there is none, the lowest d with
+// h[d] > 0.  Returns d and, in `above`, the mass of the buckets above d.
+__device__ __forceinline__ int nuc_pick(const u64* h, int nb, u64 need, int lane, u64& above) {
+  const int per = nb / kWave;
+  const int lo = lane * per;
+  u64 local = 0;
+  for (int i = 0; i < per; ++i) local += h[lo + i];
+  // mass of the lanes above this one
+  u64 suf = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const u64 y = __shfl_down(suf, o);
+    if (lane + o < kWave) suf += y;
+  }
+  u64 run = suf - local;
+  int cand = -1, low = 0x7fffffff;
+  u64 cand_above = 0, low_above = 0;
+  for (int i = per - 1; i >= 0; --i) {
+    const u64 m = h[lo + i];
+    if (m > 0) {
+      if (cand < 0 && run + m >= need) {
+        cand = lo + i;
+        cand_above = run;
+      }
+      low = lo + i;
+      low_above = run;
+    }
+    run += m;
+  }
+  int d = wave_max_i(cand);
+  u64 a = cand_above;
+  if (d < 0) {
+    d = wave_min_i(low);
+    a = low_above;
+  }
+  // the owning lane's value to every lane
+  const uint64_t owner = ballot(lo <= d && d < lo + per);
+  above = __shfl(a, owner ? __builtin_ctzll(owner) : 0);
+  return d;
+}
+
+__device__ __forceinline__ u64 block_sum_u64(u64 v, u64* sh, int lane, int wave) {
+  v = wave_sum_u64(v);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  const u64 r = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive scan over the workgroup's threads in thread order; `total` gets
+// the sum of all.
+template <typename X>
+__device__ __forceinline__ X block_excl_scan(X v, X* sh, int lane, int wave, X& total) {
+  const X inc = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  X off = 0;
+  for (int w = 0; w < wave; ++w) off += sh[w];
+  total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return off + inc - v;
+}
+
+// One workgroup per node.  Thread tid holds tokens [SEG s + E tid, + E) of
+// segment s in registers (SEG = 256 E); a row of at most SEG tokens is
+// loaded once and every walk runs from registers, a longer one is reloaded
+// segment by segment on each walk.
+template <int E>
+__global__ __launch_bounds__(kNucThreads) void nucleus_sample_kernel(int V, const float* __restrict__ logits,
+                                                                   float temperature, float top_p,
+                                                                   const float* __restrict__ uniforms,
+                                                                   RowStat* __restrict__ stats,
+                                                                   int32_t* __restrict__ samples) {
+  constexpr int SEG = kNucThreads * E;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* x = logits + static_cast<size_t>(row) * V;
+  const int nseg = (V + SEG - 1) / SEG;
+  __shared__ u64 s_hist[kNucWaves][kNucBuckets];
+  __shared__ u64 s_u64[kNucWaves];
+  __shared__ int s_int[kNucWaves];
+  __shared__ float s_max[kNucWaves];
+  __shared__ int s_digit;
+  __shared__ u64 s_need;
+  __shared__ int s_sample;
+
+  float xr[E];
+  auto load = [&](int s) {
+    const int b = s * SEG + E * tid;
+#pragma unroll
+    for (int j = 0; j < E; ++j) xr[j] = x[min(b + j, V - 1)];
+  };
+  auto ok = [&](int s, int j) { return s * SEG + E * tid + j < V; };
+  if (nseg == 1) load(0);
+
+  // (0) row maximum
+  float mx = -__builtin_huge_valf();
+  for (int s = 0; s < nseg; ++s) {
+    if (nseg > 1) load(s);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (ok(s, j)) mx = fmaxf(mx, xr[j]);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) s_max[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float sc = (1.f / temperature) * 1.44269504088896341f;   // log2(e) / temperature
+  // mass of a token, 40 fraction bits: exp((x - max) / temperature)
+  auto mass = [&](float v) -> u64 { return static_cast<u64>(exp2f((v - mx) * sc) * 0x1p40f); };
+
+  // (1-3) radix select by mass: digits [31:21], [20:10], [9:0]
+  uint32_t prefix = 0;
+  u64 need = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    const int hi_shift = pass == 1 ? 21 : 10;   // bits above this digit (passes 1, 2)
+    for (int i = tid; i < kNucWaves * kNucBuckets; i += kNucThreads) (&s_hist[0][0])[i] = 0;
+    __syncthreads();
+    u64 S = 0;
+    for (int s = 0; s < nseg; ++s) {
+      if (nseg > 1) load(s);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const uint32_t k = nuc_key(xr[j]);
+        if (ok(s, j) && (pass == 0 || (k >> hi_shift) == (prefix >> hi_shift))) {
+          const u64 m = mass(xr[j]);
+          if (m) atomicAdd(&s_hist[wave][(k >> shift) & (nb - 1)], m);
+          S += m;
+        }
+      }
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += kNucThreads)
+      s_hist[0][b] = s_hist[0][b] + s_hist[1][b] + s_hist[2][b] + s_hist[3][b];
+    if (pass == 0) {
+      const u64 total = block_sum_u64(S, s_u64, lane, wave);
+      need = static_cast<u64>(ceil(static_cast<double>(top_p) * static_cast<double>(total)));
+    } else {
+      __syncthreads();
+    }
+    if (wave == 0) {
+      u64 above;
+      const int d = nuc_pick(s_hist[0], nb, need, lane, above);
+      if (lane == 0) {
+        s_digit = d;
+        s_need = need > above ? need - above : 0;
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(s_digit) << shift;
+    need = s_need;
+    __syncthreads();   // s_hist is cleared by the next pass
+  }
+  const uint32_t kappa = prefix;   // every key above it is in the nucleus
+  const u64 m_kappa = mass(nuc_value(kappa));
+
+  // (4) the nucleus: keys above kappa, and the first c kappa tokens (by id)
+  // with c the fewest whose mass covers what is still needed
+  u64 ma_all = 0;
+  int cnt_all = 0;
+  for (int s = 0; s < nseg; ++s) {
+    if (nseg > 1) load(s);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t k = nuc_key(xr[j]);
+      if (ok(s, j) && k > kappa) ma_all += mass(xr[j]);
+      if (ok(s, j) && k == kappa) ++cnt_all;
+    }
+  }
+  const u64 MA = block_sum_u64(ma_all, s_u64, lane, wave);
+  int count_kappa;
+  block_excl_scan(cnt_all, s_int, lane, wave, count_kappa);
+  long long cq = m_kappa > 0 ? static_cast<long long>((need + m_kappa - 1) / m_kappa) : count_kappa;
+  const int c = static_cast<int>(cq < 1 ? 1 : (cq > count_kappa ? count_kappa : cq));
+  const u64 Z = MA + static_cast<u64>(c) * m_kappa;
+  const float u = fminf(fmaxf(uniforms[row], 0.f), 1.f);
+  u64 target = static_cast<u64>(floor(static_cast<double>(u) * static_cast<double>(Z)));
+  if (target >= Z) target = Z - 1;   // u = 1: the nucleus's highest id
+
+  // (5) the draw: the nucleus token whose id-ordered mass interval holds
+  // target; the sums are exact, so exactly one thread's chunk holds it
+  if (tid == 0) s_sample = -1;
+  u64 carry = 0;
+  int kcarry = 0;
+  for (int s = 0; s < nseg; ++s) {
+    if (nseg > 1) load(s);
+    u64 ma = 0;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t k = nuc_key(xr[j]);
+      if (ok(s, j) && k > kappa) ma += mass(xr[j]);
+      if (ok(s, j) && k == kappa) ++cnt;
+    }
+    int cnt_seg;
+    const int ord = kcarry + block_excl_scan(cnt, s_int, lane, wave, cnt_seg);
+    const int take = min(max(c - ord, 0), cnt);
+    const u64 w = ma + static_cast<u64>(take) * m_kappa;
+    u64 w_seg;
+    const u64 run0 = carry + block_excl_scan(w, s_u64, lane, wave, w_seg);
+    if (w > 0 && run0 <= target && target < run0 + w) {
+      u64 run = run0;
+      int kord = ord, found = -1;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const uint32_t k = nuc_key(xr[j]);
+        bool inc = false;
+        if (ok(s, j) && k > kappa) inc = true;
+        if (ok(s, j) && k == kappa) {
+          inc = kord < c;
+          ++kord;
+        }
+        if (inc) {
+          run += mass(xr[j]);
+          if (found < 0 && run > target) found = s * SEG + E * tid + j;
+        }
+      }
+      s_sample = found;
+    }
+    carry += w_seg;
+    kcarry += cnt_seg;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int sample = s_sample >= 0 ? s_sample : 0;   // always found: the sums are exact
+    stats[row] = RowStat{0.f, sample, 0.f, 0.f, 0.f};
+    if (samples != nullptr) samples[row] = sample;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rows of at most 32768 tokens: the whole row's order keys stay in LDS
+// (padded by one word per 32 so that a thread's contiguous chunk is read
+// without bank conflicts) beside one shared mass histogram; 1024 threads.
+// The mass of the keys above kappa and the number of kappa tokens come out
+// of the three exact histograms, so after the load only the first radix
+// walk evaluates every exponential; the last walk evaluates those of the
+// nucleus.
+constexpr int kNlThreads = 1024;
+constexpr int kNlWaves = kNlThreads / kWave;
+constexpr int kNlMaxV = 32768;
+constexpr int kNlChunk = kNlMaxV / kNlThreads;   // tokens per thread in the id-ordered walk
+
+__device__ __forceinline__ int nl_pad(int i) { return i + (i >> 5); }
+
+template <typename X>
+__device__ __forceinline__ X nl_block_excl_scan(X v, X* sh, int lane, int wave, X& total) {
+  const X inc = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  X off = 0, all = 0;
+  for (int w = 0; w < kNlWaves; ++w) {
+    const X y = sh[w];
+    off += w < wave ? y : X(0);
+    all += y;
+  }
+  total = all;
+  __syncthreads();
+  return off + inc - v;
+}
+
+// nuc_pick over the whole workgroup: thread tid owns buckets [2 tid, 2 tid
+// + 2) of the 2048 (one 16-byte LDS read each, no bank conflicts); the
+// mass above them is the exact total minus a prefix scan.  Every thread
+// gets the digit; `above` is valid in every thread.
+__device__ __forceinline__ int nl_pick(const u64* h, int nb, u64 need, int tid, int lane, int wave, u64* sh_u64,
+                                       int* sh_int, u64& above) {
+  const int b0 = 2 * tid;
+  const bool live = b0 < nb;
+  const u64 h0 = live ? h[b0] : 0, h1 = live ? h[b0 + 1] : 0;
+  u64 total;
+  const u64 excl = nl_block_excl_scan(h0 + h1, sh_u64, lane, wave, total);
+  const u64 up1 = total - excl - h0 - h1;   // buckets above b0 + 1
+  const u64 up0 = up1 + h1;                 // buckets above b0
+  int cand = -1, low = 0x7fffffff;
+  if (h1 > 0 && up1 + h1 >= need) cand = b0 + 1;
+  else if (h0 > 0 && up0 + h0 >= need) cand = b0;
+  if (h0 > 0) low = b0;
+  else if (h1 > 0) low = b0 + 1;
+  cand = wave_max_i(cand);
+  low = wave_min_i(low);
+  if (lane == 0) {
+    sh_int[wave] = cand;
+    sh_int[kNlWaves + wave] = low;
+  }
+  __syncthreads();
+  int d = -1, lo = 0x7fffffff;
+  for (int w = 0; w < kNlWaves; ++w) {
+    d = max(d, sh_int[w]);
+    lo = min(lo, sh_int[kNlWaves + w]);
+  }
+  if (d < 0) d = lo;
+  // the owner publishes the mass above d
+  if (d == b0 + 1) sh_u64[0] = up1;
+  if (d == b0) sh_u64[0] = up0;
+  __syncthreads();
+  above = sh_u64[0];
+  __syncthreads();
+  return d;
+}
+
+__global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, const float* __restrict__ logits,
+                                                                      float temperature, float top_p,
+                                                                      const float* __restrict__ uniforms,
+                                                                      RowStat* __restrict__ stats,
+                                                                      int32_t* __restrict__ samples) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* x = logits + static_cast<size_t>(row) * V;
+  __shared__ uint32_t s_key[kNlMaxV + kNlMaxV / 32];
+  __shared__ u64 s_hist[kNucBuckets];
+  __shared__ u64 s_u64[kNlWaves];
+  __shared__ int s_int[2 * kNlWaves];
+  __shared__ float s_max[kNlWaves];
+  __shared__ int s_sample;
+
+  // load: order keys into LDS, and the row maximum
+  float mx = -__builtin_huge_valf();
+#pragma unroll 8
+  for (int v = tid; v < V; v += kNlThreads) {
+    const float xv = x[v];
+    mx = fmaxf(mx, xv);
+    s_key[nl_pad(v)] = nuc_key(xv);
+  }
+  for (int i = tid; i < kNucBuckets; i += kNlThreads) s_hist[i] = 0;
+  mx = wave_max(mx);
+  if (lane == 0) s_max[wave] = mx;
+  __syncthreads();
+  mx = s_max[0];
+  for (int w = 1; w < kNlWaves; ++w) mx = fmaxf(mx, s_max[w]);
+  const float sc = (1.f / temperature) * 1.44269504088896341f;   // log2(e) / temperature
+  auto mass = [&](uint32_t k) -> u64 { return static_cast<u64>(exp2f((nuc_value(k) - mx) * sc) * 0x1p40f); };
+
+  // radix select by mass: digits [31:21], [20:10], [9:0]; MA collects the
+  // mass of the buckets above each chosen digit (= the keys above kappa)
+  uint32_t prefix = 0;
+  u64 need = 0, MA = 0, h_kappa = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    const int hi_shift = pass == 1 ? 21 : 10;
+    u64 S = 0;
+#pragma unroll 8
+    for (int v = tid; v < V; v += kNlThreads) {
+      const uint32_t k = s_key[nl_pad(v)];
+      if (pass == 0 || (k >> hi_shift) == (prefix >> hi_shift)) {
+        const u64 m = mass(k);
+        if (m) atomicAdd(&s_hist[(k >> shift) & (nb - 1)], m);
+        S += m;
+      }
+    }
+    if (pass == 0) {
+      S = wave_sum_u64(S);
+      if (lane == 0) s_u64[wave] = S;
+    }
+    __syncthreads();
+    if (pass == 0) {
+      u64 total = 0;
+      for (int w = 0; w < kNlWaves; ++w) total += s_u64[w];
+      need = static_cast<u64>(ceil(static_cast<double>(top_p) * static_cast<double>(total)));
+      __syncthreads();   // s_u64 is reused by the pick
+    }
+    u64 above;
+    const int d = nl_pick(s_hist, nb, need, tid, lane, wave, s_u64, s_int, above);
+    prefix |= static_cast<uint32_t>(d) << shift;
+    need = need > above ? need - above : 0;
+    MA += above;
+    h_kappa = s_hist[d];
+    __syncthreads();
+    for (int i = tid; i < kNucBuckets; i += kNlThreads) s_hist[i] = 0;
+    __syncthreads();
+  }
+  const uint32_t kappa = prefix;
+  const u64 m_kappa = mass(kappa);
+  // the last histogram's bucket is exactly key kappa: count x m_kappa
+  const int count_kappa = m_kappa > 0 ? static_cast<int>(h_kappa / m_kappa) : 1;
+  long long cq = m_kappa > 0 ? static_cast<long long>((need + m_kappa - 1) / m_kappa) : count_kappa;
+  const int c = static_cast<int>(cq < 1 ? 1 : (cq > count_kappa ? count_kappa : cq));
+  const u64 Z = MA + static_cast<u64>(c) * m_kappa;
+  const float u = fminf(fmaxf(uniforms[row], 0.f), 1.f);
+  u64 target = static_cast<u64>(floor(static_cast<double>(u) * static_cast<double>(Z)));
+  if (target >= Z) target = Z - 1;   // u = 1: the nucleus's highest id
+
+  // the draw: thread tid owns tokens [kNlChunk tid, + kNlChunk) in id order
+  const int v0 = kNlChunk * tid;
+  u64 ma = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kNlChunk; ++j) {
+    const int v = v0 + j;
+    if (v < V) {
+      const uint32_t k = s_key[nl_pad(v)];
+      if (k > kappa) ma += mass(k);
+      cnt += k == kappa ? 1 : 0;
+    }
+  }
+  int cnt_all;
+  const int ord = nl_block_excl_scan(cnt, s_int, lane, wave, cnt_all);
+  const int take = min(max(c - ord, 0), cnt);
+  const u64 w = ma + static_cast<u64>(take) * m_kappa;
+  u64 w_all;
+  const u64 run0 = nl_block_excl_scan(w, s_u64, lane, wave, w_all);
+  if (tid == 0) s_sample = -1;
+  __syncthreads();
+  if (w > 0 && run0 <= target && target < run0 + w) {
+    u64 run = run0;
+    int kord = ord, found = -1;
+#pragma unroll
+    for (int j = 0; j < kNlChunk; ++j) {
+      const int v = v0 + j;
+      if (v < V && found < 0) {
+        const uint32_t k = s_key[nl_pad(v)];
+        bool inc = k > kappa;
+        if (k == kappa) {
+          inc = kord < c;
+          ++kord;
+        }
+        if (inc) {
+          run += mass(k);
+          if (run > target) found = v;
+        }
+      }
+    }
+    s_sample = found;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int sample = s_sample >= 0 ? s_sample : 0;   // always found: the sums are exact
+    stats[row] = RowStat{0.f, sample, 0.f, 0.f, 0.f};
+    if (samples != nullptr) samples[row] = sample;
+  }
+}
+
+}  // namespace medusa
+
+namespace {
+using namespace medusa;
+size_t nuc_ws(int B, int T) { return medusa_host::round_up(static_cast<size_t>(B) * T * sizeof(RowStat), 256); }
+}  // namespace
+
+extern "C" size_t medusa_posterior_nucleus_workspace(int B, int T) {
+  if (B < 1 || B > kMaxBatch || T < 1 || T > kMaxNodes) return 0;
+  return nuc_ws(B, T);
+}
+
+extern "C" int medusa_evaluate_posterior_nucleus(int B, int T, int V, int p_max, int D, const float* logits,
+                                                 const int32_t* tree_candidates, const int32_t* retrieve,
+                                                 const int32_t* num_paths, float temperature, float top_p,
+                                                 const float* uniforms, int32_t* best_path, int32_t* accept_len,
+                                                 int32_t* next_token, int32_t* samples, void* ws, size_t ws_bytes,
+                                                 void* stream) {
+  MEDUSA_REQUIRE(B >= 1 && B <= kMaxBatch, MEDUSA_ERR_SHAPE, "%s: B=%d", __func__, B);
+  MEDUSA_REQUIRE(T >= 1 && T <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: T=%d", __func__, T);
+  MEDUSA_REQUIRE(V >= 1 && V <= kNucMaxV, MEDUSA_ERR_SHAPE, "%s: V=%d (at most %d)", __func__, V, kNucMaxV);
+  MEDUSA_REQUIRE(p_max >= 1 && p_max <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: p_max=%d", __func__, p_max);
+  MEDUSA_REQUIRE(D >= 1 && D <= kMaxHeads + 1, MEDUSA_ERR_SHAPE, "%s: D=%d", __func__, D);
+  MEDUSA_REQUIRE(temperature == temperature && temperature > 0.f && temperature < __builtin_huge_valf(),
+                 MEDUSA_ERR_VALUE, "%s: temperature must be positive and finite", __func__);
+  MEDUSA_REQUIRE(top_p > 0.f && top_p <= 1.f, MEDUSA_ERR_VALUE, "%s: top_p must lie in (0, 1]", __func__);
+  MEDUSA_REQUIRE_PTR(logits);
+  MEDUSA_REQUIRE_PTR(tree_candidates);
+  MEDUSA_REQUIRE_PTR(retrieve);
+  MEDUSA_REQUIRE_PTR(num_paths);
+  MEDUSA_REQUIRE_PTR(uniforms);
+  MEDUSA_REQUIRE_PTR(best_path);
+  MEDUSA_REQUIRE_PTR(accept_len);
+  MEDUSA_REQUIRE_PTR(next_token);
+  MEDUSA_REQUIRE(samples == nullptr || medusa_host::aligned16(samples), MEDUSA_ERR_ALIGN,
+                 "%s: samples is not 16-byte aligned", __func__);
+  MEDUSA_REQUIRE_PTR(ws);
+  MEDUSA_REQUIRE(ws_bytes >= nuc_ws(B, T), MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
+                 ws_bytes, nuc_ws(B, T));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  RowStat* draws = static_cast<RowStat*>(ws);
+  const dim3 grid(B * T), block(kNucThreads);
+  if (V <= kNlMaxV)
+    hipLaunchKernelGGL(nucleus_sample_lds_kernel, grid, dim3(kNlThreads), 0, st, V, logits, temperature, top_p,
+                       uniforms, draws, samples);
+  else if (V <= kNucThreads * 16)
+    hipLaunchKernelGGL(nucleus_sample_kernel<16>, grid, block, 0, st, V, logits, temperature, top_p, uniforms, draws,
+                       samples);
+  else if (V <= kNucThreads * 32)
+    hipLaunchKernelGGL(nucleus_sample_kernel<32>, grid, block, 0, st, V, logits, temperature, top_p, uniforms, draws,
+                       samples);
+  else if (V <= kNucThreads * 64)
+    hipLaunchKernelGGL(nucleus_sample_kernel<64>, grid, block, 0, st, V, logits, temperature, top_p, uniforms, draws,
+                       samples);
+  else
+    hipLaunchKernelGGL(nucleus_sample_kernel<128>, grid, block, 0, st, V, logits, temperature, top_p, uniforms, draws,
+                       samples);
+  int rc = medusa_host::hip_check("medusa_evaluate_posterior_nucleus sample launch");
+  if (rc != MEDUSA_OK) return rc;
+  return medusa_host::decide_on_draws(B, T, V, p_max, D, draws, tree_candidates, retrieve, num_paths, best_path,
+                                      accept_len, next_token, st);
+}

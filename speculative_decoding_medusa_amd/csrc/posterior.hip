@@ -386,4 +386,16 @@ int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, cons
   return hip_check("posterior decide launch");
 }
 
+// Acceptance on one drawn token per node (RowStat.arg): the greedy
+// decision with the draw in place of the argmax (nucleus acceptance).
+int decide_on_draws(int B, int T, int V, int p_max, int D, const medusa::RowStat* draws,
+                    const int32_t* tree_candidates, const int32_t* retrieve, const int32_t* num_paths,
+                    int32_t* best_path, int32_t* accept_len, int32_t* next_token, hipStream_t st) {
+  using namespace medusa;
+  hipLaunchKernelGGL(posterior_decide_kernel, dim3(B), dim3(kPostThreads), 0, st, T, V, 1, p_max, D,
+                     static_cast<const float*>(nullptr), tree_candidates, retrieve, num_paths, 0.f, 0.f, 0.f, draws,
+                     best_path, accept_len, next_token, static_cast<const float*>(nullptr));
+  return hip_check("posterior decide launch");
+}
+
 }  // namespace medusa_host

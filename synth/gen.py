@@ -230,3 +230,12 @@ def base_posterior_inputs(w, tree_candidates, retrieve, num_paths, seed=0, scale
             h[b, node] += np.float32(scale) * wb[tok]
         plan.append((p, A))
     return dict(hidden=bf16_bits(h).reshape(B, T, H), w_base=bf16_bits(wb).reshape(V, H), plan=plan)
+
+
+def node_uniforms(w, T, seed=0):
+    """float32 [B][T] uniform variates in [0, 1): the random numbers a
+    sampling acceptance mode draws with, one per tree node."""
+    out = np.empty((w["B"], T), dtype=np.float32)
+    for b in range(w["B"]):
+        out[b] = stream(seed, w["wid"], "uniforms", b).random(T, dtype=np.float32)
+    return out

@@ -17,6 +17,7 @@ _TENSOR_IDS = {
     "h": 1, "w1": 2, "b1": 3, "wlm": 4, "tree": 5, "topk_ids": 6, "root": 7,
     "q": 8, "k": 9, "v": 10, "logits": 11, "plant": 12, "cache_k": 13,
     "cache_v": 14, "prefix": 15, "misc": 16, "h_tree": 17, "w_base": 18,
+    "uniforms": 19,
 }
 
 _BLOCK = 1 << 20  # elements per independently seeded block

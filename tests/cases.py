@@ -147,3 +147,50 @@ def posterior_case(w, tcase, temperature, seed=0, max_retries=50):
                                         temperature, w["eps"], w["delta"])
         return dict(logits=logits, plan=plan, ref=exp, retry=retry)
     raise RuntimeError("no margin after %d redraws" % max_retries)
+
+
+# ------------------------------------------------------------------ nucleus
+def nucleus_margins(logits_row, temperature, top_p, u):
+    """How far one node's nucleus decisions sit from a float tie: the
+    probability gaps between top_p and the masses just before and at the
+    nucleus boundary, and between u * Z and the running masses around the
+    drawn token (as fractions of Z).  Returns the smallest."""
+    t, q = float(np.float32(temperature)), float(np.float32(top_p))
+    z = np.asarray(logits_row, dtype=np.float64) / t
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    V = p.shape[0]
+    order = np.lexsort((np.arange(V), -p))
+    mass = np.cumsum(p[order])
+    k = min(int(np.searchsorted(mass, q, side="left")), V - 1)
+    gaps = [mass[k] - q] if k < V - 1 else [1.0]
+    if k > 0:
+        gaps.append(q - mass[k - 1])
+    ids = np.sort(order[:k + 1])
+    w = p[ids] / p[ids].sum()
+    run = np.cumsum(w)
+    target = min(max(float(np.float32(u)), 0.0), 1.0)
+    i = int(np.searchsorted(run, target, side="right"))
+    if i < len(ids):
+        gaps.append(run[i] - target)
+        gaps.append(target - (run[i - 1] if i > 0 else 0.0))
+    return min(gaps)
+
+
+def nucleus_case(w, tcase, temperature, top_p, seed=0, tol=1e-5, max_retries=60, plant=None):
+    """Planted logits (as for the posterior) and uniforms, redrawn until
+    every node's nucleus decisions clear `tol`; with the oracle's verdict."""
+    ref = tcase["ref"]
+    T = int(np.asarray(ref["tree_candidates"]).shape[1])
+    for retry in range(max_retries):
+        logits, plan = synth.posterior_logits(w, ref["tree_candidates"], ref["retrieve"], ref["num_paths"],
+                                              ref["depth"], seed=seed + 1000 * retry, plant=plant)
+        u = synth.node_uniforms(w, T, seed=seed + 1000 * retry)
+        ok = all(nucleus_margins(logits[b, n], temperature, top_p, u[b, n]) >= tol
+                 for b in range(logits.shape[0]) for n in range(T))
+        if not ok:
+            continue
+        exp = oracle.evaluate_posterior_nucleus(logits, ref["tree_candidates"], ref["retrieve"], ref["num_paths"],
+                                                temperature, top_p, u)
+        return dict(logits=logits, uniforms=u, plan=plan, ref=exp, retry=retry)
+    raise RuntimeError("no margin after %d redraws" % max_retries)

@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 101
+    assert L.medusa_abi_version() == 102
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -189,6 +189,31 @@ def test_base_posterior_workspace_sizes():
     assert L.medusa_base_posterior_workspace(1, 64, 4096, 131073) == 0
     assert L.medusa_base_posterior_workspace(0, 64, 4096, 32000) == 0
     assert L.medusa_base_posterior_workspace(1, 64, 12, 32000) == 0
+
+
+def nuc(B=1, T=64, V=32000, p_max=64, D=6, logits=A, cand=A, ret=A, npaths=A, temp=0.7, top_p=0.8, u=A, best=A,
+        acc=A, nxt=A, samples=None, ws=A, wsb=1 << 20):
+    return L.medusa_evaluate_posterior_nucleus(B, T, V, p_max, D, logits, cand, ret, npaths, temp, top_p, u, best,
+                                               acc, nxt, samples, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(B=17), SHAPE), (dict(T=257), SHAPE), (dict(V=0), SHAPE), (dict(V=262145), SHAPE),
+    (dict(D=10), SHAPE), (dict(p_max=0), SHAPE), (dict(temp=0.0), VALUE), (dict(temp=float("inf")), VALUE),
+    (dict(temp=float("nan")), VALUE), (dict(top_p=0.0), VALUE), (dict(top_p=1.01), VALUE),
+    (dict(top_p=float("nan")), VALUE), (dict(logits=None), NULL), (dict(u=None), NULL), (dict(ws=None), NULL),
+    (dict(u=MIS), ALIGN), (dict(samples=MIS), ALIGN), (dict(wsb=16), WS),
+])
+def test_nucleus_validation(kw, code):
+    assert nuc(**kw) == code
+    assert L.medusa_last_error().decode() != ""
+
+
+def test_nucleus_workspace_sizes():
+    assert L.medusa_posterior_nucleus_workspace(1, 64) == 1280
+    assert L.medusa_posterior_nucleus_workspace(16, 256) == 16 * 256 * 20
+    assert L.medusa_posterior_nucleus_workspace(0, 64) == 0
+    assert L.medusa_posterior_nucleus_workspace(1, 257) == 0
 
 
 def test_binding_rejects_cpu_tensors():
