@@ -12,6 +12,8 @@ computes, written from the pages' descriptions of Medusa:
   commit.py     gathering the accepted path's K/V into contiguous slots
   base_head.py  the base model's lm_head over the tree nodes, and the
                 acceptance test on its logits
+  decoder.py    a tiny LLaMA-style base model (whole-sequence forward) and
+                its plain greedy decoding
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package.  It shares no code with the GPU library and imports neither it
@@ -36,10 +38,11 @@ from .posterior import node_statistics, evaluate_posterior
 from .commit import commit_kv
 from .base_head import base_logits, base_posterior
 from .nucleus import nucleus, nucleus_sample, evaluate_posterior_nucleus
+from . import decoder
 
 __all__ = [
     "as_f64", "resblock", "lm_head_logits", "topk_by_value", "heads",
     "SpecError", "parse_choices", "build_tree", "tree_attention",
     "node_statistics", "evaluate_posterior", "commit_kv", "base_logits", "base_posterior",
-    "nucleus", "nucleus_sample", "evaluate_posterior_nucleus",
+    "nucleus", "nucleus_sample", "evaluate_posterior_nucleus", "decoder",
 ]

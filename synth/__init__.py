@@ -21,7 +21,8 @@ from .trees import (full_tree_choices, random_tree_choices, worked_example_choic
                     chain_choices, choices_array, geometric_acceptance, path_probability,
                     best_tree_choices, expected_accept_length)
 from .gen import (base_head_inputs, base_posterior_inputs, heads_inputs, topk_ids_input, root_token_input, attention_inputs,
-                  posterior_logits, kv_cache, rope_rotate, prefix_lengths, node_uniforms)
+                  posterior_logits, kv_cache, rope_rotate, prefix_lengths, node_uniforms, tiny_decoder,
+                  tiny_heads)
 
 __all__ = [
     "stream", "normal_f32", "bf16_bits", "bf16_to_f32", "f32_round",
@@ -30,5 +31,6 @@ __all__ = [
     "choices_array", "geometric_acceptance", "path_probability", "best_tree_choices",
     "expected_accept_length",
     "base_head_inputs", "base_posterior_inputs", "heads_inputs", "topk_ids_input", "root_token_input", "attention_inputs",
-    "posterior_logits", "kv_cache", "rope_rotate", "prefix_lengths", "node_uniforms",
+    "posterior_logits", "kv_cache", "rope_rotate", "prefix_lengths", "node_uniforms", "tiny_decoder",
+    "tiny_heads",
 ]

@@ -239,3 +239,41 @@ def node_uniforms(w, T, seed=0):
     for b in range(w["B"]):
         out[b] = stream(seed, w["wid"], "uniforms", b).random(T, dtype=np.float32)
     return out
+
+
+def tiny_decoder(cfg, seed=0, workload_id=20):
+    """Random weights of a tiny LLaMA-style base model (bf16 bits), out x in:
+    embed [V][H] ~ N(0, 1); per layer wq, wk, wv [H][H] and w_gate, w_up
+    [I][H] ~ N(0, 1/H), wo [H][H] ~ N(0, 0.25/H), w_down [H][I] ~ N(0,
+    0.25/I); norm gains ~ 1 + N(0, 0.1^2); lm_head [V][H] ~ N(0, 4/H) (logits
+    of standard deviation about 2).  cfg: H, heads, I, layers, V, eps, theta.
+    """
+    H, I, V = cfg["H"], cfg["I"], cfg["V"]
+
+    def w(name, layer, shape, std, mean=0.0):
+        n = int(np.prod(shape))
+        return bf16_bits(normal_f32(seed, workload_id, "misc", (name, layer), n, std=std, mean=mean)).reshape(shape)
+
+    names = {"embed": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5, "w_gate": 6, "w_up": 7, "w_down": 8,
+             "attn_norm": 9, "mlp_norm": 10, "final_norm": 11, "lm_head": 12}
+    layers = []
+    for l in range(cfg["layers"]):
+        layers.append(dict(
+            attn_norm=w(names["attn_norm"], l, (H,), 0.1, 1.0),
+            wq=w(names["wq"], l, (H, H), H ** -0.5), wk=w(names["wk"], l, (H, H), H ** -0.5),
+            wv=w(names["wv"], l, (H, H), H ** -0.5), wo=w(names["wo"], l, (H, H), 0.5 * H ** -0.5),
+            mlp_norm=w(names["mlp_norm"], l, (H,), 0.1, 1.0),
+            w_gate=w(names["w_gate"], l, (I, H), H ** -0.5), w_up=w(names["w_up"], l, (I, H), H ** -0.5),
+            w_down=w(names["w_down"], l, (H, I), 0.5 * I ** -0.5)))
+    return dict(cfg=dict(cfg), embed=w(names["embed"], 0, (V, H), 1.0), layers=layers,
+                final_norm=w(names["final_norm"], 0, (H,), 0.1, 1.0),
+                lm_head=w(names["lm_head"], 0, (V, H), 2.0 * H ** -0.5))
+
+
+def tiny_heads(cfg, K, seed=0, workload_id=21):
+    """Random Medusa heads for the tiny model (bf16 bits): w1 [K][H][H],
+    b1 [K][H] ~ N(0, 0.02^2); w_lm [K][V][H] ~ N(0, 4/H)."""
+    H, V = cfg["H"], cfg["V"]
+    return dict(w1=bf16_bits(normal_f32(seed, workload_id, "w1", (), K * H * H, std=0.02)).reshape(K, H, H),
+                b1=bf16_bits(normal_f32(seed, workload_id, "b1", (), K * H, std=0.02)).reshape(K, H),
+                w_lm=bf16_bits(normal_f32(seed, workload_id, "wlm", (), K * V * H, std=2.0 * H ** -0.5)).reshape(K, V, H))
