@@ -10,6 +10,7 @@ Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --tree-sweep [--steps K]     # step cost vs heads K and tree size T
+    python bench.py --generate                   # end-to-end greedy generation, plain vs Medusa
 
 Prints one JSON line.  `roofline` covers the dominant kernel (lm_head +
 top-k): algorithmic bytes per launch over its mean duration, measured with
@@ -44,6 +45,9 @@ def parse():
                     help="skip the base lm_head timing (the step before the acceptance test)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)")
+    ap.add_argument("--generate", action="store_true",
+                    help="run only end-to-end generation on a small LLaMA-style model: plain greedy against "
+                         "Medusa greedy (one JSON line)")
     ap.add_argument("--tree-sweep", action="store_true",
                     help="run only the tree-shape sweep: step cost and expected tokens per step against the "
                          "number of heads K and tree nodes T (one JSON line)")
@@ -538,6 +542,92 @@ def tree_sweep(args):
                       "steps": args.steps, "timing": "HIP graph replays, events on the capture stream"}))
 
 
+GEN_CFG = dict(H=1024, heads=16, I=2816, layers=4, V=32000, eps=1e-6, theta=10000.0)
+
+
+def _fit_heads(hidden_rows, seq, first, K, V, scale=8.0):
+    """Heads fitted to a known continuation: ResBlocks zero (r = h) and head
+    j's lm_head the minimum-norm linear map from the final hidden state at
+    position first + r to `scale` on token seq[first + r + j + 2] (rows past
+    the sequence end get no target).  Host setup for the benchmark only."""
+    import numpy as np
+    n, H = hidden_rows.shape
+    G = hidden_rows @ hidden_rows.T + 1e-6 * np.eye(n)
+    w = np.zeros((K, V, H))
+    for j in range(K):
+        Y = np.zeros((n, V))
+        for r in range(n):
+            t = first + r + j + 2
+            if t < len(seq):
+                Y[r, seq[t]] = scale
+        w[j] = np.linalg.solve(G, Y).T @ hidden_rows
+    return w
+
+
+def generate_bench(args):
+    """End-to-end greedy generation on a small LLaMA-style model (GEN_CFG,
+    random weights) through the library's forward pieces: plain greedy (one
+    base-model forward per token) against Medusa greedy (heads, tree, one
+    forward of the tree, acceptance, commit per step) with K = 3 heads and a
+    full binary tree of depth 3 (15 nodes).  Heads: random, and fitted on
+    the host to the plain run's own continuation (an upper bound on what
+    trained heads accept).  Every run's tokens are checked against the plain
+    run's.  Wall-clock time of whole generate calls (median of 3)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from speculative_decoding_medusa_amd.decoder import TinyDecoder
+
+    dev = torch.device("cuda:0")
+    cfg = GEN_CFG
+    P, n, K, topk = 32, 128, 3, 2
+    model = synth.tiny_decoder(cfg, seed=args.seed)
+    prompt = [int(t) for t in np.random.default_rng(args.seed).integers(cfg["V"], size=P)]
+    dec = TinyDecoder(model, dev, max_slots=P + n + 64)
+    choices = torch.from_numpy(synth.choices_array(synth.full_tree_choices(K, topk), K)).to(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            out = fn()
+            torch.cuda.synchronize()
+            runs.append(time.perf_counter() - t0)
+        return out, sorted(runs)[1]
+
+    ref, t_plain = timed(lambda: dec.greedy(prompt, n))
+    # hidden states along the plain continuation, for the fitted heads
+    hidden, _ = dec.prefill(prompt + ref[:-1])
+    rows = hidden[0, P - 1:P - 1 + n].float().cpu().numpy().astype(np.float64)
+    fitted = _fit_heads(rows, prompt + ref, P - 1, K, cfg["V"])
+
+    def to_bf16(a):
+        return torch.from_numpy(synth.bf16_bits(np.asarray(a, dtype=np.float32)).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    H, V = cfg["H"], cfg["V"]
+    rnd = synth.tiny_heads(cfg, K, seed=args.seed + 1)
+    head_sets = {
+        "random_heads": {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(dev).view(torch.bfloat16)
+                         for k, v in rnd.items()},
+        "fitted_heads": dict(w1=torch.zeros((K, H, H), dtype=torch.bfloat16, device=dev),
+                             b1=torch.zeros((K, H), dtype=torch.bfloat16, device=dev),
+                             w_lm=to_bf16(fitted.reshape(K, V, H))),
+    }
+    res = {"plain": {"tokens_per_s": round(n / t_plain, 1), "ms": round(t_plain * 1e3, 2), "forwards": n}}
+    for name, heads in head_sets.items():
+        (toks, accepts, _), t = timed(lambda: dec.medusa(heads, choices, topk, prompt, n))
+        res["medusa_" + name] = {"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2), "steps": len(accepts),
+                                 "tokens_per_step": round(n / len(accepts), 3),
+                                 "speedup_vs_plain": round(t_plain / t, 3), "equal_to_plain": toks == ref}
+    print(json.dumps({"generate": res, "model": dict(cfg), "prompt_len": P, "new_tokens": n, "K": K,
+                      "tree": "full binary, depth 3 (15 nodes)", "timing": "wall clock of whole generate calls, "
+                      "median of 3, after one warm-up call", "data": "synthetic random weights"}))
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -549,6 +639,9 @@ def main():
         sys.exit(2)
     if args.tree_sweep:
         tree_sweep(args)
+        return
+    if args.generate:
+        generate_bench(args)
         return
 
     import torch

@@ -329,6 +329,44 @@ int medusa_base_posterior(int B, int T, int H, int V, int p_max, int D,
                           int32_t* best_path, int32_t* accept_len, int32_t* next_token,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * Base model forward pieces.  [API] tree_decoding runs the base model over
+ * the tree tokens with the prefix's KV cache; [NOTES] 学到什么 (greedy
+ * Medusa decoding keeps exactly what the base model would produce).  The
+ * pages do not spell the base model out; these calls follow a LLaMA layer
+ * (pre-norm RMSNorm, rotate-half RoPE, SwiGLU MLP), and its linear layers
+ * are medusa_base_lm_head (float32 out = bf16 in . W^T).  Per layer:
+ *   medusa_add_rmsnorm (x += previous block output; n = rmsnorm(x))
+ *   medusa_base_lm_head (n . Wqkv^T) -> medusa_rope_qkv -> medusa_tree_attention
+ *   medusa_base_lm_head (attn . Wo^T) -> medusa_add_rmsnorm
+ *   medusa_base_lm_head (n . [Wgate; Wup]^T) -> medusa_silu_mul
+ *   medusa_base_lm_head (. Wdown^T)
+ *
+ * medusa_embed: x [M][H] float32 = embed [V][H] bf16 rows of tokens [M]
+ *   (int32); a token outside [0, V) gives a zero row.  H % 8 == 0.
+ * medusa_add_rmsnorm: for each of M rows, x += y (y may be NULL: no add),
+ *   then out = bf16(x / sqrt(mean(x^2) + eps) * gain); x, y float32 [M][H],
+ *   gain bf16 [H], out bf16 [M][H].  x is updated in place.
+ * medusa_rope_qkv: qkv float32 [B][T][3][heads][d] (q, k, v as one GEMM
+ *   output row); positions int32 [B][T]; dims i and i + d/2 of every head of
+ *   q and k are rotated by positions[b][t] * theta^(-2i/d) (x1 cos - x2 sin,
+ *   x2 cos + x1 sin).  q -> bf16 [B][T][heads][d]; k and v -> bf16 cache
+ *   slots prefix_len[b] + t of k_cache, v_cache [B][heads][max_slots][d]
+ *   (slots outside [0, max_slots) are not written).  d even.
+ * medusa_silu_mul: gate_up float32 [M][2I] (gate in columns [0, I), up in
+ *   [I, 2I)) -> out bf16 [M][I] = silu(gate) * up.  I % 8 == 0.
+ * ------------------------------------------------------------------- */
+int medusa_embed(int M, int H, int V, const int32_t* tokens, const void* embed, float* x, void* stream);
+
+int medusa_add_rmsnorm(int M, int H, float* x, const float* y, const void* gain, float eps, void* out,
+                       void* stream);
+
+int medusa_rope_qkv(int B, int T, int heads, int d, int max_slots, const float* qkv,
+                    const int32_t* positions, const int32_t* prefix_len, float theta, void* q,
+                    void* k_cache, void* v_cache, void* stream);
+
+int medusa_silu_mul(int M, int I, const float* gate_up, void* out, void* stream);
+
 /* Text for a medusa_status value. */
 const char* medusa_status_string(int status);
 /* Detail of the last failing call on this thread ("" if none). */

@@ -15,7 +15,8 @@ from ._lib import (  # noqa: F401
     medusa_tree_attention_workspace, medusa_tree_attention, medusa_posterior_workspace,
     medusa_evaluate_posterior, medusa_posterior_nucleus_workspace, medusa_evaluate_posterior_nucleus,
     medusa_commit_kv, medusa_base_lm_head, medusa_base_lm_head_pack,
-    medusa_base_posterior_workspace, medusa_base_posterior,
+    medusa_base_posterior_workspace, medusa_base_posterior, medusa_embed, medusa_add_rmsnorm, medusa_rope_qkv,
+    medusa_silu_mul,
 )
 
 __all__ = [
@@ -25,4 +26,5 @@ __all__ = [
     "medusa_posterior_workspace", "medusa_evaluate_posterior", "medusa_posterior_nucleus_workspace",
     "medusa_evaluate_posterior_nucleus", "medusa_commit_kv", "medusa_base_lm_head",
     "medusa_base_lm_head_pack", "medusa_base_posterior_workspace", "medusa_base_posterior",
+    "medusa_embed", "medusa_add_rmsnorm", "medusa_rope_qkv", "medusa_silu_mul",
 ]

@@ -62,6 +62,10 @@ _SIGS = {
     "medusa_posterior_nucleus_workspace": (_sz, [_i, _i]),
     "medusa_evaluate_posterior_nucleus": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp,
                                                _vp, _vp, _sz, _vp]),
+    "medusa_embed": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp]),
+    "medusa_add_rmsnorm": (_i, [_i, _i, _vp, _vp, _vp, _f, _vp, _vp]),
+    "medusa_rope_qkv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp]),
+    "medusa_silu_mul": (_i, [_i, _i, _vp, _vp, _vp]),
     "medusa_status_string": (ctypes.c_char_p, [_i]),
     "medusa_last_error": (ctypes.c_char_p, []),
     "medusa_abi_version": (_i, []),
@@ -431,3 +435,58 @@ def medusa_base_posterior(hidden, w_base, tree_candidates, retrieve, num_paths, 
                                    ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_base_posterior")
     return dict(best_path=best, accept_len=acc, next_token=nxt)
+
+
+def medusa_embed(tokens, embed, x=None):
+    """tokens int32 [M] (or [B][T]) -> x float32 [M][H] (or [B][T][H])."""
+    V, H = embed.shape
+    M = tokens.numel()
+    if x is None:
+        x = torch.empty(tuple(tokens.shape) + (H,), dtype=torch.float32, device=tokens.device)
+    rc = lib.medusa_embed(M, H, V, _ptr(tokens, "tokens", torch.int32), _ptr(embed, "embed", torch.bfloat16),
+                          _ptr(x, "x", torch.float32), _stream(tokens.device))
+    _check(rc, "medusa_embed")
+    return x
+
+
+def medusa_add_rmsnorm(x, gain, eps, y=None, out=None):
+    """x float32 [..][H] (updated in place: x += y), out = bf16 rmsnorm(x) * gain."""
+    H = x.shape[-1]
+    M = x.numel() // H
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    rc = lib.medusa_add_rmsnorm(M, H, _ptr(x, "x", torch.float32), _ptr(y, "y", torch.float32, tuple(x.shape)),
+                                _ptr(gain, "gain", torch.bfloat16, (H,)), float(eps),
+                                _ptr(out, "out", torch.bfloat16, tuple(x.shape)), _stream(x.device))
+    _check(rc, "medusa_add_rmsnorm")
+    return out
+
+
+def medusa_rope_qkv(qkv, positions, prefix_len, theta, k_cache, v_cache, q=None):
+    """qkv float32 [B][T][3][heads][d]; k_cache, v_cache bf16 [B][heads][S][d]
+    (one layer): returns q bf16 [B][T][heads][d]; k, v written to slots
+    prefix_len[b] + t."""
+    B, T, three, heads, d = qkv.shape
+    S = k_cache.shape[2]
+    if q is None:
+        q = torch.empty((B, T, heads, d), dtype=torch.bfloat16, device=qkv.device)
+    rc = lib.medusa_rope_qkv(B, T, heads, d, S, _ptr(qkv, "qkv", torch.float32),
+                             _ptr(positions, "positions", torch.int32, (B, T)),
+                             _ptr(prefix_len, "prefix_len", torch.int32, (B,)), float(theta),
+                             _ptr(q, "q", torch.bfloat16, (B, T, heads, d)),
+                             _ptr(k_cache, "k_cache", torch.bfloat16, (B, heads, S, d)),
+                             _ptr(v_cache, "v_cache", torch.bfloat16, (B, heads, S, d)), _stream(qkv.device))
+    _check(rc, "medusa_rope_qkv")
+    return q
+
+
+def medusa_silu_mul(gate_up, out=None):
+    """gate_up float32 [..][2I] -> bf16 [..][I] = silu(gate) * up."""
+    I2 = gate_up.shape[-1]
+    M = gate_up.numel() // I2
+    if out is None:
+        out = torch.empty(tuple(gate_up.shape[:-1]) + (I2 // 2,), dtype=torch.bfloat16, device=gate_up.device)
+    rc = lib.medusa_silu_mul(M, I2 // 2, _ptr(gate_up, "gate_up", torch.float32), _ptr(out, "out", torch.bfloat16),
+                             _stream(gate_up.device))
+    _check(rc, "medusa_silu_mul")
+    return out

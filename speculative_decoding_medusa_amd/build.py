@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmedusa.so")
 
-SOURCES = ["abi.cpp", "heads.hip", "tree.hip", "attention.hip", "posterior.hip", "commit.hip", "base_head.hip", "nucleus.hip"]
+SOURCES = ["abi.cpp", "heads.hip", "tree.hip", "attention.hip", "posterior.hip", "commit.hip", "base_head.hip", "nucleus.hip", "decoder.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

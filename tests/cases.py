@@ -194,3 +194,37 @@ def nucleus_case(w, tcase, temperature, top_p, seed=0, tol=1e-5, max_retries=60,
                                                 temperature, top_p, u)
         return dict(logits=logits, uniforms=u, plan=plan, ref=exp, retry=retry)
     raise RuntimeError("no margin after %d redraws" % max_retries)
+
+
+# ------------------------------------------------------------------ decoder
+def fitted_heads(model, prompt, n, K, scale=8.0, decoy=0.3, seed=0):
+    """Medusa heads fitted in closed form to the oracle's own greedy
+    continuation of `prompt`: ResBlocks zero (r = h), and head j's lm_head
+    the minimum-norm linear map taking the final hidden state at each
+    position t (t = P-1 .. P+n-2) to `scale` on the token at t + j + 2; at a
+    `decoy` fraction of positions another token gets 1.3 x scale, so the
+    right token is that head's second choice.  Returns bf16 bit arrays
+    (w1, b1, w_lm) and the oracle's continuation."""
+    cfg = model["cfg"]
+    H, V = cfg["H"], cfg["V"]
+    cont, _ = oracle.decoder.greedy_decode(model, prompt, n + K + 1)
+    seq = list(prompt) + cont
+    _, hid = oracle.decoder.forward(model, seq)
+    P = len(prompt)
+    rows = list(range(P - 1, P - 1 + n))
+    Hm = hid[rows]
+    G = Hm @ Hm.T + 1e-6 * np.eye(len(rows))
+    rng = np.random.default_rng(seed)
+    w_lm = np.zeros((K, V, H))
+    for j in range(K):
+        Y = np.zeros((len(rows), V))
+        for r, t in enumerate(rows):
+            Y[r, seq[t + j + 2]] = scale
+            if rng.random() < decoy:
+                other = int(rng.integers(V - 1))
+                other += other >= seq[t + j + 2]
+                Y[r, other] = 1.3 * scale
+        w_lm[j] = np.linalg.solve(G, Y).T @ Hm
+    heads = dict(w1=np.zeros((K, H, H), dtype=np.uint16), b1=np.zeros((K, H), dtype=np.uint16),
+                 w_lm=synth.bf16_bits(w_lm.astype(np.float32)).reshape(K, V, H))
+    return heads, cont[:n]

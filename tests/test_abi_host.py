@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 102
+    assert L.medusa_abi_version() == 103
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -214,6 +214,28 @@ def test_nucleus_workspace_sizes():
     assert L.medusa_posterior_nucleus_workspace(16, 256) == 16 * 256 * 20
     assert L.medusa_posterior_nucleus_workspace(0, 64) == 0
     assert L.medusa_posterior_nucleus_workspace(1, 257) == 0
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: L.medusa_embed(0, 64, 10, A, A, A, None), SHAPE),
+    (lambda: L.medusa_embed(4, 60, 10, A, A, A, None), SHAPE),
+    (lambda: L.medusa_embed(4, 64, 10, None, A, A, None), NULL),
+    (lambda: L.medusa_embed(4, 64, 10, A, A, MIS, None), ALIGN),
+    (lambda: L.medusa_add_rmsnorm(0, 64, A, None, A, 1e-6, A, None), SHAPE),
+    (lambda: L.medusa_add_rmsnorm(4, 12, A, None, A, 1e-6, A, None), SHAPE),
+    (lambda: L.medusa_add_rmsnorm(4, 64, A, None, A, -1.0, A, None), VALUE),
+    (lambda: L.medusa_add_rmsnorm(4, 64, A, MIS, A, 1e-6, A, None), ALIGN),
+    (lambda: L.medusa_add_rmsnorm(4, 64, A, None, None, 1e-6, A, None), NULL),
+    (lambda: L.medusa_rope_qkv(0, 4, 2, 64, 100, A, A, A, 1e4, A, A, A, None), SHAPE),
+    (lambda: L.medusa_rope_qkv(1, 4, 2, 63, 100, A, A, A, 1e4, A, A, A, None), SHAPE),
+    (lambda: L.medusa_rope_qkv(1, 4, 2, 64, 100, A, A, A, 0.0, A, A, A, None), VALUE),
+    (lambda: L.medusa_rope_qkv(1, 4, 2, 64, 100, A, A, None, 1e4, A, A, A, None), NULL),
+    (lambda: L.medusa_silu_mul(4, 12, A, A, None), SHAPE),
+    (lambda: L.medusa_silu_mul(4, 64, A, None, None), NULL),
+])
+def test_decoder_piece_validation(call, code):
+    assert call() == code
+    assert L.medusa_last_error().decode() != ""
 
 
 def test_binding_rejects_cpu_tensors():
