@@ -572,7 +572,10 @@ def generate_bench(args):
     full binary tree of depth 3 (15 nodes).  Heads: random, and fitted on
     the host to the plain run's own continuation (an upper bound on what
     trained heads accept).  Every run's tokens are checked against the plain
-    run's.  Wall-clock time of whole generate calls (median of 3)."""
+    run's.  Each loop also runs with its step captured in a HIP graph and
+    replayed (bookkeeping on the device; a Medusa run may overshoot by a few
+    steps between the host's checks).  Wall-clock time of whole generate
+    calls (median of 3), prefill and graph capture included."""
     import numpy as np
     import torch
 
@@ -599,6 +602,7 @@ def generate_bench(args):
         return out, sorted(runs)[1]
 
     ref, t_plain = timed(lambda: dec.greedy(prompt, n))
+    ref_g, t_plain_g = timed(lambda: dec.greedy_graph(prompt, n))
     # hidden states along the plain continuation, for the fitted heads
     hidden, _ = dec.prefill(prompt + ref[:-1])
     rows = hidden[0, P - 1:P - 1 + n].float().cpu().numpy().astype(np.float64)
@@ -617,12 +621,18 @@ def generate_bench(args):
                              b1=torch.zeros((K, H), dtype=torch.bfloat16, device=dev),
                              w_lm=to_bf16(fitted.reshape(K, V, H))),
     }
-    res = {"plain": {"tokens_per_s": round(n / t_plain, 1), "ms": round(t_plain * 1e3, 2), "forwards": n}}
+    res = {"plain": {"tokens_per_s": round(n / t_plain, 1), "ms": round(t_plain * 1e3, 2), "forwards": n},
+           "plain_graph": {"tokens_per_s": round(n / t_plain_g, 1), "ms": round(t_plain_g * 1e3, 2),
+                           "equal_to_plain": ref_g == ref}}
     for name, heads in head_sets.items():
         (toks, accepts, _), t = timed(lambda: dec.medusa(heads, choices, topk, prompt, n))
         res["medusa_" + name] = {"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2), "steps": len(accepts),
                                  "tokens_per_step": round(n / len(accepts), 3),
                                  "speedup_vs_plain": round(t_plain / t, 3), "equal_to_plain": toks == ref}
+        (toks, steps), t = timed(lambda: dec.medusa_graph(heads, choices, topk, prompt, n))
+        res["medusa_" + name + "_graph"] = {"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2),
+                                            "steps_run": steps, "speedup_vs_plain_graph": round(t_plain_g / t, 3),
+                                            "equal_to_plain": toks == ref}
     print(json.dumps({"generate": res, "model": dict(cfg), "prompt_len": P, "new_tokens": n, "K": K,
                       "tree": "full binary, depth 3 (15 nodes)", "timing": "wall clock of whole generate calls, "
                       "median of 3, after one warm-up call", "data": "synthetic random weights"}))

@@ -63,6 +63,16 @@ class TinyDecoder:
         shape = (len(self.layers), 1, self.heads, self.S, self.d)
         self.k_cache = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
         self.v_cache = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+        # workspaces of this decoder's own (never the binding's shared cache,
+        # which a larger later call could reallocate under a captured graph)
+        self.tmax = min(256, self.S)   # largest T one forward takes (prompt or tree)
+        self.att_ws = torch.zeros(L.medusa_tree_attention_workspace(L.MEDUSA_BF16, 1, self.tmax, self.heads, self.d,
+                                                                    self.S), dtype=torch.uint8, device=dev)
+        self.post_ws = torch.zeros(L.medusa_posterior_workspace(1, self.tmax, self.V), dtype=torch.uint8, device=dev)
+        # constants of the one-node acceptance test (argmax of one row)
+        self._node0 = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+        self._npaths1 = torch.ones(1, dtype=torch.int32, device=dev)
+        self._mask1 = torch.ones((1, 1), dtype=torch.uint8, device=dev)
 
     def forward(self, tokens, positions, prefix_len, tree_mask):
         """Run tokens [1][T] (int32, device) at positions [1][T] against the
@@ -79,7 +89,8 @@ class TinyDecoder:
             qkv = L.medusa_base_lm_head(n, lw["wqkv"], V=3 * H)
             q = L.medusa_rope_qkv(qkv.view(B, T, 3, self.heads, d), positions, prefix_len, self.theta,
                                   self.k_cache[l], self.v_cache[l])
-            a = L.medusa_tree_attention(q, self.k_cache[l], self.v_cache[l], prefix_len, tree_mask, d ** -0.5)
+            a = L.medusa_tree_attention(q, self.k_cache[l], self.v_cache[l], prefix_len, tree_mask, d ** -0.5,
+                                        ws=self.att_ws)
             o = L.medusa_base_lm_head(a.view(B, T, H), lw["wo"], V=H)
             n = L.medusa_add_rmsnorm(x, lw["mlp_norm"], self.eps, y=o)
             h = L.medusa_silu_mul(L.medusa_base_lm_head(n, lw["wgu"], V=2 * I))
@@ -96,14 +107,14 @@ class TinyDecoder:
         """The base model's greedy token at the last row of logits [1][T][V]
         (the acceptance test on a one-node tree), as a device int32 [1]."""
         row = logits[:, -1:, :]
-        one = self._i32([[0]])
-        post = L.medusa_evaluate_posterior(row, one.view(1, 1), one, self._i32([1]), 0.0, 0.09, 0.3)
+        post = L.medusa_evaluate_posterior(row, self._node0, self._node0, self._npaths1, 0.0, 0.09, 0.3,
+                                           ws=self.post_ws)
         return post["next_token"]
 
     def prefill(self, prompt):
         P = len(prompt)
-        if not 1 <= P <= 256:
-            raise ValueError("prompt length must be in [1, 256]")
+        if not 1 <= P <= self.tmax:
+            raise ValueError("prompt length must be in [1, %d]" % self.tmax)
         mask = torch.tril(torch.ones((P, P), dtype=torch.uint8)).to(self.dev)
         hidden, logits = self.forward(self._i32([list(prompt)]), self._i32([list(range(P))]), self._i32([0]), mask)
         return hidden, logits
@@ -118,13 +129,47 @@ class TinyDecoder:
         _, logits = self.prefill(prompt)
         nxt = self._argmax_last(logits)
         toks = [nxt]
-        one = torch.ones((1, 1), dtype=torch.uint8, device=self.dev)
         for i in range(1, n_new):
             Lp = P + i - 1
-            _, logits = self.forward(nxt.view(1, 1), self._i32([[Lp]]), self._i32([Lp]), one)
+            _, logits = self.forward(nxt.view(1, 1), self._i32([[Lp]]), self._i32([Lp]), self._mask1)
             nxt = self._argmax_last(logits)
             toks.append(nxt)
         return [int(t) for t in torch.cat(toks).cpu()]
+
+    def greedy_graph(self, prompt, n_new):
+        """Plain greedy decoding with each step replayed from a HIP graph: the
+        step (one-token forward, argmax, bookkeeping) keeps every value on the
+        device -- the next token, its position, the prefix length and the
+        output slot -- so the host only replays.  Same tokens as greedy()."""
+        P = len(prompt)
+        if P + n_new > self.S:
+            raise ValueError("the cache holds %d slots" % self.S)
+        if n_new < 2:
+            return self.greedy(prompt, n_new)
+        _, logits = self.prefill(prompt)
+        tok = self._argmax_last(logits).clone().view(1, 1)
+        pos = self._i32([[P]])
+        plen = self._i32([P])
+        idx = torch.zeros(1, dtype=torch.int64, device=self.dev)
+        out = torch.empty(n_new, dtype=torch.int32, device=self.dev)
+        out[:1].copy_(tok.view(1))
+
+        def step():
+            _, lg = self.forward(tok, pos, plen, self._mask1)
+            nxt = self._argmax_last(lg)
+            tok.view(1).copy_(nxt)
+            pos.add_(1)
+            plen.add_(1)
+            idx.add_(1)
+            out.scatter_(0, idx, nxt)
+
+        step()   # the first step eagerly (also sizes every allocation)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(n_new - 2):
+            graph.replay()
+        return [int(t) for t in out.cpu()]
 
     def medusa(self, heads, choices, topk, prompt, n_new):
         """Medusa greedy decoding with heads = dict(w1 [K][H][H], b1 [K][H],
@@ -166,3 +211,79 @@ class TinyDecoder:
             Lp += acc + 1
             root = post["next_token"]
         return out[:n_new], accepts, paths
+
+    def medusa_graph(self, heads, choices, topk, prompt, n_new, check_every=4):
+        """Medusa greedy decoding with each step replayed from a HIP graph.
+        The step keeps its bookkeeping on the device: the emitted tokens
+        (root and accepted nodes) are scattered into an output buffer at a
+        device-side count, the next heads' input row is gathered at the last
+        accepted node, the prefix length and root advance.  The host replays
+        and reads the count every `check_every` steps.  Returns (tokens,
+        steps)."""
+        P = len(prompt)
+        K = heads["w1"].shape[0]
+        N = choices.shape[0]
+        T = N + 1
+        D = K + 1
+        dev = self.dev
+        slack = (check_every + 1) * D
+        if P + n_new + slack + T > self.S:
+            raise ValueError("the cache holds %d slots" % self.S)
+        hidden, logits = self.prefill(prompt)
+        root = self._argmax_last(logits).clone()
+        h_row = hidden[:, P - 1, :].clone()
+        plen = self._i32([P])
+        new_plen = torch.empty(1, dtype=torch.int32, device=dev)
+        cap = n_new + slack
+        out = torch.zeros(cap + 1, dtype=torch.int32, device=dev)     # last slot: discarded writes
+        count = torch.zeros(1, dtype=torch.int64, device=dev)
+        steps = torch.zeros(1, dtype=torch.int64, device=dev)
+        jj = torch.arange(D, dtype=torch.int64, device=dev)
+        trash = torch.full((D,), cap, dtype=torch.int64, device=dev)
+        ws = torch.zeros(L.medusa_heads_workspace(L.MEDUSA_BF16, 1, self.H, self.V, K, topk), dtype=torch.uint8,
+                         device=dev)
+        i32 = torch.int32
+        tree = dict(tree_candidates=torch.empty((1, T), dtype=i32, device=dev),
+                    tree_indices=torch.empty(T, dtype=i32, device=dev), parent=torch.empty(T, dtype=i32, device=dev),
+                    depth=torch.empty(T, dtype=i32, device=dev), position_ids=torch.empty((1, T), dtype=i32, device=dev),
+                    tree_mask=torch.empty((T, T), dtype=torch.uint8, device=dev),
+                    retrieve=torch.empty((T, D), dtype=i32, device=dev), num_paths=torch.empty(1, dtype=i32, device=dev),
+                    status=torch.empty(2, dtype=i32, device=dev))
+        post = {n: torch.empty(1, dtype=i32, device=dev) for n in ("best_path", "accept_len", "next_token")}
+        r = torch.empty((1, K, self.H), dtype=torch.float32, device=dev)
+        topk_out = dict(topk_ids=torch.empty((1, K, topk), dtype=i32, device=dev),
+                        topk_logits=torch.empty((1, K, topk), dtype=torch.float32, device=dev))
+
+        def step():
+            L.medusa_resblock(h_row, heads["w1"], heads["b1"], r=r)
+            L.medusa_lm_head_topk(r, heads["w_lm"], topk, out=topk_out, ws=ws)
+            L.medusa_build_tree(choices, topk_out["topk_ids"], root, plen, out=tree)
+            hid, lg = self.forward(tree["tree_candidates"], tree["position_ids"], plen, tree["tree_mask"])
+            L.medusa_evaluate_posterior(lg, tree["tree_candidates"], tree["retrieve"], tree["num_paths"], 0.0, 0.09,
+                                        0.3, out=post, ws=self.post_ws)
+            L.medusa_commit_kv(self.k_cache, self.v_cache, plen, tree["retrieve"], post["best_path"],
+                               post["accept_len"], new_prefix_len=new_plen)
+            acc = post["accept_len"].long()
+            path = tree["retrieve"].index_select(0, post["best_path"].long()).view(-1).long()   # [D]
+            toks = tree["tree_candidates"].view(-1).index_select(0, path.clamp(min=0))
+            dst = torch.where(jj <= acc, (count + jj).clamp(max=cap), trash)
+            out.scatter_(0, dst, toks)
+            count.add_(acc + 1)
+            steps.add_(1)
+            last = path.gather(0, acc)
+            h_row.copy_(hid[0].index_select(0, last))
+            plen.copy_(new_plen)
+            root.copy_(post["next_token"])
+
+        step()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        while True:
+            if int(count.item()) >= n_new:
+                break
+            for _ in range(check_every):
+                graph.replay()
+        if int(tree["status"][0].item()) != 0:
+            raise RuntimeError("tree spec rejected: %s" % tree["status"].cpu().tolist())
+        return [int(t) for t in out[:n_new].cpu()], int(steps.item())

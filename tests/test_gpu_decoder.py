@@ -172,3 +172,26 @@ def test_medusa_with_fitted_heads(gpu_device):
     assert np.mean(accepts) >= 2.0
     assert len(accepts) <= n // 2
     assert any(p != 0 for p in paths)   # second-ranked branches accepted too
+
+
+def test_generation_replayed_from_hip_graphs(gpu_device):
+    # the same loops with each step captured once and replayed: every
+    # replayed step's token lands in the device-side output buffer, and the
+    # sequences equal the eager ones (and the oracle's)
+    cfg = dict(CFG, V=1000)
+    m = synth.tiny_decoder(cfg, seed=1)
+    n, K = 40, 3
+    prompt, ref = _prompt_with_margin(m, 12, n, 0.06, range(40))
+    dec = TinyDecoder(m, gpu_device, max_slots=256)
+    assert dec.greedy_graph(prompt, n) == ref
+    hd, _ = fitted_heads(m, prompt, n, K, seed=5)
+    heads = {key: to_dev(v) for key, v in hd.items()}
+    choices = to_dev(synth.choices_array(synth.full_tree_choices(K, 2), K))
+    eager, accepts, _ = dec.medusa(heads, choices, 2, prompt, n)
+    toks, steps = dec.medusa_graph(heads, choices, 2, prompt, n, check_every=3)
+    assert eager == ref and toks == ref
+    assert steps >= len(accepts)    # may overshoot by up to check_every steps
+    # random heads: one token per step, still the same sequence
+    rnd = {key: to_dev(v) for key, v in synth.tiny_heads(cfg, K, seed=2).items()}
+    toks, steps = dec.medusa_graph(rnd, choices, 2, prompt, n)
+    assert toks == ref
