@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-base-head", action="store_true",
                     help="skip the base lm_head timing (the step before the acceptance test)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the tree-attention prefix sweep and the Vicuna-33B batch-8 legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)")
     ap.add_argument("--generate", action="store_true",
@@ -415,6 +417,113 @@ def base_head_timing(step, seed, steps):
                                    "temperature": temp}}
 
 
+def _time_calls(fn, n, warm=3):
+    """Mean microseconds per call of fn(i) over n calls, HIP events on the
+    current stream (where the library enqueues)."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1000.0 / n
+
+
+def attention_prefix_sweep(step, steps):
+    """Tree attention (64-node tree, 32 heads x 128) at prefixes 512, 1024,
+    2048 and 4096, eight layers of KV rotated so no layer sits in the
+    last-level cache; algorithmic bytes (every prefix and tree K/V row once,
+    Q in, output out) over the mean duration of the call."""
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    w = step.w
+    dev = torch.device("cuda:0")
+    T, Hq, d = step.T, w["Hq"], w["d"]
+    gen = torch.Generator(device=dev).manual_seed(3)
+    q = (torch.randn((1, T, Hq, d), generator=gen, device=dev)).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    rows = []
+    for L in w["L_sweep"]:
+        S = L + T + 8
+        nl = 8
+        kc = [torch.randn((1, Hq, S, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nl)]
+        vc = [torch.randn((1, Hq, S, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nl)]
+        plen = torch.full((1,), L, dtype=torch.int32, device=dev)
+        ws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, 1, T, Hq, d, S), dtype=torch.uint8,
+                         device=dev)
+        us = _time_calls(lambda i: md.medusa_tree_attention(q, kc[i % nl], vc[i % nl], plen, step.tree["tree_mask"],
+                                                            d ** -0.5, out=out, ws=ws), steps)
+        nbytes = 2 * Hq * (L + T) * d * 2 + 2 * T * Hq * d * 2
+        rows.append({"L": L, "us": round(us, 2), "bytes": nbytes, "achieved": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del kc, vc
+    return {"unit": "GB/s", "peak": HBM_PEAK_GBS, "T": T, "Hq": Hq, "d": d, "rows": rows}
+
+
+def batch8_33b(step, seed, steps):
+    """The Vicuna-33B batch-8 shapes: heads (5 heads, H 6656, V 32000, top-10,
+    eight sequences: one weight stream serves all eight) and one tree
+    attention layer (52 heads x 128, per-sequence prefixes drawn in
+    [1024, 4096], the 64-node tree of the 7B step; two layers of KV
+    rotated).  Random device data (timing only); algorithmic bytes over the
+    mean duration of each call."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    import synth
+    w = synth.workload("vicuna-33b-b8")
+    dev = torch.device("cuda:0")
+    B, H, V, K, k, Hq, d = w["B"], w["H"], w["V"], w["K"], w["topk"], w["Hq"], w["d"]
+    gen = torch.Generator(device=dev).manual_seed(seed + 7)
+    bf = torch.bfloat16
+    hidden = torch.randn((B, H), generator=gen, device=dev).to(bf)
+    w1 = (torch.randn((K, H, H), generator=gen, device=dev) * 0.02).to(bf)
+    b1 = (torch.randn((K, H), generator=gen, device=dev) * 0.02).to(bf)
+    w_lm = torch.empty((K, V, H), dtype=bf, device=dev)
+    for h in range(K):
+        w_lm[h] = (torch.randn((V, H), generator=gen, device=dev) * 0.02).to(bf)
+    ws = torch.zeros(md.medusa_heads_workspace(md.MEDUSA_BF16, B, H, V, K, k), dtype=torch.uint8, device=dev)
+    r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+    topk = dict(topk_ids=torch.empty((B, K, k), dtype=torch.int32, device=dev),
+                topk_logits=torch.empty((B, K, k), dtype=torch.float32, device=dev))
+
+    def heads(i):
+        md.medusa_resblock(hidden, w1, b1, r=r)
+        md.medusa_lm_head_topk(r, w_lm, k, out=topk, ws=ws)
+
+    us_heads = _time_calls(heads, max(10, steps // 4))
+    heads_bytes = K * (H * H + H * V + H) * 2 + B * H * 2
+    del w1, w_lm
+    T = step.T
+    plen_host = np.asarray(synth.prefix_lengths(w, seed=seed), dtype=np.int32)
+    S = int(plen_host.max()) + T + 8
+    nl = 2
+    kc = [torch.randn((B, Hq, S, d), generator=gen, device=dev).to(bf) for _ in range(nl)]
+    vc = [torch.randn((B, Hq, S, d), generator=gen, device=dev).to(bf) for _ in range(nl)]
+    q = torch.randn((B, T, Hq, d), generator=gen, device=dev).to(bf)
+    out = torch.empty_like(q)
+    plen = torch.from_numpy(plen_host).to(dev)
+    aws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, B, T, Hq, d, S), dtype=torch.uint8,
+                      device=dev)
+    us_att = _time_calls(lambda i: md.medusa_tree_attention(q, kc[i % nl], vc[i % nl], plen, step.tree["tree_mask"],
+                                                            d ** -0.5, out=out, ws=aws), max(10, steps // 4))
+    att_bytes = int(sum(2 * Hq * (int(L) + T) * d * 2 for L in plen_host)) + B * 2 * T * Hq * d * 2
+    return {"workload": "vicuna-33b batch 8", "B": B, "H": H, "V": V, "K": K, "topk": k, "Hq": Hq, "d": d, "T": T,
+            "prefix_lens": plen_host.tolist(), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "heads": {"us": round(us_heads, 2), "bytes": heads_bytes, "achieved": round(heads_bytes / us_heads / 1e3, 1),
+                      "frac": round(heads_bytes / us_heads / 1e3 / HBM_PEAK_GBS, 4)},
+            "tree_attention": {"us": round(us_att, 2), "bytes": att_bytes,
+                               "achieved": round(att_bytes / us_att / 1e3, 1),
+                               "frac": round(att_bytes / us_att / 1e3 / HBM_PEAK_GBS, 4)}}
+
+
 SWEEP_K = (3, 4, 5, 8)
 SWEEP_T = (16, 32, 64, 128)
 
@@ -729,6 +838,9 @@ def main():
         result["graph"] = graph_timing(step, args.steps)
     if not args.no_base_head:
         result["base_lm_head"] = base_head_timing(step, args.seed, args.steps)
+    if not args.no_extra:
+        result["attention_prefix_sweep"] = attention_prefix_sweep(step, args.steps)
+        result["batch8_33b"] = batch8_33b(step, args.seed, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)
     print(json.dumps(result))
