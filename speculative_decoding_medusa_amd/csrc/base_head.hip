@@ -64,24 +64,45 @@ __device__ __forceinline__ u32x4 bh_ld16_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Fused-epilogue arguments (STATS): instead of the logits, each workgroup
-// writes per-row statistics over its 128 vocabulary entries and the logits
-// of the tree candidates whose tokens fall among them.
-struct BhStatsArgs {
+// Epilogues of the GEMM:
+//   kEpiLogits  write the float32 logits;
+//   kEpiStats   per-row statistics over the workgroup's 128 vocabulary
+//               entries and the logits of the tree candidates whose tokens
+//               fall among them (the fused acceptance test);
+//   kEpiTopk    Medusa heads at batch > 2: grid.y = head; the 2B rows are
+//               the hi and lo bf16 planes of the head's float32 inputs, so
+//               logit[b][v] = acc[b][v] + acc[B + b][v]; each workgroup
+//               publishes every row's top-k of its 128 entries as one
+//               sorted list (value desc, id asc) for the heads' merge.
+constexpr int kEpiLogits = 0, kEpiStats = 1, kEpiTopk = 2;
+
+struct BhEpiArgs {
+  // kEpiStats
   int T;                        // nodes per sequence (rows m = b * T + node)
   float temperature;            // > 0: softmax statistics of logits / temperature
   const int32_t* candidates;    // [B][T] token of every node
   RowStat* parts;               // [M][gridDim.x]
   float* child_z;               // [B][T][T]: child_z[b][n][c] = logit of c's token at node n
+  // kEpiTopk
+  int B, K, k;
+  float* cand_v;                // [K][B][gridDim.x][k]
+  int32_t* cand_i;
+  float* logits;                // optional [B][K][V]
 };
 
-template <bool PACKED, bool STATS>
+template <bool PACKED, int EPI>
 __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, int V,
-                                                                  const uint16_t* __restrict__ hidden,
-                                                                  const uint16_t* __restrict__ w,
-                                                                  float* __restrict__ logits, BhStatsArgs sa_args) {
+                                                                  const uint16_t* __restrict__ hidden_all,
+                                                                  const uint16_t* __restrict__ w_all,
+                                                                  float* __restrict__ logits, BhEpiArgs sa_args) {
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][kBhMTile * kBhPieces];
-  const int m0 = blockIdx.y * kBhMTile;
+  // kEpiTopk: one head per grid row; its planes and weights
+  const int head = EPI == kEpiTopk ? static_cast<int>(blockIdx.y) : 0;
+  const uint16_t* __restrict__ hidden = hidden_all + static_cast<size_t>(head) * M * H;
+  const uint16_t* __restrict__ w =
+      w_all + static_cast<size_t>(head) *
+                  (PACKED ? static_cast<size_t>(bh_vtiles(V)) * bh_ksteps(H) * 512 : static_cast<size_t>(V) * H);
+  const int m0 = EPI == kEpiTopk ? 0 : blockIdx.y * kBhMTile;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -139,6 +160,7 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
   // requested now so the epilogue does not wait on them.  A 64-row tile
   // spans at most ceil(63 / T) + 1 sequences: at most 2 * kMaxNodes pairs,
   // two per thread (clamped addresses, masked at use).
+  constexpr bool STATS = EPI == kEpiStats;
   const int Tn = STATS ? sa_args.T : 1;
   const int b_lo = m0 / Tn;
   const int npair = STATS ? ((min(m0 + kBhMTile, M) - 1) / Tn - b_lo + 1) * Tn : 0;
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
     compute(0, c, wa, -1);
   }
 
-  if (!STATS) {
+  if constexpr (EPI == kEpiLogits) {
     // logits[m][v]: lane (g, n) of tile (t, mt) holds rows mt*16 + 4g + i
 #pragma unroll
     for (int t = 0; t < kBhTiles; ++t) {
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
     return;
   }
 
-  // ---- fused epilogue: the workgroup's 64 x 128 logits go to LDS (over the
+  // ---- fused epilogues: the workgroup's 64 x 128 logits go to LDS (over the
   // hidden-state buffers, once every wave is past its last chunk)
   bh_wait_lds();
   bh_barrier();
@@ -241,6 +263,73 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lg[(mt * 16 + 4 * g + i) * LD + (wave * kBhTiles + t) * 16 + n] = acc[t][mt][i];
+
+  if constexpr (EPI == kEpiTopk) {
+    // one wave per row b: lane l holds entries l and l + 64 of the block;
+    // k rounds of a wave arg-best (value desc, id asc) build the sorted list
+    // in lanes 0 .. k-1.  Entries past V and NaN logits never win; slots no
+    // entry fills hold (-inf, -1).
+    bh_wait_lds();
+    bh_barrier();
+    const int Bn = sa_args.B, kk = sa_args.k;
+    const int v0 = blockIdx.x * kBhVBlock;
+    const float NEG = -__builtin_huge_valf();
+    const int NONE = 0x7fffffff;
+    for (int b = wave; b < Bn; b += kBhWaves) {
+      float z0 = NEG, z1 = NEG;
+      int i0 = NONE, i1 = NONE;
+      if (v0 + lane < V) {
+        z0 = lg[b * LD + lane] + lg[(Bn + b) * LD + lane];
+        i0 = v0 + lane;
+      }
+      if (v0 + lane + 64 < V) {
+        z1 = lg[b * LD + lane + 64] + lg[(Bn + b) * LD + lane + 64];
+        i1 = v0 + lane + 64;
+      }
+      if (sa_args.logits != nullptr) {
+        float* lr = sa_args.logits + (static_cast<size_t>(b) * sa_args.K + head) * V;
+        if (i0 != NONE) lr[i0] = z0;
+        if (i1 != NONE) lr[i1] = z1;
+      }
+      float myv = NEG;
+      int myi = -1;
+      for (int r = 0; r < kk; ++r) {
+        float bv = z0;
+        int bi = i0;
+        if (beats(z1, i1, bv, bi)) {
+          bv = z1;
+          bi = i1;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
+          if (beats(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if (lane == r && bi != NONE) {
+          myv = bv;
+          myi = bi;
+        }
+        if (bi != NONE && i0 == bi) {
+          z0 = NEG;
+          i0 = NONE;
+        }
+        if (bi != NONE && i1 == bi) {
+          z1 = NEG;
+          i1 = NONE;
+        }
+      }
+      if (lane < kk) {
+        const size_t off = ((static_cast<size_t>(head) * Bn + b) * gridDim.x + blockIdx.x) * kk + lane;
+        sa_args.cand_v[off] = myv;
+        sa_args.cand_i[off] = myi;
+      }
+    }
+    return;
+  }
   // tree candidates whose token lies in this block: (sequence, node, column);
   // a 64-row tile spans at most 63 / T + 2 sequences, so at most 2 * kMaxNodes
   // (sequence, node) pairs are checked
@@ -320,6 +409,30 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
   }
 }
 
+// Medusa heads at batch > 2: r [B][K][H] float32 -> per head the hi and lo
+// bf16 planes [K][2B][H] (hi = r rounded to nearest even, lo = the rest
+// rounded; the GEMM sums both rows' products).  Eight elements per thread.
+__global__ __launch_bounds__(256) void heads_planes_kernel(int B, int K, int H, const float* __restrict__ r,
+                                                           uint16_t* __restrict__ planes) {
+  const long long x = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int per = H / 8;
+  if (x >= static_cast<long long>(B) * K * per) return;
+  const int c = static_cast<int>(x % per) * 8;
+  const int j = static_cast<int>((x / per) % K), b = static_cast<int>(x / per / K);
+  const float* src = r + (static_cast<size_t>(b) * K + j) * H + c;
+  u32x4 hi, lo;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = src[2 * p], e = src[2 * p + 1];
+    const uint32_t h2 = pack_bf16x2(a, e);
+    hi[p] = h2;
+    lo[p] = pack_bf16x2(a - __uint_as_float(h2 << 16), e - __uint_as_float(h2 & 0xffff0000u));
+  }
+  uint16_t* base = planes + static_cast<size_t>(j) * 2 * B * H;
+  *reinterpret_cast<u32x4*>(base + static_cast<size_t>(b) * H + c) = hi;
+  *reinterpret_cast<u32x4*>(base + static_cast<size_t>(B + b) * H + c) = lo;
+}
+
 // Row-major weights [V][H] -> the packed layout, one 16-byte piece per
 // thread (zeros past V or H).
 __global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, const uint16_t* __restrict__ w,
@@ -339,6 +452,30 @@ __global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, co
 }
 
 }  // namespace medusa
+
+namespace medusa_host {
+
+int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, float* logits_or_null,
+                  uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st) {
+  using namespace medusa;
+  const long long n = static_cast<long long>(B) * K * (H / 8);
+  hipLaunchKernelGGL(heads_planes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, B, K, H, r,
+                     planes);
+  int rc = hip_check("medusa_lm_head_topk planes launch");
+  if (rc != MEDUSA_OK) return rc;
+  BhEpiArgs ea{};
+  ea.B = B;
+  ea.K = K;
+  ea.k = k;
+  ea.cand_v = cand_v;
+  ea.cand_i = cand_i;
+  ea.logits = logits_or_null;
+  hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiTopk>), dim3(heads_gemm_lists(V), K), dim3(kBhThreads), 0, st,
+                     2 * B, H, V, planes, static_cast<const uint16_t*>(w_lm), static_cast<float*>(nullptr), ea);
+  return hip_check("medusa_lm_head_topk gemm launch");
+}
+
+}  // namespace medusa_host
 
 extern "C" size_t medusa_base_lm_head_packed_bytes(int H, int V) {
   using namespace medusa;
@@ -373,12 +510,13 @@ extern "C" int medusa_base_lm_head(int dtype, int M, int H, int V, const void* h
   MEDUSA_REQUIRE_PTR(logits);
   hipStream_t st = static_cast<hipStream_t>(stream);
   dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + kBhMTile - 1) / kBhMTile);
-  const BhStatsArgs none = {1, 0.f, nullptr, nullptr, nullptr};
+  BhEpiArgs none{};
+  none.T = 1;
   if (w_packed)
-    hipLaunchKernelGGL((base_lm_head_kernel<true, false>), grid, dim3(kBhThreads), 0, st, M, H, V,
+    hipLaunchKernelGGL((base_lm_head_kernel<true, kEpiLogits>), grid, dim3(kBhThreads), 0, st, M, H, V,
                        static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits, none);
   else
-    hipLaunchKernelGGL((base_lm_head_kernel<false, false>), grid, dim3(kBhThreads), 0, st, M, H, V,
+    hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiLogits>), grid, dim3(kBhThreads), 0, st, M, H, V,
                        static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits, none);
   return medusa_host::hip_check("medusa_base_lm_head launch");
 }
@@ -441,13 +579,18 @@ extern "C" int medusa_base_posterior(int B, int T, int H, int V, int p_max, int 
   float* child_z = reinterpret_cast<float*>(base + bp_parts_bytes(B, T, V) + bp_merged_bytes(B, T));
   const int M = B * T;
   dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + kBhMTile - 1) / kBhMTile);
-  const BhStatsArgs args = {T, temperature, tree_candidates, parts, child_z};
+  BhEpiArgs args{};
+  args.T = T;
+  args.temperature = temperature;
+  args.candidates = tree_candidates;
+  args.parts = parts;
+  args.child_z = child_z;
   if (w_packed)
-    hipLaunchKernelGGL((base_lm_head_kernel<true, true>), grid, dim3(kBhThreads), 0, st, M, H, V,
+    hipLaunchKernelGGL((base_lm_head_kernel<true, kEpiStats>), grid, dim3(kBhThreads), 0, st, M, H, V,
                        static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base),
                        static_cast<float*>(nullptr), args);
   else
-    hipLaunchKernelGGL((base_lm_head_kernel<false, true>), grid, dim3(kBhThreads), 0, st, M, H, V,
+    hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiStats>), grid, dim3(kBhThreads), 0, st, M, H, V,
                        static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base),
                        static_cast<float*>(nullptr), args);
   int rc = medusa_host::hip_check("medusa_base_posterior launch");

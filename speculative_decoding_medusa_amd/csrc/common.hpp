@@ -122,6 +122,14 @@ int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, cons
                          float delta, int32_t* best_path, int32_t* accept_len, int32_t* next_token,
                          hipStream_t st);
 
+// Medusa heads' lm_head + top-k lists at batch > 2 on the skinny-GEMM kernel
+// (base_head.hip): r's hi/lo planes into `planes` [K][2B][H], then one
+// sorted top-k list per (head, sequence, 128-entry vocabulary block) in
+// cand_v / cand_i [K][B][heads_gemm_lists(V)][k].
+inline int heads_gemm_lists(int V) { return (V + 127) / 128; }
+int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, float* logits_or_null,
+                  uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st);
+
 // Acceptance from one drawn token per node (posterior.hip; nucleus mode).
 int decide_on_draws(int B, int T, int V, int p_max, int D, const medusa::RowStat* draws,
                     const int32_t* tree_candidates, const int32_t* retrieve, const int32_t* num_paths,

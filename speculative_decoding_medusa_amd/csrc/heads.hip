@@ -1,26 +1,28 @@
 // Medusa heads on gfx950: ResBlock GEMV and lm_head GEMV with fused top-k.
 //
 // Both stages are skinny matrix products (B <= 16 rows of activations
-// against K*H resp. K*V weight rows) and bound by streaming the weights
-// from HBM.  The bf16 path feeds them through v_mfma_f32_16x16x32_bf16 with
-// the batch on the M side: lane l supplies 16 contiguous bytes of weight row
-// (l % 16) at hidden offset 8 * (l / 16) of each 32-wide K step, so every
-// weight byte is loaded once with 16-byte loads and the MFMA does the
-// multiply-accumulate (no bf16 -> f32 conversions on the VALU).  A workgroup
-// of four waves splits each 16-row tile's K range and reduces through LDS.
+// against K*H resp. K*V weight rows), bound by streaming the weights from
+// HBM once.  By shape:
 //
-// The ResBlock output r is float32.  For the lm_head product the bf16 MFMA
-// needs bf16 A operands, so r is split exactly into hi = bf16(r) and
-// lo = bf16(r - hi) and both go through the MFMA as separate M rows; their
-// products with the (exact) bf16 weights are summed in float32, which keeps
-// about 16 significant bits of r instead of 8.
+//  * bf16, batch <= 2, H <= 8192 (the verify step's shape): row-diagonal
+//    kernels.  Each wave streams a contiguous block of whole weight rows
+//    (one 1 KB wave instruction per 512 elements) and takes each row's dot
+//    product as the trace of a v_mfma_f32_16x16x32_bf16 whose A operand
+//    holds the activations at the same positions.  lm_head logits go into
+//    per-wave top-k lists in registers; the last workgroup of each head to
+//    finish (a device-scope arrival count; lists published with
+//    write-through stores) merges them, so the call is one kernel.
+//  * bf16 otherwise: the ResBlock on a split-K MFMA kernel (four waves split
+//    each 16-row tile's K range and reduce through LDS), and the lm_head on
+//    the skinny-GEMM kernel of base_head.hip, the batch's hi/lo planes as
+//    2B GEMM rows, each workgroup publishing the top-k of its 128-entry
+//    vocabulary block; a merge kernel then finishes each (sequence, head).
+//  * float32 weights: VALU kernels.
 //
-// Top-k: each wave (each workgroup in the split-K kernel) keeps sorted
-// lists per sequence in LDS and inserts the rare logits that beat its current
-// k-th entry; the lists are published to the workspace and a second, small
-// kernel merges them per (sequence, head).  Two launches rather than a
-// last-workgroup merge: on this chip a device-scope fence writes back and
-// invalidates the L2 of the issuing XCD, which every workgroup would pay.
+// The ResBlock output r is float32.  The bf16 MFMA needs bf16 operands, so
+// r enters the lm_head as hi = bf16(r) and lo = bf16(r - hi), both against
+// the exact bf16 weights with float32 sums: about 16 significant bits of r
+// instead of 8.
 #include "common.hpp"
 
 namespace medusa {
@@ -429,96 +431,30 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_rounds_kernel(int B,
 }
 
 // ------------------------------------------------------------------ K2
-// Grid (G, K).  Workgroup wg of head j owns rows [wg*rows_per_wg, ...) of
-// Wlm[j], walked in 16-row tiles.  NP = partial sums per tile (one per wave
-// for the split-K MFMA path, one for the f32 path).
-template <bool kBF16, int MT>
-__global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
+// float32 weights.  Grid (G, K).  Workgroup wg of head j owns rows
+// [wg*rows_per_wg, ...) of Wlm[j], walked in 16-row tiles; wave w computes
+// rows row0 + 4w .. +3 over the full H.  (bf16 weights take the row-diagonal
+// kernel at batch <= 2 and the skinny-GEMM kernel otherwise.)
+__global__ __launch_bounds__(kHeadsThreads) void lm_topk_f32_kernel(
     int B, int H, int V, int K, int k, int rows_per_wg, int G,
-    const float* __restrict__ r, const void* __restrict__ wlm_v,
+    const float* __restrict__ r, const float* __restrict__ wlm,
     float* __restrict__ logits_out, int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals,
     float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
-  constexpr int NP = kBF16 ? kHeadsWaves : 1;
   const int j = blockIdx.y, wg = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int n = lane & 15;
   const int r_begin = wg * rows_per_wg;
   const int r_end = min(V, r_begin + rows_per_wg);
   const float NEG = -__builtin_huge_valf();
 
-  __shared__ float red[2][NP][kMaxBatch][16];
+  __shared__ float red[2][kMaxBatch][16];
   __shared__ TopkLists tl;
   if (threadIdx.x < kMaxBatch) tl.count[threadIdx.x] = 0;
   __syncthreads();
 
-  const int nsteps = (H + 31) / 32;
-  const int s0 = wave * nsteps / kHeadsWaves, s1 = (wave + 1) * nsteps / kHeadsWaves;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-
   int buf = 0;
   for (int row0 = r_begin; row0 < r_end; row0 += 16) {
-    if constexpr (kBF16) {
-      const uint16_t* wlm = static_cast<const uint16_t*>(wlm_v);
-      const int row = row0 + n;
-      const bool row_ok = row < r_end;
-      const uint16_t* wrow = wlm + (static_cast<size_t>(j) * V + (row_ok ? row : r_begin)) * H;
-      // A operand: M row m = 2*bb + part of tile t holds the hi (part 0) or lo
-      // (part 1) half of r[b = 8t + bb]; rows past the batch are zero.
-      const float* arow[MT];
-      bool a_ok[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int b = 8 * t + (n >> 1);
-        a_ok[t] = b < B;
-        arow[t] = r + (static_cast<size_t>(a_ok[t] ? b : 0) * K + j) * H;
-      }
-      const bool lo_part = (n & 1) != 0;
-      f32x4 acc[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s = s0; s < s1; s += kUnroll) {
-        u32x4 wv[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int k0 = (s + u) * 32 + g * 8;
-          const bool ok = (s + u < s1) && (k0 < H) && row_ok;
-          wv[u] = ok ? ld16_stream(wrow + k0) : zero;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int k0 = (s + u) * 32 + g * 8;
-          const bool kok = (s + u < s1) && (k0 < H);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            u32x4 av = zero;
-            if (kok && a_ok[t]) {
-              const float4 x0 = *reinterpret_cast<const float4*>(arow[t] + k0);
-              const float4 x1 = *reinterpret_cast<const float4*>(arow[t] + k0 + 4);
-              const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-              uint32_t hb[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t hi = f32_to_bf16_bits(xs[e]);
-                hb[e] = lo_part ? f32_to_bf16_bits(xs[e] - __uint_as_float(hi << 16)) : hi;
-              }
-              av = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                         hb[6] | (hb[7] << 16)};
-            }
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(wv[u]), acc[t],
-                                                              0, 0, 0);
-          }
-        }
-      }
-      // lane (g, n) holds C[4g + i][n]: sequences 8t + 2g (i = 0 hi, 1 lo)
-      // and 8t + 2g + 1 (i = 2 hi, 3 lo) of row row0 + n.
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        red[buf][wave][8 * t + 2 * g][n] = acc[t][0] + acc[t][1];
-        red[buf][wave][8 * t + 2 * g + 1][n] = acc[t][2] + acc[t][3];
-      }
-    } else {
-      // f32 weights: wave w computes rows row0 + 4w .. +3 over the full H.
-      const float* wlm = static_cast<const float*>(wlm_v);
+    {
       for (int q = 0; q < 4; ++q) {
         const int rn = wave * 4 + q;
         const int row = row0 + rn;
@@ -542,7 +478,7 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
         for (int b = 0; b < kMaxBatch; ++b) {
           if (b < B) {
             const float s = wave_sum(acc[b]);
-            if (lane == 0) red[buf][0][b][rn] = s;
+            if (lane == 0) red[buf][b][rn] = s;
           }
         }
       }
@@ -552,9 +488,7 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
       const int row = row0 + n;
       const bool valid = lane < 16 && row < r_end;
       for (int b = 0; b < B; ++b) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < NP; ++w) v += red[buf][w][b][n];
+        const float v = red[buf][b][n];
         if (valid && logits_out != nullptr)
           logits_out[(static_cast<size_t>(b) * K + j) * V + row] = v;
         lds_vfloat* lvb = (lds_vfloat*)tl.v[b];
@@ -578,209 +512,6 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_kernel(
         cand_v[base + lane] = have ? ((lds_vfloat*)tl.v[b])[lane] : NEG;
         cand_i[base + lane] = have ? ((lds_vint*)tl.id[b])[lane] : -1;
       }
-    }
-  }
-}
-
-// ------------------------------------------------------------ K2, streamed
-// bf16 lm_head for 2*B*H*2 bytes of A planes that fit in LDS.
-//
-// The workgroup first splits r[b][j] into bf16 hi/lo planes in LDS (row
-// 2b = hi, 2b+1 = lo: exactly the MFMA A rows of lane m = l % 16).  Each wave
-// then owns `tpw` whole 16-row tiles of Wlm[j] and streams them alone: no
-// split-K, no barrier until the end.  Loads come in chunks of kChunkPairs
-// 64-wide K pairs (lane l reads 32 contiguous bytes of row l % 16, so a row
-// gets a full 128-byte line per pair) and are double-buffered in registers
-// across chunks and tiles; A operands come from LDS, whose counter is
-// separate from the vector-memory one, so consuming them never waits on the
-// weight stream.  After each tile the wave inserts its logits into its own
-// top-k lists and finally publishes them for the merge kernel.
-#ifndef MEDUSA_CHUNK_PAIRS
-#define MEDUSA_CHUNK_PAIRS 4
-#endif
-#ifndef MEDUSA_STREAM_ROTATE
-#define MEDUSA_STREAM_ROTATE 0
-#endif
-constexpr int kChunkPairs = MEDUSA_CHUNK_PAIRS;
-
-__device__ __forceinline__ int stream_chunk_pair0(int c, int cpt, int rot) {
-  int q = c - (c / cpt) * cpt + rot;
-  if (q >= cpt) q -= cpt;
-  return q * kChunkPairs;
-}
-
-__device__ __forceinline__ void stream_load_chunk(const uint16_t* __restrict__ wbase, int V, int H, int t0, int cpt,
-                                                  int rot, int n, int g, int c, u32x4 (&buf)[2 * kChunkPairs]) {
-  const int tq = c / cpt;
-  const int p0 = stream_chunk_pair0(c, cpt, rot);
-  const int row = (t0 + tq) * 16 + n;
-  const bool row_ok = row < V;
-  const uint16_t* wrow = wbase + static_cast<size_t>(row_ok ? row : V - 1) * H;
-  // Loads are unconditional, from clamped in-bounds addresses, and nothing
-  // consumes them here: with no branch or select behind them the compiler
-  // can count them and later wait only for the chunk being consumed, not for
-  // the prefetch issued after it.  Rows past V load row V-1 (their logits are
-  // discarded); the K tail is masked when the chunk is consumed.
-#pragma unroll
-  for (int u = 0; u < kChunkPairs; ++u) {
-    const int k0 = (p0 + u) * 64 + g * 16;
-    buf[2 * u] = ld16_stream(wrow + min(k0, H - 8));
-    buf[2 * u + 1] = ld16_stream(wrow + min(k0 + 8, H - 8));
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void stream_mfma_chunk(const uint16_t* __restrict__ A, int B, int H, int cpt, int rot, int n,
-                                                  int g, int c, const u32x4 (&buf)[2 * kChunkPairs], f32x4 (&acc)[MT]) {
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int p0 = stream_chunk_pair0(c, cpt, rot);
-#pragma unroll
-  for (int u = 0; u < kChunkPairs; ++u) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int k0 = (p0 + u) * 64 + g * 16 + 8 * h2;
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int ar = t * 16 + n;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(ar < 2 * B ? ar : 0) * H +
-                                                         min(k0, H - 8));
-        const u32x4 a = (ar < 2 * B && k0 < H) ? x : zero;
-        const u32x4 w = k0 < H ? buf[2 * u + h2] : zero;
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(w), acc[t], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// End of a tile: lane (g, n) holds C[4g + i][n] of each M tile t, i.e. the
-// hi/lo halves of sequences 8t + 2g (i = 0, 1) and 8t + 2g + 1 (i = 2, 3) at
-// row `row`.  Writes the optional logits and offers them to the wave's lists.
-template <int MT>
-__device__ __forceinline__ void stream_tile_epilogue(int B, int K, int V, int k, int j, int row, int g, int lane,
-                                                     f32x4 (&acc)[MT], float* __restrict__ logits_out,
-                                                     lds_vfloat* my_v, lds_vint* my_i, lds_vint* my_c) {
-  const bool valid = row < V;
-  // the two sequences of each M tile, as plain scalars (no indexed array)
-  const float v00 = acc[0][0] + acc[0][1], v01 = acc[0][2] + acc[0][3];
-  const float v10 = MT > 1 ? acc[MT - 1][0] + acc[MT - 1][1] : 0.f;
-  const float v11 = MT > 1 ? acc[MT - 1][2] + acc[MT - 1][3] : 0.f;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (logits_out != nullptr && valid) {
-    const int b0 = 2 * g;
-    if (b0 < B) logits_out[(static_cast<size_t>(b0) * K + j) * V + row] = v00;
-    if (b0 + 1 < B) logits_out[(static_cast<size_t>(b0 + 1) * K + j) * V + row] = v01;
-    if (MT > 1 && b0 + 8 < B) logits_out[(static_cast<size_t>(b0 + 8) * K + j) * V + row] = v10;
-    if (MT > 1 && b0 + 9 < B) logits_out[(static_cast<size_t>(b0 + 9) * K + j) * V + row] = v11;
-  }
-  for (int b = 0; b < B; ++b) {
-    const bool odd = (b & 1) != 0;
-    const float v = b < 8 ? (odd ? v01 : v00) : (odd ? v11 : v10);
-    const int cnt = my_c[b];
-    const bool ok = valid && g == ((b & 7) >> 1) && (v == v) &&
-                    (cnt < k || beats(v, row, my_v[b * k + k - 1], my_i[b * k + k - 1]));
-    const uint64_t m = ballot(ok);
-    if (m) topk_insert_list(my_v + b * k, my_i + b * k, my_c + b, k, v, row, m, lane);
-  }
-}
-
-template <int MT>
-__global__ __launch_bounds__(kHeadsThreads) void lm_topk_stream_kernel(
-    int B, int H, int V, int K, int k, int tpw, int G, const float* __restrict__ r,
-    const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int j = blockIdx.y, wg = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const float NEG = -__builtin_huge_valf();
-
-  uint16_t* A = reinterpret_cast<uint16_t*>(smem);                       // [2B][H]
-  const size_t a_bytes = (static_cast<size_t>(2 * B) * H * 2 + 15) / 16 * 16;
-  float* lv = reinterpret_cast<float*>(smem + a_bytes);                  // [4][B][k]
-  int* li = reinterpret_cast<int*>(lv + kHeadsWaves * B * k);            // [4][B][k]
-  int* lc = li + kHeadsWaves * B * k;                                    // [4][B]
-
-  // split r into hi/lo bf16 planes
-  const int h4 = H / 4;
-  for (int e4 = tid; e4 < B * h4; e4 += kHeadsThreads) {
-    const int b = e4 / h4, e = (e4 - b * h4) * 4;
-    const float4 x = *reinterpret_cast<const float4*>(r + (static_cast<size_t>(b) * K + j) * H + e);
-    const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t hi = f32_to_bf16_bits(xs[c]);
-      const uint32_t lo = f32_to_bf16_bits(xs[c] - __uint_as_float(hi << 16));
-      A[static_cast<size_t>(2 * b) * H + e + c] = static_cast<uint16_t>(hi);
-      A[static_cast<size_t>(2 * b + 1) * H + e + c] = static_cast<uint16_t>(lo);
-    }
-  }
-  for (int e = tid; e < kHeadsWaves * B; e += kHeadsThreads) lc[e] = 0;
-  __syncthreads();
-
-  const int tiles = (V + 15) / 16;
-  const int t0 = (wg * kHeadsWaves + wave) * tpw;
-  const int t1 = min(t0 + tpw, tiles);
-  const int npairs = (H + 63) / 64;
-  const int cpt = (npairs + kChunkPairs - 1) / kChunkPairs;
-  const int nchunks = t1 > t0 ? (t1 - t0) * cpt : 0;
-  const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
-#if MEDUSA_STREAM_ROTATE
-  // waves start their rows at different K offsets, so concurrent requests
-  // spread over more HBM channels
-  const int rot = ((j * gridDim.x + wg) * kHeadsWaves + wave) % cpt;
-#else
-  const int rot = 0;
-#endif
-  lds_vfloat* my_v = (lds_vfloat*)(lv + wave * B * k);
-  lds_vint* my_i = (lds_vint*)(li + wave * B * k);
-  lds_vint* my_c = (lds_vint*)(lc + wave * B);
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Rotated double buffer (as in the row-diagonal kernel): both buffers are
-  // in flight before the loop, refills past the end reload the last chunk,
-  // so every MFMA waits only for the loads it consumes.
-  u32x4 wa[2 * kChunkPairs], wb[2 * kChunkPairs];
-#define MEDUSA_STREAM_STEP(cc, buf)                                                                       \
-  do {                                                                                                    \
-    stream_mfma_chunk<MT>(A, B, H, cpt, rot, n, g, (cc), buf, acc);                                       \
-    if ((cc) % cpt == cpt - 1)                                                                            \
-      stream_tile_epilogue<MT>(B, K, V, k, j, (t0 + (cc) / cpt) * 16 + n, g, lane, acc, logits_out, my_v, \
-                               my_i, my_c);                                                               \
-  } while (0)
-  if (nchunks > 0) {
-    const int lastc = nchunks - 1;
-    stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, 0, wa);
-    stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, min(1, lastc), wb);
-    int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
-      __builtin_amdgcn_sched_barrier(0);
-      stream_mfma_chunk<MT>(A, B, H, cpt, rot, n, g, c, wa, acc);
-      stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, min(c + 2, lastc), wa);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c % cpt == cpt - 1)
-        stream_tile_epilogue<MT>(B, K, V, k, j, (t0 + c / cpt) * 16 + n, g, lane, acc, logits_out, my_v, my_i,
-                                 my_c);
-      stream_mfma_chunk<MT>(A, B, H, cpt, rot, n, g, c + 1, wb, acc);
-      stream_load_chunk(wbase, V, H, t0, cpt, rot, n, g, min(c + 3, lastc), wb);
-      __builtin_amdgcn_sched_barrier(0);
-      if ((c + 1) % cpt == cpt - 1)
-        stream_tile_epilogue<MT>(B, K, V, k, j, (t0 + (c + 1) / cpt) * 16 + n, g, lane, acc, logits_out, my_v,
-                                 my_i, my_c);
-    }
-    if (c < nchunks) MEDUSA_STREAM_STEP(c, wa);
-  }
-#undef MEDUSA_STREAM_STEP
-  // every wave publishes its own lists (list wg * 4 + wave of head j)
-  const int nlists = G * kHeadsWaves;
-  for (int b = 0; b < B; ++b) {
-    const size_t base = ((static_cast<size_t>(j) * B + b) * nlists + wg * kHeadsWaves + wave) * k;
-    if (lane < k) {
-      const bool have = lane < my_c[b];
-      cand_v[base + lane] = have ? my_v[b * k + lane] : NEG;
-      cand_i[base + lane] = have ? my_i[b * k + lane] : -1;
     }
   }
 }
@@ -1145,27 +876,19 @@ constexpr size_t kCounterBytes = 256;
 
 struct LmGrid {
   bool diag;       // row-diagonal kernel (B <= 2)
+  bool gemm;       // bf16 otherwise: the skinny-GEMM kernel with a top-k epilogue
   int nst;         // 512-element steps per row
   int rows_per_wave;
-  bool stream;     // streamed kernel (A planes in LDS) or the split-K kernel
-  int rows_per_wg; // split-K kernel
-  int tpw;         // streamed kernel: 16-row tiles per wave
+  int rows_per_wg; // f32 kernel
   int G;           // workgroups per head
-  int lists;       // published top-k lists per head (one per wave, or per workgroup for split-K)
-  size_t lds;      // dynamic LDS of the streamed kernel
+  int lists;       // published top-k lists per head (per wave, per vocabulary block or per workgroup)
 };
 
-constexpr size_t kStreamLdsMax = 64 * 1024;
 // Resident waves per SIMD the row-diagonal lm_head grid is sized for: one
 // measured best at the Vicuna-7B shape (fewer, longer contiguous streams,
 // and fewer lists to merge).
 constexpr int kDiagWavesPerSimd = 1;
 constexpr int kMaxWavesPerSimd = 8;
-
-size_t stream_lds(int B, int H, int topk) {
-  return (static_cast<size_t>(2 * B) * H * 2 + 15) / 16 * 16 +
-         static_cast<size_t>(kHeadsWaves) * B * topk * 8 + static_cast<size_t>(kHeadsWaves) * B * 4;
-}
 
 // Grid of the lm_head kernel for `wps` resident waves per SIMD: sized so that
 // every wave is resident at once (one round, no tail).  The launch passes the
@@ -1179,6 +902,12 @@ LmGrid lm_grid(int dtype, int B, int H, int V, int K, int topk, int wps) {
   // workgroups, rounded down so the whole grid is one round
   long long wgh = 256LL * wps / K;
   if (wgh < 1) wgh = 1;
+  lg.gemm = dtype == MEDUSA_BF16 && !lg.diag;
+  if (lg.gemm) {   // one list per (head, sequence, 128-entry vocabulary block)
+    lg.G = medusa_host::heads_gemm_lists(V);
+    lg.lists = lg.G;
+    return lg;
+  }
   if (lg.diag) {
     long long rpw = (V + kHeadsWaves * wgh - 1) / (kHeadsWaves * wgh);
     const long long min_rpw = (V + kHeadsWaves * 1024LL - 1) / (kHeadsWaves * 1024LL);
@@ -1188,20 +917,7 @@ LmGrid lm_grid(int dtype, int B, int H, int V, int K, int topk, int wps) {
     lg.lists = lg.G * kHeadsWaves;
     return lg;
   }
-  lg.lds = stream_lds(B, H, topk);
-  lg.stream = dtype == MEDUSA_BF16 && lg.lds <= kStreamLdsMax;
-  if (lg.stream) {
-    const long long tiles = (V + 15) / 16;
-    long long tpw = (tiles + kHeadsWaves * wgh - 1) / (kHeadsWaves * wgh);
-    if (tpw < 1) tpw = 1;
-    const long long min_tpw = (tiles + kHeadsWaves * 1024LL - 1) / (kHeadsWaves * 1024LL);
-    if (tpw < min_tpw) tpw = min_tpw;
-    lg.tpw = static_cast<int>(tpw);
-    lg.G = static_cast<int>((tiles + kHeadsWaves * tpw - 1) / (kHeadsWaves * tpw));
-    lg.lists = lg.G * kHeadsWaves;
-    return lg;
-  }
-  // split-K kernel: about four resident workgroups per CU over the grid
+  // float32 weights: about four resident workgroups per CU over the grid
   const int target = 1024;
   int g0 = (target + K - 1) / K;
   if (g0 < 1) g0 = 1;
@@ -1314,7 +1030,11 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
   float* cand_v = reinterpret_cast<float*>(base + kCounterBytes);
   int32_t* cand_i = reinterpret_cast<int32_t*>(base + kCounterBytes + cb);
   bool fused = false;
-  if (lg.diag) {
+  if (lg.gemm) {
+    uint16_t* planes = reinterpret_cast<uint16_t*>(base + kCounterBytes + 2 * cb);
+    int rc = medusa_host::heads_lm_gemm(B, H, V, K, topk, r, w_lm, logits, planes, cand_v, cand_i, st);
+    if (rc != MEDUSA_OK) return rc;
+  } else if (lg.diag) {
     const uint16_t* w = static_cast<const uint16_t*>(w_lm);
 #define MEDUSA_DIAG_LAUNCH(NS, NB)                                                                            \
   do {                                                                                                        \
@@ -1340,31 +1060,9 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
       if (B == 1) MEDUSA_DIAG_LAUNCH(16, 1); else MEDUSA_DIAG_LAUNCH(16, 2);
     }
 #undef MEDUSA_DIAG_LAUNCH
-  } else if (lg.stream) {
-    const uint16_t* w = static_cast<const uint16_t*>(w_lm);
-    if (B <= 8) {
-      const int wps = occupancy_wps(lm_topk_stream_kernel<1>, lg.lds);
-      lg = lm_grid(dtype, B, H, V, K, topk, wps);
-      hipLaunchKernelGGL((lm_topk_stream_kernel<1>), dim3(lg.G, K), dim3(kHeadsThreads), lg.lds, st, B, H, V, K,
-                         topk, lg.tpw, lg.G, r, w, logits, ids, vals, cand_v, cand_i);
-    } else {
-      const int wps = occupancy_wps(lm_topk_stream_kernel<2>, lg.lds);
-      lg = lm_grid(dtype, B, H, V, K, topk, wps);
-      hipLaunchKernelGGL((lm_topk_stream_kernel<2>), dim3(lg.G, K), dim3(kHeadsThreads), lg.lds, st, B, H, V, K,
-                         topk, lg.tpw, lg.G, r, w, logits, ids, vals, cand_v, cand_i);
-    }
-  } else if (dtype == MEDUSA_BF16) {
-    dim3 grid(lg.G, K);
-    if (B <= 8)
-      hipLaunchKernelGGL((lm_topk_kernel<true, 1>), grid, dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
-                         lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
-    else
-      hipLaunchKernelGGL((lm_topk_kernel<true, 2>), grid, dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
-                         lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
   } else {
-    dim3 grid(lg.G, K);
-    hipLaunchKernelGGL((lm_topk_kernel<false, 1>), grid, dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
-                       lg.rows_per_wg, lg.G, r, w_lm, logits, ids, vals, cand_v, cand_i);
+    hipLaunchKernelGGL(lm_topk_f32_kernel, dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, V, K, topk,
+                       lg.rows_per_wg, lg.G, r, static_cast<const float*>(w_lm), logits, ids, vals, cand_v, cand_i);
   }
   int rc = medusa_host::hip_check("medusa_lm_head_topk launch");
   if (rc != MEDUSA_OK || fused) return rc;
@@ -1388,8 +1086,14 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
   return medusa_host::hip_check("medusa_lm_head_topk merge launch");
 }
 
+// the GEMM path's hi/lo planes of r, [K][2B][H] bf16
+size_t planes_bytes(int dtype, int B, int H, int V, int K, int topk) {
+  if (!lm_grid(dtype, B, H, V, K, topk, kMaxWavesPerSimd).gemm) return 0;
+  return medusa_host::round_up(static_cast<size_t>(K) * 2 * B * H * 2, 256);
+}
+
 size_t lm_ws_bytes(int dtype, int B, int H, int V, int K, int topk) {
-  return kCounterBytes + 2 * cand_bytes(dtype, B, H, V, K, topk);
+  return kCounterBytes + 2 * cand_bytes(dtype, B, H, V, K, topk) + planes_bytes(dtype, B, H, V, K, topk);
 }
 
 }  // namespace

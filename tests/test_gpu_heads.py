@@ -100,6 +100,7 @@ def test_heads_back_to_back_inputs_share_workspace(gpu_device):
 @pytest.mark.parametrize("B,H,V,K,k", [
     (1, 6656, 3001, 2, 10),    # 13 row steps of 512 (the 33B hidden size, batch 1)
     (2, 8192, 2000, 1, 8),     # 16 row steps, two sequences per wave
+    (1, 8200, 700, 2, 5),      # past 16 row steps: the skinny-GEMM path at batch 1
 ])
 def test_heads_bf16_wide_rows(gpu_device, B, H, V, K, k):
     w = synth.workload("vicuna-7b", B=B, H=H, V=V, K=K, topk=k)
