@@ -119,6 +119,26 @@ int medusa_lm_head_topk(int dtype, int B, int H, int V, int K, int topk,
                         int32_t* topk_ids, float* topk_logits, float* logits_or_null,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* The same lm_head + top-k on head weights packed once by
+ * medusa_heads_pack (bf16 only, H <= 65536): the skinny-GEMM kernel at any
+ * batch (per head, r's hi/lo bf16 planes as 2B rows; every 128-entry
+ * vocabulary block publishes each sequence's top-k, merged in a second
+ * kernel).  From the packed layout one wave instruction reads 1 KB of
+ * weights contiguously; meant for batch > 2, where the row-major call runs
+ * the same GEMM on row-major weights.  Same outputs as medusa_lm_head_topk;
+ * workspace: medusa_heads_workspace() bytes (it covers both calls). */
+int medusa_lm_head_topk_packed(int dtype, int B, int H, int V, int K, int topk,
+                               const float* r, const void* w_lm_packed,
+                               int32_t* topk_ids, float* topk_logits, float* logits_or_null,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Pack w_lm [K][V][H] (bf16) into w_packed: each head in the layout of
+ * medusa_base_lm_head_pack, heads one after another.  Size:
+ * medusa_heads_packed_bytes() (0 for invalid sizes).  The buffers must not
+ * alias. */
+size_t medusa_heads_packed_bytes(int K, int H, int V);
+int medusa_heads_pack(int dtype, int K, int H, int V, const void* w_lm, void* w_packed, void* stream);
+
 /* Both stages.  r_or_null: optional float32 [B][K][H] output of the
  * ResBlocks (kept inside the workspace otherwise). */
 int medusa_heads(int dtype, int B, int H, int V, int K, int topk,

@@ -46,6 +46,9 @@ _SIGS = {
     "medusa_resblock": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "medusa_lm_head_topk": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "medusa_lm_head_topk_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "medusa_heads_packed_bytes": (_sz, [_i, _i, _i]),
+    "medusa_heads_pack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
     "medusa_build_tree": (_i, [_i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp]),
     "medusa_tree_attention_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "medusa_tree_attention": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _sz, _vp]),
@@ -169,6 +172,46 @@ def medusa_lm_head_topk(r, w_lm, topk, keep_logits=False, out=None, ws=None):
                                  _ptr(logits, "logits", torch.float32, (B, K, V)),
                                  _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_lm_head_topk")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits)
+
+
+def medusa_heads_pack(w_lm):
+    """bf16 [K][V][H] head weights -> the packed layout (uint8 tensor)."""
+    K, V, H = w_lm.shape
+    nbytes = int(lib.medusa_heads_packed_bytes(K, H, V))
+    if nbytes == 0:
+        raise MedusaError(_ERR_SHAPE, "medusa_heads_pack", "unsupported shape K=%d H=%d V=%d" % (K, H, V))
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w_lm.device)
+    rc = lib.medusa_heads_pack(MEDUSA_BF16, K, H, V, _ptr(w_lm, "w_lm", torch.bfloat16), _ptr(out, "w_packed"),
+                               _stream(w_lm.device))
+    _check(rc, "medusa_heads_pack")
+    return out
+
+
+def medusa_lm_head_topk_packed(r, w_packed, V, topk, keep_logits=False, out=None, ws=None):
+    """lm_head + top-k on packed head weights (medusa_heads_pack); r float32 [B][K][H]."""
+    B, K, H = r.shape
+    dev = r.device
+    out = out or {}
+    ids = out.get("topk_ids")
+    vals = out.get("topk_logits")
+    logits = out.get("logits")
+    if ids is None:
+        ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    if keep_logits and logits is None:
+        logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    need = medusa_heads_workspace(MEDUSA_BF16, B, H, V, K, topk)
+    if ws is None:
+        ws = workspace("heads", dev, need)
+    rc = lib.medusa_lm_head_topk_packed(MEDUSA_BF16, B, H, V, K, topk, _ptr(r, "r", torch.float32, (B, K, H)),
+                                        _ptr(w_packed, "w_packed", torch.uint8),
+                                        _ptr(ids, "topk_ids", torch.int32, (B, K, topk)),
+                                        _ptr(vals, "topk_logits", torch.float32, (B, K, topk)),
+                                        _ptr(logits, "logits", torch.float32, (B, K, V)),
+                                        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_lm_head_topk_packed")
     return dict(topk_ids=ids, topk_logits=vals, logits=logits)
 
 

@@ -455,8 +455,8 @@ __global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, co
 
 namespace medusa_host {
 
-int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, float* logits_or_null,
-                  uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st) {
+int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, int packed,
+                  float* logits_or_null, uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st) {
   using namespace medusa;
   const long long n = static_cast<long long>(B) * K * (H / 8);
   hipLaunchKernelGGL(heads_planes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, B, K, H, r,
@@ -470,8 +470,12 @@ int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void*
   ea.cand_v = cand_v;
   ea.cand_i = cand_i;
   ea.logits = logits_or_null;
-  hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiTopk>), dim3(heads_gemm_lists(V), K), dim3(kBhThreads), 0, st,
-                     2 * B, H, V, planes, static_cast<const uint16_t*>(w_lm), static_cast<float*>(nullptr), ea);
+  if (packed)
+    hipLaunchKernelGGL((base_lm_head_kernel<true, kEpiTopk>), dim3(heads_gemm_lists(V), K), dim3(kBhThreads), 0, st,
+                       2 * B, H, V, planes, static_cast<const uint16_t*>(w_lm), static_cast<float*>(nullptr), ea);
+  else
+    hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiTopk>), dim3(heads_gemm_lists(V), K), dim3(kBhThreads), 0, st,
+                       2 * B, H, V, planes, static_cast<const uint16_t*>(w_lm), static_cast<float*>(nullptr), ea);
   return hip_check("medusa_lm_head_topk gemm launch");
 }
 
@@ -496,6 +500,30 @@ extern "C" int medusa_base_lm_head_pack(int dtype, int H, int V, const void* w_b
                      static_cast<hipStream_t>(stream), H, V, static_cast<const uint16_t*>(w_base),
                      static_cast<uint16_t*>(w_packed), npieces);
   return medusa_host::hip_check("medusa_base_lm_head_pack launch");
+}
+
+extern "C" size_t medusa_heads_packed_bytes(int K, int H, int V) {
+  using namespace medusa;
+  if (K < 1 || K > kMaxHeads) return 0;
+  return static_cast<size_t>(K) * medusa_base_lm_head_packed_bytes(H, V);
+}
+
+extern "C" int medusa_heads_pack(int dtype, int K, int H, int V, const void* w_lm, void* w_packed, void* stream) {
+  using namespace medusa;
+  MEDUSA_REQUIRE(K >= 1 && K <= kMaxHeads, MEDUSA_ERR_SHAPE, "%s: K=%d", __func__, K);
+  MEDUSA_REQUIRE(dtype == MEDUSA_BF16, MEDUSA_ERR_DTYPE, "%s: dtype %d (bf16 only)", __func__, dtype);
+  MEDUSA_REQUIRE(H >= 8 && H <= (1 << 16) && H % 8 == 0, MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE(V >= 1 && V <= (1 << 24), MEDUSA_ERR_SHAPE, "%s: V=%d", __func__, V);
+  MEDUSA_REQUIRE_PTR(w_lm);
+  MEDUSA_REQUIRE_PTR(w_packed);
+  MEDUSA_REQUIRE(w_packed != w_lm, MEDUSA_ERR_ALIAS, "%s: w_packed must not alias w_lm", __func__);
+  const size_t head_in = static_cast<size_t>(V) * H, head_out = medusa_base_lm_head_packed_bytes(H, V) / 2;
+  for (int j = 0; j < K; ++j) {
+    const int rc = medusa_base_lm_head_pack(dtype, H, V, static_cast<const uint16_t*>(w_lm) + j * head_in,
+                                            static_cast<uint16_t*>(w_packed) + j * head_out, stream);
+    if (rc != MEDUSA_OK) return rc;
+  }
+  return MEDUSA_OK;
 }
 
 extern "C" int medusa_base_lm_head(int dtype, int M, int H, int V, const void* hidden, const void* w_base,

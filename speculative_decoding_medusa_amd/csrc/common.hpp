@@ -127,8 +127,8 @@ int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, cons
 // sorted top-k list per (head, sequence, 128-entry vocabulary block) in
 // cand_v / cand_i [K][B][heads_gemm_lists(V)][k].
 inline int heads_gemm_lists(int V) { return (V + 127) / 128; }
-int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, float* logits_or_null,
-                  uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st);
+int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, int packed,
+                  float* logits_or_null, uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st);
 
 // Acceptance from one drawn token per node (posterior.hip; nucleus mode).
 int decide_on_draws(int B, int T, int V, int p_max, int D, const medusa::RowStat* draws,

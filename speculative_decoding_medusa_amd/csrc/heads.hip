@@ -1021,6 +1021,29 @@ int launch_resblock(int dtype, int B, int H, int K, const void* hidden, const vo
   return medusa_host::hip_check("medusa_resblock launch");
 }
 
+// The merge kernel over `lists` published lists of k per (sequence, head).
+int launch_topk_merge(int B, int K, int topk, int lists, const float* cand_v, const int32_t* cand_i, int32_t* ids,
+                      float* vals, hipStream_t st) {
+  const int per = (lists * topk + kMergeThreads - 1) / kMergeThreads;
+  const dim3 mg(B, K), mb(kMergeThreads);
+  if (per <= 1)
+    hipLaunchKernelGGL(topk_merge_kernel<1>, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids, vals);
+  else if (per <= 2)
+    hipLaunchKernelGGL(topk_merge_kernel<2>, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids, vals);
+  else if (per <= 4)
+    hipLaunchKernelGGL(topk_merge_kernel<4>, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids, vals);
+  else if (per <= 8)
+    hipLaunchKernelGGL(topk_merge_kernel<8>, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids, vals);
+  else if (per <= 16)
+    hipLaunchKernelGGL(topk_merge_kernel<16>, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids, vals);
+  else if (per <= kMergeMaxKeys)
+    hipLaunchKernelGGL(topk_merge_kernel<kMergeMaxKeys>, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids,
+                       vals);
+  else
+    hipLaunchKernelGGL(topk_merge_rounds_kernel, mg, mb, 0, st, B, K, topk, lists, cand_v, cand_i, ids, vals);
+  return medusa_host::hip_check("medusa_lm_head_topk merge launch");
+}
+
 int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float* r, const void* w_lm,
                    int32_t* ids, float* vals, float* logits, void* ws, hipStream_t st) {
   LmGrid lg = lm_grid(dtype, B, H, V, K, topk, kMaxWavesPerSimd);
@@ -1032,7 +1055,7 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
   bool fused = false;
   if (lg.gemm) {
     uint16_t* planes = reinterpret_cast<uint16_t*>(base + kCounterBytes + 2 * cb);
-    int rc = medusa_host::heads_lm_gemm(B, H, V, K, topk, r, w_lm, logits, planes, cand_v, cand_i, st);
+    int rc = medusa_host::heads_lm_gemm(B, H, V, K, topk, r, w_lm, 0, logits, planes, cand_v, cand_i, st);
     if (rc != MEDUSA_OK) return rc;
   } else if (lg.diag) {
     const uint16_t* w = static_cast<const uint16_t*>(w_lm);
@@ -1066,24 +1089,7 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
   }
   int rc = medusa_host::hip_check("medusa_lm_head_topk launch");
   if (rc != MEDUSA_OK || fused) return rc;
-  const int per = (lg.lists * topk + kMergeThreads - 1) / kMergeThreads;
-  const dim3 mg(B, K), mb(kMergeThreads);
-  if (per <= 1)
-    hipLaunchKernelGGL(topk_merge_kernel<1>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
-  else if (per <= 2)
-    hipLaunchKernelGGL(topk_merge_kernel<2>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
-  else if (per <= 4)
-    hipLaunchKernelGGL(topk_merge_kernel<4>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
-  else if (per <= 8)
-    hipLaunchKernelGGL(topk_merge_kernel<8>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
-  else if (per <= 16)
-    hipLaunchKernelGGL(topk_merge_kernel<16>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
-  else if (per <= kMergeMaxKeys)
-    hipLaunchKernelGGL(topk_merge_kernel<kMergeMaxKeys>, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids,
-                       vals);
-  else
-    hipLaunchKernelGGL(topk_merge_rounds_kernel, mg, mb, 0, st, B, K, topk, lg.lists, cand_v, cand_i, ids, vals);
-  return medusa_host::hip_check("medusa_lm_head_topk merge launch");
+  return launch_topk_merge(B, K, topk, lg.lists, cand_v, cand_i, ids, vals, st);
 }
 
 // the GEMM path's hi/lo planes of r, [K][2B][H] bf16
@@ -1092,8 +1098,20 @@ size_t planes_bytes(int dtype, int B, int H, int V, int K, int topk) {
   return medusa_host::round_up(static_cast<size_t>(K) * 2 * B * H * 2, 256);
 }
 
+// the skinny-GEMM path as medusa_lm_head_topk_packed takes it at any batch
+size_t gemm_cand_bytes(int B, int V, int K, int topk) {
+  return medusa_host::round_up(static_cast<size_t>(K) * B * medusa_host::heads_gemm_lists(V) * topk * 4, 256);
+}
+size_t gemm_ws_bytes(int B, int H, int V, int K, int topk) {
+  return kCounterBytes + 2 * gemm_cand_bytes(B, V, K, topk) +
+         medusa_host::round_up(static_cast<size_t>(K) * 2 * B * H * 2, 256);
+}
+
 size_t lm_ws_bytes(int dtype, int B, int H, int V, int K, int topk) {
-  return kCounterBytes + 2 * cand_bytes(dtype, B, H, V, K, topk) + planes_bytes(dtype, B, H, V, K, topk);
+  const size_t own = kCounterBytes + 2 * cand_bytes(dtype, B, H, V, K, topk) + planes_bytes(dtype, B, H, V, K, topk);
+  if (dtype != MEDUSA_BF16) return own;
+  const size_t g = gemm_ws_bytes(B, H, V, K, topk);
+  return own > g ? own : g;
 }
 
 }  // namespace
@@ -1129,6 +1147,32 @@ extern "C" int medusa_lm_head_topk(int dtype, int B, int H, int V, int K, int to
                  "%s: workspace %zu < %zu bytes", __func__, ws_bytes, lm_ws_bytes(dtype, B, H, V, K, topk));
   return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws,
                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int medusa_lm_head_topk_packed(int dtype, int B, int H, int V, int K, int topk, const float* r,
+                                          const void* w_lm_packed, int32_t* topk_ids, float* topk_logits,
+                                          float* logits_or_null, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_heads_shape(__func__, dtype, B, H, V, K, topk);
+  if (rc != MEDUSA_OK) return rc;
+  MEDUSA_REQUIRE(dtype == MEDUSA_BF16, MEDUSA_ERR_DTYPE, "%s: packed weights are bf16", __func__);
+  MEDUSA_REQUIRE(H <= (1 << 16), MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE_PTR(r);
+  MEDUSA_REQUIRE_PTR(w_lm_packed);
+  MEDUSA_REQUIRE_PTR(topk_ids);
+  MEDUSA_REQUIRE_PTR(topk_logits);
+  MEDUSA_REQUIRE_PTR(ws);
+  if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
+  MEDUSA_REQUIRE(ws_bytes >= lm_ws_bytes(dtype, B, H, V, K, topk), MEDUSA_ERR_WORKSPACE,
+                 "%s: workspace %zu < %zu bytes", __func__, ws_bytes, lm_ws_bytes(dtype, B, H, V, K, topk));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const size_t cb = gemm_cand_bytes(B, V, K, topk);
+  float* cand_v = reinterpret_cast<float*>(base + kCounterBytes);
+  int32_t* cand_i = reinterpret_cast<int32_t*>(base + kCounterBytes + cb);
+  uint16_t* planes = reinterpret_cast<uint16_t*>(base + kCounterBytes + 2 * cb);
+  rc = medusa_host::heads_lm_gemm(B, H, V, K, topk, r, w_lm_packed, 1, logits_or_null, planes, cand_v, cand_i, st);
+  if (rc != MEDUSA_OK) return rc;
+  return launch_topk_merge(B, K, topk, medusa_host::heads_gemm_lists(V), cand_v, cand_i, topk_ids, topk_logits, st);
 }
 
 extern "C" int medusa_heads(int dtype, int B, int H, int V, int K, int topk, const void* hidden,

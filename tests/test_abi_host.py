@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 103
+    assert L.medusa_abi_version() == 104
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -236,6 +236,25 @@ def test_nucleus_workspace_sizes():
 def test_decoder_piece_validation(call, code):
     assert call() == code
     assert L.medusa_last_error().decode() != ""
+
+
+def test_packed_heads_validation_and_sizes():
+    assert L.medusa_heads_packed_bytes(5, 4096, 32000) == 5 * 2000 * 128 * 1024
+    assert L.medusa_heads_packed_bytes(0, 4096, 32000) == 0
+    assert L.medusa_heads_packed_bytes(9, 4096, 32000) == 0
+    assert L.medusa_heads_pack(1, 0, 64, 100, A, A + 4096, None) == SHAPE
+    assert L.medusa_heads_pack(0, 2, 64, 100, A, A + 4096, None) == DTYPE
+    assert L.medusa_heads_pack(1, 2, 60, 100, A, A + 4096, None) == SHAPE
+    assert L.medusa_heads_pack(1, 2, 64, 100, A, A, None) == ALIAS
+    assert L.medusa_heads_pack(1, 2, 64, 100, None, A, None) == NULL
+    ws = L.medusa_heads_workspace(1, 8, 4096, 32000, 5, 10)
+    call = L.medusa_lm_head_topk_packed
+    assert call(0, 8, 4096, 32000, 5, 10, A, A, A, A, None, A, ws, None) == DTYPE
+    assert call(1, 17, 4096, 32000, 5, 10, A, A, A, A, None, A, ws, None) == SHAPE
+    assert call(1, 8, 4096, 32000, 5, 10, A, None, A, A, None, A, ws, None) == NULL
+    assert call(1, 8, 4096, 32000, 5, 10, A, A, A, A, None, A, 16, None) == WS
+    # the workspace covers the packed call at batch 1 too
+    assert L.medusa_heads_workspace(1, 1, 4096, 32000, 5, 10) >= 256 + 2 * 5 * 250 * 10 * 4 + 5 * 2 * 4096 * 2
 
 
 def test_binding_rejects_cpu_tensors():

@@ -113,3 +113,50 @@ def test_heads_vicuna33b_batch8(gpu_device):
     w = synth.workload("vicuna-33b-b8")
     case = heads_case(w, seed=0)
     _check(case, _run(case, w, keep_logits=False), w)
+
+
+def _run_packed(case, w, keep_logits=True):
+    x = case["inputs"]
+    h, w1, b1, wlm = (to_dev(x[n]) for n in ("hidden", "w1", "b1", "w_lm"))
+    r = md.medusa_resblock(h, w1, b1)
+    packed = md.medusa_heads_pack(wlm)
+    out = md.medusa_lm_head_topk_packed(r, packed, w["V"], w["topk"], keep_logits=keep_logits)
+    out["r"] = r
+    torch.cuda.synchronize()
+    return {k: (to_host(v) if v is not None else None) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("B,H,V,K,k", [
+    (1, 264, 1000, 3, 5),      # batch 1, partial last K chunk
+    (3, 1048, 5003, 2, 7),     # odd V: ragged last vocabulary block
+    (8, 520, 777, 4, 16),
+    (16, 136, 300, 5, 64),     # maximum batch and top-k
+    (1, 8, 64, 1, 64),         # k == V
+])
+def test_heads_packed_bf16(gpu_device, B, H, V, K, k):
+    w = synth.workload("vicuna-7b", B=B, H=H, V=V, K=K, topk=k)
+    case = heads_case(w, seed=B * 5 + K, margin=1e-5, max_retries=400)
+    _check(case, _run_packed(case, w), w)
+
+
+def test_heads_packed_matches_row_major(gpu_device):
+    # packed and row-major weights give identical top-k ids and logits on
+    # the same r (same products, same summation order per output)
+    w = synth.workload("vicuna-7b", B=4, H=1024, V=9000, K=3, topk=10)
+    case = heads_case(w, seed=31)
+    x = case["inputs"]
+    h, w1, b1, wlm = (to_dev(x[n]) for n in ("hidden", "w1", "b1", "w_lm"))
+    r = md.medusa_resblock(h, w1, b1)
+    a = md.medusa_lm_head_topk(r, wlm, 10, keep_logits=True)
+    b = md.medusa_lm_head_topk_packed(r, md.medusa_heads_pack(wlm), 9000, 10, keep_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a["topk_ids"], b["topk_ids"])
+    assert rel_err(to_host(b["topk_logits"]), to_host(a["topk_logits"])) < 1e-6
+    assert rel_err(to_host(b["logits"]), to_host(a["logits"])) < 1e-6
+
+
+@pytest.mark.slow
+def test_heads_packed_vicuna33b_batch8(gpu_device):
+    w = synth.workload("vicuna-33b-b8")
+    case = heads_case(w, seed=0)
+    _check(case, _run_packed(case, w, keep_logits=False), w)
