@@ -139,6 +139,18 @@ int medusa_lm_head_topk_packed(int dtype, int B, int H, int V, int K, int topk,
 size_t medusa_heads_packed_bytes(int K, int H, int V);
 int medusa_heads_pack(int dtype, int K, int H, int V, const void* w_lm, void* w_packed, void* stream);
 
+/* Both stages on packed weights (bf16 only, H <= 65536): w1_packed is
+ * medusa_heads_pack(K, H, V = H) of W1 [K][H][H], w_lm_packed that of
+ * w_lm [K][V][H].  The ResBlock products run on the skinny-GEMM kernel with
+ * the reduction split into slices (float32 partial sums in the workspace),
+ * a second kernel finishes r = h + SiLU(sum + b1) and its bf16 planes, then
+ * the lm_head + top-k as medusa_lm_head_topk_packed.  Same outputs as
+ * medusa_heads; workspace: medusa_heads_workspace() bytes. */
+int medusa_heads_packed(int dtype, int B, int H, int V, int K, int topk, const void* hidden,
+                        const void* w1_packed, const void* b1, const void* w_lm_packed,
+                        int32_t* topk_ids, float* topk_logits, float* logits_or_null, float* r_or_null,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* Both stages.  r_or_null: optional float32 [B][K][H] output of the
  * ResBlocks (kept inside the workspace otherwise). */
 int medusa_heads(int dtype, int B, int H, int V, int K, int topk,

@@ -48,6 +48,7 @@ _SIGS = {
     "medusa_heads": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_lm_head_topk_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_packed_bytes": (_sz, [_i, _i, _i]),
+    "medusa_heads_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_pack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
     "medusa_build_tree": (_i, [_i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp]),
     "medusa_tree_attention_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -175,6 +176,13 @@ def medusa_lm_head_topk(r, w_lm, topk, keep_logits=False, out=None, ws=None):
     return dict(topk_ids=ids, topk_logits=vals, logits=logits)
 
 
+def _check_packed(t, name, K, H, V):
+    need = int(lib.medusa_heads_packed_bytes(K, H, V))
+    if t.dtype != torch.uint8 or t.numel() < need:
+        raise MedusaError(_ERR_SHAPE, name, "expected >= %d packed bytes (uint8), got %s of %d elements"
+                          % (need, t.dtype, t.numel()))
+
+
 def medusa_heads_pack(w_lm):
     """bf16 [K][V][H] head weights -> the packed layout (uint8 tensor)."""
     K, V, H = w_lm.shape
@@ -202,6 +210,7 @@ def medusa_lm_head_topk_packed(r, w_packed, V, topk, keep_logits=False, out=None
         vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
     if keep_logits and logits is None:
         logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    _check_packed(w_packed, "w_packed", K, H, V)
     need = medusa_heads_workspace(MEDUSA_BF16, B, H, V, K, topk)
     if ws is None:
         ws = workspace("heads", dev, need)
@@ -213,6 +222,43 @@ def medusa_lm_head_topk_packed(r, w_packed, V, topk, keep_logits=False, out=None
                                         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_lm_head_topk_packed")
     return dict(topk_ids=ids, topk_logits=vals, logits=logits)
+
+
+def medusa_heads_packed(hidden, w1_packed, b1, w_lm_packed, V, topk, keep_logits=False, keep_r=False, out=None,
+                        ws=None):
+    """Both head stages on packed weights (medusa_heads_pack of W1 with V = H
+    and of w_lm); hidden bf16 [B][H], b1 bf16 [K][H]."""
+    B, H = hidden.shape
+    K = b1.shape[0]
+    dev = hidden.device
+    out = out or {}
+    ids = out.get("topk_ids")
+    vals = out.get("topk_logits")
+    logits = out.get("logits")
+    r = out.get("r")
+    if ids is None:
+        ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    if keep_logits and logits is None:
+        logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    if keep_r and r is None:
+        r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+    _check_packed(w1_packed, "w1_packed", K, H, H)
+    _check_packed(w_lm_packed, "w_lm_packed", K, H, V)
+    need = medusa_heads_workspace(MEDUSA_BF16, B, H, V, K, topk)
+    if ws is None:
+        ws = workspace("heads", dev, need)
+    rc = lib.medusa_heads_packed(MEDUSA_BF16, B, H, V, K, topk, _ptr(hidden, "hidden", torch.bfloat16, (B, H)),
+                                 _ptr(w1_packed, "w1_packed", torch.uint8), _ptr(b1, "b1", torch.bfloat16, (K, H)),
+                                 _ptr(w_lm_packed, "w_lm_packed", torch.uint8),
+                                 _ptr(ids, "topk_ids", torch.int32, (B, K, topk)),
+                                 _ptr(vals, "topk_logits", torch.float32, (B, K, topk)),
+                                 _ptr(logits, "logits", torch.float32, (B, K, V)),
+                                 _ptr(r, "r", torch.float32, (B, K, H)),
+                                 _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_heads_packed")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r)
 
 
 def medusa_heads(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, ws=None):

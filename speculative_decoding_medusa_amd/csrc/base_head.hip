@@ -32,7 +32,6 @@ constexpr int kBhMTile = 64;                          // hidden rows per workgro
 constexpr int kBhKC = 256;                            // K elements per chunk
 constexpr int kBhSteps = kBhKC / 32;                  // MFMA k-steps per chunk
 constexpr int kBhPieces = kBhKC / 8;                  // 16-byte pieces of a row chunk
-constexpr int kBhStage = kBhMTile * kBhPieces / kBhThreads;   // pieces staged per thread
 
 // Packed weights: tile vt (rows 16 vt ..), k step ks (elements 32 ks ..),
 // lane l = 16 g + n -> the 16 bytes W[16 vt + n][32 ks + 8 g .. + 8], zero
@@ -73,8 +72,12 @@ __device__ __forceinline__ u32x4 bh_ld16_stream(const uint16_t* p) {
 //               the hi and lo bf16 planes of the head's float32 inputs, so
 //               logit[b][v] = acc[b][v] + acc[B + b][v]; each workgroup
 //               publishes every row's top-k of its 128 entries as one
-//               sorted list (value desc, id asc) for the heads' merge.
-constexpr int kEpiLogits = 0, kEpiStats = 1, kEpiTopk = 2;
+//               sorted list (value desc, id asc) for the heads' merge;
+//   kEpiPart    the heads' ResBlock products W1[j] . h on packed W1:
+//               grid.y = head, grid.z = a slice of K (split so the grid
+//               fills the chip); every row's float32 partial sums go to
+//               part[z][head][m][v] for heads_res_finish_kernel.
+constexpr int kEpiLogits = 0, kEpiStats = 1, kEpiTopk = 2, kEpiPart = 3;
 
 struct BhEpiArgs {
   // kEpiStats
@@ -88,25 +91,38 @@ struct BhEpiArgs {
   float* cand_v;                // [K][B][gridDim.x][k]
   int32_t* cand_i;
   float* logits;                // optional [B][K][V]
+  // kEpiPart
+  float* part;                  // [gridDim.z][K][M][V]
 };
 
-template <bool PACKED, int EPI>
+// MT: 16-row M blocks per workgroup (the statistics epilogue takes 4; the
+// heads take 1 or 2, enough for their 2B plane rows).
+template <bool PACKED, int EPI, int MT>
 __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, int V,
                                                                   const uint16_t* __restrict__ hidden_all,
                                                                   const uint16_t* __restrict__ w_all,
                                                                   float* __restrict__ logits, BhEpiArgs sa_args) {
-  __shared__ __attribute__((aligned(16))) u32x4 sa[2][kBhMTile * kBhPieces];
-  // kEpiTopk: one head per grid row; its planes and weights
-  const int head = EPI == kEpiTopk ? static_cast<int>(blockIdx.y) : 0;
-  const uint16_t* __restrict__ hidden = hidden_all + static_cast<size_t>(head) * M * H;
+  constexpr int MTILE = 16 * MT;
+  constexpr int STAGE = MTILE * kBhPieces / kBhThreads;   // pieces staged per thread
+  static_assert(MT == 1 || MT == 2 || MT == 4, "M blocks");
+  static_assert(EPI != kEpiStats || MT == 4, "the statistics epilogue assumes 64-row tiles");
+  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MTILE * kBhPieces];
+  // kEpiTopk / kEpiPart: one head per grid row; its weights and (kEpiTopk)
+  // its planes (kEpiPart: every head reads the same hidden rows)
+  constexpr bool PER_HEAD = EPI == kEpiTopk || EPI == kEpiPart;
+  const int head = PER_HEAD ? static_cast<int>(blockIdx.y) : 0;
+  const uint16_t* __restrict__ hidden = hidden_all + (EPI == kEpiTopk ? static_cast<size_t>(head) * M * H : 0);
   const uint16_t* __restrict__ w =
       w_all + static_cast<size_t>(head) *
                   (PACKED ? static_cast<size_t>(bh_vtiles(V)) * bh_ksteps(H) * 512 : static_cast<size_t>(V) * H);
-  const int m0 = EPI == kEpiTopk ? 0 : blockIdx.y * kBhMTile;
+  const int m0 = PER_HEAD ? 0 : blockIdx.y * MTILE;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
+  // this workgroup's chunks [c_begin, c_end) (grid.z > 1: a slice of K)
   const int nch = (H + kBhKC - 1) / kBhKC;
+  const int c_per = (nch + static_cast<int>(gridDim.z) - 1) / static_cast<int>(gridDim.z);
+  const int c_begin = static_cast<int>(blockIdx.z) * c_per, c_end = min(nch, c_begin + c_per);
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
   // this lane's weight row in each tile (rows past V reload row V-1 or the
@@ -130,17 +146,17 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
   };
 
   // staging of the hidden chunk: thread tid moves pieces tid + 256 q
-  auto load_a = [&](int c, u32x4 (&ra)[kBhStage]) {
+  auto load_a = [&](int c, u32x4 (&ra)[STAGE]) {
 #pragma unroll
-    for (int q = 0; q < kBhStage; ++q) {
+    for (int q = 0; q < STAGE; ++q) {
       const int x = q * kBhThreads + tid;
       const int r = x / kBhPieces, p = x % kBhPieces;
       ra[q] = bh_ld16(hidden + static_cast<size_t>(min(m0 + r, M - 1)) * H + min(c * kBhKC + 8 * p, H - 8));
     }
   };
-  auto store_a = [&](int buf, int c, const u32x4 (&ra)[kBhStage]) {
+  auto store_a = [&](int buf, int c, const u32x4 (&ra)[STAGE]) {
 #pragma unroll
-    for (int q = 0; q < kBhStage; ++q) {
+    for (int q = 0; q < STAGE; ++q) {
       const int x = q * kBhThreads + tid;
       const int r = x / kBhPieces, p = x % kBhPieces;
       const bool ok = m0 + r < M && c * kBhKC + 8 * p < H;
@@ -172,26 +188,26 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
       ctok[u] = sa_args.candidates[static_cast<size_t>(b_lo) * Tn + min(u * kBhThreads + tid, npair - 1)];
   }
 
-  f32x4 acc[kBhTiles][4];
+  f32x4 acc[kBhTiles][MT];
 #pragma unroll
   for (int t = 0; t < kBhTiles; ++t)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // chunk c from LDS buffer buf and weight buffer bw; each piece of bw is
   // refilled with chunk cn right after its MFMAs (cn < 0: no refill)
   auto compute = [&](int buf, int c, u32x4 (&bw)[kBhTiles][kBhSteps], int cn) {
 #pragma unroll
     for (int s = 0; s < kBhSteps; ++s) {
-      u32x4 a[4];
+      u32x4 a[MT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = sa[buf][bh_slot(mt * 16 + n, 4 * s + g)];
+      for (int mt = 0; mt < MT; ++mt) a[mt] = sa[buf][bh_slot(mt * 16 + n, 4 * s + g)];
       const bool kin = c * kBhKC + 32 * s + 8 * g < H;   // K tail: the hidden side is zero too
 #pragma unroll
       for (int t = 0; t < kBhTiles; ++t) {
         const u32x4 b = kin ? bw[t][s] : zero;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
           acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[mt]), as_bf16x8(b), acc[t][mt], 0, 0, 0);
       }
       if (cn >= 0) {
@@ -207,16 +223,17 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
   // weights two chunks ahead piece by piece), stage the next hidden chunk,
   // prefetch the one after.  An LDS buffer is rewritten only after the
   // barrier that follows its last reads.
-  u32x4 ra[kBhStage];
+  u32x4 ra[STAGE];
   u32x4 wa[kBhTiles][kBhSteps], wb[kBhTiles][kBhSteps];
-  const int lastc = nch - 1;
-  load_a(0, ra);
-  load_w(0, wa);
-  load_w(min(1, lastc), wb);
-  store_a(0, 0, ra);
-  load_a(min(1, lastc), ra);
-  int c = 0;
-  for (; c + 1 < nch; c += 2) {
+  const int lastc = c_end - 1;
+  if (c_begin < c_end) {   // uniform per workgroup (the host leaves no slice empty)
+  load_a(c_begin, ra);
+  load_w(c_begin, wa);
+  load_w(min(c_begin + 1, lastc), wb);
+  store_a(0, c_begin, ra);
+  load_a(min(c_begin + 1, lastc), ra);
+  int c = c_begin;
+  for (; c + 1 < c_end; c += 2) {
     bh_wait_lds();
     bh_barrier();
     compute(0, c, wa, min(c + 2, lastc));
@@ -228,10 +245,27 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
     store_a(0, c + 2, ra);
     load_a(min(c + 3, lastc), ra);
   }
-  if (c < nch) {
+  if (c < c_end) {
     bh_wait_lds();
     bh_barrier();
     compute(0, c, wa, -1);
+  }
+  }
+
+  if constexpr (EPI == kEpiPart) {
+    float* out = sa_args.part + (static_cast<size_t>(blockIdx.z) * sa_args.K + head) * M * V;
+#pragma unroll
+    for (int t = 0; t < kBhTiles; ++t) {
+      if (vrow[t] >= V) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mt * 16 + 4 * g + i;
+          if (m < M) out[static_cast<size_t>(m) * V + vrow[t]] = acc[t][mt][i];
+        }
+    }
+    return;
   }
 
   if constexpr (EPI == kEpiLogits) {
@@ -240,7 +274,7 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
     for (int t = 0; t < kBhTiles; ++t) {
       if (vrow[t] >= V) continue;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + mt * 16 + 4 * g + i;
@@ -256,11 +290,11 @@ __global__ __launch_bounds__(kBhThreads) void base_lm_head_kernel(int M, int H, 
   bh_barrier();
   constexpr int LD = kBhVBlock + 1;   // padded row
   float* lg = reinterpret_cast<float*>(&sa[0][0]);
-  static_assert(kBhMTile * LD * 4 <= 2 * kBhMTile * kBhPieces * 16, "logit tile fits the LDS buffers");
+  static_assert(MTILE * LD * 4 <= 2 * MTILE * kBhPieces * 16, "logit tile fits the LDS buffers");
 #pragma unroll
   for (int t = 0; t < kBhTiles; ++t)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lg[(mt * 16 + 4 * g + i) * LD + (wave * kBhTiles + t) * 16 + n] = acc[t][mt][i];
 
@@ -433,6 +467,61 @@ __global__ __launch_bounds__(256) void heads_planes_kernel(int B, int K, int H, 
   *reinterpret_cast<u32x4*>(base + static_cast<size_t>(B + b) * H + c) = lo;
 }
 
+// The ResBlock from the split products: u = sum_z part[z][j][b] + b1[j],
+// r[b][j] = h[b] + SiLU(u), written as float32 (optional) and as the hi/lo
+// bf16 planes [K][2B][H] of the heads' lm_head.  Eight elements per thread.
+__global__ __launch_bounds__(256) void heads_res_finish_kernel(int B, int K, int H, int S,
+                                                               const float* __restrict__ part,
+                                                               const uint16_t* __restrict__ hidden,
+                                                               const uint16_t* __restrict__ b1, float* __restrict__ r,
+                                                               uint16_t* __restrict__ planes) {
+  const long long x = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int per = H / 8;
+  if (x >= static_cast<long long>(K) * B * per) return;
+  const int c = static_cast<int>(x % per) * 8;
+  const int b = static_cast<int>((x / per) % B), j = static_cast<int>(x / per / B);
+  const u32x4 bw = *reinterpret_cast<const u32x4*>(b1 + static_cast<size_t>(j) * H + c);
+  const u32x4 hw = *reinterpret_cast<const u32x4*>(hidden + static_cast<size_t>(b) * H + c);
+  float u[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    u[2 * p] = 0.f;
+    u[2 * p + 1] = 0.f;
+  }
+  for (int z = 0; z < S; ++z) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(part + ((static_cast<size_t>(z) * K + j) * B + b) * H + c);
+    const f32x4 lo4 = src[0], hi4 = src[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] += lo4[e];
+      u[4 + e] += hi4[e];
+    }
+  }
+  float v[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float u0 = u[2 * p] + __uint_as_float(bw[p] << 16);
+    const float u1 = u[2 * p + 1] + __uint_as_float(bw[p] & 0xffff0000u);
+    v[2 * p] = __uint_as_float(hw[p] << 16) + u0 / (1.0f + expf(-u0));
+    v[2 * p + 1] = __uint_as_float(hw[p] & 0xffff0000u) + u1 / (1.0f + expf(-u1));
+  }
+  if (r != nullptr) {
+    f32x4* dst = reinterpret_cast<f32x4*>(r + (static_cast<size_t>(b) * K + j) * H + c);
+    dst[0] = f32x4{v[0], v[1], v[2], v[3]};
+    dst[1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+  u32x4 hi, lo;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t h2 = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+    hi[p] = h2;
+    lo[p] = pack_bf16x2(v[2 * p] - __uint_as_float(h2 << 16), v[2 * p + 1] - __uint_as_float(h2 & 0xffff0000u));
+  }
+  uint16_t* base = planes + static_cast<size_t>(j) * 2 * B * H;
+  *reinterpret_cast<u32x4*>(base + static_cast<size_t>(b) * H + c) = hi;
+  *reinterpret_cast<u32x4*>(base + static_cast<size_t>(B + b) * H + c) = lo;
+}
+
 // Row-major weights [V][H] -> the packed layout, one 16-byte piece per
 // thread (zeros past V or H).
 __global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, const uint16_t* __restrict__ w,
@@ -454,15 +543,71 @@ __global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, co
 }  // namespace medusa
 
 namespace medusa_host {
+namespace {
+// One launch of the GEMM with the smallest M tile that holds min(M, 64) rows
+// (a 16- or 32-row tile stages less, skips the empty MFMA blocks and lets
+// more workgroups share a compute unit).
+template <bool PACKED, int EPI>
+void bh_launch(int M, int H, int V, dim3 grid, const uint16_t* hidden, const uint16_t* w, float* logits,
+               const medusa::BhEpiArgs& ea, hipStream_t st) {
+  using namespace medusa;
+  if constexpr (EPI != kEpiStats) {
+    const int rows = EPI == kEpiTopk || EPI == kEpiPart ? M : min(M, kBhMTile);
+    if (rows <= 16) {
+      hipLaunchKernelGGL((base_lm_head_kernel<PACKED, EPI, 1>), grid, dim3(kBhThreads), 0, st, M, H, V, hidden, w,
+                         logits, ea);
+      return;
+    }
+    if (rows <= 32) {
+      hipLaunchKernelGGL((base_lm_head_kernel<PACKED, EPI, 2>), grid, dim3(kBhThreads), 0, st, M, H, V, hidden, w,
+                         logits, ea);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((base_lm_head_kernel<PACKED, EPI, 4>), grid, dim3(kBhThreads), 0, st, M, H, V, hidden, w,
+                     logits, ea);
+}
+int bh_mtile(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : medusa::kBhMTile; }
+}  // namespace
+
+int heads_res_splits(int H, int K) {
+  const int nch = (H + medusa::kBhKC - 1) / medusa::kBhKC;
+  const int wg = heads_gemm_lists(H) * K;
+  int s = (1024 + wg - 1) / wg;   // about four workgroups per compute unit
+  if (s > kHeadsResMaxSplits) s = kHeadsResMaxSplits;
+  if (s > nch) s = nch;
+  const int per = (nch + s - 1) / s;
+  return (nch + per - 1) / per;   // no empty slice
+}
+
+int heads_res_gemm(int B, int H, int K, const uint16_t* hidden, const void* w1_packed, const uint16_t* b1,
+                   float* r_or_null, float* part, uint16_t* planes, hipStream_t st) {
+  using namespace medusa;
+  const int S = heads_res_splits(H, K);
+  BhEpiArgs ea{};
+  ea.B = B;
+  ea.K = K;
+  ea.part = part;
+  bh_launch<true, kEpiPart>(B, H, H, dim3(heads_gemm_lists(H), K, S), hidden, static_cast<const uint16_t*>(w1_packed),
+                            nullptr, ea, st);
+  int rc = hip_check("medusa_heads_packed resblock launch");
+  if (rc != MEDUSA_OK) return rc;
+  const long long n = static_cast<long long>(B) * K * (H / 8);
+  hipLaunchKernelGGL(heads_res_finish_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, B, K, H,
+                     S, part, hidden, b1, r_or_null, planes);
+  return hip_check("medusa_heads_packed resblock finish launch");
+}
 
 int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, int packed,
                   float* logits_or_null, uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st) {
   using namespace medusa;
-  const long long n = static_cast<long long>(B) * K * (H / 8);
-  hipLaunchKernelGGL(heads_planes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, B, K, H, r,
-                     planes);
-  int rc = hip_check("medusa_lm_head_topk planes launch");
-  if (rc != MEDUSA_OK) return rc;
+  if (r != nullptr) {
+    const long long n = static_cast<long long>(B) * K * (H / 8);
+    hipLaunchKernelGGL(heads_planes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, B, K, H,
+                       r, planes);
+    int rc = hip_check("medusa_lm_head_topk planes launch");
+    if (rc != MEDUSA_OK) return rc;
+  }
   BhEpiArgs ea{};
   ea.B = B;
   ea.K = K;
@@ -470,12 +615,12 @@ int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void*
   ea.cand_v = cand_v;
   ea.cand_i = cand_i;
   ea.logits = logits_or_null;
+  // the 2B plane rows of a head fit one tile (B <= 16)
+  const dim3 grid(heads_gemm_lists(V), K);
   if (packed)
-    hipLaunchKernelGGL((base_lm_head_kernel<true, kEpiTopk>), dim3(heads_gemm_lists(V), K), dim3(kBhThreads), 0, st,
-                       2 * B, H, V, planes, static_cast<const uint16_t*>(w_lm), static_cast<float*>(nullptr), ea);
+    bh_launch<true, kEpiTopk>(2 * B, H, V, grid, planes, static_cast<const uint16_t*>(w_lm), nullptr, ea, st);
   else
-    hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiTopk>), dim3(heads_gemm_lists(V), K), dim3(kBhThreads), 0, st,
-                       2 * B, H, V, planes, static_cast<const uint16_t*>(w_lm), static_cast<float*>(nullptr), ea);
+    bh_launch<false, kEpiTopk>(2 * B, H, V, grid, planes, static_cast<const uint16_t*>(w_lm), nullptr, ea, st);
   return hip_check("medusa_lm_head_topk gemm launch");
 }
 
@@ -537,15 +682,16 @@ extern "C" int medusa_base_lm_head(int dtype, int M, int H, int V, const void* h
   MEDUSA_REQUIRE_PTR(w_base);
   MEDUSA_REQUIRE_PTR(logits);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + kBhMTile - 1) / kBhMTile);
+  const int mt = medusa_host::bh_mtile(M);
+  dim3 grid((V + kBhVBlock - 1) / kBhVBlock, (M + mt - 1) / mt);
   BhEpiArgs none{};
   none.T = 1;
+  const auto* h16 = static_cast<const uint16_t*>(hidden);
+  const auto* w16 = static_cast<const uint16_t*>(w_base);
   if (w_packed)
-    hipLaunchKernelGGL((base_lm_head_kernel<true, kEpiLogits>), grid, dim3(kBhThreads), 0, st, M, H, V,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits, none);
+    medusa_host::bh_launch<true, kEpiLogits>(M, H, V, grid, h16, w16, logits, none, st);
   else
-    hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiLogits>), grid, dim3(kBhThreads), 0, st, M, H, V,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base), logits, none);
+    medusa_host::bh_launch<false, kEpiLogits>(M, H, V, grid, h16, w16, logits, none, st);
   return medusa_host::hip_check("medusa_base_lm_head launch");
 }
 
@@ -614,13 +760,11 @@ extern "C" int medusa_base_posterior(int B, int T, int H, int V, int p_max, int 
   args.parts = parts;
   args.child_z = child_z;
   if (w_packed)
-    hipLaunchKernelGGL((base_lm_head_kernel<true, kEpiStats>), grid, dim3(kBhThreads), 0, st, M, H, V,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base),
-                       static_cast<float*>(nullptr), args);
+    medusa_host::bh_launch<true, kEpiStats>(M, H, V, grid, static_cast<const uint16_t*>(hidden),
+                                            static_cast<const uint16_t*>(w_base), nullptr, args, st);
   else
-    hipLaunchKernelGGL((base_lm_head_kernel<false, kEpiStats>), grid, dim3(kBhThreads), 0, st, M, H, V,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_base),
-                       static_cast<float*>(nullptr), args);
+    medusa_host::bh_launch<false, kEpiStats>(M, H, V, grid, static_cast<const uint16_t*>(hidden),
+                                             static_cast<const uint16_t*>(w_base), nullptr, args, st);
   int rc = medusa_host::hip_check("medusa_base_posterior launch");
   if (rc != MEDUSA_OK) return rc;
   return medusa_host::posterior_from_parts(B, T, V, p_max, D, static_cast<int>(grid.x), parts, merged, child_z,

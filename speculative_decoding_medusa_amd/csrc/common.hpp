@@ -126,9 +126,19 @@ int posterior_from_parts(int B, int T, int V, int p_max, int D, int nparts, cons
 // (base_head.hip): r's hi/lo planes into `planes` [K][2B][H], then one
 // sorted top-k list per (head, sequence, 128-entry vocabulary block) in
 // cand_v / cand_i [K][B][heads_gemm_lists(V)][k].
+// r == nullptr: the planes are already in place (heads_res_gemm).
 inline int heads_gemm_lists(int V) { return (V + 127) / 128; }
 int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void* w_lm, int packed,
                   float* logits_or_null, uint16_t* planes, float* cand_v, int32_t* cand_i, hipStream_t st);
+
+// The heads' ResBlock on packed W1 (medusa_heads_pack with V = H) on the same
+// kernel, K split into heads_res_splits(H, K) slices whose float32 partial
+// sums go to `part` [S][K][B][H]; a second kernel adds them up, applies bias,
+// SiLU and the residual and writes r (optional, [B][K][H]) and its planes.
+constexpr int kHeadsResMaxSplits = 8;
+int heads_res_splits(int H, int K);
+int heads_res_gemm(int B, int H, int K, const uint16_t* hidden, const void* w1_packed, const uint16_t* b1,
+                   float* r_or_null, float* part, uint16_t* planes, hipStream_t st);
 
 // Acceptance from one drawn token per node (posterior.hip; nucleus mode).
 int decide_on_draws(int B, int T, int V, int p_max, int D, const medusa::RowStat* draws,

@@ -1114,11 +1114,25 @@ size_t lm_ws_bytes(int dtype, int B, int H, int V, int K, int topk) {
   return own > g ? own : g;
 }
 
+// medusa_heads_packed: the ResBlock's split partial sums, [S][K][B][H] float32
+size_t res_part_bytes(int B, int H, int K) {
+  return medusa_host::round_up(
+      static_cast<size_t>(medusa_host::heads_res_splits(H, K)) * K * B * H * sizeof(float), 256);
+}
+
+// the tail of the workspace: r (medusa_heads) or the partial sums (packed)
+size_t tail_bytes(int dtype, int B, int H, int K) {
+  const size_t rb = r_bytes(B, K, H);
+  if (dtype != MEDUSA_BF16) return rb;
+  const size_t pb = res_part_bytes(B, H, K);
+  return rb > pb ? rb : pb;
+}
+
 }  // namespace
 
 extern "C" size_t medusa_heads_workspace(int dtype, int B, int H, int V, int K, int topk) {
   if (check_heads_shape("medusa_heads_workspace", dtype, B, H, V, K, topk) != MEDUSA_OK) return 0;
-  return lm_ws_bytes(dtype, B, H, V, K, topk) + r_bytes(B, K, H);
+  return lm_ws_bytes(dtype, B, H, V, K, topk) + tail_bytes(dtype, B, H, K);
 }
 
 extern "C" int medusa_resblock(int dtype, int B, int H, int K, const void* hidden, const void* w1,
@@ -1190,7 +1204,7 @@ extern "C" int medusa_heads(int dtype, int B, int H, int V, int K, int topk, con
   MEDUSA_REQUIRE_PTR(ws);
   if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
   if (r_or_null != nullptr) MEDUSA_REQUIRE_PTR(r_or_null);
-  const size_t need = lm_ws_bytes(dtype, B, H, V, K, topk) + r_bytes(B, K, H);
+  const size_t need = lm_ws_bytes(dtype, B, H, V, K, topk) + tail_bytes(dtype, B, H, K);
   MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
                  ws_bytes, need);
   float* r = r_or_null != nullptr
@@ -1200,4 +1214,40 @@ extern "C" int medusa_heads(int dtype, int B, int H, int V, int K, int topk, con
   rc = launch_resblock(dtype, B, H, K, hidden, w1, b1, r, st);
   if (rc != MEDUSA_OK) return rc;
   return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws, st);
+}
+
+extern "C" int medusa_heads_packed(int dtype, int B, int H, int V, int K, int topk, const void* hidden,
+                                   const void* w1_packed, const void* b1, const void* w_lm_packed,
+                                   int32_t* topk_ids, float* topk_logits, float* logits_or_null, float* r_or_null,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_heads_shape(__func__, dtype, B, H, V, K, topk);
+  if (rc != MEDUSA_OK) return rc;
+  MEDUSA_REQUIRE(dtype == MEDUSA_BF16, MEDUSA_ERR_DTYPE, "%s: packed weights are bf16", __func__);
+  MEDUSA_REQUIRE(H <= (1 << 16), MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE_PTR(hidden);
+  MEDUSA_REQUIRE_PTR(w1_packed);
+  MEDUSA_REQUIRE_PTR(b1);
+  MEDUSA_REQUIRE_PTR(w_lm_packed);
+  MEDUSA_REQUIRE_PTR(topk_ids);
+  MEDUSA_REQUIRE_PTR(topk_logits);
+  MEDUSA_REQUIRE_PTR(ws);
+  if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
+  if (r_or_null != nullptr) MEDUSA_REQUIRE_PTR(r_or_null);
+  const size_t lm = lm_ws_bytes(dtype, B, H, V, K, topk), need = lm + tail_bytes(dtype, B, H, K);
+  MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                 need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const size_t cb = gemm_cand_bytes(B, V, K, topk);
+  float* cand_v = reinterpret_cast<float*>(base + kCounterBytes);
+  int32_t* cand_i = reinterpret_cast<int32_t*>(base + kCounterBytes + cb);
+  uint16_t* planes = reinterpret_cast<uint16_t*>(base + kCounterBytes + 2 * cb);
+  float* part = reinterpret_cast<float*>(base + lm);
+  rc = medusa_host::heads_res_gemm(B, H, K, static_cast<const uint16_t*>(hidden), w1_packed,
+                                   static_cast<const uint16_t*>(b1), r_or_null, part, planes, st);
+  if (rc != MEDUSA_OK) return rc;
+  rc = medusa_host::heads_lm_gemm(B, H, V, K, topk, nullptr, w_lm_packed, 1, logits_or_null, planes, cand_v, cand_i,
+                                  st);
+  if (rc != MEDUSA_OK) return rc;
+  return launch_topk_merge(B, K, topk, medusa_host::heads_gemm_lists(V), cand_v, cand_i, topk_ids, topk_logits, st);
 }

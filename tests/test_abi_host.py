@@ -253,6 +253,11 @@ def test_packed_heads_validation_and_sizes():
     assert call(1, 17, 4096, 32000, 5, 10, A, A, A, A, None, A, ws, None) == SHAPE
     assert call(1, 8, 4096, 32000, 5, 10, A, None, A, A, None, A, ws, None) == NULL
     assert call(1, 8, 4096, 32000, 5, 10, A, A, A, A, None, A, 16, None) == WS
+    hp = L.medusa_heads_packed
+    assert hp(0, 8, 4096, 32000, 5, 10, A, A, A, A, A, A, None, None, A, ws, None) == DTYPE
+    assert hp(1, 8, 4096, 32000, 5, 10, A, None, A, A, A, A, None, None, A, ws, None) == NULL
+    assert hp(1, 8, 4096, 32000, 5, 10, A, A, A, A, A, A, None, None, A, 16, None) == WS
+    assert hp(1, 8, 4100, 32000, 5, 10, A, A, A, A, A, A, None, None, A, ws, None) == SHAPE
     # the workspace covers the packed call at batch 1 too
     assert L.medusa_heads_workspace(1, 1, 4096, 32000, 5, 10) >= 256 + 2 * 5 * 250 * 10 * 4 + 5 * 2 * 4096 * 2
 

@@ -160,3 +160,35 @@ def test_heads_packed_vicuna33b_batch8(gpu_device):
     w = synth.workload("vicuna-33b-b8")
     case = heads_case(w, seed=0)
     _check(case, _run_packed(case, w, keep_logits=False), w)
+
+
+def _run_heads_packed(case, w, keep_logits=True):
+    x = case["inputs"]
+    h, w1, b1, wlm = (to_dev(x[n]) for n in ("hidden", "w1", "b1", "w_lm"))
+    out = md.medusa_heads_packed(h, md.medusa_heads_pack(w1), b1, md.medusa_heads_pack(wlm), w["V"], w["topk"],
+                                 keep_logits=keep_logits, keep_r=True)
+    torch.cuda.synchronize()
+    return {k: (to_host(v) if v is not None else None) for k, v in out.items()}
+
+
+# margins: the logit error of the hi/lo planes grows like sqrt(H) (about
+# 4e-6 at H = 2056, 1e-5 at H = 8192), so wide rows take wider gaps
+@pytest.mark.parametrize("B,H,V,K,k,margin", [
+    (1, 264, 1000, 3, 5, 1e-5),       # two chunks: one full, one partial
+    (3, 1048, 5003, 2, 7, 1e-5),      # five chunks in slices, odd V
+    (8, 520, 777, 4, 16, 1e-5),
+    (16, 2056, 3000, 5, 16, 1e-4),    # maximum batch, nine chunks in five slices
+    (2, 8192, 2000, 1, 8, 1e-3),      # 32 chunks: eight slices of four
+    (1, 8, 64, 1, 64, 1e-5),          # k == V, H of one MFMA piece
+])
+def test_heads_packed_both_stages(gpu_device, B, H, V, K, k, margin):
+    w = synth.workload("vicuna-7b", B=B, H=H, V=V, K=K, topk=k)
+    case = heads_case(w, seed=B * 3 + K, margin=margin, max_retries=400)
+    _check(case, _run_heads_packed(case, w), w)
+
+
+@pytest.mark.slow
+def test_heads_packed_both_stages_vicuna33b_batch8(gpu_device):
+    w = synth.workload("vicuna-33b-b8")
+    case = heads_case(w, seed=1)
+    _check(case, _run_heads_packed(case, w, keep_logits=False), w)
