@@ -33,10 +33,40 @@ constexpr int kStages = 8;         // LDS ring depth: up to kStages - 2 chunks i
 constexpr int kSplit = 256;        // target keys per split
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Splits of a (sequence, head): about kSplit keys each, whole chunks.
-__host__ __device__ inline int num_splits(int total_keys) {
-  const int s = total_keys / kSplit;
+// Splits of a (sequence, head): split_keys (a multiple of kChunk, at least
+// kSplit) to twice that many keys each, whole chunks.
+__host__ __device__ inline int num_splits(int total_keys, int split_keys) {
+  const int s = total_keys / split_keys;
   return s < 1 ? 1 : s;
+}
+
+// Keys per split for a launch.  A workgroup's ring fills most of a compute
+// unit's LDS, so one runs per unit and a launch of W workgroups takes
+// ceil(W / 256) rounds; each workgroup costs a fixed part (Q load, ring
+// fill, partial-result write: about 11 us measured on MI355X) plus its K/V
+// bytes at about 38 GB/s per unit.  With every sequence taken at max_slots
+// keys, the number of splits n minimising rounds(n) * (fixed + bytes / n)
+// is chosen and split_keys = max_slots / n (whole chunks, at least kSplit).
+// Long prefixes at batch 1 get one full round of workgroups; many
+// (sequence, head) pairs get one split each.
+inline int attn_split_keys(int B, int Hq, int d, int nqb, int max_slots) {
+  const double kFixedUs = 11.0, kUsPerByte = 1.0 / 38000.0;
+  const long long units = static_cast<long long>(B) * Hq * nqb;
+  const int nmax = num_splits(max_slots, kSplit);
+  int best_s = kSplit;
+  double best = 1e300;
+  for (int n = 1; n <= nmax; ++n) {
+    long long sk = static_cast<long long>(max_slots) / n / kChunk * kChunk;
+    if (sk < kSplit) sk = kSplit;
+    const int ns = num_splits(max_slots, static_cast<int>(sk));
+    const long long rounds = (units * ns + 255) / 256;
+    const double est = static_cast<double>(rounds) * (kFixedUs + kUsPerByte * 4.0 * d * max_slots / ns);
+    if (est < best) {
+      best = est;
+      best_s = static_cast<int>(sk);
+    }
+  }
+  return best_s;
 }
 
 __device__ __forceinline__ u32x4 ld16g(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -240,7 +270,7 @@ __device__ __forceinline__ void ring_barrier() {
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
-    int T, int Hq, int max_slots, int nsplit_max, int nqb,
+    int T, int Hq, int max_slots, int nsplit_max, int split_keys, int nqb,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ prefix_len, const uint8_t* __restrict__ tree_mask, float scale_log2,
     float* __restrict__ part_o, float2* __restrict__ part_ml) {
@@ -258,7 +288,7 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
   if (L > max_slots - T) L = max_slots - T;
   if (L < 0) L = 0;
   const int total = L + T;
-  const int ns = num_splits(total);
+  const int ns = num_splits(total, split_keys);
   if (split >= ns) return;
 
   // whole chunks per split, spread evenly; only a head's last chunk is ragged
@@ -440,7 +470,7 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
 // (never written by this call) are dropped by selects, never multiplied.
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, int Hq, int max_slots, int nsplit_max,
-                                                              const int32_t* __restrict__ prefix_len,
+                                                              int split_keys, const int32_t* __restrict__ prefix_len,
                                                               const float* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml,
                                                               OutT* __restrict__ out) {
@@ -470,7 +500,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
   int L = prefix_len[b];
   if (L > max_slots - T) L = max_slots - T;
   if (L < 0) L = 0;
-  const int ns = num_splits(L + T);
+  const int ns = num_splits(L + T, split_keys);
   for (int s0 = 0; s0 < ns; s0 += U) {
     if (s0 > 0) load(s0, ns);
     float bm = NEG;
@@ -568,11 +598,12 @@ namespace {
 using namespace medusa;
 
 size_t attn_part_o_bytes(int B, int T, int Hq, int d, int max_slots) {
-  const size_t nsm = static_cast<size_t>(num_splits(max_slots));
+  // sized for the shortest splits (every launch uses at most this many)
+  const size_t nsm = static_cast<size_t>(num_splits(max_slots, kSplit));
   return medusa_host::round_up(static_cast<size_t>(B) * Hq * nsm * T * d * 4, 256);
 }
 size_t attn_part_ml_bytes(int B, int T, int Hq, int max_slots) {
-  const size_t nsm = static_cast<size_t>(num_splits(max_slots));
+  const size_t nsm = static_cast<size_t>(num_splits(max_slots, kSplit));
   return medusa_host::round_up(static_cast<size_t>(B) * Hq * nsm * T * 8, 256);
 }
 
@@ -620,18 +651,19 @@ extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int
   const size_t need = attn_part_o_bytes(B, T, Hq, d, max_slots) + attn_part_ml_bytes(B, T, Hq, max_slots);
   MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
                  need);
-  const int nsm = num_splits(max_slots);
   const int nqb = (T + kQBlock - 1) / kQBlock;
+  const int sk = attn_split_keys(B, Hq, d, nqb, max_slots);
+  const int nsm = num_splits(max_slots, sk);
   float* part_o = static_cast<float*>(ws);
   float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + attn_part_o_bytes(B, T, Hq, d, max_slots));
   const float sl2 = scale * kLog2e;
   dim3 grid(nsm, Hq, B * nqb);
   if (d == 128)
-    hipLaunchKernelGGL(tree_attn_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, st, T, Hq, max_slots, nsm, nqb,
+    hipLaunchKernelGGL(tree_attn_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, st, T, Hq, max_slots, nsm, sk, nqb,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                        static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml);
   else
-    hipLaunchKernelGGL(tree_attn_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, st, T, Hq, max_slots, nsm, nqb,
+    hipLaunchKernelGGL(tree_attn_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, st, T, Hq, max_slots, nsm, sk, nqb,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                        static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml);
   rc = medusa_host::hip_check("medusa_tree_attention launch");
@@ -639,9 +671,9 @@ extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int
   const unsigned cgrid = static_cast<unsigned>((B * Hq * T * (d / 4) + 255) / 256);
   if (d == 128)
     hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 128>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
-                       nsm, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
+                       nsm, sk, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
   else
     hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 64>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
-                       nsm, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
+                       nsm, sk, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
   return medusa_host::hip_check("medusa_tree_attention combine launch");
 }

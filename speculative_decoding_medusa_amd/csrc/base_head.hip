@@ -570,10 +570,13 @@ void bh_launch(int M, int H, int V, dim3 grid, const uint16_t* hidden, const uin
 int bh_mtile(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : medusa::kBhMTile; }
 }  // namespace
 
+#ifndef MEDUSA_RES_WG_TARGET
+#define MEDUSA_RES_WG_TARGET 1024   // about four workgroups per compute unit
+#endif
 int heads_res_splits(int H, int K) {
   const int nch = (H + medusa::kBhKC - 1) / medusa::kBhKC;
   const int wg = heads_gemm_lists(H) * K;
-  int s = (1024 + wg - 1) / wg;   // about four workgroups per compute unit
+  int s = (MEDUSA_RES_WG_TARGET + wg - 1) / wg;
   if (s > kHeadsResMaxSplits) s = kHeadsResMaxSplits;
   if (s > nch) s = nch;
   const int per = (nch + s - 1) / s;

@@ -4,7 +4,9 @@ Slots past each sequence's tree hold NaN, so a read beyond L + T shows up as
 NaN in the output.  Cases: the tiny fp32 workload, bf16 shapes that are
 ragged against the 64-key chunk and 256-key split (including L = 0 and a
 prefix shorter than one split), trees larger than one 64-query block, the
-full Vicuna-7B layer at every swept prefix and the Vicuna-33B batch of 8.
+full Vicuna-7B layer at every swept prefix, a batch whose sequences get
+different split counts, and the Vicuna-33B batch of 8 (one long split per
+sequence and head).
 """
 
 import math
@@ -69,6 +71,14 @@ def test_attention_large_trees(gpu_device, counts):
 def test_attention_vicuna7b(gpu_device, L):
     w = synth.workload("vicuna-7b", L=L, S_max=L + 64)
     _run_case(w, seed=0)
+
+
+def test_attention_batch_mixed_split_counts(gpu_device):
+    # four sequences at the 7B layer shape with max_slots 2120: the launch
+    # takes splits of about 1056 keys, so the longest sequences get two
+    # splits (with a ragged last chunk) and the others one
+    w = synth.workload("vicuna-7b", B=4, L=2048, S_max=2120)
+    _run_case(w, seed=2, plen=[2048, 1500, 1999, 610])
 
 
 @pytest.mark.slow
