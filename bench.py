@@ -2,7 +2,8 @@
 
 One step = every stage of the verify step on one HIP stream:
   ResBlock (5 heads, H 4096)  ->  lm_head + top-10 (5 x 32000 x 4096 bf16)
-  -> candidate tree (64 nodes)  ->  tree attention (32 heads x 128, prefix
+  -> candidate tree (64 nodes: built once per tree spec, this step's
+  candidates and positions gathered through it)  ->  tree attention (32 heads x 128, prefix
   2048, one layer; the layer rotates over the 32-layer cache)
   -> typical acceptance (T 0.7, eps 0.09, delta 0.3) over [64][32000] logits
   -> KV commit across 32 layers x 32 heads.
@@ -119,9 +120,11 @@ class Step:
             ("retrieve", (T, K + 1), torch.int32), ("num_paths", (1,), torch.int32),
             ("status", (2,), torch.int32)]}
 
-        # one heads + tree pass to get this step's candidates (planted logits need them)
+        # one heads pass and the tree build (once per tree spec, as the
+        # pages build the tree buffers once per medusa_choices); the planted
+        # logits need this step's candidates
         self.run_heads()
-        self.run_tree()
+        self.run_build_tree()
         torch.cuda.synchronize()
         assert self.tree["status"].cpu().tolist() == [0, -1]
         cand = self.tree["tree_candidates"].cpu().numpy()
@@ -173,6 +176,16 @@ class Step:
         self.run_lm()
 
     def run_tree(self):
+        """The per-step half of the tree: this step's top-k, root tokens and
+        prefix lengths gathered through the tree built at setup."""
+        w, L, t = self.w, self.md.lib, self.tree
+        rc = L.medusa_tree_candidates(w["B"], self.T, w["K"], w["topk"], t["tree_indices"].data_ptr(),
+                                      t["depth"].data_ptr(), self.topk_ids.data_ptr(), self.root.data_ptr(),
+                                      self.plen.data_ptr(), t["tree_candidates"].data_ptr(),
+                                      t["position_ids"].data_ptr(), self.stream)
+        assert rc == 0, rc
+
+    def run_build_tree(self):
         w, L, t = self.w, self.md.lib, self.tree
         rc = L.medusa_build_tree(w["B"], w["K"], w["topk"], self.N, self.choices.data_ptr(),
                                  self.topk_ids.data_ptr(), self.root.data_ptr(), self.plen.data_ptr(),
@@ -211,7 +224,7 @@ class Step:
                                 p["accept_len"].data_ptr(), self.new_plen.data_ptr(), self.stream)
         assert rc == 0, rc
 
-    STAGES = ("resblock", "lm_head_topk", "build_tree", "tree_attention", "posterior", "commit_kv")
+    STAGES = ("resblock", "lm_head_topk", "tree_candidates", "tree_attention", "posterior", "commit_kv")
 
     def run(self, events=None, lm_events=None):
         """One verify step.  events: one per stage boundary (breakdown pass);
@@ -635,9 +648,13 @@ def tree_sweep(args):
             ws_p = torch.zeros(md.medusa_posterior_workspace(B, T, V), dtype=torch.uint8, device=dev)
             new_plen = torch.empty(B, dtype=i32, device=dev)
 
+            run_heads()
+            md.medusa_build_tree(ch, heads["topk_ids"], root, plen, p_max=T, out=tree)   # once per tree
+
             def run_step():
                 run_heads()
-                md.medusa_build_tree(ch, heads["topk_ids"], root, plen, p_max=T, out=tree)
+                md.medusa_tree_candidates(tree["tree_indices"], tree["depth"], heads["topk_ids"], root, plen,
+                                          out=tree)
                 md.medusa_tree_attention(q, kc[0], vc[0], plen, tree["tree_mask"], dh ** -0.5, out=att, ws=ws_a)
                 md.medusa_evaluate_posterior(logits, tree["tree_candidates"], tree["retrieve"], tree["num_paths"],
                                              w["temperature"], w["eps"], w["delta"], out=post, ws=ws_p)
@@ -840,7 +857,10 @@ def main():
                      "bytes_per_launch": lm_bytes(w),
                      "mean_launch_us": round(lm_mean_s * 1e6, 2)},
         "stages": stages,
-        "stages_note": "per-stage means from a separate untimed pass of %d steps" % nb,
+        "stages_note": "per-stage means from a separate untimed pass of %d steps; the tree itself "
+                       "(medusa_build_tree) is built once per tree spec, per step only its candidates "
+                       "and positions are gathered (medusa_tree_candidates)" % nb,
+        "build_tree_us": round(_time_calls(lambda i: step.run_build_tree(), 50), 2),
         "tokens_per_step": acc + 1,
     }
     if not args.no_graph:

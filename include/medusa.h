@@ -195,6 +195,21 @@ int medusa_build_tree(int B, int K, int topk, int n_choices,
                       uint8_t* tree_mask, int32_t* retrieve, int32_t* num_paths,
                       int p_max, int32_t* status, void* stream);
 
+/* The per-step half of the candidate tree.  [API] generate_candidates:
+ * the tree's buffers (mask, tree_indices, retrieve paths, depths) depend
+ * only on medusa_choices and are built once; each step only gathers the new
+ * top-k through tree_indices and offsets the positions.  Given tree_indices
+ * and depth from a medusa_build_tree call on the same spec, K and topk:
+ *   tree_candidates[b][t] = [root_token[b], topk_ids[b][0][..], topk_ids[b][1][..], ...][tree_indices[t]]
+ *   position_ids[b][t]    = prefix_len[b] + depth[t]
+ * exactly the tree_candidates and position_ids medusa_build_tree writes for
+ * these topk_ids, root_token and prefix_len.  An index outside
+ * [0, 1 + K * topk) reads the root token.  int32 throughout; topk_ids
+ * [B][K][topk]; outputs [B][T] must not alias each other or the inputs. */
+int medusa_tree_candidates(int B, int T, int K, int topk, const int32_t* tree_indices, const int32_t* depth,
+                           const int32_t* topk_ids, const int32_t* root_token, const int32_t* prefix_len,
+                           int32_t* tree_candidates, int32_t* position_ids, void* stream);
+
 /* ---------------------------------------------------------------------
  * Tree attention.  [NOTES] 核心要点 (tree attention verifies every
  * candidate in one forward) and 实践案例 案例 3 (ancestor-only mask);

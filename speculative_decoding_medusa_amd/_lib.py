@@ -48,6 +48,7 @@ _SIGS = {
     "medusa_heads": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_lm_head_topk_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_packed_bytes": (_sz, [_i, _i, _i]),
+    "medusa_tree_candidates": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "medusa_heads_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_pack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
     "medusa_build_tree": (_i, [_i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp]),
@@ -320,6 +321,30 @@ def medusa_build_tree(choices, topk_ids, root_token, prefix_len, p_max=None, out
                                _ptr(res["status"], "status", torch.int32, (2,)), _stream(dev))
     _check(rc, "medusa_build_tree")
     return res
+
+
+def medusa_tree_candidates(tree_indices, depth, topk_ids, root_token, prefix_len, out=None):
+    """Per-step gather on a tree built by medusa_build_tree: tree_candidates and
+    position_ids [B][T] for new topk_ids [B][K][topk], root_token, prefix_len [B]."""
+    B, K, topk = topk_ids.shape
+    T = tree_indices.shape[0]
+    dev = topk_ids.device
+    o = out or {}
+    cand = o.get("tree_candidates")
+    pos = o.get("position_ids")
+    if cand is None:
+        cand = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if pos is None:
+        pos = torch.empty((B, T), dtype=torch.int32, device=dev)
+    rc = lib.medusa_tree_candidates(B, T, K, topk, _ptr(tree_indices, "tree_indices", torch.int32, (T,)),
+                                    _ptr(depth, "depth", torch.int32, (T,)),
+                                    _ptr(topk_ids, "topk_ids", torch.int32, (B, K, topk)),
+                                    _ptr(root_token, "root_token", torch.int32, (B,)),
+                                    _ptr(prefix_len, "prefix_len", torch.int32, (B,)),
+                                    _ptr(cand, "tree_candidates", torch.int32, (B, T)),
+                                    _ptr(pos, "position_ids", torch.int32, (B, T)), _stream(dev))
+    _check(rc, "medusa_tree_candidates")
+    return dict(tree_candidates=cand, position_ids=pos)
 
 
 def medusa_tree_attention_workspace(dtype, B, T, Hq, d, max_slots):

@@ -294,7 +294,54 @@ __global__ __launch_bounds__(kTreeThreads) void build_tree_kernel(
   }
 }
 
+// The per-step gather: one thread per (sequence, node).  Node t's token is
+// entry tree_indices[t] of [root, head-1 top-k, head-2 top-k, ...]; indices
+// outside that range read the root.
+__global__ __launch_bounds__(256) void tree_candidates_kernel(int B, int T, int K, int topk,
+                                                              const int32_t* __restrict__ tree_indices,
+                                                              const int32_t* __restrict__ depth,
+                                                              const int32_t* __restrict__ topk_ids,
+                                                              const int32_t* __restrict__ root_token,
+                                                              const int32_t* __restrict__ prefix_len,
+                                                              int32_t* __restrict__ tree_candidates,
+                                                              int32_t* __restrict__ position_ids) {
+  const int x = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+  if (x >= B * T) return;
+  const int b = x / T, t = x - b * T;
+  const int ti = tree_indices[t];
+  const int dp = depth[t];
+  const int root = root_token[b];
+  const int L = prefix_len[b];
+  const bool in = ti >= 1 && ti <= K * topk;
+  const int tok = in ? topk_ids[static_cast<size_t>(b) * K * topk + (ti - 1)] : root;
+  tree_candidates[x] = tok;
+  position_ids[x] = L + dp;
+}
+
 }  // namespace medusa
+
+extern "C" int medusa_tree_candidates(int B, int T, int K, int topk, const int32_t* tree_indices,
+                                      const int32_t* depth, const int32_t* topk_ids, const int32_t* root_token,
+                                      const int32_t* prefix_len, int32_t* tree_candidates, int32_t* position_ids,
+                                      void* stream) {
+  using namespace medusa;
+  MEDUSA_REQUIRE(B >= 1 && B <= kMaxBatch, MEDUSA_ERR_SHAPE, "%s: B=%d", __func__, B);
+  MEDUSA_REQUIRE(T >= 1 && T <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: T=%d", __func__, T);
+  MEDUSA_REQUIRE(K >= 1 && K <= kMaxHeads, MEDUSA_ERR_SHAPE, "%s: K=%d", __func__, K);
+  MEDUSA_REQUIRE(topk >= 1 && topk <= kMaxTopk, MEDUSA_ERR_SHAPE, "%s: topk=%d", __func__, topk);
+  MEDUSA_REQUIRE_PTR(tree_indices);
+  MEDUSA_REQUIRE_PTR(depth);
+  MEDUSA_REQUIRE_PTR(topk_ids);
+  MEDUSA_REQUIRE_PTR(root_token);
+  MEDUSA_REQUIRE_PTR(prefix_len);
+  MEDUSA_REQUIRE_PTR(tree_candidates);
+  MEDUSA_REQUIRE_PTR(position_ids);
+  MEDUSA_REQUIRE(tree_candidates != position_ids, MEDUSA_ERR_ALIAS, "%s: outputs must not alias", __func__);
+  hipLaunchKernelGGL(tree_candidates_kernel, dim3(static_cast<unsigned>((B * T + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), B, T, K, topk, tree_indices, depth, topk_ids, root_token,
+                     prefix_len, tree_candidates, position_ids);
+  return medusa_host::hip_check("medusa_tree_candidates launch");
+}
 
 extern "C" int medusa_build_tree(int B, int K, int topk, int n_choices, const int32_t* choices,
                                  const int32_t* topk_ids, const int32_t* root_token,

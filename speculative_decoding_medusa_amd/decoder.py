@@ -188,11 +188,15 @@ class TinyDecoder:
         out, accepts, paths = [], [], []
         ws = torch.zeros(L.medusa_heads_workspace(L.MEDUSA_BF16, 1, self.H, self.V, K, topk), dtype=torch.uint8,
                          device=self.dev)
+        tree = None
         while len(out) < n_new:
             r = L.medusa_resblock(h_row, heads["w1"], heads["b1"])
             ids = L.medusa_lm_head_topk(r, heads["w_lm"], topk, ws=ws)["topk_ids"]
             plen = self._i32([Lp])
-            tree = L.medusa_build_tree(choices, ids, root, plen)
+            if tree is None:    # the tree's buffers once; each step gathers its candidates
+                tree = L.medusa_build_tree(choices, ids, root, plen)
+            else:
+                L.medusa_tree_candidates(tree["tree_indices"], tree["depth"], ids, root, plen, out=tree)
             hidden, logits = self.forward(tree["tree_candidates"], tree["position_ids"], plen, tree["tree_mask"])
             post = L.medusa_evaluate_posterior(logits, tree["tree_candidates"], tree["retrieve"], tree["num_paths"],
                                                0.0, 0.09, 0.3)
@@ -251,13 +255,16 @@ class TinyDecoder:
                     status=torch.empty(2, dtype=i32, device=dev))
         post = {n: torch.empty(1, dtype=i32, device=dev) for n in ("best_path", "accept_len", "next_token")}
         r = torch.empty((1, K, self.H), dtype=torch.float32, device=dev)
-        topk_out = dict(topk_ids=torch.empty((1, K, topk), dtype=i32, device=dev),
+        topk_out = dict(topk_ids=torch.zeros((1, K, topk), dtype=i32, device=dev),
                         topk_logits=torch.empty((1, K, topk), dtype=torch.float32, device=dev))
+
+        # the tree's buffers once (its candidates are gathered every step)
+        L.medusa_build_tree(choices, topk_out["topk_ids"], root, plen, out=tree)
 
         def step():
             L.medusa_resblock(h_row, heads["w1"], heads["b1"], r=r)
             L.medusa_lm_head_topk(r, heads["w_lm"], topk, out=topk_out, ws=ws)
-            L.medusa_build_tree(choices, topk_out["topk_ids"], root, plen, out=tree)
+            L.medusa_tree_candidates(tree["tree_indices"], tree["depth"], topk_out["topk_ids"], root, plen, out=tree)
             hid, lg = self.forward(tree["tree_candidates"], tree["position_ids"], plen, tree["tree_mask"])
             L.medusa_evaluate_posterior(lg, tree["tree_candidates"], tree["retrieve"], tree["num_paths"], 0.0, 0.09,
                                         0.3, out=post, ws=self.post_ws)

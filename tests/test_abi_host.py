@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 104
+    assert L.medusa_abi_version() == 105
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -260,6 +260,16 @@ def test_packed_heads_validation_and_sizes():
     assert hp(1, 8, 4100, 32000, 5, 10, A, A, A, A, A, A, None, None, A, ws, None) == SHAPE
     # the workspace covers the packed call at batch 1 too
     assert L.medusa_heads_workspace(1, 1, 4096, 32000, 5, 10) >= 256 + 2 * 5 * 250 * 10 * 4 + 5 * 2 * 4096 * 2
+
+
+def test_tree_candidates_validation():
+    tc = L.medusa_tree_candidates
+    assert tc(0, 5, 2, 3, A, A, A, A, A, A, A + 4096, None) == SHAPE
+    assert tc(1, 257, 2, 3, A, A, A, A, A, A, A + 4096, None) == SHAPE
+    assert tc(1, 5, 9, 3, A, A, A, A, A, A, A + 4096, None) == SHAPE
+    assert tc(1, 5, 2, 65, A, A, A, A, A, A, A + 4096, None) == SHAPE
+    assert tc(1, 5, 2, 3, None, A, A, A, A, A, A + 4096, None) == NULL
+    assert tc(1, 5, 2, 3, A, A, A, A, A, A, A, None) == ALIAS
 
 
 def test_binding_rejects_cpu_tensors():

@@ -116,3 +116,44 @@ def test_too_many_paths(gpu_device):
     got = _gpu_tree(ch, ids, np.array([1], np.int32), np.array([0], np.int32), 8)
     assert got["status"].tolist() == [6, 9]
     assert int(got["num_paths"][0]) == 1
+
+
+def _gather(tree, ids, root, plen):
+    out = md.medusa_tree_candidates(tree["tree_indices"], tree["depth"], to_dev(ids), to_dev(root), to_dev(plen))
+    torch.cuda.synchronize()
+    return {k: to_host(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("wl,kw,p_max", [
+    ("tiny-f32", {}, 8),
+    ("vicuna-7b", dict(B=3, L_range=(1, 5000)), 64),
+    ("vicuna-7b", dict(B=16, K=8, topk=64, tree="random", depth_counts=(40, 60, 60, 40, 25, 15, 10, 5)), 256),
+])
+def test_tree_candidates_gather_matches_a_full_build(gpu_device, wl, kw, p_max):
+    # the tree is built once from one step's top-k; later steps' top-k, root
+    # tokens and prefix lengths go through the gather, which must give the
+    # candidates and positions the oracle builds from scratch for them
+    w = synth.workload(wl, **kw)
+    c = tree_case(w, seed=5)
+    tree = md.medusa_build_tree(to_dev(c["choices"]), to_dev(c["topk_ids"]), to_dev(c["root"]),
+                                to_dev(c["prefix_len"]), p_max=p_max)
+    for step in range(1, 4):
+        ids = synth.topk_ids_input(w, seed=5 + 100 * step)
+        root = synth.root_token_input(w, seed=5 + 100 * step)
+        plen = synth.prefix_lengths(w, seed=5 + 100 * step)
+        ref = oracle.build_tree(c["choices"], w["K"], w["topk"], ids, root, plen)
+        got = _gather(tree, ids, root, plen)
+        assert np.array_equal(got["tree_candidates"], ref["tree_candidates"])
+        assert np.array_equal(got["position_ids"], ref["position_ids"])
+
+
+def test_tree_candidates_on_a_spec_error_tree_are_the_root(gpu_device):
+    # a failed build describes the root alone (depth 0, index 0): every node
+    # then gathers the root token at the prefix length
+    ch = np.array([[0, -1], [0, -1]], dtype=np.int32)
+    ids = np.arange(4, dtype=np.int32).reshape(1, 2, 2)
+    tree = md.medusa_build_tree(to_dev(ch), to_dev(ids), to_dev(np.array([7], np.int32)),
+                                to_dev(np.array([3], np.int32)), p_max=8)
+    got = _gather(tree, ids + 10, np.array([9], np.int32), np.array([40], np.int32))
+    assert np.all(got["tree_candidates"] == 9)
+    assert np.all(got["position_ids"] == 40)
