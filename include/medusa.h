@@ -4,7 +4,11 @@
  *
  * One verify step is, in order (every call enqueues on one HIP stream):
  *   medusa_heads               K Medusa heads: ResBlock, lm_head, top-k
- *   medusa_build_tree          candidate tree from a medusa_choices spec
+ *                              (or medusa_heads_packed on weights packed
+ *                              once by medusa_heads_pack: batch > 2)
+ *   medusa_build_tree          candidate tree from a medusa_choices spec,
+ *                              once per spec; then every step
+ *   medusa_tree_candidates     this step's candidates and positions
  *   medusa_tree_attention      tree-masked attention over the KV prefix
  *   medusa_base_lm_head        base lm_head at the tree nodes -> logits
  *                              (or medusa_base_posterior: both fused)
