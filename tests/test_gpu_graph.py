@@ -6,7 +6,10 @@ one attention layer, posterior, commit) captures into a single graph.  The
 graph is replayed several times; between replays eager work poisons every
 output and restores the in-place KV caches, with synchronisations around
 each replay, and every output of every replay must equal the eager step's
-bit for bit (the kernels are deterministic).
+bit for bit (the kernels are deterministic).  Two steps: batch 1 with
+row-major heads and a full tree build, and batch 4 with packed heads (the
+sliced ResBlock GEMM, its finisher, the lm_head GEMM and the merge) and the
+per-step tree gather on a tree built before capture.
 """
 
 import pytest
@@ -16,9 +19,9 @@ import speculative_decoding_medusa_amd as md
 import synth
 
 
-def _setup(dev):
-    g = torch.Generator().manual_seed(11)
-    B, H, V, K, k = 1, 1024, 3000, 3, 4
+def _setup(dev, B=1):
+    g = torch.Generator().manual_seed(11 + B)
+    H, V, K, k = 1024, 3000, 3, 4
     Hq, d, L, NL = 4, 128, 300, 2
     choices = synth.choices_array(synth.random_tree_choices([4, 6, 5], k, seed=1), K)
     T = choices.shape[0] + 1
@@ -30,8 +33,8 @@ def _setup(dev):
         b1=(torch.randn(K, H, generator=g) * 0.02).to(bf).to(dev),
         w_lm=(torch.randn(K, V, H, generator=g) * 0.02).to(bf).to(dev),
         choices=torch.from_numpy(choices).to(dev),
-        root=torch.tensor([5], dtype=torch.int32, device=dev),
-        plen=torch.tensor([L], dtype=torch.int32, device=dev),
+        root=torch.tensor([5 + 7 * b for b in range(B)], dtype=torch.int32, device=dev),
+        plen=torch.tensor([L - 37 * b for b in range(B)], dtype=torch.int32, device=dev),
         q=torch.randn(B, T, Hq, d, generator=g).to(bf).to(dev),
         kc0=torch.randn(NL, B, Hq, S, d, generator=g).to(bf).to(dev),
         vc0=torch.randn(NL, B, Hq, S, d, generator=g).to(bf).to(dev),
@@ -59,15 +62,24 @@ def _setup(dev):
                          device=dev),
         ws_p=torch.zeros(md.medusa_posterior_workspace(B, T, V), dtype=torch.uint8, device=dev),
     )
+    x["w1_packed"] = md.medusa_heads_pack(x["w1"])
+    x["w_lm_packed"] = md.medusa_heads_pack(x["w_lm"])
     return x, o, k, d
 
 
-def _step(x, o, k, d):
-    md.medusa_resblock(x["hidden"], x["w1"], x["b1"], r=o["r"])
-    md.medusa_lm_head_topk(o["r"], x["w_lm"], k, out=o["heads"], ws=o["ws_h"])
+def _step(x, o, k, d, packed=False):
     t = o["tree"]
-    md.medusa_build_tree(x["choices"], o["heads"]["topk_ids"], x["root"], x["plen"], p_max=t["retrieve"].shape[0],
-                         out=t)
+    if packed:
+        o["heads"]["r"] = o["r"]
+        md.medusa_heads_packed(x["hidden"], x["w1_packed"], x["b1"], x["w_lm_packed"], x["w_lm"].shape[1], k,
+                               keep_r=True, out=o["heads"], ws=o["ws_h"])
+        del o["heads"]["r"]
+        md.medusa_tree_candidates(t["tree_indices"], t["depth"], o["heads"]["topk_ids"], x["root"], x["plen"], out=t)
+    else:
+        md.medusa_resblock(x["hidden"], x["w1"], x["b1"], r=o["r"])
+        md.medusa_lm_head_topk(o["r"], x["w_lm"], k, out=o["heads"], ws=o["ws_h"])
+        md.medusa_build_tree(x["choices"], o["heads"]["topk_ids"], x["root"], x["plen"],
+                             p_max=t["retrieve"].shape[0], out=t)
     md.medusa_tree_attention(x["q"], o["kc"][0], o["vc"][0], x["plen"], t["tree_mask"], d ** -0.5, out=o["att"],
                              ws=o["ws_a"])
     md.medusa_evaluate_posterior(x["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], 0.7, 0.09, 0.3,
@@ -76,17 +88,24 @@ def _step(x, o, k, d):
                         new_prefix_len=o["new_plen"])
 
 
-def _outputs(o):
+PER_STEP_TREE = ("tree_candidates", "position_ids")
+
+
+def _outputs(o, gather=False):
+    """Every output of a step (with the per-step gather, the tree's own
+    buffers are inputs built once, so only its candidates and positions)."""
     out = {"r": o["r"], "att": o["att"], "new_plen": o["new_plen"], "kc": o["kc"], "vc": o["vc"]}
     for grp in ("heads", "tree", "post"):
         for n, tns in o[grp].items():
+            if gather and grp == "tree" and n not in PER_STEP_TREE:
+                continue
             out[grp + "." + n] = tns
     return out
 
 
-def _reset(x, o):
+def _reset(x, o, gather=False):
     """Eager work between replays: poison every output, restore the caches."""
-    for n, tns in _outputs(o).items():
+    for n, tns in _outputs(o, gather).items():
         if n in ("kc", "vc"):
             continue
         if tns.dtype.is_floating_point:
@@ -98,26 +117,34 @@ def _reset(x, o):
 
 
 @pytest.mark.gpu
-def test_step_graph_replays_equal_eager(gpu_device):
-    x, o, k, d = _setup(gpu_device)
-    _reset(x, o)
+@pytest.mark.parametrize("B,packed", [(1, False), (4, True)])
+def test_step_graph_replays_equal_eager(gpu_device, B, packed):
+    x, o, k, d = _setup(gpu_device, B)
+    t = o["tree"]
+    if packed:   # the tree's buffers, once, before any step
+        md.medusa_build_tree(x["choices"], o["heads"]["topk_ids"].zero_(), x["root"], x["plen"],
+                             p_max=t["retrieve"].shape[0], out=t)
+        torch.cuda.synchronize()
+        assert t["status"].tolist() == [0, -1]
+    _reset(x, o, packed)
     torch.cuda.synchronize()
-    _step(x, o, k, d)
+    _step(x, o, k, d, packed)
     torch.cuda.synchronize()
-    ref = {n: t.clone() for n, t in _outputs(o).items()}
-    assert int(ref["tree.status"][0]) == 0
+    ref = {n: v.clone() for n, v in _outputs(o, packed).items()}
+    if not packed:
+        assert int(ref["tree.status"][0]) == 0
 
     graph = torch.cuda.CUDAGraph()
-    _reset(x, o)
+    _reset(x, o, packed)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        _step(x, o, k, d)
+        _step(x, o, k, d, packed)
     torch.cuda.synchronize()
 
     for rep in range(4):
-        _reset(x, o)
+        _reset(x, o, packed)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for n, t in _outputs(o).items():
-            assert torch.equal(t, ref[n]), "replay %d: %s differs from the eager step" % (rep, n)
+        for n, v in _outputs(o, packed).items():
+            assert torch.equal(v, ref[n]), "replay %d: %s differs from the eager step" % (rep, n)
