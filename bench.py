@@ -480,13 +480,16 @@ def attention_prefix_sweep(step, steps):
 
 
 def batch8_33b(step, seed, steps):
-    """The Vicuna-33B batch-8 shapes: heads (5 heads, H 6656, V 32000, top-10,
-    eight sequences: one weight stream serves all eight; W1 and lm_head
-    weights packed once, the row-major calls timed beside it) and one tree
-    attention layer (52 heads x 128, per-sequence prefixes drawn in
-    [1024, 4096], the 64-node tree of the 7B step; two layers of KV
-    rotated).  Random device data (timing only); algorithmic bytes over the
-    mean duration of each call."""
+    """A whole verify step at the Vicuna-33B batch-8 shape: heads (5 heads,
+    H 6656, V 32000, top-10, eight sequences: one weight stream serves all
+    eight; W1 and lm_head weights packed once, the row-major calls timed
+    beside it), the per-step tree gather on the 64-node tree of the 7B step,
+    one tree attention layer (52 heads x 128, per-sequence prefixes drawn in
+    [1024, 4096]; two layers of KV rotated), typical acceptance (T 0.7) over
+    [8][64][32000] logits and the commit across a 60-layer cache.  Random
+    device data (timing only; the layers attention does not read are left
+    uninitialised).  Each stage timed alone with HIP events, then the chained
+    step; algorithmic bytes over the mean duration of each call."""
     import numpy as np
     import torch
 
@@ -495,8 +498,9 @@ def batch8_33b(step, seed, steps):
     w = synth.workload("vicuna-33b-b8")
     dev = torch.device("cuda:0")
     B, H, V, K, k, Hq, d = w["B"], w["H"], w["V"], w["K"], w["topk"], w["Hq"], w["d"]
+    n_layers = 60
     gen = torch.Generator(device=dev).manual_seed(seed + 7)
-    bf = torch.bfloat16
+    bf, i32 = torch.bfloat16, torch.int32
     hidden = torch.randn((B, H), generator=gen, device=dev).to(bf)
     w1 = (torch.randn((K, H, H), generator=gen, device=dev) * 0.02).to(bf)
     b1 = (torch.randn((K, H), generator=gen, device=dev) * 0.02).to(bf)
@@ -505,11 +509,11 @@ def batch8_33b(step, seed, steps):
         w_lm[h] = (torch.randn((V, H), generator=gen, device=dev) * 0.02).to(bf)
     ws = torch.zeros(md.medusa_heads_workspace(md.MEDUSA_BF16, B, H, V, K, k), dtype=torch.uint8, device=dev)
     r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
-    topk = dict(topk_ids=torch.empty((B, K, k), dtype=torch.int32, device=dev),
+    topk = dict(topk_ids=torch.empty((B, K, k), dtype=i32, device=dev),
                 topk_logits=torch.empty((B, K, k), dtype=torch.float32, device=dev))
-
     w_packed = md.medusa_heads_pack(w_lm)
     w1_packed = md.medusa_heads_pack(w1)
+    nrep = max(10, steps // 4)
 
     def heads(i):
         md.medusa_heads_packed(hidden, w1_packed, b1, w_packed, V, k, out=topk, ws=ws)
@@ -518,32 +522,80 @@ def batch8_33b(step, seed, steps):
         md.medusa_resblock(hidden, w1, b1, r=r)
         md.medusa_lm_head_topk(r, w_lm, k, out=topk, ws=ws)
 
-    us_heads = _time_calls(heads, max(10, steps // 4))
-    us_heads_rm = _time_calls(heads_row_major, max(10, steps // 4))
+    us_heads_rm = _time_calls(heads_row_major, nrep)
+    del w1, w_lm
     heads_bytes = K * (H * H + H * V + H) * 2 + B * H * 2
-    del w1, w_lm, w_packed, w1_packed
+
+    # the tree (built once from the 7B step's spec) and its per-step gather
     T = step.T
     plen_host = np.asarray(synth.prefix_lengths(w, seed=seed), dtype=np.int32)
     S = int(plen_host.max()) + T + 8
-    nl = 2
-    kc = [torch.randn((B, Hq, S, d), generator=gen, device=dev).to(bf) for _ in range(nl)]
-    vc = [torch.randn((B, Hq, S, d), generator=gen, device=dev).to(bf) for _ in range(nl)]
-    q = torch.randn((B, T, Hq, d), generator=gen, device=dev).to(bf)
-    out = torch.empty_like(q)
     plen = torch.from_numpy(plen_host).to(dev)
+    root = torch.randint(0, V, (B,), generator=gen, device=dev, dtype=i32)
+    heads(0)
+    tree = md.medusa_build_tree(step.choices, topk["topk_ids"], root, plen, p_max=T)
+    torch.cuda.synchronize()
+    assert tree["status"].cpu().tolist() == [0, -1]
+
+    def gather(i):
+        md.medusa_tree_candidates(tree["tree_indices"], tree["depth"], topk["topk_ids"], root, plen, out=tree)
+
+    # 60-layer caches; attention rotates over two initialised layers
+    kc = torch.empty((n_layers, B, Hq, S, d), dtype=bf, device=dev)
+    vc = torch.empty_like(kc)
+    for layer in range(2):
+        kc[layer].normal_(generator=gen)
+        vc[layer].normal_(generator=gen)
+    q = torch.randn((B, T, Hq, d), generator=gen, device=dev).to(bf)
+    att = torch.empty_like(q)
     aws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, B, T, Hq, d, S), dtype=torch.uint8,
                       device=dev)
-    us_att = _time_calls(lambda i: md.medusa_tree_attention(q, kc[i % nl], vc[i % nl], plen, step.tree["tree_mask"],
-                                                            d ** -0.5, out=out, ws=aws), max(10, steps // 4))
+
+    def attention(i):
+        md.medusa_tree_attention(q, kc[i % 2], vc[i % 2], plen, tree["tree_mask"], d ** -0.5, out=att, ws=aws)
+
+    logits = torch.randn((B, T, V), generator=gen, device=dev) * w["logit_std"]
+    post = {n: torch.empty(B, dtype=i32, device=dev) for n in ("best_path", "accept_len", "next_token")}
+    pws = torch.zeros(md.medusa_posterior_workspace(B, T, V), dtype=torch.uint8, device=dev)
+
+    def posterior(i):
+        md.medusa_evaluate_posterior(logits, tree["tree_candidates"], tree["retrieve"], tree["num_paths"],
+                                     w["temperature"], w["eps"], w["delta"], out=post, ws=pws)
+
+    new_plen = torch.empty(B, dtype=i32, device=dev)
+
+    def commit(i):
+        md.medusa_commit_kv(kc, vc, plen, tree["retrieve"], post["best_path"], post["accept_len"],
+                            new_prefix_len=new_plen)
+
+    def whole(i):
+        heads(i)
+        gather(i)
+        attention(i)
+        posterior(i)
+        commit(i)
+
+    us = {name: _time_calls(fn, nrep) for name, fn in (("heads", heads), ("tree_candidates", gather),
+                                                        ("tree_attention", attention), ("posterior", posterior),
+                                                        ("commit_kv", commit))}
+    us_step = _time_calls(whole, nrep)
     att_bytes = int(sum(2 * Hq * (int(L) + T) * d * 2 for L in plen_host)) + B * 2 * T * Hq * d * 2
-    return {"workload": "vicuna-33b batch 8", "B": B, "H": H, "V": V, "K": K, "topk": k, "Hq": Hq, "d": d, "T": T,
-            "prefix_lens": plen_host.tolist(), "unit": "GB/s", "peak": HBM_PEAK_GBS,
-            "heads": {"us": round(us_heads, 2), "bytes": heads_bytes, "achieved": round(heads_bytes / us_heads / 1e3, 1),
-                      "frac": round(heads_bytes / us_heads / 1e3 / HBM_PEAK_GBS, 4), "weights": "packed",
+    del w_packed, w1_packed, kc, vc
+    return {"workload": "vicuna-33b verify step, batch 8", "B": B, "H": H, "V": V, "K": K, "topk": k, "Hq": Hq,
+            "d": d, "T": T, "n_layers": n_layers, "prefix_lens": plen_host.tolist(), "unit": "GB/s",
+            "peak": HBM_PEAK_GBS,
+            "steps_per_s": round(1e6 / us_step, 2), "step_us": round(us_step, 2),
+            "stages_us": {n: round(v, 2) for n, v in us.items()},
+            "heads": {"us": round(us["heads"], 2), "bytes": heads_bytes,
+                      "achieved": round(heads_bytes / us["heads"] / 1e3, 1),
+                      "frac": round(heads_bytes / us["heads"] / 1e3 / HBM_PEAK_GBS, 4), "weights": "packed",
                       "us_row_major_weights": round(us_heads_rm, 2)},
-            "tree_attention": {"us": round(us_att, 2), "bytes": att_bytes,
-                               "achieved": round(att_bytes / us_att / 1e3, 1),
-                               "frac": round(att_bytes / us_att / 1e3 / HBM_PEAK_GBS, 4)}}
+            "tree_attention": {"us": round(us["tree_attention"], 2), "bytes": att_bytes,
+                               "achieved": round(att_bytes / us["tree_attention"] / 1e3, 1),
+                               "frac": round(att_bytes / us["tree_attention"] / 1e3 / HBM_PEAK_GBS, 4)},
+            "note": "each stage timed alone over %d calls, then the chained step over %d; HIP events on the "
+                    "library's stream (a stage of one small kernel timed alone is bound by the host's launch "
+                    "rate through the Python binding)" % (nrep, nrep)}
 
 
 SWEEP_K = (3, 4, 5, 8)
