@@ -480,25 +480,35 @@ def attention_prefix_sweep(step, steps):
 
 
 def batch8_33b(step, seed, steps):
-    """A whole verify step at the Vicuna-33B batch-8 shape: heads (5 heads,
-    H 6656, V 32000, top-10, eight sequences: one weight stream serves all
-    eight; W1 and lm_head weights packed once, the row-major calls timed
-    beside it), the per-step tree gather on the 64-node tree of the 7B step,
-    one tree attention layer (52 heads x 128, per-sequence prefixes drawn in
-    [1024, 4096]; two layers of KV rotated), typical acceptance (T 0.7) over
-    [8][64][32000] logits and the commit across a 60-layer cache.  Random
-    device data (timing only; the layers attention does not read are left
-    uninitialised).  Each stage timed alone with HIP events, then the chained
-    step; algorithmic bytes over the mean duration of each call."""
+    """The whole verify step at the Vicuna-33B batch-8 shape (packed heads)."""
+    return whole_step(step, "vicuna-33b-b8", seed, steps, packed=True)
+
+
+def vicuna13b(step, seed, steps):
+    """The whole verify step at the Vicuna-13B shape, batch 1 (row-major heads)."""
+    return whole_step(step, "vicuna-13b", seed, steps, packed=False)
+
+
+def whole_step(step, wname, seed, steps, packed):
+    """A whole verify step at a named workload's shape: the heads (5 heads,
+    top-10; packed: W1 and lm_head packed once and medusa_heads_packed, the
+    row-major calls timed beside it; else the row-major calls, the packed
+    ones timed beside them), the per-step tree gather on the 64-node tree of
+    the 7B step, one tree attention layer (two layers of KV rotated), typical
+    acceptance (T 0.7) over [B][64][32000] logits and the commit across every
+    layer of the cache.  Random device data (timing only; the layers
+    attention does not read are left uninitialised).  Each stage timed alone
+    with HIP events, then the chained step; algorithmic bytes over the mean
+    duration of each call."""
     import numpy as np
     import torch
 
     import speculative_decoding_medusa_amd as md
     import synth
-    w = synth.workload("vicuna-33b-b8")
+    w = synth.workload(wname)
     dev = torch.device("cuda:0")
     B, H, V, K, k, Hq, d = w["B"], w["H"], w["V"], w["K"], w["topk"], w["Hq"], w["d"]
-    n_layers = 60
+    n_layers = w["n_layers"]
     gen = torch.Generator(device=dev).manual_seed(seed + 7)
     bf, i32 = torch.bfloat16, torch.int32
     hidden = torch.randn((B, H), generator=gen, device=dev).to(bf)
@@ -515,21 +525,21 @@ def batch8_33b(step, seed, steps):
     w1_packed = md.medusa_heads_pack(w1)
     nrep = max(10, steps // 4)
 
-    def heads(i):
+    def heads_packed(i):
         md.medusa_heads_packed(hidden, w1_packed, b1, w_packed, V, k, out=topk, ws=ws)
 
     def heads_row_major(i):
         md.medusa_resblock(hidden, w1, b1, r=r)
         md.medusa_lm_head_topk(r, w_lm, k, out=topk, ws=ws)
 
-    us_heads_rm = _time_calls(heads_row_major, nrep)
-    del w1, w_lm
+    heads, other = (heads_packed, heads_row_major) if packed else (heads_row_major, heads_packed)
+    us_heads_other = _time_calls(other, nrep)
     heads_bytes = K * (H * H + H * V + H) * 2 + B * H * 2
 
     # the tree (built once from the 7B step's spec) and its per-step gather
     T = step.T
     plen_host = np.asarray(synth.prefix_lengths(w, seed=seed), dtype=np.int32)
-    S = int(plen_host.max()) + T + 8
+    S = max(int(plen_host.max()) + T + 8, w["S_max"])
     plen = torch.from_numpy(plen_host).to(dev)
     root = torch.randint(0, V, (B,), generator=gen, device=dev, dtype=i32)
     heads(0)
@@ -580,16 +590,18 @@ def batch8_33b(step, seed, steps):
                                                         ("commit_kv", commit))}
     us_step = _time_calls(whole, nrep)
     att_bytes = int(sum(2 * Hq * (int(L) + T) * d * 2 for L in plen_host)) + B * 2 * T * Hq * d * 2
-    del w_packed, w1_packed, kc, vc
-    return {"workload": "vicuna-33b verify step, batch 8", "B": B, "H": H, "V": V, "K": K, "topk": k, "Hq": Hq,
+    del w1, w_lm, w_packed, w1_packed, kc, vc
+    label = "%s verify step, batch %d" % (wname.split("-b")[0] if wname.endswith("-b8") else wname, B)
+    return {"workload": label, "B": B, "H": H, "V": V, "K": K, "topk": k, "Hq": Hq,
             "d": d, "T": T, "n_layers": n_layers, "prefix_lens": plen_host.tolist(), "unit": "GB/s",
             "peak": HBM_PEAK_GBS,
             "steps_per_s": round(1e6 / us_step, 2), "step_us": round(us_step, 2),
             "stages_us": {n: round(v, 2) for n, v in us.items()},
             "heads": {"us": round(us["heads"], 2), "bytes": heads_bytes,
                       "achieved": round(heads_bytes / us["heads"] / 1e3, 1),
-                      "frac": round(heads_bytes / us["heads"] / 1e3 / HBM_PEAK_GBS, 4), "weights": "packed",
-                      "us_row_major_weights": round(us_heads_rm, 2)},
+                      "frac": round(heads_bytes / us["heads"] / 1e3 / HBM_PEAK_GBS, 4),
+                      "weights": "packed" if packed else "row-major",
+                      ("us_row_major_weights" if packed else "us_packed_weights"): round(us_heads_other, 2)},
             "tree_attention": {"us": round(us["tree_attention"], 2), "bytes": att_bytes,
                                "achieved": round(att_bytes / us["tree_attention"] / 1e3, 1),
                                "frac": round(att_bytes / us["tree_attention"] / 1e3 / HBM_PEAK_GBS, 4)},
@@ -921,6 +933,7 @@ def main():
         result["base_lm_head"] = base_head_timing(step, args.seed, args.steps)
     if not args.no_extra:
         result["attention_prefix_sweep"] = attention_prefix_sweep(step, args.steps)
+        result["vicuna13b"] = vicuna13b(step, args.seed, args.steps)
         result["batch8_33b"] = batch8_33b(step, args.seed, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)

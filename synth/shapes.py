@@ -2,7 +2,8 @@
 
 Each workload is a plain dict of sizes and rule parameters.  The Vicuna
 shapes follow the LLaMA family the pages name (7B: hidden 4096, 32 heads of
-128; 33B: hidden 6656, 52 heads of 128, 60 layers; vocab 32000); K = 5 heads
+128; 13B: hidden 5120, 40 heads of 128, 40 layers; 33B: hidden 6656, 52 heads
+of 128, 60 layers; vocab 32000); K = 5 heads
 is the pages' default head count.
 
 Keys:
@@ -36,6 +37,13 @@ WORKLOADS = {
         wid=1, dtype="bf16", B=1, H=4096, V=32000, K=5, topk=10, tree="random",
         depth_counts=(10, 20, 16, 10, 7), Hq=32, d=128, L=2048,
         L_sweep=(512, 1024, 2048, 4096), n_layers=32, S_max=2048 + 64,
+        logit_std=4.0, planted=True, temperature=0.7, eps=0.09, delta=0.3,
+        h_rms_norm=True,
+    ),
+    # Vicuna-13B verify step (batch 1): hidden 5120, 40 heads of 128, 40 layers.
+    "vicuna-13b": dict(
+        wid=2, dtype="bf16", B=1, H=5120, V=32000, K=5, topk=10, tree="random",
+        depth_counts=(10, 20, 16, 10, 7), Hq=40, d=128, L=2048, n_layers=40, S_max=2048 + 64,
         logit_std=4.0, planted=True, temperature=0.7, eps=0.09, delta=0.3,
         h_rms_norm=True,
     ),

@@ -85,3 +85,9 @@ def test_attention_batch_mixed_split_counts(gpu_device):
 def test_attention_vicuna33b_batch8(gpu_device):
     w = synth.workload("vicuna-33b-b8")
     _run_case(w, seed=0)
+
+
+def test_attention_vicuna13b(gpu_device):
+    # 40 heads x 128 at prefix 2048
+    w = synth.workload("vicuna-13b")
+    _run_case(w, seed=1)

@@ -192,3 +192,10 @@ def test_heads_packed_both_stages_vicuna33b_batch8(gpu_device):
     w = synth.workload("vicuna-33b-b8")
     case = heads_case(w, seed=1)
     _check(case, _run_heads_packed(case, w, keep_logits=False), w)
+
+
+def test_heads_vicuna13b(gpu_device):
+    # H 5120: ten 512-element row steps, the row-diagonal kernels' ragged case
+    w = synth.workload("vicuna-13b")
+    case = heads_case(w, seed=0)
+    _check(case, _run(case, w, keep_logits=False), w)
