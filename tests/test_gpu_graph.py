@@ -70,10 +70,8 @@ def _setup(dev, B=1):
 def _step(x, o, k, d, packed=False):
     t = o["tree"]
     if packed:
-        o["heads"]["r"] = o["r"]
         md.medusa_heads_packed(x["hidden"], x["w1_packed"], x["b1"], x["w_lm_packed"], x["w_lm"].shape[1], k,
-                               keep_r=True, out=o["heads"], ws=o["ws_h"])
-        del o["heads"]["r"]
+                               keep_r=True, out=dict(o["heads"], r=o["r"]), ws=o["ws_h"])
         md.medusa_tree_candidates(t["tree_indices"], t["depth"], o["heads"]["topk_ids"], x["root"], x["plen"], out=t)
     else:
         md.medusa_resblock(x["hidden"], x["w1"], x["b1"], r=o["r"])
