@@ -157,3 +157,20 @@ def test_tree_candidates_on_a_spec_error_tree_are_the_root(gpu_device):
     got = _gather(tree, ids + 10, np.array([9], np.int32), np.array([40], np.int32))
     assert np.all(got["tree_candidates"] == 9)
     assert np.all(got["position_ids"] == 40)
+
+
+def test_tree_candidates_out_of_range_indices_read_the_root(gpu_device):
+    # the header's rule: an index outside [0, 1 + K * topk) reads the root
+    K, k, B = 2, 3, 2
+    ids = (np.arange(B * K * k, dtype=np.int32) + 100).reshape(B, K, k)
+    ti = np.array([0, 1, 6, -5, 7, 1 << 30], dtype=np.int32)
+    depth = np.array([0, 1, 2, 1, 2, 3], dtype=np.int32)
+    root = np.array([7, 8], dtype=np.int32)
+    plen = np.array([10, 20], dtype=np.int32)
+    out = md.medusa_tree_candidates(to_dev(ti), to_dev(depth), to_dev(ids), to_dev(root), to_dev(plen))
+    torch.cuda.synchronize()
+    cand, pos = to_host(out["tree_candidates"]), to_host(out["position_ids"])
+    for b in range(B):
+        flat = [root[b]] + ids[b].ravel().tolist()
+        assert cand[b].tolist() == [flat[0], flat[1], flat[6], root[b], root[b], root[b]]
+        assert pos[b].tolist() == (plen[b] + depth).tolist()
