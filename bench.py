@@ -802,9 +802,28 @@ def generate_bench(args):
 
     ref, t_plain = timed(lambda: dec.greedy(prompt, n))
     ref_g, t_plain_g = timed(lambda: dec.greedy_graph(prompt, n))
-    # hidden states along the plain continuation, for the fitted heads
-    hidden, _ = dec.prefill(prompt + ref[:-1])
+    # hidden states along the plain continuation, for the fitted heads; the
+    # same forward's logits give every step's top-2 gap
+    hidden, logits = dec.prefill(prompt + ref[:-1])
     rows = hidden[0, P - 1:P - 1 + n].float().cpu().numpy().astype(np.float64)
+    zz = logits[0, P - 1:P - 1 + n].float().cpu().numpy()
+    z = np.sort(zz, axis=1)
+    gaps = z[:, -1] - z[:, -2]
+
+    # the activations are bf16, so forwards that sum in different orders (one
+    # token, a 15-node tree, a prefill) agree on a logit only to about 1e-2,
+    # and a continuation can leave another at a near-tie; where one does,
+    # the gap between the two tokens (by the prefill, a third summation
+    # order) is reported
+    def compare(toks):
+        diff = [i for i in range(n) if i >= len(toks) or toks[i] != ref[i]]
+        out = {"equal_to_plain": toks == ref}
+        if diff:
+            i = diff[0]
+            out["first_difference"] = i
+            if i < len(toks):
+                out["logit_gap_there"] = round(float(abs(zz[i, ref[i]] - zz[i, toks[i]])), 5)
+        return out
     fitted = _fit_heads(rows, prompt + ref, P - 1, K, cfg["V"])
 
     def to_bf16(a):
@@ -821,18 +840,22 @@ def generate_bench(args):
                              w_lm=to_bf16(fitted.reshape(K, V, H))),
     }
     res = {"plain": {"tokens_per_s": round(n / t_plain, 1), "ms": round(t_plain * 1e3, 2), "forwards": n},
-           "plain_graph": {"tokens_per_s": round(n / t_plain_g, 1), "ms": round(t_plain_g * 1e3, 2),
-                           "equal_to_plain": ref_g == ref}}
+           "plain_graph": dict({"tokens_per_s": round(n / t_plain_g, 1), "ms": round(t_plain_g * 1e3, 2)},
+                               **compare(ref_g))}
     for name, heads in head_sets.items():
         (toks, accepts, _), t = timed(lambda: dec.medusa(heads, choices, topk, prompt, n))
-        res["medusa_" + name] = {"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2), "steps": len(accepts),
-                                 "tokens_per_step": round(n / len(accepts), 3),
-                                 "speedup_vs_plain": round(t_plain / t, 3), "equal_to_plain": toks == ref}
+        res["medusa_" + name] = dict({"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2),
+                                      "steps": len(accepts), "tokens_per_step": round(n / len(accepts), 3),
+                                      "speedup_vs_plain": round(t_plain / t, 3)}, **compare(toks))
         (toks, steps), t = timed(lambda: dec.medusa_graph(heads, choices, topk, prompt, n))
-        res["medusa_" + name + "_graph"] = {"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2),
-                                            "steps_run": steps, "speedup_vs_plain_graph": round(t_plain_g / t, 3),
-                                            "equal_to_plain": toks == ref}
-    print(json.dumps({"generate": res, "model": dict(cfg), "prompt_len": P, "new_tokens": n, "K": K,
+        res["medusa_" + name + "_graph"] = dict({"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2),
+                                                 "steps_run": steps,
+                                                 "speedup_vs_plain_graph": round(t_plain_g / t, 3)},
+                                                **compare(toks))
+    print(json.dumps({"generate": res, "plain_top2_gap": {"smallest": round(float(gaps.min()), 5),
+                                                         "at_step": int(np.argmin(gaps)),
+                                                         "median": round(float(np.median(gaps)), 5)},
+                      "model": dict(cfg), "prompt_len": P, "new_tokens": n, "K": K,
                       "tree": "full binary, depth 3 (15 nodes)", "timing": "wall clock of whole generate calls, "
                       "median of 3, after one warm-up call", "data": "synthetic random weights"}))
 

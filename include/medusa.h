@@ -352,6 +352,20 @@ int medusa_base_lm_head_pack(int dtype, int H, int V, const void* w_base, void* 
 int medusa_base_lm_head(int dtype, int M, int H, int V, const void* hidden, const void* w_base,
                         int w_packed, float* logits, void* stream);
 
+/* The same product, y[m][v] = x[m] . W[v] (float32 out), for the base
+ * model's other projections (QKV, O, gate/up, down: [API] tree_decoding runs
+ * the whole base model over the tree), whose outputs can be too narrow to
+ * fill the chip: with at most 64 rows and fewer than 128 blocks of 128
+ * outputs, the reduction over H is split into slices (float32 partial sums
+ * [S][M][V] in the workspace, summed by a second kernel in slice order, so
+ * results are deterministic); otherwise it is medusa_base_lm_head.
+ * w_packed: medusa_base_lm_head_pack layout (bf16 only).  Workspace:
+ * medusa_linear_workspace(M, H, V) bytes (256 when no split is taken; no
+ * initialisation); calls sharing it must not overlap. */
+size_t medusa_linear_workspace(int M, int H, int V);
+int medusa_linear(int dtype, int M, int H, int V, const void* x, const void* w_packed, float* y, void* ws,
+                  size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------
  * Base lm_head fused with the acceptance test.  [API] tree_decoding
  * (base logits at every tree node) and evaluate_posterior.

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MEDUSA_BF16, MEDUSA_F32, SPEC_STATUS, EXPORTED, LIB_PATH, MedusaError, lib, workspace,
     medusa_heads_workspace, medusa_resblock, medusa_lm_head_topk, medusa_heads, medusa_build_tree,
     medusa_heads_pack, medusa_lm_head_topk_packed, medusa_heads_packed, medusa_tree_candidates,
+    medusa_linear_workspace, medusa_linear,
     medusa_tree_attention_workspace, medusa_tree_attention, medusa_posterior_workspace,
     medusa_evaluate_posterior, medusa_posterior_nucleus_workspace, medusa_evaluate_posterior_nucleus,
     medusa_commit_kv, medusa_base_lm_head, medusa_base_lm_head_pack,
@@ -23,7 +24,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "MEDUSA_BF16", "MEDUSA_F32", "SPEC_STATUS", "MedusaError", "workspace",
     "medusa_heads_workspace", "medusa_resblock", "medusa_lm_head_topk", "medusa_heads", "medusa_heads_pack",
-    "medusa_lm_head_topk_packed", "medusa_heads_packed", "medusa_tree_candidates",
+    "medusa_lm_head_topk_packed", "medusa_heads_packed", "medusa_tree_candidates", "medusa_linear_workspace",
+    "medusa_linear",
     "medusa_build_tree", "medusa_tree_attention_workspace", "medusa_tree_attention",
     "medusa_posterior_workspace", "medusa_evaluate_posterior", "medusa_posterior_nucleus_workspace",
     "medusa_evaluate_posterior_nucleus", "medusa_commit_kv", "medusa_base_lm_head",

@@ -49,6 +49,8 @@ _SIGS = {
     "medusa_lm_head_topk_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_packed_bytes": (_sz, [_i, _i, _i]),
     "medusa_tree_candidates": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "medusa_linear_workspace": (_sz, [_i, _i, _i]),
+    "medusa_linear": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_pack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
     "medusa_build_tree": (_i, [_i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp]),
@@ -474,6 +476,35 @@ def medusa_base_lm_head_pack(w_base):
                                       _stream(w_base.device))
     _check(rc, "medusa_base_lm_head_pack")
     return packed
+
+
+def medusa_linear_workspace(M, H, V):
+    return int(lib.medusa_linear_workspace(M, H, V))
+
+
+def medusa_linear(x, w_packed, V, out=None, ws=None):
+    """x bf16 [..][H] -> float32 [..][V] on packed weights (medusa_base_lm_head_pack),
+    the reduction split into slices when the output is narrow."""
+    shape = x.shape
+    H = shape[-1]
+    M = 1
+    for s_ in shape[:-1]:
+        M *= s_
+    need = int(lib.medusa_base_lm_head_packed_bytes(H, V))
+    if w_packed.dtype != torch.uint8 or w_packed.numel() != need:
+        raise MedusaError(_ERR_SHAPE, "medusa_linear", "packed weights: expected %d uint8 bytes for H=%d V=%d"
+                          % (need, H, V))
+    dev = x.device
+    if out is None:
+        out = torch.empty(tuple(shape[:-1]) + (V,), dtype=torch.float32, device=dev)
+    nb = medusa_linear_workspace(M, H, V)
+    if ws is None:
+        ws = workspace("linear", dev, nb)
+    rc = lib.medusa_linear(MEDUSA_BF16, M, H, V, _ptr(x, "x", torch.bfloat16), _ptr(w_packed, "w_packed"),
+                           _ptr(out, "y", torch.float32), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                           _stream(dev))
+    _check(rc, "medusa_linear")
+    return out
 
 
 def medusa_base_lm_head(hidden, w_base, logits=None, V=None):

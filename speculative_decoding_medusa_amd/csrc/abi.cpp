@@ -48,4 +48,4 @@ extern "C" const char* medusa_status_string(int status) {
 
 extern "C" const char* medusa_last_error(void) { return g_last_error; }
 
-extern "C" int medusa_abi_version(void) { return 105; }
+extern "C" int medusa_abi_version(void) { return 106; }

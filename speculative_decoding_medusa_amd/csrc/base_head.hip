@@ -522,6 +522,16 @@ __global__ __launch_bounds__(256) void heads_res_finish_kernel(int B, int K, int
   *reinterpret_cast<u32x4*>(base + static_cast<size_t>(B + b) * H + c) = lo;
 }
 
+// y[i] = sum over z of part[z][i], z in order (medusa_linear's split path).
+__global__ __launch_bounds__(256) void linear_reduce_kernel(int S, long long n, const float* __restrict__ part,
+                                                            float* __restrict__ y) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = part[i];
+  for (int z = 1; z < S; ++z) acc += part[static_cast<size_t>(z) * n + i];
+  y[i] = acc;
+}
+
 // Row-major weights [V][H] -> the packed layout, one 16-byte piece per
 // thread (zeros past V or H).
 __global__ __launch_bounds__(256) void base_lm_head_pack_kernel(int H, int V, const uint16_t* __restrict__ w,
@@ -628,6 +638,68 @@ int heads_lm_gemm(int B, int H, int V, int K, int k, const float* r, const void*
 }
 
 }  // namespace medusa_host
+
+namespace {
+// medusa_linear: slices of the reduction when the output alone gives too few
+// workgroups (one M tile of at most 64 rows, fewer than 128 vocabulary
+// blocks): enough slices for about 256 workgroups, at most 16, none empty.
+constexpr int kLinearMaxSplits = 16;
+int linear_splits(int M, int H, int V) {
+  using namespace medusa;
+  const int blocks = (V + kBhVBlock - 1) / kBhVBlock;
+  const int nch = (H + kBhKC - 1) / kBhKC;
+  if (M > kBhMTile || blocks >= 128 || nch < 2) return 1;
+  int s = (256 + blocks - 1) / blocks;
+  if (s > kLinearMaxSplits) s = kLinearMaxSplits;
+  if (s > nch) s = nch;
+  const int per = (nch + s - 1) / s;
+  return (nch + per - 1) / per;
+}
+size_t linear_ws(int M, int H, int V) {
+  const int S = linear_splits(M, H, V);
+  if (S <= 1) return 256;
+  return medusa_host::round_up(static_cast<size_t>(S) * M * V * sizeof(float), 256);
+}
+}  // namespace
+
+extern "C" size_t medusa_linear_workspace(int M, int H, int V) {
+  using namespace medusa;
+  if (M < 1 || M > kMaxBatch * kMaxNodes || H < 8 || H > (1 << 16) || H % 8 != 0 || V < 1 || V > (1 << 24))
+    return 0;
+  return linear_ws(M, H, V);
+}
+
+extern "C" int medusa_linear(int dtype, int M, int H, int V, const void* x, const void* w_packed, float* y, void* ws,
+                             size_t ws_bytes, void* stream) {
+  using namespace medusa;
+  MEDUSA_REQUIRE(dtype == MEDUSA_BF16, MEDUSA_ERR_DTYPE, "%s: dtype %d (bf16 only)", __func__, dtype);
+  MEDUSA_REQUIRE(M >= 1 && M <= kMaxBatch * kMaxNodes, MEDUSA_ERR_SHAPE, "%s: M=%d", __func__, M);
+  MEDUSA_REQUIRE(H >= 8 && H <= (1 << 16) && H % 8 == 0, MEDUSA_ERR_SHAPE, "%s: H=%d", __func__, H);
+  MEDUSA_REQUIRE(V >= 1 && V <= (1 << 24), MEDUSA_ERR_SHAPE, "%s: V=%d", __func__, V);
+  MEDUSA_REQUIRE_PTR(x);
+  MEDUSA_REQUIRE_PTR(w_packed);
+  MEDUSA_REQUIRE_PTR(y);
+  MEDUSA_REQUIRE_PTR(ws);
+  MEDUSA_REQUIRE(ws_bytes >= linear_ws(M, H, V), MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
+                 ws_bytes, linear_ws(M, H, V));
+  const int S = linear_splits(M, H, V);
+  if (S <= 1) return medusa_base_lm_head(dtype, M, H, V, x, w_packed, 1, y, stream);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(ws);
+  BhEpiArgs ea{};
+  ea.B = M;
+  ea.K = 1;
+  ea.part = part;
+  medusa_host::bh_launch<true, kEpiPart>(M, H, V, dim3((V + kBhVBlock - 1) / kBhVBlock, 1, S),
+                                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_packed),
+                                         nullptr, ea, st);
+  int rc = medusa_host::hip_check("medusa_linear launch");
+  if (rc != MEDUSA_OK) return rc;
+  const long long n = static_cast<long long>(M) * V;
+  hipLaunchKernelGGL(linear_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, S, n, part,
+                     y);
+  return medusa_host::hip_check("medusa_linear reduce launch");
+}
 
 extern "C" size_t medusa_base_lm_head_packed_bytes(int H, int V) {
   using namespace medusa;

@@ -5,8 +5,9 @@ This module only sequences library calls and keeps loop bookkeeping
 (prefix lengths, the tokens a step emits); every computation runs in the
 library's kernels.  The base model's layer is the one the C header
 documents beside medusa_embed / medusa_add_rmsnorm / medusa_rope_qkv /
-medusa_silu_mul; its linear layers run on medusa_base_lm_head with weights
-packed once.
+medusa_silu_mul; its linear layers run on medusa_linear (the base lm_head's
+GEMM, its reduction split when the output is narrow) with weights packed
+once.
 
 Medusa greedy decoding ([API] medusa_generate, tree_decoding,
 evaluate_posterior; [NOTES] 核心要点, 学到什么): the heads read the base
@@ -69,6 +70,11 @@ class TinyDecoder:
         self.att_ws = torch.zeros(L.medusa_tree_attention_workspace(L.MEDUSA_BF16, 1, self.tmax, self.heads, self.d,
                                                                     self.S), dtype=torch.uint8, device=dev)
         self.post_ws = torch.zeros(L.medusa_posterior_workspace(1, self.tmax, self.V), dtype=torch.uint8, device=dev)
+        # the projections' split-reduction partials (largest at 64 rows)
+        H, I = self.H, self.I
+        lin = max(L.medusa_linear_workspace(64, hin, vout)
+                  for hin, vout in ((H, 3 * H), (H, H), (H, 2 * I), (I, H), (H, self.V)))
+        self.lin_ws = torch.zeros(lin, dtype=torch.uint8, device=dev)
         # constants of the one-node acceptance test (argmax of one row)
         self._node0 = torch.zeros((1, 1), dtype=torch.int32, device=dev)
         self._npaths1 = torch.ones(1, dtype=torch.int32, device=dev)
@@ -86,17 +92,17 @@ class TinyDecoder:
         y = None
         for l, lw in enumerate(self.layers):
             n = L.medusa_add_rmsnorm(x, lw["attn_norm"], self.eps, y=y)
-            qkv = L.medusa_base_lm_head(n, lw["wqkv"], V=3 * H)
+            qkv = L.medusa_linear(n, lw["wqkv"], 3 * H, ws=self.lin_ws)
             q = L.medusa_rope_qkv(qkv.view(B, T, 3, self.heads, d), positions, prefix_len, self.theta,
                                   self.k_cache[l], self.v_cache[l])
             a = L.medusa_tree_attention(q, self.k_cache[l], self.v_cache[l], prefix_len, tree_mask, d ** -0.5,
                                         ws=self.att_ws)
-            o = L.medusa_base_lm_head(a.view(B, T, H), lw["wo"], V=H)
+            o = L.medusa_linear(a.view(B, T, H), lw["wo"], H, ws=self.lin_ws)
             n = L.medusa_add_rmsnorm(x, lw["mlp_norm"], self.eps, y=o)
-            h = L.medusa_silu_mul(L.medusa_base_lm_head(n, lw["wgu"], V=2 * I))
-            y = L.medusa_base_lm_head(h, lw["wdown"], V=H)
+            h = L.medusa_silu_mul(L.medusa_linear(n, lw["wgu"], 2 * I, ws=self.lin_ws))
+            y = L.medusa_linear(h, lw["wdown"], H, ws=self.lin_ws)
         hidden = L.medusa_add_rmsnorm(x, self.final_norm, self.eps, y=y)
-        return hidden, L.medusa_base_lm_head(hidden, self.lm_head, V=self.V)
+        return hidden, L.medusa_linear(hidden, self.lm_head, self.V, ws=self.lin_ws)
 
     # ------------------------------------------------------------ helpers
     def _i32(self, values, shape=None):

@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 105
+    assert L.medusa_abi_version() == 106
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -270,6 +270,23 @@ def test_tree_candidates_validation():
     assert tc(1, 5, 2, 65, A, A, A, A, A, A, A + 4096, None) == SHAPE
     assert tc(1, 5, 2, 3, None, A, A, A, A, A, A + 4096, None) == NULL
     assert tc(1, 5, 2, 3, A, A, A, A, A, A, A, None) == ALIAS
+
+
+def test_linear_workspace_and_validation():
+    # a narrow output splits its reduction: 8 blocks of 128 outputs over
+    # eleven 256-element chunks -> 11 slices of [M][V] float32
+    assert L.medusa_linear_workspace(1, 2816, 1024) == 11 * 1 * 1024 * 4
+    assert L.medusa_linear_workspace(15, 2816, 1024) >= 11 * 15 * 1024 * 4
+    assert L.medusa_linear_workspace(1, 4096, 32000) == 256      # 250 blocks: no split
+    assert L.medusa_linear_workspace(65, 1024, 1024) == 256      # more than one M tile: no split
+    assert L.medusa_linear_workspace(1, 200, 1024) == 256        # one chunk: nothing to split
+    assert L.medusa_linear_workspace(0, 1024, 1024) == 0
+    assert L.medusa_linear_workspace(1, 1020, 1024) == 0
+    need = L.medusa_linear_workspace(1, 2816, 1024)
+    assert L.medusa_linear(0, 1, 2816, 1024, A, A, A, A, need, None) == DTYPE
+    assert L.medusa_linear(1, 1, 2816, 1024, None, A, A, A, need, None) == NULL
+    assert L.medusa_linear(1, 1, 2816, 1024, A, A, A, A, need - 4, None) == WS
+    assert L.medusa_linear(1, 0, 2816, 1024, A, A, A, A, need, None) == SHAPE
 
 
 def test_binding_rejects_cpu_tensors():

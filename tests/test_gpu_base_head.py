@@ -231,3 +231,24 @@ def test_base_posterior_fused_equals_unfused_greedy(gpu_device, shape):
 def tree_case_ref(w, seed=0):
     from cases import tree_case
     return tree_case(w, seed=seed)["ref"]
+
+
+@pytest.mark.parametrize("M,H,V", [
+    (1, 2816, 1024),    # eleven chunks in eleven slices (the tiny model's down projection)
+    (15, 1024, 3072),   # four slices, a 15-node tree through QKV
+    (32, 1032, 300),    # a partial last chunk in the last slice, ragged V
+    (64, 4096, 5632),   # the widest M that splits
+    (65, 1024, 1024),   # two M tiles: no split
+    (1, 1024, 32000),   # 250 vocabulary blocks: no split
+    (3, 200, 64),       # one chunk: nothing to split
+])
+def test_linear_matches_oracle_and_is_deterministic(gpu_device, M, H, V):
+    h, w = _inputs(M, H, V, seed=3 * M + H + V)
+    print("case", M, H, V, md.medusa_linear_workspace(M, H, V), flush=True)
+    wp = md.medusa_base_lm_head_pack(to_dev(w))
+    x = to_dev(h)
+    a = md.medusa_linear(x, wp, V)
+    b = md.medusa_linear(x, wp, V)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(a), oracle.base_logits(h, w)) < 1e-4
+    assert torch.equal(a, b)
