@@ -447,6 +447,33 @@ def _time_calls(fn, n, warm=3):
     return start.elapsed_time(end) * 1000.0 / n
 
 
+def nucleus_timing(step, seed, steps):
+    """Nucleus (top-p 0.8, temperature 0.7) acceptance over the step's
+    [64][32000] logits and tree: the whole call (one draw per node, then the
+    decision), HIP events around the calls.  The sampling kernel reads the
+    logits in its passes from LDS or registers, so its HBM floor is one read
+    of T x V x 4 bytes."""
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    import synth
+    w = step.w
+    t = step.tree
+    B, T, V = w["B"], step.T, w["V"]
+    u = torch.from_numpy(synth.node_uniforms(w, T, seed=seed)).to(step.dev)
+    out = {n: torch.empty(B, dtype=torch.int32, device=step.dev) for n in ("best_path", "accept_len", "next_token")}
+    ws = torch.zeros(md.medusa_posterior_nucleus_workspace(B, T), dtype=torch.uint8, device=step.dev)
+    us = _time_calls(lambda i: md.medusa_evaluate_posterior_nucleus(step.logits, t["tree_candidates"], t["retrieve"],
+                                                                    t["num_paths"], 0.7, 0.8, u, out=out, ws=ws),
+                     steps)
+    byt = B * T * V * 4
+    return {"us": round(us, 2), "top_p": 0.8, "temperature": 0.7, "bytes": byt,
+            "achieved": round(byt / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(byt / us / 1e3 / HBM_PEAK_GBS, 4),
+            "note": "latency- and LDS-bound: three radix passes over each node's vocabulary on one workgroup "
+                    "per node"}
+
+
 def attention_prefix_sweep(step, steps):
     """Tree attention (64-node tree, 32 heads x 128) at prefixes 512, 1024,
     2048 and 4096, eight layers of KV rotated so no layer sits in the
@@ -955,6 +982,7 @@ def main():
     if not args.no_base_head:
         result["base_lm_head"] = base_head_timing(step, args.seed, args.steps)
     if not args.no_extra:
+        result["nucleus"] = nucleus_timing(step, args.seed, args.steps)
         result["attention_prefix_sweep"] = attention_prefix_sweep(step, args.steps)
         result["vicuna13b"] = vicuna13b(step, args.seed, args.steps)
         result["batch8_33b"] = batch8_33b(step, args.seed, args.steps)
