@@ -228,3 +228,152 @@ def fitted_heads(model, prompt, n, K, scale=8.0, decoy=0.3, seed=0):
     heads = dict(w1=np.zeros((K, H, H), dtype=np.uint16), b1=np.zeros((K, H), dtype=np.uint16),
                  w_lm=synth.bf16_bits(w_lm.astype(np.float32)).reshape(K, V, H))
     return heads, cont[:n]
+
+
+# ------------------------------------------------------------------ typical acceptance near its threshold
+def _chunk_stats(z, chunk):
+    """Per-chunk (max, sum exp(z - max), sum (z - max) exp(z - max)) of one
+    row, each against its own chunk maximum (the kernel's partial sums)."""
+    out = []
+    for lo in range(0, z.shape[0], chunk):
+        c = z[lo:lo + chunk]
+        m = c.max()
+        e = np.exp(c - m)
+        out.append((m, e.sum(), ((c - m) * e).sum()))
+    return out
+
+
+def merged_entropy(z, chunk, drop_shift=False, batch=None, drop_batch_shift=False):
+    """Entropy of softmax(z) assembled from per-chunk partial sums by
+    log-sum-exp merging, `batch` chunks at a time, optionally with a planted
+    mistake: drop_shift leaves out the (m_c - M) * S_c term of each chunk's
+    shifted A, drop_batch_shift the same term of the running sums' rescale
+    between batches.  Used only to show that a case can tell a correct
+    merge from a broken one."""
+    st = _chunk_stats(z, chunk)
+    batch = batch or len(st)
+    m_run, S_run, A_run = -np.inf, 0.0, 0.0
+    for b0 in range(0, len(st), batch):
+        part = st[b0:b0 + batch]
+        mb = max([m_run] + [p[0] for p in part])
+        if m_run != -np.inf:
+            w0 = np.exp(m_run - mb)
+            A_run = w0 * (A_run + (0.0 if drop_batch_shift else (m_run - mb) * S_run))
+            S_run *= w0
+        for m, S, A in part:
+            w = np.exp(m - mb)
+            S_run += w * S
+            A_run += w * (A + (0.0 if drop_shift else (m - mb) * S))
+        m_run = mb
+    return np.log(S_run) - A_run / S_run
+
+
+def _walk(flags_fn, ret, P, D):
+    """Longest leading run of accepted steps per path; lowest-index best."""
+    best, best_len = 0, -1
+    for p in range(P):
+        ell = 0
+        for j in range(1, D):
+            c = int(ret[p, j])
+            if c < 0 or not flags_fn(int(ret[p, j - 1]), c):
+                break
+            ell += 1
+        if ell > best_len:
+            best, best_len = p, ell
+    return best, best_len
+
+
+def typical_threshold_case(w, tcase, temperature=0.7, seed=0, chunk=4096, lo=1.05, hi=3.0, max_retries=30,
+                           require=("shift",)):
+    """Logits [B][T][V] whose typical-acceptance decisions sit close to the
+    threshold: every parent's distribution has its entropy branch binding
+    (delta * exp(-H) < eps), each child's probability is a factor drawn
+    log-uniformly in [lo, hi] above or below its parent's threshold, some
+    accepted children have p < eps, and some parent accepts two siblings.
+    Rows are N(0, 2.1^2) plus a random offset per `chunk`-wide block of the
+    vocabulary, so the mass spreads over blocks whose maxima differ and the
+    entropy depends on every block's shifted partial sums; past 8 blocks,
+    half the rows lift the later blocks so that their maximum comes after
+    the first 8.  Returns the
+    logits, the oracle's verdict and, for each of two planted merge
+    mistakes, how many child decisions flip and whether the step's output
+    changes; the draw is repeated until the output changes under each
+    mistake named in `require`."""
+    ref = tcase["ref"]
+    cand, parent = ref["tree_candidates"], ref["parent"]
+    ret, P = ref["retrieve"], int(ref["num_paths"])
+    D = ret.shape[1]
+    B, T, V = w["B"], int(cand.shape[1]), w["V"]
+    t, eps, delta = float(np.float32(temperature)), float(np.float32(w["eps"])), float(np.float32(w["delta"]))
+    kids = [[c for c in range(1, T) if int(parent[c]) == n] for n in range(T)]
+    for retry in range(max_retries):
+        logits = np.empty((B, T, V), dtype=np.float32)
+        factors = {}
+        for b in range(B):
+            g = synth.rng.stream(seed + 1000 * retry, w["wid"], "logits", b, 7)
+            off = g.uniform(-1.5, 1.5, size=(V + chunk - 1) // chunk)
+            for n in range(T):
+                o = off.copy()
+                if o.shape[0] > 8 and g.random() < 0.5:
+                    o[8:] += 0.7   # the maximum often in a later batch of 8 chunks: the running sums rescale
+                x = g.standard_normal(V) * 2.1 + np.repeat(o, chunk)[:V]
+                z = x / t
+                f = []
+                for c in kids[n]:
+                    up = g.random() < 0.5
+                    r = np.exp(g.uniform(np.log(lo), np.log(hi)))
+                    f.append(r if up else 1.0 / r)
+                for _ in range(60):
+                    m = z.max()
+                    e = np.exp(z - m)
+                    S = e.sum()
+                    H = np.log(S) - ((z - m) * e).sum() / S
+                    thr = min(eps, delta * np.exp(-H))
+                    for c, fc in zip(kids[n], f):
+                        z[int(cand[b, c])] = m + np.log(fc * thr * S)
+                logits[b, n] = (z * t).astype(np.float32)
+                for c, fc in zip(kids[n], f):
+                    factors[(b, c)] = fc
+        # verify on the float32 logits with the oracle's statistics
+        ok = True
+        two = False
+        small = False
+        flips = {"shift": 0, "batch": 0}
+        changed = {"shift": False, "batch": False}
+        exp = oracle.evaluate_posterior(logits, cand, ret, P, temperature, w["eps"], w["delta"])
+        for b in range(B):
+            st = exp["stats"][b]
+            x = logits[b].astype(np.float64)
+            top2 = -np.sort(-x, axis=1)[:, :2]
+            if np.any(top2[:, 0] - top2[:, 1] < 1e-3):
+                ok = False
+            for n in range(T):
+                if not kids[n]:
+                    continue
+                if delta * np.exp(-st["H"][n]) >= eps:
+                    ok = False
+                acc = 0
+                for c in kids[n]:
+                    p = np.exp(st["z"][n, cand[b, c]] - st["m"][n]) / st["S"][n]
+                    ratio = p / st["thr"][n]
+                    if not (lo / 1.01 <= ratio <= hi * 1.01 or 1 / (hi * 1.01) <= ratio <= 1.01 / lo):
+                        ok = False
+                    if ratio > 1:
+                        acc += 1
+                        small = small or p < eps
+                two = two or acc >= 2
+            for name, kw in (("shift", dict(drop_shift=True, batch=8)), ("batch", dict(drop_batch_shift=True, batch=8))):
+                thr_w = np.array([min(eps, delta * np.exp(-merged_entropy(st["z"][n], chunk, **kw)))
+                                  for n in range(T)])
+
+                def flag(n, c, thr_n=None):
+                    p = np.exp(st["z"][n, cand[b, c]] - st["m"][n]) / st["S"][n]
+                    return np.float32(p) > np.float32(thr_n[n] if thr_n is not None else st["thr"][n])
+
+                flips[name] += sum(flag(n, c) != flag(n, c, thr_w) for n in range(T) for c in kids[n])
+                bw, lw = _walk(lambda n, c: flag(n, c, thr_w), ret, P, D)
+                if (bw, lw) != (int(exp["best_path"][b]), int(exp["accept_len"][b])):
+                    changed[name] = True
+        if ok and two and small and all(changed[r] for r in require):
+            return dict(logits=logits, ref=exp, retry=retry, flips=flips, changed=changed, factors=factors)
+    raise RuntimeError("no near-threshold case after %d redraws" % max_retries)

@@ -177,7 +177,12 @@ def _fused(x, ref, w, temperature, packed):
 
 # (workload overrides, generator settings)
 _FUSED_SHAPES = {
-    # the 64-node Vicuna-7B tree, one sequence (H, V cut for the oracle)
+    # the 64-node Vicuna-7B tree, one sequence, at the full 4096 x 32000
+    # lm_head (the shape the fused form is timed at); node logits of std
+    # about 1.3, so at temperature 0.7 the entropy branch sets the
+    # thresholds and decides the unplanted children
+    "vicuna7b-full": (dict(), dict()),
+    # the same tree with H and V cut
     "vicuna7b-tree": (dict(H=1024, V=8000), dict()),
     # 5 sequences of 15 nodes: M = 75, the first 64-row tile holds five
     # sequences, the second a partial one; ragged V (last block 57 wide)

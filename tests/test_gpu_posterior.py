@@ -10,7 +10,7 @@ import torch
 import oracle
 import speculative_decoding_medusa_amd as md
 import synth
-from cases import posterior_case, to_dev, to_host, tree_case
+from cases import posterior_case, to_dev, to_host, tree_case, typical_threshold_case
 
 pytestmark = pytest.mark.gpu
 
@@ -118,3 +118,22 @@ def test_posterior_256_nodes(gpu_device, temperature):
     got = _gpu(pc["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], temperature, w["eps"],
                w["delta"])
     _compare(got, pc["ref"])
+
+
+@pytest.mark.parametrize("V", [32000, 40000])
+@pytest.mark.parametrize("seed", range(3))
+def test_posterior_typical_near_threshold(gpu_device, V, seed):
+    # every child's probability within a factor 1.05-3 of its parent's
+    # threshold, the entropy branch binding, two siblings accepted at some
+    # parent; the vocabulary spans 8 (V 32000) or 10 (V 40000, two batches
+    # of chunk statistics) 4096-entry chunks with different maxima, and the
+    # case is drawn so that dropping the shift term of the chunk merge (or,
+    # at V 40000, of the rescale between batches) changes the output
+    w = synth.workload("vicuna-7b", V=V)
+    tc = tree_case(w, seed=seed)
+    req = ("shift", "batch") if V > 8 * 4096 else ("shift",)
+    c = typical_threshold_case(w, tc, seed=seed, require=req)
+    print("retry", c["retry"], "flips", c["flips"], "accept", c["ref"]["accept_len"], flush=True)
+    t = tc["ref"]
+    got = _gpu(c["logits"], t["tree_candidates"], t["retrieve"], t["num_paths"], 0.7, w["eps"], w["delta"])
+    _compare(got, c["ref"])
