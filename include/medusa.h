@@ -162,6 +162,26 @@ int medusa_heads(int dtype, int B, int H, int V, int K, int topk,
                  int32_t* topk_ids, float* topk_logits, float* logits_or_null,
                  float* r_or_null, void* ws, size_t ws_bytes, void* stream);
 
+/* medusa_heads without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs, kernels and
+ * results as medusa_heads; the workspace is instead a scratch array of
+ * MEDUSA_HEADS_NOALLOC_SCRATCH_BYTES held by the library on each GPU it
+ * runs on until the process ends.  The call itself allocates and frees
+ * nothing.  A shape whose medusa_heads_workspace() exceeds that size
+ * returns MEDUSA_ERR_WORKSPACE (before any HIP call).  The first call on a
+ * device (the current device) looks the array up and enqueues a small
+ * kernel on `stream` that zeroes its arrival counts; a failure there
+ * returns MEDUSA_ERR_HIP.  Every call on one GPU shares that GPU's array
+ * and leaves it holding the last call's lists: calls that overlap on one
+ * GPU (concurrent streams, threads) race and must be serialised by the
+ * caller. */
+#define MEDUSA_HEADS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int medusa_heads_noalloc(int dtype, int B, int H, int V, int K, int topk,
+                         const void* hidden, const void* w1, const void* b1, const void* w_lm,
+                         int32_t* topk_ids, float* topk_logits, float* logits_or_null,
+                         float* r_or_null, void* stream);
+
 /* ---------------------------------------------------------------------
  * Candidate tree.  [API] medusa_generate (medusa_choices),
  * generate_candidates (tree_indices, retrieve_indices), tree_decoding

@@ -46,6 +46,7 @@ _SIGS = {
     "medusa_resblock": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "medusa_lm_head_topk": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "medusa_heads_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "medusa_lm_head_topk_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_packed_bytes": (_sz, [_i, _i, _i]),
     "medusa_tree_candidates": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -124,8 +125,13 @@ _WS = {}
 
 
 def workspace(kind, device, nbytes):
-    """A cached workspace of at least ``nbytes`` bytes (one per kind and device)."""
-    key = (kind, torch.device(device).index)
+    """A cached workspace of at least ``nbytes`` bytes, one per kind, device
+    and stream: calls that share a workspace must not overlap, and calls on
+    different streams may, so each stream gets its own.  (Two threads
+    issuing calls on the same stream still share one; pass ``ws`` to keep
+    them apart.)"""
+    dev = torch.device(device)
+    key = (kind, dev.index, torch.cuda.current_stream(dev).cuda_stream)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -282,6 +288,38 @@ def medusa_heads(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, ws
                           _ptr(vals, "topk_logits"), _ptr(logits, "logits"), _ptr(r, "r"),
                           _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_heads")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r)
+
+
+def medusa_heads_noalloc(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, out=None):
+    """medusa_heads on the library's per-GPU scratch (no workspace).  Outputs
+    come from ``out`` (topk_ids, topk_logits and optionally logits, r) or are
+    allocated here; the C call itself allocates nothing."""
+    dt = _dtype_code(hidden)
+    B, H = hidden.shape
+    K, V = w_lm.shape[0], w_lm.shape[1]
+    dev = hidden.device
+    o = out or {}
+    ids = o.get("topk_ids")
+    vals = o.get("topk_logits")
+    logits = o.get("logits")
+    r = o.get("r")
+    if ids is None:
+        ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    if logits is None and keep_logits:
+        logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    if r is None and keep_r:
+        r = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+    rc = lib.medusa_heads_noalloc(dt, B, H, V, K, topk, _ptr(hidden, "hidden"),
+                                  _ptr(w1, "w1", hidden.dtype, (K, H, H)), _ptr(b1, "b1", hidden.dtype, (K, H)),
+                                  _ptr(w_lm, "w_lm", hidden.dtype, (K, V, H)),
+                                  _ptr(ids, "topk_ids", torch.int32, (B, K, topk)),
+                                  _ptr(vals, "topk_logits", torch.float32, (B, K, topk)),
+                                  _ptr(logits, "logits", torch.float32, (B, K, V)),
+                                  _ptr(r, "r", torch.float32, (B, K, H)), _stream(dev))
+    _check(rc, "medusa_heads_noalloc")
     return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r)
 
 

@@ -23,6 +23,8 @@
 // r enters the lm_head as hi = bf16(r) and lo = bf16(r - hi), both against
 // the exact bf16 weights with float32 sums: about 16 significant bits of r
 // instead of 8.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace medusa {
@@ -1189,31 +1191,58 @@ extern "C" int medusa_lm_head_topk_packed(int dtype, int B, int H, int V, int K,
   return launch_topk_merge(B, K, topk, medusa_host::heads_gemm_lists(V), cand_v, cand_i, topk_ids, topk_logits, st);
 }
 
+namespace {
+
+// Both stages of medusa_heads on a validated workspace of at least
+// lm_ws_bytes + tail_bytes bytes.
+int run_heads(int dtype, int B, int H, int V, int K, int topk, const void* hidden, const void* w1, const void* b1,
+              const void* w_lm, int32_t* topk_ids, float* topk_logits, float* logits_or_null, float* r_or_null,
+              void* ws, hipStream_t st) {
+  float* r = r_or_null != nullptr
+                 ? r_or_null
+                 : reinterpret_cast<float*>(static_cast<char*>(ws) + lm_ws_bytes(dtype, B, H, V, K, topk));
+  int rc = launch_resblock(dtype, B, H, K, hidden, w1, b1, r, st);
+  if (rc != MEDUSA_OK) return rc;
+  return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws, st);
+}
+
+int check_heads_args(const char* fn, int dtype, int B, int H, int V, int K, int topk, const void* hidden,
+                     const void* w1, const void* b1, const void* w_lm, const int32_t* topk_ids,
+                     const float* topk_logits, const float* logits_or_null, const float* r_or_null) {
+  int rc = check_heads_shape(fn, dtype, B, H, V, K, topk);
+  if (rc != MEDUSA_OK) return rc;
+#define MEDUSA_ARG_PTR(p)                                                                   \
+  do {                                                                                     \
+    MEDUSA_REQUIRE((p) != nullptr, MEDUSA_ERR_NULL, "%s: %s is NULL", fn, #p);             \
+    MEDUSA_REQUIRE(medusa_host::aligned16(p), MEDUSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+  MEDUSA_ARG_PTR(hidden);
+  MEDUSA_ARG_PTR(w1);
+  MEDUSA_ARG_PTR(b1);
+  MEDUSA_ARG_PTR(w_lm);
+  MEDUSA_ARG_PTR(topk_ids);
+  MEDUSA_ARG_PTR(topk_logits);
+  if (logits_or_null != nullptr) MEDUSA_ARG_PTR(logits_or_null);
+  if (r_or_null != nullptr) MEDUSA_ARG_PTR(r_or_null);
+#undef MEDUSA_ARG_PTR
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
 extern "C" int medusa_heads(int dtype, int B, int H, int V, int K, int topk, const void* hidden,
                             const void* w1, const void* b1, const void* w_lm, int32_t* topk_ids,
                             float* topk_logits, float* logits_or_null, float* r_or_null, void* ws,
                             size_t ws_bytes, void* stream) {
-  int rc = check_heads_shape(__func__, dtype, B, H, V, K, topk);
+  int rc = check_heads_args(__func__, dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits,
+                            logits_or_null, r_or_null);
   if (rc != MEDUSA_OK) return rc;
-  MEDUSA_REQUIRE_PTR(hidden);
-  MEDUSA_REQUIRE_PTR(w1);
-  MEDUSA_REQUIRE_PTR(b1);
-  MEDUSA_REQUIRE_PTR(w_lm);
-  MEDUSA_REQUIRE_PTR(topk_ids);
-  MEDUSA_REQUIRE_PTR(topk_logits);
   MEDUSA_REQUIRE_PTR(ws);
-  if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
-  if (r_or_null != nullptr) MEDUSA_REQUIRE_PTR(r_or_null);
   const size_t need = lm_ws_bytes(dtype, B, H, V, K, topk) + tail_bytes(dtype, B, H, K);
   MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
                  ws_bytes, need);
-  float* r = r_or_null != nullptr
-                 ? r_or_null
-                 : reinterpret_cast<float*>(static_cast<char*>(ws) + lm_ws_bytes(dtype, B, H, V, K, topk));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = launch_resblock(dtype, B, H, K, hidden, w1, b1, r, st);
-  if (rc != MEDUSA_OK) return rc;
-  return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws, st);
+  return run_heads(dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits, logits_or_null, r_or_null,
+                   ws, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int medusa_heads_packed(int dtype, int B, int H, int V, int K, int topk, const void* hidden,
@@ -1250,4 +1279,78 @@ extern "C" int medusa_heads_packed(int dtype, int B, int H, int V, int K, int to
                                   st);
   if (rc != MEDUSA_OK) return rc;
   return launch_topk_merge(B, K, topk, medusa_host::heads_gemm_lists(V), cand_v, cand_i, topk_ids, topk_logits, st);
+}
+
+// ---------------------------------------------------------------- medusa_heads_noalloc
+// medusa_heads for callers that cannot allocate (code under graph capture,
+// tight serving loops): the workspace is one file-scope device array per
+// GPU instead of a caller buffer.  In host code the array's name is only a
+// stand-in; its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept, and only that
+// address is ever handed to a kernel.
+
+namespace {
+constexpr size_t kHeadsScratchBytes = MEDUSA_HEADS_NOALLOC_SCRATCH_BYTES;   // per GPU
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kHeadsScratchBytes];
+
+namespace {
+
+// The arrival counts at the head of the scratch start at zero.
+__global__ __launch_bounds__(64) void scratch_clear_kernel(uint32_t* p, int n) {
+  if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+// Device address of this GPU's scratch.  The first call on a device looks
+// it up (with that device current) and clears the arrival counts with a
+// fill kernel on `st`; every later call on the device reuses the address.
+int heads_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    medusa_host::set_error("medusa_heads_noalloc: no usable current device (%s, device %d)",
+                           hipGetErrorString(e), dev);
+    return MEDUSA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      medusa_host::set_error("medusa_heads_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+      return MEDUSA_ERR_HIP;
+    }
+    hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(64), 0, st, static_cast<uint32_t*>(p),
+                       static_cast<int>(kCounterBytes / 4));
+    const int rc = medusa_host::hip_check("medusa_heads_noalloc scratch clear");
+    if (rc != MEDUSA_OK) return rc;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" int medusa_heads_noalloc(int dtype, int B, int H, int V, int K, int topk, const void* hidden,
+                                    const void* w1, const void* b1, const void* w_lm, int32_t* topk_ids,
+                                    float* topk_logits, float* logits_or_null, float* r_or_null, void* stream) {
+  int rc = check_heads_args(__func__, dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits,
+                            logits_or_null, r_or_null);
+  if (rc != MEDUSA_OK) return rc;
+  const size_t need = lm_ws_bytes(dtype, B, H, V, K, topk) + tail_bytes(dtype, B, H, K);
+  MEDUSA_REQUIRE(need <= kHeadsScratchBytes, MEDUSA_ERR_WORKSPACE,
+                 "%s: this shape needs %zu bytes of scratch, more than the %zu bytes held per GPU", __func__, need,
+                 kHeadsScratchBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  rc = heads_scratch(st, &ws);
+  if (rc != MEDUSA_OK) return rc;
+  return run_heads(dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits, logits_or_null, r_or_null,
+                   ws, st);
 }

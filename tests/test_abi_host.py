@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 106
+    assert L.medusa_abi_version() == 107
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -53,6 +53,33 @@ def heads(dt=1, B=1, H=64, V=100, K=2, k=4, hidden=A, w1=A, b1=A, wlm=A, ids=A, 
 def test_heads_validation(kw, code):
     assert heads(**kw) == code
     assert L.medusa_last_error().decode() != ""
+
+
+def heads_noalloc(dt=1, B=1, H=64, V=100, K=2, k=4, hidden=A, w1=A, b1=A, wlm=A, ids=A, vals=A, logits=None,
+                  r=None):
+    return L.medusa_heads_noalloc(dt, B, H, V, K, k, hidden, w1, b1, wlm, ids, vals, logits, r, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE), (dict(B=17), SHAPE), (dict(K=9), SHAPE), (dict(k=65), SHAPE), (dict(hidden=None), NULL),
+    (dict(ids=None), NULL), (dict(w1=MIS), ALIGN), (dict(r=MIS), ALIGN),
+    # a shape whose workspace exceeds the library's per-GPU scratch
+    (dict(B=16, H=8192, V=1 << 20, K=8, k=64), WS),
+])
+def test_heads_noalloc_validation(kw, code):
+    assert heads_noalloc(**kw) == code
+    assert L.medusa_last_error().decode() != ""
+
+
+def test_heads_noalloc_scratch_limit_is_stated():
+    # the header's MEDUSA_HEADS_NOALLOC_SCRATCH_BYTES: 16 MiB; the Vicuna-7B
+    # and Vicuna-33B batch-8 head shapes fit, the rejected case above does not
+    src = open(HEADER).read()
+    assert "#define MEDUSA_HEADS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in src
+    lim = 16 << 20
+    assert md.medusa_heads_workspace(1, 1, 4096, 32000, 5, 10) <= lim
+    assert md.medusa_heads_workspace(1, 8, 6656, 32000, 5, 10) <= lim
+    assert md.medusa_heads_workspace(1, 16, 8192, 1 << 20, 8, 64) > lim
 
 
 def test_heads_workspace_sizes():
