@@ -1,24 +1,28 @@
 // Tree attention on gfx950: T tree queries against a KV prefix plus the
 // ancestor-only mask among the tree's own keys.
 //
-// bf16 path.  The key range [0, L+T) of each (sequence, head) is cut into
-// num_splits splits of whole 32-key chunks, one workgroup each.  A workgroup
-// holds up to 64 queries in two groups of four waves (16 queries a wave);
-// the groups take alternate chunks of the split.  K and V chunks go from HBM
-// straight into an eight-stage LDS ring with 16-byte direct-to-LDS loads (up
-// to six chunks in flight), so the stream needs no registers and no LDS
-// stores; rows are kept whole and the 16-byte pieces within a row are
-// XOR-swizzled by row so the MFMA operand reads are free of bank conflicts.
-// Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_16x16x32_bf16: a lane then holds four consecutive keys of one
-// query, which is the B-operand layout P^T needs for O^T += V^T P^T, so
-// probabilities never leave registers.  The V^T operand is read from the
-// row-major V chunk with the LDS transpose read (ds_read_b64_tr_b16).
-// Online softmax in base 2, fp32 accumulators.  The second group hands its
-// (O, m, l) to the first through LDS; each split writes (O unnormalised, m,
-// l) and a second kernel merges the splits (log-sum-exp).  Every global load
-// is unconditional with a clamped index (masked at use), so no load waits
-// behind a branch.
+// bf16 path, one kernel.  The key range [0, L+T) of each (sequence, head) is
+// cut into splits of whole 32-key chunks, one workgroup per (split, 64-query
+// block).  A workgroup is eight waves: two halves of the query block (32
+// queries, two 16-query MFMA tiles each) times four key groups.  Chunks go
+// in rounds of four, one per key group, so every chunk is read from LDS by
+// the two waves of its group only, and the four groups work unsynchronised
+// within a round.  K and V chunks (and the block's Q) go from HBM straight
+// into LDS with 16-byte direct-to-LDS loads: a ring of two rounds (eight
+// chunks) in flight, no staging registers, no LDS stores; rows are kept
+// whole with their 16-byte pieces XOR-swizzled by row, so the MFMA operand
+// reads are free of bank conflicts.  Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: a lane then holds four
+// consecutive keys of one query, which is the B-operand layout P^T needs for
+// O^T += V^T P^T, so probabilities never leave registers; each K and V
+// operand read serves both query tiles of the wave.  The V^T operand comes
+// from the row-major V chunk through the LDS transpose read
+// (ds_read_b64_tr_b16).  Online softmax in base 2 with fp32 accumulators and
+// a lazily raised reference.  After the last round the four key groups'
+// states are merged through LDS.  A sequence with one split writes its
+// output directly; otherwise each split writes its partial (O unnormalised,
+// m, l) and a second kernel merges the splits (log-sum-exp) and writes the
+// output.
 //
 // f32 path: one wave per (sequence, head, query), online softmax over
 // 64-key chunks on the VALU.
@@ -26,50 +30,49 @@
 
 namespace medusa {
 
-constexpr int kAttnThreads = 512;   // two groups of four waves
+constexpr int kAttnThreads = 512;  // eight waves: two query halves x four key groups
 constexpr int kQBlock = 64;        // queries per workgroup
 constexpr int kChunk = 32;         // keys per LDS stage
-constexpr int kStages = 8;         // LDS ring depth: up to kStages - 2 chunks in flight
-constexpr int kSplit = 256;        // target keys per split
+constexpr int kGroups = 4;         // key groups = chunks per round
+constexpr int kStages = 2 * kGroups;   // LDS ring: two rounds
+constexpr int kEarly = 2;          // chunks issued together with Q
+constexpr int kMinSplitKeys = 128; // shortest split
+constexpr int kMaxSplits = 16;     // most splits of one (sequence, head)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Splits of a (sequence, head): split_keys (a multiple of kChunk, at least
-// kSplit) to twice that many keys each, whole chunks.
+// Splits of a (sequence, head): total_keys / split_keys (at least one, at
+// most kMaxSplits); the chunks are spread evenly over them.
 __host__ __device__ inline int num_splits(int total_keys, int split_keys) {
   const int s = total_keys / split_keys;
-  return s < 1 ? 1 : s;
+  return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
-// Keys per split for a launch.  A workgroup's ring fills most of a compute
-// unit's LDS, so one runs per unit and a launch of W workgroups takes
-// ceil(W / 256) rounds; each workgroup costs a fixed part (Q load, ring
-// fill, partial-result write: about 11 us measured on MI355X) plus its K/V
-// bytes at about 38 GB/s per unit.  With every sequence taken at max_slots
-// keys, the number of splits n minimising rounds(n) * (fixed + bytes / n)
-// is chosen and split_keys = max_slots / n (whole chunks, at least kSplit).
-// Long prefixes at batch 1 get one full round of workgroups; many
-// (sequence, head) pairs get one split each.
+// Keys per split for a launch.  One workgroup runs per compute unit (its LDS
+// ring fills most of one), so W workgroups take ceil(W / 256) rounds.  A
+// workgroup's time was measured on MI355X (64 queries, d 128, batch 1) as a
+// fixed part (launch, Q, the first round's latency, merge and partial
+// write: about 9.6 us) plus about 0.0227 us per key (its K/V stream runs at
+// the rate its ring in flight sustains, about 23 GB/s); the split count
+// minimising rounds x (fixed + keys per split x rate) is used, splits of at
+// least kMinSplitKeys keys, with every sequence taken at max_slots keys.
 inline int attn_split_keys(int B, int Hq, int d, int nqb, int max_slots) {
-  const double kFixedUs = 11.0, kUsPerByte = 1.0 / 38000.0;
+  const double kFixedUs = 9.6, kUsPerKey = 0.0227 * d / 128.0;
   const long long units = static_cast<long long>(B) * Hq * nqb;
-  const int nmax = num_splits(max_slots, kSplit);
-  int best_s = kSplit;
+  int best_keys = max_slots;
   double best = 1e300;
-  for (int n = 1; n <= nmax; ++n) {
-    long long sk = static_cast<long long>(max_slots) / n / kChunk * kChunk;
-    if (sk < kSplit) sk = kSplit;
-    const int ns = num_splits(max_slots, static_cast<int>(sk));
+  for (int ns = 1; ns <= kMaxSplits; ++ns) {
+    const long long sk = (static_cast<long long>(max_slots) + ns - 1) / ns;
+    if (sk < kMinSplitKeys) break;
+    if (num_splits(max_slots, static_cast<int>(sk)) != ns) continue;
     const long long rounds = (units * ns + 255) / 256;
-    const double est = static_cast<double>(rounds) * (kFixedUs + kUsPerByte * 4.0 * d * max_slots / ns);
-    if (est < best) {
+    const double est = static_cast<double>(rounds) * (kFixedUs + kUsPerKey * static_cast<double>(sk));
+    if (est < best - 1e-9) {
       best = est;
-      best_s = static_cast<int>(sk);
+      best_keys = static_cast<int>(sk);
     }
   }
-  return best_s;
+  return best_keys;
 }
-
-__device__ __forceinline__ u32x4 ld16g(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define LDSB(x) ((MEDUSA_LDS uint8_t*)(x))
@@ -98,6 +101,7 @@ struct AttnLayout {
   static constexpr int ROWB = D * 2;                         // bytes per row
   static constexpr int TILE = kChunk * ROWB;                 // bytes of K (or V) per chunk
   static constexpr int PER = 2 * TILE / 16 / kAttnThreads;   // direct loads per thread per chunk (K and V)
+  static constexpr int QPER = kQBlock * ROWB / 16 / kAttnThreads;   // direct loads per thread for Q
   static constexpr int SH = D == 128 ? 0 : 1;                // rows sharing a bank base
   // LDS slot of piece pc of row `row`
   __device__ static int k_slot(int row, int pc) { return pc ^ ((row >> SH) & (PIECES - 1)); }
@@ -129,7 +133,7 @@ __device__ __forceinline__ void attn_issue(const uint16_t* kbase, const uint16_t
   }
 }
 
-// Allowed keys of one 32-key chunk for this lane's query, bit p = key c0 + p:
+// Allowed keys of one 32-key chunk for one query, bit p = key c0 + p:
 // inside the split, and either in the prefix or an ancestor (or self) in
 // the tree.  mb: the query's ancestor words (LDS), bit j = tree key L + j.
 __device__ __forceinline__ uint32_t chunk_allowed(int c0, int k_hi, int L, const MEDUSA_LDS uint64_t* mb) {
@@ -153,80 +157,102 @@ __device__ __forceinline__ uint32_t chunk_allowed(int c0, int k_hi, int L, const
   return allow;
 }
 
-// One chunk [c0, c0 + kChunk) from a ring stage: scores, online softmax, PV.
-// mrow: this lane's query row of ancestor words (LDS).  The running
-// reference m_run is raised only when some lane's chunk maximum exceeds it
-// by more than kLazy (log2 units): exponentials then stay below 2^kLazy,
-// and O and l, both taken against the same reference, stay exact.
+// Online-softmax state of one wave: its 32 queries (two tiles of 16; lane
+// n + 16g holds query n of each tile, and d rows 16t + 4g .. +3 of O^T).
+template <int D>
+struct AttnState {
+  f32x4 o[2][D / 16];
+  float m_run[2];
+  float l_part[2];   // this lane's share: its keys of the chunks seen
+};
+
+// One chunk [c0, c0 + kChunk) from a ring stage for the wave's two query
+// tiles: scores, online softmax, PV.  mrow[u]: the ancestor words of this
+// lane's query in tile u (LDS).  The running reference m_run is raised only
+// when some lane's chunk maximum exceeds it by more than kLazy (log2
+// units): exponentials then stay below 2^kLazy, and O and l, both taken
+// against the same reference, stay exact.  `full`: every key of the chunk
+// is an allowed prefix key (no mask).
 constexpr float kLazy = 8.f;
 template <int D>
-__device__ __forceinline__ void attn_chunk(const u32x4 (&qv)[D / 32], f32x4 (&o)[D / 16], float& m_run,
-                                           float& l_part, int c0, int k_hi, int L, int lane, float scale_log2,
-                                           const uint64_t* mrow, const uint8_t* kst, const uint8_t* vst) {
+__device__ __forceinline__ void attn_chunk(const u32x4 (&qv)[2][D / 32], AttnState<D>& st, int c0, int k_hi, int L,
+                                           bool full, int lane, float scale_log2,
+                                           const MEDUSA_LDS uint64_t* const (&mrow)[2], const uint8_t* kst,
+                                           const uint8_t* vst) {
   using Lay = AttnLayout<D>;
   constexpr int DT = D / 16, DS = D / 32;
   const int n = lane & 15, g = lane >> 4;
   const MEDUSA_LDS uint8_t* Kc = (const MEDUSA_LDS uint8_t*)kst;
   const MEDUSA_LDS uint8_t* Vc = (const MEDUSA_LDS uint8_t*)vst;
-  const uint32_t allow = chunk_allowed(c0, k_hi, L, (const MEDUSA_LDS uint64_t*)mrow);
 
-  // scores S^T[key = kt*16 + 4g + i][query n]
-  f32x4 s[2];
+  // scores S^T[key = kt*16 + 4g + i][query n] of both tiles; each K operand
+  // read serves both
+  f32x4 s[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[u][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int row = kt * 16 + n;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const u32x4 a = *(const MEDUSA_LDS u32x4*)(Kc + row * Lay::ROWB + Lay::k_slot(row, ds * 4 + g) * 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                    __builtin_bit_cast(bf16x8, qv[ds]), acc, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        s[u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, qv[u][ds]), s[u][kt], 0, 0, 0);
     }
-    s[kt] = acc;
   }
   const float NEG = -__builtin_huge_valf();
-  float mloc = NEG;
+  u32x4 pv[2];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int u = 0; u < 2; ++u) {
+    if (!full) {
+      const uint32_t allow = chunk_allowed(c0, k_hi, L, mrow[u]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = ((allow >> (kt * 16 + 4 * g + i)) & 1u) ? s[kt][i] * scale_log2 : NEG;
-      s[kt][i] = x;
-      mloc = fmaxf(mloc, x);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((allow >> (kt * 16 + 4 * g + i)) & 1u)) s[u][kt][i] = NEG;
     }
-  }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  if (ballot(mloc > m_run + kLazy) != 0) {   // uniform: raise the reference
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = m_run == NEG ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_part *= alpha;
+    // the chunk maximum of this lane's query, in log2 units
+    float mloc = fmaxf(fmaxf(fmaxf(s[u][0][0], s[u][0][1]), fmaxf(s[u][0][2], s[u][0][3])),
+                       fmaxf(fmaxf(s[u][1][0], s[u][1][1]), fmaxf(s[u][1][2], s[u][1][3])));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc *= scale_log2;
+    if (ballot(mloc > st.m_run[u] + kLazy) != 0) {   // uniform: raise the reference
+      const float m_new = fmaxf(st.m_run[u], mloc);
+      const float alpha = st.m_run[u] == NEG ? 0.f : __builtin_amdgcn_exp2f(st.m_run[u] - m_new);
+      st.l_part[u] *= alpha;
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      o[t][0] *= alpha;
-      o[t][1] *= alpha;
-      o[t][2] *= alpha;
-      o[t][3] *= alpha;
+      for (int t = 0; t < DT; ++t) {
+        st.o[u][t][0] *= alpha;
+        st.o[u][t][1] *= alpha;
+        st.o[u][t][2] *= alpha;
+        st.o[u][t][3] *= alpha;
+      }
+      st.m_run[u] = m_new;
     }
-    m_run = m_new;
-  }
-  const float ref = m_run == NEG ? 0.f : m_run;
-  float p[2][4];
+    const float nref = st.m_run[u] == NEG ? 0.f : -st.m_run[u];
+    float p[2][4];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[kt][i] = __builtin_amdgcn_exp2f(s[kt][i] - ref);
-      l_part += p[kt][i];
-    }
+      for (int i = 0; i < 4; ++i) {
+        p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][kt][i], scale_log2, nref));
+        st.l_part[u] += p[kt][i];
+      }
+    pv[u] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                  pack_bf16x2(p[1][2], p[1][3])};
   }
   // O^T[d][q] += V^T[d][keys] P^T[keys][q]; the k-slots of group g are keys
   // 4g + (0..3) and 16 + 4g + (0..3).  The transpose read gives lane m of a
   // 16-lane group element m%4 of the 8 bytes addressed by lane 4c + m/4 of
   // the group, as component c; so lane (c, qd) addresses row 16r + 4g + c,
-  // columns 16t + 4qd .. +3 of the row-major V chunk.
-  const u32x4 pv = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+  // columns 16t + 4qd .. +3 of the row-major V chunk.  Each V^T operand
+  // serves both query tiles.
   const int vrow = 4 * g + ((lane & 15) >> 2), qd = lane & 3;
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -237,13 +263,15 @@ __device__ __forceinline__ void attn_chunk(const u32x4 (&qv)[D / 32], f32x4 (&o)
       const int pc = 2 * t + (qd >> 1);
       const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (MEDUSA_LDS v4s*)(Vc + row * Lay::ROWB + Lay::v_slot(row, pc) * 16 + (qd & 1) * 8));
-      const uint2 u = __builtin_bit_cast(uint2, x);
-      w4[2 * r] = u.x;
-      w4[2 * r + 1] = u.y;
+      const uint2 w = __builtin_bit_cast(uint2, x);
+      w4[2 * r] = w.x;
+      w4[2 * r + 1] = w.y;
     }
     const u32x4 av = {w4[0], w4[1], w4[2], w4[3]};
-    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                   __builtin_bit_cast(bf16x8, pv), o[t], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      st.o[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, pv[u]), st.o[u][t], 0, 0, 0);
   }
 }
 
@@ -259,9 +287,9 @@ __device__ __forceinline__ void wait_chunks(int k) {
   }
 }
 
-// Make chunk c visible to every wave: each thread waits for its own direct
-// loads of chunk c (later chunks stay in flight), then a bare barrier
-// publishes it -- a fenced barrier would also drain the chunks in flight.
+// Make the loads waited for visible to every wave: each thread waits for its
+// own direct loads (later ones stay in flight), then a bare barrier
+// publishes them -- a fenced barrier would also drain the loads in flight.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -269,192 +297,242 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
-    int T, int Hq, int max_slots, int nsplit_max, int split_keys, int nqb,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ prefix_len, const uint8_t* __restrict__ tree_mask, float scale_log2,
-    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+__global__ __launch_bounds__(kAttnThreads, 1) void tree_attn_bf16_kernel(
+    int T, int Hq, int max_slots, int nsplit_max, int split_keys, int nqb, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_len,
+    const uint8_t* __restrict__ tree_mask, float scale_log2, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, uint16_t* __restrict__ out) {
   using Lay = AttnLayout<D>;
   constexpr int DT = D / 16, DS = D / 32;
-  constexpr int NW = kAttnThreads / kWave;           // waves: two groups of four
-  static_assert(Lay::PER * kAttnThreads * 16 == 2 * Lay::TILE, "chunk must split into whole loads");
-  static_assert(kStages >= 4 && kStages % 2 == 0, "chunks are consumed in pairs");
+  constexpr int PER = Lay::PER, QPER = Lay::QPER;
+  static_assert(PER * kAttnThreads * 16 == 2 * Lay::TILE, "chunk must split into whole loads");
+  static_assert(QPER * kAttnThreads * 16 == kQBlock * Lay::ROWB, "Q block must split into whole loads");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][Lay::TILE];   // [stage][K, V]
-  __shared__ uint64_t mbits[NW][16][kMaxNodes / 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t qtile[kQBlock * Lay::ROWB];
+  __shared__ uint64_t mbits[kQBlock][kMaxNodes / 64];
 
   const int split = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z / nqb, qb = blockIdx.z - b * nqb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qh = wave & 1, kg = wave >> 1;             // query half, key group
+  const int n = lane & 15, g = lane >> 4;
+
+  // Q of the block's 64 queries (rows past T repeat row T - 1), swizzled
+  // like K; issued before the prefix length is known
+#pragma unroll
+  for (int i = 0; i < QPER; ++i) {
+    const int x = i * kAttnThreads + tid;
+    const int row = x / Lay::PIECES, slot = x % Lay::PIECES;
+    const int qq = min(qb * kQBlock + row, T - 1);
+    const uint16_t* src = q + ((static_cast<size_t>(b) * T + qq) * Hq + h) * D + Lay::k_slot(row, slot) * 8;
+    lds_dma16(src, LDSB(qtile) + (x & ~63) * 16);
+  }
+
   int L = prefix_len[b];
   if (L > max_slots - T) L = max_slots - T;
   if (L < 0) L = 0;
   const int total = L + T;
   const int ns = num_splits(total, split_keys);
-  if (split >= ns) return;
-
+  if (split >= ns) {
+    wait_vm<0>();   // no direct load may land in LDS after the workgroup leaves
+    return;
+  }
   // whole chunks per split, spread evenly; only a head's last chunk is ragged
   const int nc_all = (total + kChunk - 1) / kChunk;
   const int c_base = nc_all / ns, c_rem = nc_all % ns;
   const int k_lo = kChunk * (split * c_base + min(split, c_rem));
   const int k_hi = min(total, k_lo + kChunk * (c_base + (split < c_rem ? 1 : 0)));
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int grp = wave >> 2, wq = wave & 3;            // chunk group, query wave
-  const int n = lane & 15, g = lane >> 4;
-  const int qi = qb * kQBlock + wq * 16 + n;           // this lane's query
-  const bool q_ok = qi < T;
   const size_t bh = static_cast<size_t>(b) * Hq + h;
   const uint16_t* kbase = kc + bh * max_slots * D;
   const uint16_t* vbase = vc + bh * max_slots * D;
-  constexpr int PER = Lay::PER;
   const int nch = (k_hi - k_lo + kChunk - 1) / kChunk;
+  const int nrounds = (nch + kGroups - 1) / kGroups;
 
-  // Q of the block's 64 queries goes through the same direct-load path into
-  // the last ring stage (rows 0-31 in its K half, 32-63 in its V half,
-  // swizzled like K), ahead of the first chunks; that stage is first
-  // refilled after the barrier that ends the Q reads.  Rows past T repeat
-  // row T - 1.
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int x = i * kAttnThreads + tid;                // piece of the 64 x D tile
-    const int row = x / Lay::PIECES, slot = x % Lay::PIECES;
-    const int qq = min(qb * kQBlock + row, T - 1);
-    const uint16_t* src = q + ((static_cast<size_t>(b) * T + qq) * Hq + h) * D + Lay::k_slot(row, slot) * 8;
-    const int half = x * 16 < Lay::TILE ? 0 : 1;
-    lds_dma16(src, LDSB(ring[kStages - 1][half]) + ((x & ~63) * 16 - half * Lay::TILE));
-  }
-  const int n0 = min(kStages - 2, nch);   // chunks issued ahead of the loop
-  for (int c = 0; c < n0; ++c)
-    attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, tid, ring[c][0], ring[c][1]);
-
-  // Ancestor words of the wave's queries (only in a split that reaches the
-  // tree): word ww of query row r is a ballot over one coalesced 64-byte
-  // load of the mask row; every wave builds the rows of its own 16 queries.
-  // The bytes of word 0 are loaded here, but the ballots wait until the
-  // wave's first chunk that reaches the tree: waiting for a load waits for
-  // every load issued before it, and by then only the split's last chunks
-  // are still in flight.
+  // Ancestor words of the block's queries (only in a split that reaches
+  // the tree): word ww of query row r is a ballot over a coalesced load of
+  // the mask row; each wave builds eight rows.  The bytes of word 0 are
+  // loaded here, behind Q and ahead of the K/V stream, so the wait for Q
+  // covers them; the ballots wait until the first round that reaches the
+  // tree, since the compiler's wait before them is a wait for every load
+  // issued so far.
   const bool has_tree = k_hi > L;
-  uint8_t mbv[16];
+  uint8_t mbv[8];
   if (has_tree) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qq = qb * kQBlock + wq * 16 + r;
+    for (int r = 0; r < 8; ++r) {
+      const int qq = qb * kQBlock + wave * 8 + r;
       mbv[r] = tree_mask[static_cast<size_t>(min(qq, T - 1)) * T + min(lane, T - 1)];
     }
   }
+
+  // The first kEarly chunks go out with Q; the rest of rounds 0 and 1 only
+  // once Q has landed, so that Q and the first chunks are not queued behind
+  // the whole burst of every workgroup's loads.
+  const int n0 = min(kStages, nch);
+  const int ne = min(kEarly, n0);
+  for (int c = 0; c < ne; ++c)
+    attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, tid, ring[c][0], ring[c][1]);
   bool mask_ready = !has_tree;
   auto build_mask = [&]() {
     const int nw = (T + 63) >> 6;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qq = qb * kQBlock + wq * 16 + r;
+    for (int r = 0; r < 8; ++r) {
+      const int qq = qb * kQBlock + wave * 8 + r;
       const uint64_t word = ballot(qq < T && lane < T && mbv[r] != 0);
-      if (lane == 0) mbits[wave][r][0] = word;
+      if (lane == 0) mbits[wave * 8 + r][0] = word;
     }
 #pragma unroll 1
     for (int ww = 1; ww < nw; ++ww) {   // trees of more than 64 nodes
       const int j = ww * 64 + lane;
-      uint8_t mw[16];
+      uint8_t mw[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = qb * kQBlock + wq * 16 + r;
+      for (int r = 0; r < 8; ++r) {
+        const int qq = qb * kQBlock + wave * 8 + r;
         mw[r] = tree_mask[static_cast<size_t>(min(qq, T - 1)) * T + min(j, T - 1)];
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = qb * kQBlock + wq * 16 + r;
+      for (int r = 0; r < 8; ++r) {
+        const int qq = qb * kQBlock + wave * 8 + r;
         const uint64_t word = ballot(qq < T && j < T && mw[r] != 0);
-        if (lane == 0) mbits[wave][r][ww] = word;
+        if (lane == 0) mbits[wave * 8 + r][ww] = word;
       }
     }
   };
-  const uint64_t* mrow = mbits[wave][n];
 
-  // Q from LDS into registers once its loads (the oldest in flight) are in
-  wait_chunks<PER, kStages - 2>(n0);
+  // Q from LDS into registers once its loads (the oldest in flight, with
+  // the mask bytes) are in
+  wait_chunks<PER, kEarly>(ne);
   ring_barrier();
-  u32x4 qv[DS];   // Q[qi][s*32 + 8g .. +8]: the B operand of S^T
-  {
-    const int row = wq * 16 + n;
-    const MEDUSA_LDS uint8_t* qt = LDSB(ring[kStages - 1][row < 32 ? 0 : 1]) + (row & 31) * Lay::ROWB;
+  for (int c = ne; c < n0; ++c)
+    attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, tid, ring[c][0], ring[c][1]);
+  u32x4 qv[2][DS];   // Q[query][s*32 + 8g .. +8]: the B operand of S^T, per tile
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qv[s] = *(const MEDUSA_LDS u32x4*)(qt + Lay::k_slot(row, s * 4 + g) * 16);
+  for (int u = 0; u < 2; ++u) {
+    const int row = qh * 32 + u * 16 + n;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qv[u][s] = *(const MEDUSA_LDS u32x4*)(LDSB(qtile) + row * Lay::ROWB + Lay::k_slot(row, s * 4 + g) * 16);
+  }
+  const MEDUSA_LDS uint64_t* const mrow[2] = {(const MEDUSA_LDS uint64_t*)mbits[qh * 32 + n],
+                                              (const MEDUSA_LDS uint64_t*)mbits[qh * 32 + 16 + n]};
+
+  AttnState<D> st;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    st.m_run[u] = -__builtin_huge_valf();
+    st.l_part[u] = 0.f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) st.o[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  float m_run = -__builtin_huge_valf();
-  float l_part = 0.f;
-  f32x4 o[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Chunks go in pairs: group 0 takes chunk c, group 1 chunk c + 1, each
-  // with its own online-softmax state.  Chunk c sits in stage c % kStages;
-  // after the barrier of pair c the stages of pair c - 2 are free and take
-  // chunks c + kStages - 2 and c + kStages - 1.
-  for (int c = 0; c < nch; c += 2) {
-    const int need_hi = min(c + 1, nch - 1);
-    const int issued_hi = min(c + kStages - 3, nch - 1);
-    wait_chunks<PER, kStages - 4>(issued_hi - need_hi);
+  // Round r holds chunks 4r .. 4r+3 in ring set r % 2; key group kg takes
+  // chunk 4r + kg.  After the barrier of round r (r >= 1) every wave is done
+  // with round r - 1, whose set then takes round r + 1.
+  for (int r = 0; r < nrounds; ++r) {
+    const int need_hi = min(kGroups * r + kGroups - 1, nch - 1);
+    const int issued_hi = min(kGroups * (r < 1 ? 2 : r + 1) - 1, nch - 1);
+    wait_chunks<PER, kGroups>(issued_hi - need_hi);
+    if (!mask_ready && k_lo + kChunk * min(kGroups * r + kGroups, nch) > L) {   // uniform: first round reaching the tree
+      build_mask();
+      mask_ready = true;
+    }
     ring_barrier();
+    if (r >= 1) {
+#pragma unroll 1
+      for (int c = kGroups * (r + 1); c < min(kGroups * (r + 2), nch); ++c) {
+        const int sn = c % kStages;
+        attn_issue<D>(kbase, vbase, k_lo + c * kChunk, k_hi, tid, ring[sn][0], ring[sn][1]);
+      }
+    }
+    const int c = kGroups * r + kg;
+    if (c < nch) {
+      const int c0 = k_lo + c * kChunk;
+      const bool full = c0 + kChunk <= min(L, k_hi);
+      const int sn = c % kStages;
+      attn_chunk<D>(qv, st, c0, k_hi, L, full, lane, scale_log2, mrow, ring[sn][0], ring[sn][1]);
+    }
+  }
+
+  // Key groups 1-3 hand their states to group 0 through LDS (the ring is
+  // free: every direct load has landed and every chunk has been read):
+  // per lane 2 * DT + 1 16-byte words (O of both tiles, then m and l of
+  // both), each wave instruction writing or reading 1 KB contiguously.
+  constexpr int NF4 = 2 * DT + 1;
+  static_assert(3 * 2 * NF4 * kWave * 16 <= kStages * 2 * Lay::TILE, "merge area must fit the ring");
+  f32x4* xfer = reinterpret_cast<f32x4*>(&ring[0][0][0]);
+  ring_barrier();
+  if (kg != 0) {
+    f32x4* xw = xfer + ((kg - 1) * 2 + qh) * NF4 * kWave + lane;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) xw[(u * DT + t) * kWave] = st.o[u][t];
+    xw[2 * DT * kWave] = f32x4{st.m_run[0], st.m_run[1], st.l_part[0], st.l_part[1]};
+  }
+  ring_barrier();
+  const float NEG = -__builtin_huge_valf();
+  if (kg == 0) {
+    f32x4 ml[kGroups - 1];
+#pragma unroll
+    for (int k = 1; k < kGroups; ++k) ml[k - 1] = xfer[(((k - 1) * 2 + qh) * NF4 + 2 * DT) * kWave + lane];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int cn = c + kStages - 2 + u;
-      if (cn < nch) {
-        const int sn = cn % kStages;
-        attn_issue<D>(kbase, vbase, k_lo + cn * kChunk, k_hi, tid, ring[sn][0], ring[sn][1]);
-      }
-    }
-    const int cc = c + grp;
-    if (cc < nch) {
-      if (!mask_ready && k_lo + (cc + 1) * kChunk > L) {   // uniform: the wave's first chunk reaching the tree
-        build_mask();
-        mask_ready = true;
-      }
-      const int st = cc % kStages;
-      attn_chunk<D>(qv, o, m_run, l_part, k_lo + cc * kChunk, k_hi, L, lane, scale_log2, mrow, ring[st][0],
-                    ring[st][1]);
-    }
-  }
-
-  // Group 1 hands its state to group 0 through LDS (the ring is free: every
-  // direct load has landed and every chunk has been read), then group 0
-  // merges the two -- each taken against its own reference -- and writes
-  // the split's partial.
-  constexpr int NF = 4 * DT + 2;                       // floats per lane: O, m, l
-  float* xfer = reinterpret_cast<float*>(&ring[0][0][0]);
-  ring_barrier();
-  if (grp == 1) {
+      float M = st.m_run[u];
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xfer[(wq * NF + 4 * t + i) * kWave + lane] = o[t][i];
-    xfer[(wq * NF + 4 * DT) * kWave + lane] = m_run;
-    xfer[(wq * NF + 4 * DT + 1) * kWave + lane] = l_part;
-  }
-  ring_barrier();
-  if (grp == 0) {
-    const float NEG = -__builtin_huge_valf();
-    const float m1 = xfer[(wq * NF + 4 * DT) * kWave + lane];
-    const float l1 = xfer[(wq * NF + 4 * DT + 1) * kWave + lane];
-    const float M = fmaxf(m_run, m1);
-    const float a0 = m_run == NEG ? 0.f : exp2f(m_run - M);
-    const float a1 = m1 == NEG ? 0.f : exp2f(m1 - M);
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * a0 + xfer[(wq * NF + 4 * t + i) * kWave + lane] * a1;
-    l_part = l_part * a0 + l1 * a1;
-    m_run = M;
-
-    float l = l_part + __shfl_xor(l_part, 16);
-    l += __shfl_xor(l, 32);
-    if (q_ok) {
-      const size_t row = (bh * nsplit_max + split) * T + qi;
-      float* orow = part_o + row * D;
+      for (int k = 1; k < kGroups; ++k) M = fmaxf(M, ml[k - 1][u]);
+      const float a0 = st.m_run[u] == NEG ? 0.f : exp2f(st.m_run[u] - M);
+      st.l_part[u] *= a0;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        *reinterpret_cast<float4*>(orow + t * 16 + 4 * g) = float4{o[t][0], o[t][1], o[t][2], o[t][3]};
-      if (g == 0) part_ml[row] = float2{m_run, l};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[u][t][i] *= a0;
+#pragma unroll
+      for (int k = 1; k < kGroups; ++k) {
+        const f32x4* xw = xfer + ((k - 1) * 2 + qh) * NF4 * kWave + lane;
+        const float mk = ml[k - 1][u];
+        const float ak = mk == NEG ? 0.f : exp2f(mk - M);
+        st.l_part[u] += ak * ml[k - 1][2 + u];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const f32x4 x = xw[(u * DT + t) * kWave];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st.o[u][t][i] += ak * x[i];
+        }
+      }
+      st.m_run[u] = M;
+      float l = st.l_part[u] + __shfl_xor(st.l_part[u], 16);
+      st.l_part[u] = l + __shfl_xor(l, 32);     // the query's total over its four lanes
+    }
+    if (ns == 1) {
+      // the only split: normalise and write the output
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qi = qb * kQBlock + qh * 32 + u * 16 + n;
+        if (qi < T) {
+          const float inv = 1.f / st.l_part[u];
+          uint16_t* orow = out + ((static_cast<size_t>(b) * T + qi) * Hq + h) * D;
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            uint2 w;
+            w.x = pack_bf16x2(st.o[u][t][0] * inv, st.o[u][t][1] * inv);
+            w.y = pack_bf16x2(st.o[u][t][2] * inv, st.o[u][t][3] * inv);
+            *reinterpret_cast<uint2*>(orow + t * 16 + 4 * g) = w;
+          }
+        }
+      }
+      return;
+    }
+    // this split's partial: [group][split][64 rows][D] and
+    // [group][split][64] (m, l), group = (sequence, head, query block)
+    const size_t grp = bh * nqb + qb;
+    float* po = part_o + (grp * nsplit_max + split) * kQBlock * D;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = qh * 32 + u * 16 + n;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + row * D + t * 16 + 4 * g) = st.o[u][t];
+      if (g == 0) part_ml[(grp * nsplit_max + split) * kQBlock + row] = float2{st.m_run[u], st.l_part[u]};
     }
   }
 }
@@ -462,18 +540,19 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_bf16_kernel(
 // Merge the splits of each (sequence, head, query) by log-sum-exp.  D/4
 // threads per query, four output columns each (16-byte partial loads); a
 // 256-thread workgroup takes 1024/D consecutive queries of one (sequence,
-// head), so its loads of one split are one contiguous run.  Splits are taken
-// eight at a time with all their loads issued together, merged online
-// against a running maximum.  The first eight are addressed within the
-// workspace's nsplit_max splits, so their loads go out with the prefix
-// length's in one round trip; splits at or past the sequence's own count
-// (never written by this call) are dropped by selects, never multiplied.
-template <typename OutT, int D>
+// head), so a wave instruction reads 1 KB of one split contiguously.
+// Splits are taken eight at a time with all their loads issued together,
+// merged online against a running maximum.  The first eight are addressed
+// within the workspace's nsplit_max splits, so their loads go out with the
+// prefix length's in one round trip; splits at or past the sequence's own
+// count (never written by this call) are dropped by selects, never
+// multiplied.  A sequence with one split was written by the main kernel.
+template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, int Hq, int max_slots, int nsplit_max,
                                                               int split_keys, const int32_t* __restrict__ prefix_len,
                                                               const float* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml,
-                                                              OutT* __restrict__ out) {
+                                                              uint16_t* __restrict__ out) {
   constexpr int TPQ = D / 4, QPW = 256 / TPQ, U = 8;
   const int t = threadIdx.x % TPQ;
   // B * Hq * T * D / 4 stays below 2^31 (B <= 16, Hq <= 1024, T <= 256)
@@ -482,7 +561,9 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
   const int qi = static_cast<int>(Q % static_cast<unsigned>(T));
   const int h = static_cast<int>((Q / static_cast<unsigned>(T)) % static_cast<unsigned>(Hq));
   const int b = static_cast<int>(Q / static_cast<unsigned>(T * Hq));
-  const size_t bh = static_cast<size_t>(b) * Hq + h;
+  const int nqb = (T + kQBlock - 1) / kQBlock;
+  const size_t grp = (static_cast<size_t>(b) * Hq + h) * nqb + qi / kQBlock;
+  const int row = qi % kQBlock;
   const float NEG = -__builtin_huge_valf();
   float M = NEG, den = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -491,9 +572,9 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
   auto load = [&](int s0, int smax) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t row = (bh * nsplit_max + min(s0 + u, smax - 1)) * T + qi;
-      ml[u] = part_ml[row];
-      ov[u] = *reinterpret_cast<const float4*>(part_o + row * D + 4 * t);
+      const size_t r = (grp * nsplit_max + min(s0 + u, smax - 1)) * kQBlock + row;
+      ml[u] = part_ml[r];
+      ov[u] = *reinterpret_cast<const float4*>(part_o + r * D + 4 * t);
     }
   };
   load(0, nsplit_max);
@@ -501,6 +582,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
   if (L > max_slots - T) L = max_slots - T;
   if (L < 0) L = 0;
   const int ns = num_splits(L + T, split_keys);
+  if (ns == 1) return;
   for (int s0 = 0; s0 < ns; s0 += U) {
     if (s0 > 0) load(s0, ns);
     float bm = NEG;
@@ -526,14 +608,10 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
     M = Mn;
   }
   const size_t o = ((static_cast<size_t>(b) * T + qi) * Hq + h) * D + 4 * t;
-  if constexpr (sizeof(OutT) == 2) {
-    uint2 w;
-    w.x = f32_to_bf16_bits(acc[0] / den) | (f32_to_bf16_bits(acc[1] / den) << 16);
-    w.y = f32_to_bf16_bits(acc[2] / den) | (f32_to_bf16_bits(acc[3] / den) << 16);
-    *reinterpret_cast<uint2*>(out + o) = w;
-  } else {
-    *reinterpret_cast<float4*>(out + o) = float4{acc[0] / den, acc[1] / den, acc[2] / den, acc[3] / den};
-  }
+  uint2 w;
+  w.x = pack_bf16x2(acc[0] / den, acc[1] / den);
+  w.y = pack_bf16x2(acc[2] / den, acc[3] / den);
+  *reinterpret_cast<uint2*>(out + o) = w;
 }
 
 // f32: one wave per (sequence, head, query); lanes over keys for scores,
@@ -597,14 +675,20 @@ namespace {
 
 using namespace medusa;
 
+// Workspace: the splits' partials (O unnormalised [group][split][64][d]
+// float32 and (m, l) [group][split][64]; group = (sequence, head, query
+// block)), sized for the most splits any launch at this max_slots uses.
+int attn_nsplit_max(int max_slots) { return num_splits(max_slots, kMinSplitKeys); }
 size_t attn_part_o_bytes(int B, int T, int Hq, int d, int max_slots) {
-  // sized for the shortest splits (every launch uses at most this many)
-  const size_t nsm = static_cast<size_t>(num_splits(max_slots, kSplit));
-  return medusa_host::round_up(static_cast<size_t>(B) * Hq * nsm * T * d * 4, 256);
+  const size_t nqb = static_cast<size_t>((T + kQBlock - 1) / kQBlock);
+  return medusa_host::round_up(static_cast<size_t>(B) * Hq * nqb * attn_nsplit_max(max_slots) * kQBlock * d * 4, 256);
 }
 size_t attn_part_ml_bytes(int B, int T, int Hq, int max_slots) {
-  const size_t nsm = static_cast<size_t>(num_splits(max_slots, kSplit));
-  return medusa_host::round_up(static_cast<size_t>(B) * Hq * nsm * T * 8, 256);
+  const size_t nqb = static_cast<size_t>((T + kQBlock - 1) / kQBlock);
+  return medusa_host::round_up(static_cast<size_t>(B) * Hq * nqb * attn_nsplit_max(max_slots) * kQBlock * 8, 256);
+}
+size_t attn_ws_bytes(int B, int T, int Hq, int d, int max_slots) {
+  return attn_part_o_bytes(B, T, Hq, d, max_slots) + attn_part_ml_bytes(B, T, Hq, max_slots);
 }
 
 int check_attn(const char* fn, int dtype, int B, int T, int Hq, int d, int max_slots) {
@@ -623,7 +707,7 @@ int check_attn(const char* fn, int dtype, int B, int T, int Hq, int d, int max_s
 extern "C" size_t medusa_tree_attention_workspace(int dtype, int B, int T, int Hq, int d, int max_slots) {
   if (check_attn("medusa_tree_attention_workspace", dtype, B, T, Hq, d, max_slots) != MEDUSA_OK) return 0;
   if (dtype == MEDUSA_F32) return 256;
-  return attn_part_o_bytes(B, T, Hq, d, max_slots) + attn_part_ml_bytes(B, T, Hq, max_slots);
+  return attn_ws_bytes(B, T, Hq, d, max_slots);
 }
 
 extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int max_slots, const void* q,
@@ -648,32 +732,35 @@ extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int
     return medusa_host::hip_check("medusa_tree_attention launch");
   }
   MEDUSA_REQUIRE_PTR(ws);
-  const size_t need = attn_part_o_bytes(B, T, Hq, d, max_slots) + attn_part_ml_bytes(B, T, Hq, max_slots);
+  const size_t need = attn_ws_bytes(B, T, Hq, d, max_slots);
   MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
                  need);
   const int nqb = (T + kQBlock - 1) / kQBlock;
   const int sk = attn_split_keys(B, Hq, d, nqb, max_slots);
-  const int nsm = num_splits(max_slots, sk);
-  float* part_o = static_cast<float*>(ws);
-  float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + attn_part_o_bytes(B, T, Hq, d, max_slots));
+  const int nsm = attn_nsplit_max(max_slots);
+  const int nsl = num_splits(max_slots, sk);   // splits of the launch (no sequence uses more)
+  char* base = static_cast<char*>(ws);
+  float* part_o = reinterpret_cast<float*>(base);
+  float2* part_ml = reinterpret_cast<float2*>(base + attn_part_o_bytes(B, T, Hq, d, max_slots));
   const float sl2 = scale * kLog2e;
-  dim3 grid(nsm, Hq, B * nqb);
+  dim3 grid(nsl, Hq, B * nqb);
+  uint16_t* o16 = static_cast<uint16_t*>(out);
   if (d == 128)
     hipLaunchKernelGGL(tree_attn_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, st, T, Hq, max_slots, nsm, sk, nqb,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                       static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml);
+                       static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml, o16);
   else
     hipLaunchKernelGGL(tree_attn_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, st, T, Hq, max_slots, nsm, sk, nqb,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                       static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml);
+                       static_cast<const uint16_t*>(v_cache), prefix_len, tree_mask, sl2, part_o, part_ml, o16);
   rc = medusa_host::hip_check("medusa_tree_attention launch");
-  if (rc != MEDUSA_OK) return rc;
+  if (rc != MEDUSA_OK || nsl == 1) return rc;   // one split everywhere: no merge
   const unsigned cgrid = static_cast<unsigned>((B * Hq * T * (d / 4) + 255) / 256);
   if (d == 128)
-    hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 128>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
-                       nsm, sk, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
+    hipLaunchKernelGGL(tree_attn_combine_kernel<128>, dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots, nsm, sk,
+                       prefix_len, part_o, part_ml, o16);
   else
-    hipLaunchKernelGGL((tree_attn_combine_kernel<uint16_t, 64>), dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots,
-                       nsm, sk, prefix_len, part_o, part_ml, static_cast<uint16_t*>(out));
+    hipLaunchKernelGGL(tree_attn_combine_kernel<64>, dim3(cgrid), dim3(256), 0, st, B, T, Hq, max_slots, nsm, sk,
+                       prefix_len, part_o, part_ml, o16);
   return medusa_host::hip_check("medusa_tree_attention combine launch");
 }
