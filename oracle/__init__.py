@@ -9,6 +9,8 @@ computes, written from the pages' descriptions of Medusa:
   posterior.py  greedy / typical acceptance and the longest accepted prefix
   nucleus.py    nucleus (top-p) acceptance: a sample per node, children
                 accepted when they equal their parent's sample
+  sampling.py   Philox4x64-10 uniforms keyed by (seed, step, sequence,
+                node, purpose) and the typical-mode sampled next token
   commit.py     gathering the accepted path's K/V into contiguous slots
   base_head.py  the base model's lm_head over the tree nodes, and the
                 acceptance test on its logits
@@ -38,11 +40,12 @@ from .posterior import node_statistics, evaluate_posterior
 from .commit import commit_kv
 from .base_head import base_logits, base_posterior
 from .nucleus import nucleus, nucleus_sample, evaluate_posterior_nucleus
+from . import sampling
 from . import decoder
 
 __all__ = [
     "as_f64", "resblock", "lm_head_logits", "topk_by_value", "heads",
     "SpecError", "parse_choices", "build_tree", "tree_attention",
     "node_statistics", "evaluate_posterior", "commit_kv", "base_logits", "base_posterior",
-    "nucleus", "nucleus_sample", "evaluate_posterior_nucleus", "decoder",
+    "nucleus", "nucleus_sample", "evaluate_posterior_nucleus", "sampling", "decoder",
 ]
