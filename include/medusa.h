@@ -13,7 +13,9 @@
  *   medusa_base_lm_head        base lm_head at the tree nodes -> logits
  *                              (or medusa_base_posterior: both fused)
  *   medusa_evaluate_posterior  greedy / typical acceptance, best path
- *                              (or medusa_evaluate_posterior_nucleus: top-p)
+ *                              (or medusa_evaluate_posterior_nucleus: top-p,
+ *                              its draws from medusa_philox_uniforms)
+ *   medusa_sample_typical      typical mode: the sampled next token
  *   medusa_commit_kv           gather the accepted rows into contiguous slots
  *
  * Conventions shared by every call
@@ -319,6 +321,45 @@ int medusa_evaluate_posterior_nucleus(int B, int T, int V, int p_max, int D,
                                       float temperature, float top_p, const float* uniforms,
                                       int32_t* best_path, int32_t* accept_len, int32_t* next_token,
                                       int32_t* samples, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Random numbers and the sampled next token.  [API] medusa_generate and
+ * generate_candidates (temperature, posterior_threshold, posterior_alpha,
+ * top_p, sampling='typical'): with a positive temperature the tree's root
+ * -- the base model's token after the last accepted one, which is also the
+ * step's bonus token -- is drawn under the sampling mode, not taken as the
+ * argmax.
+ *
+ * medusa_philox_uniforms: out[b][n] (float32 [B][T]) = the uniform of
+ * (seed, step, b, n, purpose) in [0, 1): the top 24 bits of the first
+ * output word of Philox4x64-10 (Salmon, Moraes, Dror and Shaw, SC 2011)
+ * with counter (n, b, step, purpose) and key (seed, 0), times 2^-24 --
+ * bit-identical on any machine.  Purpose 0 is the nucleus draw of each node
+ * (the `uniforms` of medusa_evaluate_posterior_nucleus), purpose 1 the
+ * typical-mode next token.  B <= 16, T <= 256, purpose >= 0.
+ *
+ * medusa_sample_typical: for each sequence b, n = retrieve[best_path[b]]
+ * [accept_len[b]] (clamped into the tables; an entry outside [0, T) reads
+ * node 0), p = softmax(logits[b][n] / temperature); the allowed tokens are
+ * those with p(x) > min(eps, delta * exp(-H(p))) -- the typical acceptance
+ * test -- and next_token[b] is drawn from them renormalised with the
+ * purpose-1 uniform u of (seed, step, b, node 0): walking the allowed tokens
+ * in id order, the first whose running mass exceeds u times their total.
+ * Masses are e^(z - max) in fixed point with 40 fraction bits (exact sums);
+ * the test p > threshold is taken in float32.  Requires temperature > 0,
+ * eps > 0 and 0 < delta < 1 (the argmax is then always allowed), else
+ * MEDUSA_ERR_VALUE.  Layouts as medusa_evaluate_posterior; best_path and
+ * accept_len are that call's outputs.  For a plain (non-tree) draw pass
+ * T = 1, a one-entry retrieve {0} (p_max = D = 1) and zero best_path and
+ * accept_len.  One workgroup per sequence; no workspace.
+ * ------------------------------------------------------------------- */
+int medusa_philox_uniforms(uint64_t seed, uint64_t step, int purpose, int B, int T, float* out,
+                           void* stream);
+
+int medusa_sample_typical(int B, int T, int V, int p_max, int D, const float* logits,
+                          const int32_t* retrieve, const int32_t* best_path, const int32_t* accept_len,
+                          float temperature, float eps, float delta, uint64_t seed, uint64_t step,
+                          int32_t* next_token, void* stream);
 
 /* ---------------------------------------------------------------------
  * KV commit.  [API] tree_decoding (tree K/V appended to past_key_values);

@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
     medusa_evaluate_posterior, medusa_posterior_nucleus_workspace, medusa_evaluate_posterior_nucleus,
     medusa_commit_kv, medusa_base_lm_head, medusa_base_lm_head_pack,
     medusa_base_posterior_workspace, medusa_base_posterior, medusa_embed, medusa_add_rmsnorm, medusa_rope_qkv,
-    medusa_silu_mul,
+    medusa_silu_mul, medusa_philox_uniforms, medusa_sample_typical, PURPOSE_NUCLEUS, PURPOSE_NEXT_TOKEN,
 )
 
 __all__ = [
@@ -33,4 +33,5 @@ __all__ = [
     "medusa_evaluate_posterior_nucleus", "medusa_commit_kv", "medusa_base_lm_head",
     "medusa_base_lm_head_pack", "medusa_base_posterior_workspace", "medusa_base_posterior",
     "medusa_embed", "medusa_add_rmsnorm", "medusa_rope_qkv", "medusa_silu_mul",
+    "medusa_philox_uniforms", "medusa_sample_typical", "PURPOSE_NUCLEUS", "PURPOSE_NEXT_TOKEN",
 ]

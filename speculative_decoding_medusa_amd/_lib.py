@@ -70,6 +70,9 @@ _SIGS = {
     "medusa_posterior_nucleus_workspace": (_sz, [_i, _i]),
     "medusa_evaluate_posterior_nucleus": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp,
                                                _vp, _vp, _sz, _vp]),
+    "medusa_philox_uniforms": (_i, [ctypes.c_uint64, ctypes.c_uint64, _i, _i, _i, _vp, _vp]),
+    "medusa_sample_typical": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _f, ctypes.c_uint64,
+                                   ctypes.c_uint64, _vp, _vp]),
     "medusa_embed": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp]),
     "medusa_add_rmsnorm": (_i, [_i, _i, _vp, _vp, _vp, _f, _vp, _vp]),
     "medusa_rope_qkv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp]),
@@ -289,6 +292,40 @@ def medusa_heads(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, ws
                           _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_heads")
     return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r)
+
+
+PURPOSE_NUCLEUS = 0
+PURPOSE_NEXT_TOKEN = 1
+
+
+def medusa_philox_uniforms(seed, step, purpose, B, T, device="cuda", out=None):
+    """float32 [B][T] counter-based uniforms of (seed, step, sequence, node,
+    purpose)."""
+    if out is None:
+        out = torch.empty((B, T), dtype=torch.float32, device=device)
+    dev = out.device
+    rc = lib.medusa_philox_uniforms(int(seed) & ((1 << 64) - 1), int(step) & ((1 << 64) - 1), int(purpose), B, T,
+                                    _ptr(out, "out", torch.float32, (B, T)), _stream(dev))
+    _check(rc, "medusa_philox_uniforms")
+    return out
+
+
+def medusa_sample_typical(logits, retrieve, best_path, accept_len, temperature, eps, delta, seed, step,
+                          out=None):
+    """Typical-mode next token per sequence, drawn at the last accepted node."""
+    B, T, V = logits.shape
+    p_max, D = retrieve.shape
+    dev = logits.device
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = lib.medusa_sample_typical(B, T, V, p_max, D, _ptr(logits, "logits", torch.float32),
+                                   _ptr(retrieve, "retrieve", torch.int32),
+                                   _ptr(best_path, "best_path", torch.int32, (B,)),
+                                   _ptr(accept_len, "accept_len", torch.int32, (B,)), float(temperature), float(eps),
+                                   float(delta), int(seed) & ((1 << 64) - 1), int(step) & ((1 << 64) - 1),
+                                   _ptr(out, "next_token", torch.int32, (B,)), _stream(dev))
+    _check(rc, "medusa_sample_typical")
+    return out
 
 
 def medusa_heads_noalloc(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, out=None):

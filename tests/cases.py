@@ -377,3 +377,31 @@ def typical_threshold_case(w, tcase, temperature=0.7, seed=0, chunk=4096, lo=1.0
         if ok and two and small and all(changed[r] for r in require):
             return dict(logits=logits, ref=exp, retry=retry, flips=flips, changed=changed, factors=factors)
     raise RuntimeError("no near-threshold case after %d redraws" % max_retries)
+
+
+# ------------------------------------------------------------------ sampled next token
+def typical_sample_robust(row, temperature, eps, delta, u, rel=1e-5, thr_rel=1e-3):
+    """Whether one typical-mode draw is decided far from float error: the
+    draw is the same with every near-threshold token (|p - thr| < thr_rel *
+    thr) counted in and counted out, and u times the allowed mass lies at
+    least rel of that mass away from every running-sum boundary."""
+    from oracle import sampling as smp
+    t = float(np.float32(temperature))
+    z = np.asarray(row, dtype=np.float64) / t
+    e = np.exp(z - z.max())
+    S = e.sum()
+    H = np.log(S) - ((z - z.max()) * e).sum() / S
+    thr = min(float(np.float32(eps)), float(np.float32(delta)) * np.exp(-H))
+    p = e / S
+    near = np.abs(p - thr) < thr_rel * thr
+    draws = []
+    for keep in (p > thr) | near, (p > thr) & ~near:
+        ids = np.flatnonzero(keep)
+        w = p[ids]
+        target = float(np.float32(u)) * w.sum()
+        run = np.cumsum(w)
+        if np.min(np.abs(run - target)) < rel * w.sum():
+            return False
+        i = int(np.searchsorted(run, target, side="right"))
+        draws.append(int(ids[min(i, len(ids) - 1)]))
+    return draws[0] == draws[1] == smp.typical_sample(row, temperature, eps, delta, u)

@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 107
+    assert L.medusa_abi_version() == 108
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -320,3 +320,26 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         md._lib._ptr(torch.zeros(4), "x")
+
+
+def test_philox_uniforms_validation():
+    f = L.medusa_philox_uniforms
+    assert f(1, 2, 0, 0, 4, A, None) == SHAPE
+    assert f(1, 2, 0, 17, 4, A, None) == SHAPE
+    assert f(1, 2, 0, 1, 257, A, None) == SHAPE
+    assert f(1, 2, -1, 1, 4, A, None) == VALUE
+    assert f(1, 2, 0, 1, 4, None, None) == NULL
+    assert f(1, 2, 0, 1, 4, MIS, None) == ALIGN
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(T=300), SHAPE), (dict(V=0), SHAPE), (dict(D=10), SHAPE), (dict(p_max=0), SHAPE),
+    (dict(t=0.0), VALUE), (dict(t=-1.0), VALUE), (dict(eps=0.0), VALUE), (dict(delta=1.0), VALUE),
+    (dict(delta=0.0), VALUE), (dict(logits=None), NULL), (dict(nxt=None), NULL), (dict(best=MIS), ALIGN),
+])
+def test_sample_typical_validation(kw, code):
+    a = dict(B=1, T=7, V=100, p_max=4, D=3, logits=A, ret=A, best=A, acc=A, t=0.7, eps=0.09, delta=0.3, nxt=A)
+    a.update(kw)
+    rc = L.medusa_sample_typical(a["B"], a["T"], a["V"], a["p_max"], a["D"], a["logits"], a["ret"], a["best"],
+                                 a["acc"], a["t"], a["eps"], a["delta"], 5, 6, a["nxt"], None)
+    assert rc == code
