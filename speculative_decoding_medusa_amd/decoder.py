@@ -18,6 +18,15 @@ prefix and their ancestors); the longest greedily accepted path and the
 root are kept (their K/V moved into place), and the base model's token
 after the last accepted node becomes the next root.  The emitted tokens are
 exactly the base model's greedy continuation.
+
+Sampled decoding (the pages' ``sampling='typical'`` with a positive
+temperature, and the ``top_p`` nucleus mode): the same loop with the
+typical acceptance test (medusa_evaluate_posterior at that temperature) and
+a root -- the first token after the prompt, then each step's bonus token --
+drawn by medusa_sample_typical, or with nucleus acceptance on the library's
+Philox uniforms (medusa_philox_uniforms, medusa_evaluate_posterior_nucleus),
+whose draw at the last accepted node is the next root.  Step s of a
+generation draws with the keys (seed, s); the prompt's root is step 0.
 """
 
 import numpy as np
@@ -79,6 +88,8 @@ class TinyDecoder:
         self._node0 = torch.zeros((1, 1), dtype=torch.int32, device=dev)
         self._npaths1 = torch.ones(1, dtype=torch.int32, device=dev)
         self._mask1 = torch.ones((1, 1), dtype=torch.uint8, device=dev)
+        self._zero1 = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.nuc_ws = torch.zeros(L.medusa_posterior_nucleus_workspace(1, self.tmax), dtype=torch.uint8, device=dev)
 
     def forward(self, tokens, positions, prefix_len, tree_mask):
         """Run tokens [1][T] (int32, device) at positions [1][T] against the
@@ -116,6 +127,20 @@ class TinyDecoder:
         post = L.medusa_evaluate_posterior(row, self._node0, self._node0, self._npaths1, 0.0, 0.09, 0.3,
                                            ws=self.post_ws)
         return post["next_token"]
+
+    def _sample_last(self, logits, mode, temperature, eps, delta, top_p, seed, step):
+        """The sampled token at the last row of logits [1][T][V] under `mode`
+        ('typical' or 'nucleus'), keys (seed, step), as a device int32 [1]."""
+        row = logits[:, -1:, :]
+        if mode == "typical":
+            return L.medusa_sample_typical(row, self._node0, self._zero1, self._zero1, temperature, eps, delta, seed,
+                                           step)
+        if mode == "nucleus":
+            u = L.medusa_philox_uniforms(seed, step, L.PURPOSE_NUCLEUS, 1, 1, device=self.dev)
+            post = L.medusa_evaluate_posterior_nucleus(row, self._node0, self._node0, self._npaths1, temperature, top_p,
+                                                       u, ws=self.nuc_ws)
+            return post["next_token"]
+        raise ValueError("mode must be 'typical' or 'nucleus'")
 
     def prefill(self, prompt):
         P = len(prompt)
@@ -300,3 +325,88 @@ class TinyDecoder:
         if int(tree["status"][0].item()) != 0:
             raise RuntimeError("tree spec rejected: %s" % tree["status"].cpu().tolist())
         return [int(t) for t in out[:n_new].cpu()], int(steps.item())
+
+    # ------------------------------------------------------ sampled modes
+    def sample(self, prompt, n_new, mode="typical", temperature=0.7, eps=0.09, delta=0.3, top_p=0.8, seed=0):
+        """Plain sampled decoding, one token per forward: token i (i = 0 after
+        the prompt) drawn under `mode` with keys (seed, i)."""
+        P = len(prompt)
+        if P + n_new > self.S:
+            raise ValueError("the cache holds %d slots" % self.S)
+        _, logits = self.prefill(prompt)
+        nxt = self._sample_last(logits, mode, temperature, eps, delta, top_p, seed, 0)
+        toks = [nxt]
+        for i in range(1, n_new):
+            Lp = P + i - 1
+            _, logits = self.forward(nxt.view(1, 1), self._i32([[Lp]]), self._i32([Lp]), self._mask1)
+            nxt = self._sample_last(logits, mode, temperature, eps, delta, top_p, seed, i)
+            toks.append(nxt)
+        return [int(t) for t in torch.cat(toks).cpu()]
+
+    def medusa_sampled(self, heads, choices, topk, prompt, n_new, mode="typical", temperature=0.7, eps=0.09,
+                       delta=0.3, top_p=0.8, seed=0, record=None):
+        """Medusa decoding in a sampled mode: typical acceptance with a drawn
+        bonus token ('typical'), or nucleus acceptance on Philox uniforms
+        ('nucleus').  The prompt's root is drawn with keys (seed, 0), step s
+        of the loop (s = 1, 2, ...) with (seed, s).  `record`, if a list,
+        receives per step the host copies a caller needs to replay the
+        step's decisions: logits [1][T][V], tree candidates, retrieve, path
+        count, best path, accepted length, next root and the step index
+        (step 0: the prompt's last logits row and the first root).
+        Returns (tokens, accepted length per step)."""
+        if mode not in ("typical", "nucleus"):
+            raise ValueError("mode must be 'typical' or 'nucleus'")
+        P = len(prompt)
+        K = heads["w1"].shape[0]
+        T = choices.shape[0] + 1
+        if P + n_new + T > self.S:
+            raise ValueError("the cache holds %d slots" % self.S)
+        hidden, logits = self.prefill(prompt)
+        root = self._sample_last(logits, mode, temperature, eps, delta, top_p, seed, 0)
+        if record is not None:
+            record.append(dict(step=0, logits=logits[:, -1:, :].cpu().numpy(), next_token=int(root[0])))
+        h_row = hidden[:, P - 1, :]
+        Lp = P
+        out, accepts = [], []
+        ws = torch.zeros(L.medusa_heads_workspace(L.MEDUSA_BF16, 1, self.H, self.V, K, topk), dtype=torch.uint8,
+                         device=self.dev)
+        tree = None
+        s = 0
+        while len(out) < n_new:
+            s += 1
+            r = L.medusa_resblock(h_row, heads["w1"], heads["b1"])
+            ids = L.medusa_lm_head_topk(r, heads["w_lm"], topk, ws=ws)["topk_ids"]
+            plen = self._i32([Lp])
+            if tree is None:
+                tree = L.medusa_build_tree(choices, ids, root, plen)
+            else:
+                L.medusa_tree_candidates(tree["tree_indices"], tree["depth"], ids, root, plen, out=tree)
+            hidden, logits = self.forward(tree["tree_candidates"], tree["position_ids"], plen, tree["tree_mask"])
+            if mode == "typical":
+                post = L.medusa_evaluate_posterior(logits, tree["tree_candidates"], tree["retrieve"],
+                                                   tree["num_paths"], temperature, eps, delta, ws=self.post_ws)
+                nxt = L.medusa_sample_typical(logits, tree["retrieve"], post["best_path"], post["accept_len"],
+                                              temperature, eps, delta, seed, s)
+            else:
+                u = L.medusa_philox_uniforms(seed, s, L.PURPOSE_NUCLEUS, 1, T, device=self.dev)
+                post = L.medusa_evaluate_posterior_nucleus(logits, tree["tree_candidates"], tree["retrieve"],
+                                                           tree["num_paths"], temperature, top_p, u, ws=self.nuc_ws)
+                nxt = post["next_token"]
+            L.medusa_commit_kv(self.k_cache, self.v_cache, plen, tree["retrieve"], post["best_path"],
+                               post["accept_len"])
+            status = tree["status"].cpu().tolist()
+            if status[0] != 0:
+                raise RuntimeError("tree spec rejected: %s" % status)
+            best, acc = int(post["best_path"][0]), int(post["accept_len"][0])
+            path = tree["retrieve"][best].cpu().tolist()
+            cand = tree["tree_candidates"][0].cpu().tolist()
+            out.extend(cand[path[j]] for j in range(acc + 1))
+            accepts.append(acc)
+            if record is not None:
+                record.append(dict(step=s, logits=logits.cpu().numpy(), tree_candidates=np.array([cand], np.int32),
+                                   retrieve=tree["retrieve"].cpu().numpy(), num_paths=int(tree["num_paths"][0]),
+                                   best_path=best, accept_len=acc, next_token=int(nxt[0])))
+            h_row = hidden[:, path[acc], :]
+            Lp += acc + 1
+            root = nxt.clone()
+        return out[:n_new], accepts

@@ -195,3 +195,93 @@ def test_generation_replayed_from_hip_graphs(gpu_device):
     rnd = {key: to_dev(v) for key, v in synth.tiny_heads(cfg, K, seed=2).items()}
     toks, steps = dec.medusa_graph(rnd, choices, 2, prompt, n)
     assert toks == ref
+
+
+def _tree_parents(choices, K, topk):
+    # the tree's parent array depends only on the spec
+    return oracle.build_tree(choices, K, topk, np.zeros((1, K, topk), dtype=np.int32), np.zeros(1, np.int32),
+                             np.zeros(1, np.int32))["parent"]
+
+
+@pytest.mark.parametrize("mode", ["typical", "nucleus"])
+def test_sampled_medusa_decisions_match_oracle(gpu_device, mode):
+    # Medusa decoding in a sampled mode; every step's decisions -- best path,
+    # accepted length, the drawn next root, and the prompt's first root --
+    # equal the oracle's on the step's own logits (the base forward is
+    # checked against the oracle's on its own elsewhere) with the same
+    # Philox keys, wherever the decision clears float error
+    from cases import nucleus_margins, posterior_margins_ok, typical_sample_robust
+    from oracle import sampling as smp
+    cfg = dict(CFG, V=1000)
+    m = synth.tiny_decoder(cfg, seed=1)
+    n, K, k = 40, 3, 2
+    prompt, _ = _prompt_with_margin(m, 12, n, 0.06, range(40))
+    hd, _ = fitted_heads(m, prompt, n, K, seed=5)
+    heads = {key: to_dev(v) for key, v in hd.items()}
+    choices = synth.choices_array(synth.full_tree_choices(K, k), K)
+    parent = _tree_parents(choices, K, k)
+    t, eps, delta, top_p, seed = 0.7, 0.09, 0.3, 0.8, 21
+    dec = TinyDecoder(m, gpu_device, max_slots=256)
+    rec = []
+    toks, accepts = dec.medusa_sampled(heads, to_dev(choices), k, prompt, n, mode=mode, temperature=t, eps=eps,
+                                       delta=delta, top_p=top_p, seed=seed, record=rec)
+    print("mode", mode, "accepts", accepts, flush=True)
+    checked = 0
+    r0 = rec[0]
+    row0 = r0["logits"][0, 0]
+    if mode == "typical":
+        u = smp.uniform(seed, 0, 0, 0, smp.PURPOSE_NEXT_TOKEN)
+        if typical_sample_robust(row0, t, eps, delta, u):
+            assert r0["next_token"] == smp.typical_sample(row0, t, eps, delta, u)
+            checked += 1
+    else:
+        u = smp.uniform(seed, 0, 0, 0, smp.PURPOSE_NUCLEUS)
+        if nucleus_margins(row0, t, top_p, u) >= 1e-5:
+            assert r0["next_token"] == oracle.nucleus_sample(row0, t, top_p, u)
+            checked += 1
+    emitted = []
+    root = r0["next_token"]
+    for r in rec[1:]:
+        s, lg, cand, ret, P = r["step"], r["logits"], r["tree_candidates"], r["retrieve"], r["num_paths"]
+        assert int(cand[0, 0]) == root
+        T = cand.shape[1]
+        if mode == "typical":
+            ok = posterior_margins_ok(lg, dict(tree_candidates=cand, parent=parent), t, eps, delta)
+            if ok:
+                exp = oracle.evaluate_posterior(lg, cand, ret, P, t, eps, delta)
+                assert (r["best_path"], r["accept_len"]) == (int(exp["best_path"][0]), int(exp["accept_len"][0]))
+                node = int(ret[r["best_path"], r["accept_len"]])
+                u = smp.uniform(seed, s, 0, 0, smp.PURPOSE_NEXT_TOKEN)
+                if typical_sample_robust(lg[0, node], t, eps, delta, u):
+                    assert r["next_token"] == smp.typical_sample(lg[0, node], t, eps, delta, u)
+                    checked += 1
+        else:
+            u = smp.uniforms(seed, s, 1, T, smp.PURPOSE_NUCLEUS)
+            if all(nucleus_margins(lg[0, j], t, top_p, u[0, j]) >= 1e-5 for j in range(T)):
+                exp = oracle.evaluate_posterior_nucleus(lg, cand, ret, P, t, top_p, u)
+                assert (r["best_path"], r["accept_len"], r["next_token"]) == (
+                    int(exp["best_path"][0]), int(exp["accept_len"][0]), int(exp["next_token"][0]))
+                checked += 1
+        path = ret[r["best_path"]]
+        emitted.extend(int(cand[0, path[j]]) for j in range(r["accept_len"] + 1))
+        root = r["next_token"]
+    assert emitted[:n] == toks
+    assert checked >= 0.8 * len(rec), (checked, len(rec))
+
+
+def test_sampling_at_low_temperature_is_greedy(gpu_device):
+    # as the temperature goes to 0 the typical set shrinks to the argmax:
+    # plain and Medusa sampled decoding then emit the greedy tokens
+    cfg = dict(CFG, V=1000)
+    m = synth.tiny_decoder(cfg, seed=1)
+    n, K = 24, 3
+    prompt, ref = _prompt_with_margin(m, 12, n, 0.06, range(40))
+    dec = TinyDecoder(m, gpu_device, max_slots=256)
+    assert dec.sample(prompt, n, mode="typical", temperature=1e-3, seed=4) == ref
+    hd, _ = fitted_heads(m, prompt, n, K, seed=5)
+    heads = {key: to_dev(v) for key, v in hd.items()}
+    choices = to_dev(synth.choices_array(synth.full_tree_choices(K, 2), K))
+    toks, accepts = TinyDecoder(m, gpu_device, max_slots=256).medusa_sampled(heads, choices, 2, prompt, n,
+                                                                             mode="typical", temperature=1e-3,
+                                                                             seed=4)
+    assert toks == ref and np.mean(accepts) >= 1.5
