@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--generate", action="store_true",
                     help="run only end-to-end generation on a small LLaMA-style model: plain greedy against "
                          "Medusa greedy (one JSON line)")
+    ap.add_argument("--attention", type=int, default=0, metavar="L",
+                    help="run only tree attention (64-node tree, 32 x 128 heads) at prefix L, --steps calls over "
+                         "eight rotated layers (for kernel traces and counters; one JSON line)")
     ap.add_argument("--tree-sweep", action="store_true",
                     help="run only the tree-shape sweep: step cost and expected tokens per step against the "
                          "number of heads K and tree nodes T (one JSON line)")
@@ -76,6 +79,8 @@ def copy_probe():
 
 class Step:
     """All buffers and pre-marshalled arguments of one verify step."""
+
+    NLOGITS = 64
 
     def __init__(self, w, seed):
         import numpy as np
@@ -145,10 +150,20 @@ class Step:
         self.att_ws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, B, T, Hq, dh, S),
                                   dtype=torch.uint8, device=dev)
 
-        logits, plan = synth.posterior_logits(w, cand, ret, npaths, depth, seed=seed)
-        self.plan = plan
-        self.logits = d(logits)
-        del logits
+        # the acceptance test reads one of NLOGITS logits sets per step, each
+        # with its own planted path (accepted lengths vary from step to
+        # step), 8.19 MB each: 524 MB in all, so a step's logits never sit in
+        # the 256 MB last-level cache
+        self.logit_sets = []
+        self.plans = []
+        for i in range(self.NLOGITS):
+            logits, plan = synth.posterior_logits(w, cand, ret, npaths, depth, seed=seed + 7919 * i)
+            self.logit_sets.append(d(logits))
+            self.plans.append(plan)
+            del logits
+        self.plan = self.plans[0]
+        self.logits = self.logit_sets[0]
+        self.logit_index = 0
         self.post = {n: torch.empty(B, dtype=torch.int32, device=dev)
                      for n in ("best_path", "accept_len", "next_token")}
         self.post_ws = torch.zeros(md.medusa_posterior_workspace(B, T, V), dtype=torch.uint8, device=dev)
@@ -208,6 +223,8 @@ class Step:
 
     def run_posterior(self):
         w, L, t, p = self.w, self.md.lib, self.tree, self.post
+        self.logits = self.logit_sets[self.logit_index]
+        self.logit_index = (self.logit_index + 1) % self.NLOGITS
         rc = L.medusa_evaluate_posterior(w["B"], self.T, w["V"], self.p_max, w["K"] + 1, self.logits.data_ptr(),
                                          t["tree_candidates"].data_ptr(), t["retrieve"].data_ptr(),
                                          t["num_paths"].data_ptr(), w["temperature"], w["eps"], w["delta"],
@@ -274,26 +291,41 @@ def lm_bytes(w):
     return K * V * H * 2 + B * K * H * 4 + B * K * k * 8
 
 
-def cpu_baseline(w, seed, min_steps=3, min_seconds=10.0, max_steps=30):
-    """The oracle on full steps of the same workload, on this host: whole
-    steps are timed until at least ``min_seconds`` of oracle work (and at
-    least ``min_steps`` steps) have run; the median step is reported.
-    Inputs are generated outside the timing."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_inputs(w, seed):
     import oracle
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     x = synth.heads_inputs(w, seed=seed)
     choices = synth.choices_array(
         synth.random_tree_choices(w["depth_counts"], w["topk"], seed=seed, workload_id=w["wid"]), w["K"])
     root = synth.root_token_input(w, seed=seed)
     plen = synth.prefix_lengths(w, seed=seed)
     kc, vc = synth.kv_cache(dict(w, Hkv=w["Hq"]), seed=seed)
-    att = logits = None
+    hd = oracle.heads(x["hidden"], x["w1"], x["b1"], x["w_lm"], w["topk"])
+    tr = oracle.build_tree(choices, w["K"], w["topk"], hd["topk_ids"], root, plen)
+    att = synth.attention_inputs(w, tr["depth"], plen, seed=seed)
+    logits, _ = synth.posterior_logits(w, tr["tree_candidates"], tr["retrieve"], tr["num_paths"], tr["depth"],
+                                       seed=seed)
+    return dict(x=x, choices=choices, root=root, plen=plen, kc=kc, vc=vc, att=att, logits=logits)
+
+
+def _oracle_steps(w, inp, min_steps, min_seconds, max_steps):
+    """Whole oracle verify steps, timed until at least ``min_seconds`` of
+    oracle work (and ``min_steps`` steps) have run; the median step."""
+    import oracle
+
+    x, choices, root, plen, kc, vc = (inp[k] for k in ("x", "choices", "root", "plen", "kc", "vc"))
+    att, logits = inp["att"], inp["logits"]
     runs = []
     spent = 0.0
     while len(runs) < max_steps and (len(runs) < min_steps or spent < min_seconds):
@@ -304,10 +336,6 @@ def cpu_baseline(w, seed, min_steps=3, min_seconds=10.0, max_steps=30):
         tr = oracle.build_tree(choices, w["K"], w["topk"], hd["topk_ids"], root, plen)
         t2 = time.perf_counter()
         times["heads"], times["build_tree"] = t1 - t0, t2 - t1
-        if att is None:
-            att = synth.attention_inputs(w, tr["depth"], plen, seed=seed)
-            logits, _ = synth.posterior_logits(w, tr["tree_candidates"], tr["retrieve"], tr["num_paths"],
-                                               tr["depth"], seed=seed)
         t2 = time.perf_counter()
         oracle.tree_attention(att["q"], att["k_cache"], att["v_cache"], plen, tr["tree_mask"],
                               1.0 / math.sqrt(w["d"]))
@@ -321,13 +349,39 @@ def cpu_baseline(w, seed, min_steps=3, min_seconds=10.0, max_steps=30):
         runs.append(times)
         spent += sum(times.values())
     runs.sort(key=lambda t: sum(t.values()))
-    med = runs[len(runs) // 2]
+    return runs[len(runs) // 2], len(runs), spent
+
+
+def cpu_baseline(w, seed, min_steps=3, min_seconds=10.0, max_steps=30):
+    """The oracle on full steps of the same workload on this host, twice: with
+    every core NumPy's thread pools use, and with one thread pinned to the
+    first core of this process's affinity set.  Inputs are generated outside
+    the timing; each run reports the median step."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    inp = _oracle_inputs(w, seed)
+    med, n, spent = _oracle_steps(w, inp, min_steps, min_seconds, max_steps)
     total = sum(med.values())
+    cpus = sorted(os.sched_getaffinity(0))
+    single = None
+    try:
+        os.sched_setaffinity(0, {cpus[0]})
+        with threadpool_limits(limits=1):
+            smed, sn, sspent = _oracle_steps(w, inp, 2, min_seconds, max_steps)
+        stotal = sum(smed.values())
+        single = {"value": round(1.0 / stotal, 4), "unit": "steps/s", "cores": 1, "pinned_cpu": cpus[0],
+                  "seconds_per_step": round(stotal, 3), "stage_seconds": {k: round(v, 3) for k, v in smed.items()},
+                  "sample": "median of %d full verify steps (%.1f s)" % (sn, sspent)}
+    finally:
+        os.sched_setaffinity(0, set(cpus))
     return {"value": round(1.0 / total, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": "median of %d full verify steps (%.1f s of oracle work) at the same shapes "
                       "(5 heads, 64-node tree, one attention layer at prefix 2048, typical posterior over "
-                      "64x32000, 32-layer commit), fp64 NumPy" % (len(runs), spent),
-            "seconds_per_step": round(total, 3), "stage_seconds": {k: round(v, 3) for k, v in med.items()}}
+                      "64x32000, 32-layer commit), fp64 NumPy, all cores" % (n, spent),
+            "seconds_per_step": round(total, 3), "stage_seconds": {k: round(v, 3) for k, v in med.items()},
+            "single_thread": single, "nproc": os.cpu_count(), "affinity_cpus": len(cpus),
+            "cpu_model": _cpu_model()}
 
 
 def graph_timing(step, steps):
@@ -504,6 +558,40 @@ def attention_prefix_sweep(step, steps):
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
         del kc, vc
     return {"unit": "GB/s", "peak": HBM_PEAK_GBS, "T": T, "Hq": Hq, "d": d, "rows": rows}
+
+
+def attention_only(args):
+    """Tree attention alone at prefix args.attention: the Vicuna-7B layer
+    (64-node tree of the bench's spec, 32 heads x 128, bf16), eight layers of
+    KV rotated, args.steps calls timed with events on the library's stream."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    import synth
+    w = synth.workload("vicuna-7b")
+    dev = torch.device("cuda:0")
+    choices = synth.random_tree_choices(w["depth_counts"], w["topk"], seed=args.seed, workload_id=w["wid"])
+    T, Hq, d, L = len(choices) + 1, w["Hq"], w["d"], args.attention
+    ids = torch.zeros((1, w["K"], w["topk"]), dtype=torch.int32, device=dev)
+    tree = md.medusa_build_tree(torch.from_numpy(synth.choices_array(choices, w["K"])).to(dev), ids,
+                                torch.zeros(1, dtype=torch.int32, device=dev),
+                                torch.full((1,), L, dtype=torch.int32, device=dev))
+    gen = torch.Generator(device=dev).manual_seed(3)
+    q = torch.randn((1, T, Hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    S, nl = L + T, 8
+    kc = [torch.randn((1, Hq, S, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    vc = [torch.randn((1, Hq, S, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    plen = torch.full((1,), L, dtype=torch.int32, device=dev)
+    ws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, 1, T, Hq, d, S), dtype=torch.uint8,
+                     device=dev)
+    us = _time_calls(lambda i: md.medusa_tree_attention(q, kc[i % nl], vc[i % nl], plen, tree["tree_mask"],
+                                                        d ** -0.5, out=out, ws=ws), args.steps)
+    nbytes = 2 * Hq * (L + T) * d * 2 + 2 * T * Hq * d * 2
+    print(json.dumps({"attention": {"L": L, "T": T, "Hq": Hq, "d": d, "max_slots": S, "calls": args.steps,
+                                    "us": round(us, 2), "bytes": nbytes, "achieved": round(nbytes / us / 1e3, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s"}}))
 
 
 def batch8_33b(step, seed, steps):
@@ -869,16 +957,35 @@ def generate_bench(args):
     res = {"plain": {"tokens_per_s": round(n / t_plain, 1), "ms": round(t_plain * 1e3, 2), "forwards": n},
            "plain_graph": dict({"tokens_per_s": round(n / t_plain_g, 1), "ms": round(t_plain_g * 1e3, 2)},
                                **compare(ref_g))}
+    def histogram(accepts):
+        h = [0] * (K + 1)
+        for a in accepts:
+            h[a] += 1
+        return h
+
     for name, heads in head_sets.items():
         (toks, accepts, _), t = timed(lambda: dec.medusa(heads, choices, topk, prompt, n))
         res["medusa_" + name] = dict({"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2),
                                       "steps": len(accepts), "tokens_per_step": round(n / len(accepts), 3),
+                                      "accept_len_histogram": histogram(accepts),
                                       "speedup_vs_plain": round(t_plain / t, 3)}, **compare(toks))
         (toks, steps), t = timed(lambda: dec.medusa_graph(heads, choices, topk, prompt, n))
         res["medusa_" + name + "_graph"] = dict({"tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2),
                                                  "steps_run": steps,
                                                  "speedup_vs_plain_graph": round(t_plain_g / t, 3)},
                                                 **compare(toks))
+    # sampled modes (temperature 0.7): plain sampling one token per forward,
+    # and Medusa with typical acceptance and a drawn bonus token, fitted heads
+    samp = dict(temperature=0.7, eps=0.09, delta=0.3, seed=args.seed + 5)
+    st, t_ps = timed(lambda: dec.sample(prompt, n, mode="typical", **samp))
+    res["plain_sampled_typical"] = {"tokens_per_s": round(n / t_ps, 1), "ms": round(t_ps * 1e3, 2)}
+    heads = head_sets["fitted_heads"]
+    (toks, accepts), t = timed(lambda: dec.medusa_sampled(heads, choices, topk, prompt, n, mode="typical", **samp))
+    res["medusa_sampled_typical_fitted_heads"] = {
+        "tokens_per_s": round(n / t, 1), "ms": round(t * 1e3, 2), "steps": len(accepts),
+        "tokens_per_step": round(n / len(accepts), 3), "accept_len_histogram": histogram(accepts),
+        "speedup_vs_plain_sampled": round(t_ps / t, 3),
+        "note": "heads fitted to the greedy continuation; sampled continuations leave it, so fewer are accepted"}
     print(json.dumps({"generate": res, "plain_top2_gap": {"smallest": round(float(gaps.min()), 5),
                                                          "at_step": int(np.argmin(gaps)),
                                                          "median": round(float(np.median(gaps)), 5)},
@@ -898,6 +1005,9 @@ def main():
         sys.exit(2)
     if args.tree_sweep:
         tree_sweep(args)
+        return
+    if args.attention:
+        attention_only(args)
         return
     if args.generate:
         generate_bench(args)
@@ -938,6 +1048,11 @@ def main():
         step.run(ev[s])
     torch.cuda.synchronize()
     stage_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(nb)] for i in range(nst)]
+    # accepted lengths over one pass of the logits sets (untimed)
+    hist = [0] * (w["K"] + 1)
+    for _ in range(Step.NLOGITS):
+        step.run_posterior()
+        hist[int(step.post["accept_len"].cpu()[0])] += 1
 
     def stats(xs):
         xs = sorted(xs)
@@ -947,7 +1062,6 @@ def main():
     stages = {name: stats(stage_ms[i]) for i, name in enumerate(Step.STAGES)}
     lm_mean_s = sum(lm_ms) / len(lm_ms) / 1000.0
     achieved = lm_bytes(w) / lm_mean_s / 1e9
-    acc = int(step.post["accept_len"].cpu()[0])
 
     result = {
         "metric": METRIC,
@@ -975,7 +1089,11 @@ def main():
                        "(medusa_build_tree) is built once per tree spec, per step only its candidates "
                        "and positions are gathered (medusa_tree_candidates)" % nb,
         "build_tree_us": round(_time_calls(lambda i: step.run_build_tree(), 50), 2),
-        "tokens_per_step": acc + 1,
+        "tokens_per_step": round(1.0 + sum(a * c for a, c in enumerate(hist)) / sum(hist), 4),
+        "accept_len_histogram": hist,
+        "accept_len_note": "accepted lengths of the %d rotated logits sets, each with a planted path of "
+                           "Binomial(depth, 1/2) steps (the pages' 2.5-3 tokens per step); tokens per step = "
+                           "accepted length + 1 (the bonus token)" % Step.NLOGITS,
     }
     if not args.no_graph:
         result["graph"] = graph_timing(step, args.steps)

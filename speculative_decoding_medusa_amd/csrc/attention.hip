@@ -20,9 +20,9 @@
 // (ds_read_b64_tr_b16).  Online softmax in base 2 with fp32 accumulators and
 // a lazily raised reference.  After the last round the four key groups'
 // states are merged through LDS.  A sequence with one split writes its
-// output directly; otherwise each split writes its partial (O unnormalised,
-// m, l) and a second kernel merges the splits (log-sum-exp) and writes the
-// output.
+// output directly; otherwise each split writes its partial (O / l in half
+// precision, m and l in float32) and a second kernel merges the splits
+// (log-sum-exp) and writes the output.
 //
 // f32 path: one wave per (sequence, head, query), online softmax over
 // 64-key chunks on the VALU.
@@ -300,7 +300,7 @@ template <int D>
 __global__ __launch_bounds__(kAttnThreads, 1) void tree_attn_bf16_kernel(
     int T, int Hq, int max_slots, int nsplit_max, int split_keys, int nqb, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_len,
-    const uint8_t* __restrict__ tree_mask, float scale_log2, float* __restrict__ part_o,
+    const uint8_t* __restrict__ tree_mask, float scale_log2, _Float16* __restrict__ part_o,
     float2* __restrict__ part_ml, uint16_t* __restrict__ out) {
   using Lay = AttnLayout<D>;
   constexpr int DT = D / 16, DS = D / 32;
@@ -311,8 +311,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void tree_attn_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t qtile[kQBlock * Lay::ROWB];
   __shared__ uint64_t mbits[kQBlock][kMaxNodes / 64];
 
-  const int split = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z / nqb, qb = blockIdx.z - b * nqb;
+  // Workgroup i is dispatched to XCD i % 8 (round robin): the splits of a
+  // (sequence, head, query block) group take ids congruent mod 8 where the
+  // grid allows, so they share one L2 for their Q and mask loads.  Only the
+  // placement depends on this; any order is correct.
+  int split, gi;
+  {
+    const int ns_l = static_cast<int>(gridDim.x);
+    const int ng = static_cast<int>(gridDim.y * gridDim.z);
+    const int i = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int blk = i / (8 * ns_l), rem = i - blk * 8 * ns_l;
+    const int width = min(8, ng - 8 * blk);   // groups in this block of ids
+    split = rem / width;
+    gi = 8 * blk + rem % width;
+  }
+  const int h = gi % Hq, bz = gi / Hq;
+  const int b = bz / nqb, qb = bz - b * nqb;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int qh = wave & 1, kg = wave >> 1;             // query half, key group
@@ -523,24 +537,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void tree_attn_bf16_kernel(
       }
       return;
     }
-    // this split's partial: [group][split][64 rows][D] and
-    // [group][split][64] (m, l), group = (sequence, head, query block)
+    // this split's partial: O / l in half precision [group][split][64
+    // rows][D] and (m, l) in float32 [group][split][64], group = (sequence,
+    // head, query block).  O / l is a convex combination of V rows, so its
+    // range is theirs; the merge weights each by l e^(m - M).
     const size_t grp = bh * nqb + qb;
-    float* po = part_o + (grp * nsplit_max + split) * kQBlock * D;
+    _Float16* po = part_o + (grp * nsplit_max + split) * kQBlock * D;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int row = qh * 32 + u * 16 + n;
+      const float inv = st.l_part[u] > 0.f ? 1.f / st.l_part[u] : 0.f;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + row * D + t * 16 + 4 * g) = st.o[u][t];
+      for (int t = 0; t < DT; ++t) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 v = {static_cast<_Float16>(st.o[u][t][0] * inv), static_cast<_Float16>(st.o[u][t][1] * inv),
+                      static_cast<_Float16>(st.o[u][t][2] * inv), static_cast<_Float16>(st.o[u][t][3] * inv)};
+        *reinterpret_cast<h4*>(po + row * D + t * 16 + 4 * g) = v;
+      }
       if (g == 0) part_ml[(grp * nsplit_max + split) * kQBlock + row] = float2{st.m_run[u], st.l_part[u]};
     }
   }
 }
 
 // Merge the splits of each (sequence, head, query) by log-sum-exp.  D/4
-// threads per query, four output columns each (16-byte partial loads); a
-// 256-thread workgroup takes 1024/D consecutive queries of one (sequence,
-// head), so a wave instruction reads 1 KB of one split contiguously.
+// threads per query, four output columns each (8-byte half-precision
+// partial loads); a 256-thread workgroup takes 1024/D consecutive queries of
+// one (sequence, head), so a wave instruction reads 512 bytes of one split
+// contiguously.
 // Splits are taken eight at a time with all their loads issued together,
 // merged online against a running maximum.  The first eight are addressed
 // within the workspace's nsplit_max splits, so their loads go out with the
@@ -550,10 +573,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void tree_attn_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, int Hq, int max_slots, int nsplit_max,
                                                               int split_keys, const int32_t* __restrict__ prefix_len,
-                                                              const float* __restrict__ part_o,
+                                                              const _Float16* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml,
                                                               uint16_t* __restrict__ out) {
   constexpr int TPQ = D / 4, QPW = 256 / TPQ, U = 8;
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   const int t = threadIdx.x % TPQ;
   // B * Hq * T * D / 4 stays below 2^31 (B <= 16, Hq <= 1024, T <= 256)
   const unsigned Q = blockIdx.x * QPW + threadIdx.x / TPQ;
@@ -568,13 +592,13 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
   float M = NEG, den = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float2 ml[U];
-  float4 ov[U];
+  h4 ov[U];
   auto load = [&](int s0, int smax) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const size_t r = (grp * nsplit_max + min(s0 + u, smax - 1)) * kQBlock + row;
       ml[u] = part_ml[r];
-      ov[u] = *reinterpret_cast<const float4*>(part_o + r * D + 4 * t);
+      ov[u] = *reinterpret_cast<const h4*>(part_o + r * D + 4 * t);
     }
   };
   load(0, nsplit_max);
@@ -597,12 +621,12 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(int B, int T, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < ns && ml[u].x != NEG) {
-        const float w = exp2f(ml[u].x - ref);
-        acc[0] += w * ov[u].x;
-        acc[1] += w * ov[u].y;
-        acc[2] += w * ov[u].z;
-        acc[3] += w * ov[u].w;
-        den += w * ml[u].y;
+        const float w = exp2f(ml[u].x - ref) * ml[u].y;   // the split's weight: l e^(m - M)
+        acc[0] += w * static_cast<float>(ov[u][0]);
+        acc[1] += w * static_cast<float>(ov[u][1]);
+        acc[2] += w * static_cast<float>(ov[u][2]);
+        acc[3] += w * static_cast<float>(ov[u][3]);
+        den += w;
       }
     }
     M = Mn;
@@ -675,13 +699,13 @@ namespace {
 
 using namespace medusa;
 
-// Workspace: the splits' partials (O unnormalised [group][split][64][d]
-// float32 and (m, l) [group][split][64]; group = (sequence, head, query
-// block)), sized for the most splits any launch at this max_slots uses.
+// Workspace: the splits' partials (O / l [group][split][64][d] half
+// precision and (m, l) [group][split][64] float32; group = (sequence, head,
+// query block)), sized for the most splits any launch at this max_slots uses.
 int attn_nsplit_max(int max_slots) { return num_splits(max_slots, kMinSplitKeys); }
 size_t attn_part_o_bytes(int B, int T, int Hq, int d, int max_slots) {
   const size_t nqb = static_cast<size_t>((T + kQBlock - 1) / kQBlock);
-  return medusa_host::round_up(static_cast<size_t>(B) * Hq * nqb * attn_nsplit_max(max_slots) * kQBlock * d * 4, 256);
+  return medusa_host::round_up(static_cast<size_t>(B) * Hq * nqb * attn_nsplit_max(max_slots) * kQBlock * d * 2, 256);
 }
 size_t attn_part_ml_bytes(int B, int T, int Hq, int max_slots) {
   const size_t nqb = static_cast<size_t>((T + kQBlock - 1) / kQBlock);
@@ -740,7 +764,7 @@ extern "C" int medusa_tree_attention(int dtype, int B, int T, int Hq, int d, int
   const int nsm = attn_nsplit_max(max_slots);
   const int nsl = num_splits(max_slots, sk);   // splits of the launch (no sequence uses more)
   char* base = static_cast<char*>(ws);
-  float* part_o = reinterpret_cast<float*>(base);
+  _Float16* part_o = reinterpret_cast<_Float16*>(base);
   float2* part_ml = reinterpret_cast<float2*>(base + attn_part_o_bytes(B, T, Hq, d, max_slots));
   const float sl2 = scale * kLog2e;
   dim3 grid(nsl, Hq, B * nqb);

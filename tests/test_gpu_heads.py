@@ -199,3 +199,25 @@ def test_heads_vicuna13b(gpu_device):
     w = synth.workload("vicuna-13b")
     case = heads_case(w, seed=0)
     _check(case, _run(case, w, keep_logits=False), w)
+
+
+@pytest.mark.parametrize("H", [4096, 5120, 6656])
+def test_heads_logit_error_from_r_planes(gpu_device, H):
+    # r enters the lm_head GEMV as two bf16 planes (hi = bf16(r), lo =
+    # bf16(r - hi)), about 16 significant bits of the float32 r; the logits
+    # of that product stay within the float32 bar (1e-4) of the fp64 oracle's
+    # z = Wlm r at the Vicuna-7B, 13B and 33B hidden sizes
+    import oracle
+    w = synth.workload("vicuna-7b", H=H, K=2)
+    x = synth.heads_inputs(w, seed=H)
+    h, w1, b1, wlm = (to_dev(x[n]) for n in ("hidden", "w1", "b1", "w_lm"))
+    got = md.medusa_heads(h, w1, b1, wlm, w["topk"], keep_logits=True, keep_r=True)
+    torch.cuda.synchronize()
+    r = oracle.resblock(x["hidden"], x["w1"], x["b1"])
+    z = np.stack([oracle.lm_head_logits(r, x["w_lm"], head=j) for j in range(w["K"])], axis=1)
+    gl = to_host(got["logits"]).astype(np.float64)
+    err = rel_err(gl, z)
+    abs_err = float(np.max(np.abs(gl - z)))
+    print("H %d logits max rel err %.3e, max abs err %.3e (logit std %.3f)" % (H, err, abs_err, float(z.std())),
+          flush=True)
+    assert err < 1e-4
