@@ -201,12 +201,13 @@ def test_heads_vicuna13b(gpu_device):
     _check(case, _run(case, w, keep_logits=False), w)
 
 
-@pytest.mark.parametrize("H", [4096, 5120, 6656])
+@pytest.mark.parametrize("H", [4096, 5120, 6656, 8192])
 def test_heads_logit_error_from_r_planes(gpu_device, H):
     # r enters the lm_head GEMV as two bf16 planes (hi = bf16(r), lo =
     # bf16(r - hi)), about 16 significant bits of the float32 r; the logits
     # of that product stay within the float32 bar (1e-4) of the fp64 oracle's
-    # z = Wlm r at the Vicuna-7B, 13B and 33B hidden sizes
+    # z = Wlm r at the Vicuna-7B, 13B and 33B hidden sizes and at 8192, the
+    # largest hidden size the row-diagonal kernels take
     import oracle
     w = synth.workload("vicuna-7b", H=H, K=2)
     x = synth.heads_inputs(w, seed=H)
