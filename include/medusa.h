@@ -401,8 +401,10 @@ int medusa_commit_kv(int dtype, int B, int n_layers, int H, int d, int max_slots
  * Packed layout (medusa_base_lm_head_packed_bytes(H, V) bytes): for tile
  * t = v / 16, k step s = k / 32 and lane l = 16 g + n, the 16 bytes
  * W[16 t + n][32 s + 8 g .. 32 s + 8 g + 7] sit at byte offset
- * (((t / 2) * ceil(H / 32) + s) * 2 + t % 2) * 1024 + l * 16, with the
- * tile count padded to an even number; entries past V or H are zero.
+ * ((s * P + t / 2) * 2 + t % 2) * 1024 + l * 16, with P = ceil(V / 32)
+ * tile pairs (the tile count padded to an even number); entries past V or
+ * H are zero.  k steps outermost: all workgroups stream one k range of the
+ * whole matrix at a time.
  * The weights are static, so a caller packs them once.
  * medusa_base_lm_head_packed_bytes returns 0 for invalid sizes.
  * ------------------------------------------------------------------- */

@@ -5,8 +5,9 @@
 // HBM once.  By shape:
 //
 //  * bf16, batch <= 2, H <= 8192 (the verify step's shape): row-diagonal
-//    kernels.  Each wave streams a contiguous block of whole weight rows
-//    (one 1 KB wave instruction per 512 elements) and takes each row's dot
+//    kernels.  Each wave streams whole weight rows (one 1 KB wave
+//    instruction per 512 elements; the ResBlock's waves take contiguous
+//    blocks of rows, the lm_head's interleave) and takes each row's dot
 //    product as the trace of a v_mfma_f32_16x16x32_bf16 whose A operand
 //    holds the activations at the same positions.  lm_head logits go into
 //    per-wave top-k lists in registers; the last workgroup of each head to
@@ -529,10 +530,43 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_f32_kernel(
 // (g, n) over k): the trace of C accumulated over s is the row's logit.
 // Only the diagonal is used, but at two MFMAs (r's hi and lo bf16 halves)
 // per KB the matrix cores stay far below the time the KB takes to arrive.
-// Each wave streams its own contiguous block of rows (hundreds of KB), row
-// loads double-buffered in registers; r's split planes stay in registers for
+// Each wave streams rows w, w + S, w + 2S, ... of its head (w its index
+// among the head's S waves: see DiagRows), row loads double-buffered in
+// registers; r's split planes stay in registers for
 // the whole kernel.  Logits of 64 consecutive rows gather one per lane and
 // are offered to the wave's top-k lists together.
+// The rows a wave streams: n rows r0, r0 + rs, ... of `total`.  With
+// row_stride 1 each wave takes its own contiguous block of rows_per_wave
+// rows; with row_stride = the waves per head, wave w takes rows w, w + rs,
+// ..., so at any moment the waves of a head read neighbouring rows and the
+// head's reads sweep its weights front to back (fewer DRAM pages and
+// translations open at once than a thousand scattered streams).  row(i)
+// clamps to the wave's last row (to row `total` - 1 for a wave with none),
+// so prefetches past the end stay in bounds.
+struct DiagRows {
+  int r0, rs, n;
+  __device__ __forceinline__ int row(int i) const {
+    const int last = n > 0 ? r0 + (n - 1) * rs : r0;
+    return min(min(r0 + i * rs, last), total_m1);
+  }
+  int total_m1;
+};
+
+__device__ __forceinline__ DiagRows diag_rows(int wv, int rows_per_wave, int row_stride, int total) {
+  DiagRows d;
+  d.total_m1 = total - 1;
+  if (row_stride <= 1) {
+    d.r0 = wv * rows_per_wave;
+    d.rs = 1;
+    d.n = max(0, min(rows_per_wave, total - d.r0));
+  } else {
+    d.r0 = wv;
+    d.rs = row_stride;
+    d.n = wv < total ? (total - 1 - wv) / row_stride + 1 : 0;
+  }
+  return d;
+}
+
 __host__ __device__ constexpr int diag_nstmax(int nst) { return nst <= 4 ? 4 : (nst <= 8 ? 8 : (nst <= 13 ? 13 : 16)); }
 
 template <int NSTMAX>
@@ -628,6 +662,7 @@ __device__ __forceinline__ float put_lane(float v, float x, int slot) {
 // rows in parallel, one coalesced store per sequence.
 template <int NSTMAX, int NB, bool FULL>
 __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int H, int K, int rows_per_wave,
+                                                                      int row_stride,
                                                                       const uint16_t* __restrict__ hidden,
                                                                       const uint16_t* __restrict__ w1,
                                                                       const uint16_t* __restrict__ b1,
@@ -644,20 +679,21 @@ __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int
     for (int s = 0; s < NSTMAX; ++s)
       ah[b][s] = (b < B && 512 * s + e0 < H) ? ld16(hidden + static_cast<size_t>(b) * H + 512 * s + e0) : zero;
 
-  const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
-  const int r1 = min(r0 + rows_per_wave, H);
-  if (r1 <= r0) return;
+  const DiagRows dr = diag_rows(wg * kHeadsWaves + wave, rows_per_wave, row_stride, H);
+  if (dr.n == 0) return;
   const uint16_t* wbase = w1 + static_cast<size_t>(j) * H * H;
   float gath[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) gath[b] = 0.f;
 
-  auto take = [&](int row, const float (&dot)[NB]) {
-    const int slot = (row - r0) & 63;
+  // row i of the wave's sequence: its dot product into lane i % 64; every
+  // 64 rows (and at the end) the gathered rows are finished in parallel
+  auto take = [&](int i, const float (&dot)[NB]) {
+    const int slot = i & 63;
 #pragma unroll
     for (int b = 0; b < NB; ++b) gath[b] = put_lane(gath[b], dot[b], slot);
-    if (slot == 63 || row == r1 - 1) {
-      const int myrow = row - slot + lane;
+    if (slot == 63 || i == dr.n - 1) {
+      const int myrow = dr.r0 + (i - slot + lane) * dr.rs;
       if (lane <= slot) {
         const float bias = bf16_to_f32(b1[static_cast<size_t>(j) * H + myrow]);
 #pragma unroll
@@ -675,27 +711,26 @@ __global__ __launch_bounds__(kHeadsThreads) void resblock_diag_kernel(int B, int
   // rotated double buffer, as in the row-diagonal lm_head kernel
   u32x4 wa[NSTMAX], wb[NSTMAX];
   float dot[NB];
-  const int last = r1 - 1;
-  diag_load_row<NSTMAX>(wbase + static_cast<size_t>(r0) * H, H, e0, wa);
-  diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0 + 1, last)) * H, H, e0, wb);
-  int row = r0;
-  for (; row + 1 < r1; row += 2) {
+  diag_load_row<NSTMAX>(wbase + static_cast<size_t>(dr.row(0)) * H, H, e0, wa);
+  diag_load_row<NSTMAX>(wbase + static_cast<size_t>(dr.row(1)) * H, H, e0, wb);
+  int i = 0;
+  for (; i + 1 < dr.n; i += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_dot<NSTMAX, NB, FULL, true>(wa, ah, H, e0, wbase + static_cast<size_t>(min(row + 2, last)) * H, dot);
-    take(row, dot);
+    diag_row_dot<NSTMAX, NB, FULL, true>(wa, ah, H, e0, wbase + static_cast<size_t>(dr.row(i + 2)) * H, dot);
+    take(i, dot);
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_dot<NSTMAX, NB, FULL, true>(wb, ah, H, e0, wbase + static_cast<size_t>(min(row + 3, last)) * H, dot);
-    take(row + 1, dot);
+    diag_row_dot<NSTMAX, NB, FULL, true>(wb, ah, H, e0, wbase + static_cast<size_t>(dr.row(i + 3)) * H, dot);
+    take(i + 1, dot);
   }
-  if (row < r1) {
+  if (i < dr.n) {
     diag_row_dot<NSTMAX, NB, FULL, false>(wa, ah, H, e0, wbase, dot);
-    take(row, dot);
+    take(i, dot);
   }
 }
 
 template <int NSTMAX, int NB, bool FULL>
 __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
-    int B, int H, int V, int K, int k, int rows_per_wave, int G, const float* __restrict__ r,
+    int B, int H, int V, int K, int k, int rows_per_wave, int row_stride, int G, const float* __restrict__ r,
     const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i,
     int* __restrict__ counters, int fuse) {
@@ -708,9 +743,8 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   const int e0 = 8 * lane;
   const float NEG = -__builtin_huge_valf();
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int r0 = (wg * kHeadsWaves + wave) * rows_per_wave;
-  const int r1 = min(r0 + rows_per_wave, V);
-  const int last = r1 - 1;   // r1 >= 1; an empty block (r0 > last) still loads row `last`
+  // a wave with no rows (n == 0) still loads a valid row (dr.row clamps)
+  const DiagRows dr = diag_rows(wg * kHeadsWaves + wave, rows_per_wave, row_stride, V);
   const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
 
   // Prologue in one memory round trip: a round of r loads (clamped, with no
@@ -736,8 +770,8 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
       }
     }
     if (p0 == 0) {
-      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0, last)) * H, H, e0, wa);
-      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(r0 + 1, last)) * H, H, e0, wb);
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(dr.row(0)) * H, H, e0, wa);
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(dr.row(1)) * H, H, e0, wb);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -773,16 +807,18 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     cnt[b] = 0;
   }
 
-  // gather row `row`'s logits into lane (row - r0) % 64; flush every 64 rows
-  auto offer = [&](int row, const float (&lg)[NB]) {
-    const int slot = (row - r0) & 63;
+  // gather the logits of row i of the wave's sequence into lane i % 64;
+  // flush every 64 rows
+  auto offer = [&](int i, const float (&lg)[NB]) {
+    const int slot = i & 63;
+    const int row = dr.r0 + i * dr.rs;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       gath[b] = put_lane(gath[b], lg[b], slot);
       if (logits_out != nullptr && lane == 0 && b < B) logits_out[(static_cast<size_t>(b) * K + j) * V + row] = lg[b];
     }
-    if (slot == 63 || row == r1 - 1) {
-      const int myrow = row - slot + lane;
+    if (slot == 63 || i == dr.n - 1) {
+      const int myrow = dr.r0 + (i - slot + lane) * dr.rs;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         if (b >= B) continue;
@@ -806,20 +842,18 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   // neither the loop nor the tail; with no branch around both, the
   // prologue's loads cannot be sunk below its conversions.
   float lg[NB];
-  int row = r0;
-  for (; row + 1 < r1; row += 2) {
+  int i = 0;
+  for (; i + 1 < dr.n; i += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_logits<NSTMAX, NB, FULL, true>(wa, ahi, alo, H, e0, wbase + static_cast<size_t>(min(row + 2, last)) * H,
-                                            lg);
-    offer(row, lg);
+    diag_row_logits<NSTMAX, NB, FULL, true>(wa, ahi, alo, H, e0, wbase + static_cast<size_t>(dr.row(i + 2)) * H, lg);
+    offer(i, lg);
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_logits<NSTMAX, NB, FULL, true>(wb, ahi, alo, H, e0, wbase + static_cast<size_t>(min(row + 3, last)) * H,
-                                            lg);
-    offer(row + 1, lg);
+    diag_row_logits<NSTMAX, NB, FULL, true>(wb, ahi, alo, H, e0, wbase + static_cast<size_t>(dr.row(i + 3)) * H, lg);
+    offer(i + 1, lg);
   }
-  if (row < r1) {
+  if (i < dr.n) {
     diag_row_logits<NSTMAX, NB, FULL, false>(wa, ahi, alo, H, e0, wbase, lg);
-    offer(row, lg);
+    offer(i, lg);
   }
   // every wave publishes its own lists (list wg * 4 + wave of head j)
   const int nlists = G * kHeadsWaves;
@@ -887,8 +921,8 @@ struct LmGrid {
 };
 
 // Resident waves per SIMD the row-diagonal lm_head grid is sized for: one
-// measured best at the Vicuna-7B shape (fewer, longer contiguous streams,
-// and fewer lists to merge).
+// measured best at the Vicuna-7B shape (fewer loads in flight per compute
+// unit, fewer lists to merge; two per SIMD: 207 us against 204.6 us).
 constexpr int kDiagWavesPerSimd = 1;
 constexpr int kMaxWavesPerSimd = 8;
 
@@ -979,6 +1013,14 @@ int resblock_rows_per_wave(int H, int K, int wps) {
   return static_cast<int>(rpw < 1 ? 1 : rpw);
 }
 
+// Row order of the row-diagonal kernels with G workgroups per head.  The
+// lm_head (V rows of 8 KB per head at H 4096) interleaves its waves over the
+// rows: 204.6 us per call at the Vicuna-7B shape against 207.6-209 us with a
+// contiguous block per wave.  The ResBlock (H rows, about twenty per wave)
+// measured 0.3-0.6 us faster with contiguous blocks, and keeps them.
+int lm_row_stride(int G) { return G * kHeadsWaves; }
+int res_row_stride(int /*G*/) { return 1; }
+
 int launch_resblock(int dtype, int B, int H, int K, const void* hidden, const void* w1, const void* b1,
                     float* r, hipStream_t st) {
   const int nst = (H + 511) / 512;
@@ -992,10 +1034,10 @@ int launch_resblock(int dtype, int B, int H, int K, const void* hidden, const vo
     const int G = (H + kHeadsWaves * rpw - 1) / (kHeadsWaves * rpw);                                       \
     if (H == (NS) * 512)                                                                                   \
       hipLaunchKernelGGL((resblock_diag_kernel<NS, NB, true>), dim3(G, K), dim3(kHeadsThreads), 0, st, B, H, \
-                         K, rpw, hh, ww, bb, r);                                                             \
+                         K, rpw, res_row_stride(G), hh, ww, bb, r);                                         \
     else                                                                                                   \
       hipLaunchKernelGGL((resblock_diag_kernel<NS, NB, false>), dim3(G, K), dim3(kHeadsThreads), 0, st, B, \
-                         H, K, rpw, hh, ww, bb, r);                                                          \
+                         H, K, rpw, res_row_stride(G), hh, ww, bb, r);                                      \
   } while (0)
     const int ns = diag_nstmax(nst);
     if (ns == 4) {
@@ -1067,11 +1109,13 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
     fused = lg.lists * topk <= kHeadsThreads * kFusedMergeKeys;                                               \
     if (H == (NS) * 512)                                                                                      \
       hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, true>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H,  \
-                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i,           \
+                         V, K, topk, lg.rows_per_wave, lm_row_stride(lg.G), lg.G, r, w, logits, ids, vals,    \
+                         cand_v, cand_i,                                                                        \
                          counters, fused ? 1 : 0);                                                              \
     else                                                                                                      \
       hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, false>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, \
-                         V, K, topk, lg.rows_per_wave, lg.G, r, w, logits, ids, vals, cand_v, cand_i,           \
+                         V, K, topk, lg.rows_per_wave, lm_row_stride(lg.G), lg.G, r, w, logits, ids, vals,    \
+                         cand_v, cand_i,                                                                        \
                          counters, fused ? 1 : 0);                                                              \
   } while (0)
     const int ns = diag_nstmax(lg.nst);

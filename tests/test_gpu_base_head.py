@@ -40,14 +40,14 @@ def _inputs(M, H, V, seed):
 def _packed_reference(w):
     """The documented packed layout of bf16 bits w [V][H]: for tile t, k step
     s and lane l = 16 g + n, 8 elements W[16 t + n][32 s + 8 g ..] (zero past
-    V or H, tile count padded to even), ordered tile pair, step, tile within
+    V or H, tile count padded to even), ordered step, tile pair, tile within
     the pair, lane."""
     V, H = w.shape
     Vt, S = (V + 31) // 32 * 2, (H + 31) // 32
     pad = np.zeros((Vt * 16, S * 32), dtype=np.uint16)
     pad[:V, :H] = w
     t = pad.reshape(Vt // 2, 2, 16, S, 4, 8)          # [pair][q][n][s][g][e]
-    return np.ascontiguousarray(t.transpose(0, 3, 1, 4, 2, 5)).reshape(-1)   # [pair][s][q][g][n][e]
+    return np.ascontiguousarray(t.transpose(3, 0, 1, 4, 2, 5)).reshape(-1)   # [s][pair][q][g][n][e]
 
 
 @pytest.mark.parametrize("V,H", [(1, 8), (17, 40), (300, 72), (1000, 264)])
