@@ -317,73 +317,33 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_sample_kernel(int V, cons
 // ---------------------------------------------------------------------------
 // Rows of at most 32768 tokens: the whole row's order keys stay in LDS
 // (padded by one word per 32 so that a thread's contiguous chunk is read
-// without bank conflicts) beside one shared mass histogram; 1024 threads.
-// The mass of the keys above kappa and the number of kappa tokens come out
-// of the three exact histograms, so after the load only the first radix
-// walk evaluates every exponential; the last walk evaluates those of the
-// nucleus.
+// without bank conflicts), 1024 threads.  The boundary key kappa is found in
+// five walks, each a 256-bucket histogram of masses followed by a pick on
+// one wave:
+//   A. over every token, buckets linear in (max - x) / temperature over the
+//      row's range (at most 40 binary orders of magnitude of mass: below
+//      that masses are zero), so equal values share a bucket and a higher
+//      bucket holds only larger values; the masses spread over many
+//      buckets, so the LDS atomics rarely collide;
+//   B-E. 8-bit radix digits of the order key over the tokens of the bucket
+//      chosen in A (a contiguous range of keys), first gathered into a short
+//      LDS list when they are few, so that these walks touch only them.  A
+//      bucket of at most 256 tokens (the usual case) skips B-E: each of its
+//      tokens sums the masses above and at its own key over the bucket.
+// The first c kappa tokens (by id) complete the nucleus as in the kernel
+// above.  The draw is one workgroup scan of every thread's (mass above
+// kappa, kappa count) over its chunk of 32 tokens in id order; the one
+// thread whose interval holds the target walks its chunk.  The same
+// fixed-point masses give the same draws as the kernel above.
 constexpr int kNlThreads = 1024;
 constexpr int kNlWaves = kNlThreads / kWave;
 constexpr int kNlMaxV = 32768;
 constexpr int kNlChunk = kNlMaxV / kNlThreads;   // tokens per thread in the id-ordered walk
+constexpr int kNlBuckets = 256;
+constexpr int kNlList = 4096;                    // bucket A's tokens gathered for walks B-E
+constexpr int kNlSmall = 256;                    // a bucket this small is resolved directly
 
 __device__ __forceinline__ int nl_pad(int i) { return i + (i >> 5); }
-
-template <typename X>
-__device__ __forceinline__ X nl_block_excl_scan(X v, X* sh, int lane, int wave, X& total) {
-  const X inc = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) sh[wave] = inc;
-  __syncthreads();
-  X off = 0, all = 0;
-  for (int w = 0; w < kNlWaves; ++w) {
-    const X y = sh[w];
-    off += w < wave ? y : X(0);
-    all += y;
-  }
-  total = all;
-  __syncthreads();
-  return off + inc - v;
-}
-
-// nuc_pick over the whole workgroup: thread tid owns buckets [2 tid, 2 tid
-// + 2) of the 2048 (one 16-byte LDS read each, no bank conflicts); the
-// mass above them is the exact total minus a prefix scan.  Every thread
-// gets the digit; `above` is valid in every thread.
-__device__ __forceinline__ int nl_pick(const u64* h, int nb, u64 need, int tid, int lane, int wave, u64* sh_u64,
-                                       int* sh_int, u64& above) {
-  const int b0 = 2 * tid;
-  const bool live = b0 < nb;
-  const u64 h0 = live ? h[b0] : 0, h1 = live ? h[b0 + 1] : 0;
-  u64 total;
-  const u64 excl = nl_block_excl_scan(h0 + h1, sh_u64, lane, wave, total);
-  const u64 up1 = total - excl - h0 - h1;   // buckets above b0 + 1
-  const u64 up0 = up1 + h1;                 // buckets above b0
-  int cand = -1, low = 0x7fffffff;
-  if (h1 > 0 && up1 + h1 >= need) cand = b0 + 1;
-  else if (h0 > 0 && up0 + h0 >= need) cand = b0;
-  if (h0 > 0) low = b0;
-  else if (h1 > 0) low = b0 + 1;
-  cand = wave_max_i(cand);
-  low = wave_min_i(low);
-  if (lane == 0) {
-    sh_int[wave] = cand;
-    sh_int[kNlWaves + wave] = low;
-  }
-  __syncthreads();
-  int d = -1, lo = 0x7fffffff;
-  for (int w = 0; w < kNlWaves; ++w) {
-    d = max(d, sh_int[w]);
-    lo = min(lo, sh_int[kNlWaves + w]);
-  }
-  if (d < 0) d = lo;
-  // the owner publishes the mass above d
-  if (d == b0 + 1) sh_u64[0] = up1;
-  if (d == b0) sh_u64[0] = up0;
-  __syncthreads();
-  above = sh_u64[0];
-  __syncthreads();
-  return d;
-}
 
 __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, const float* __restrict__ logits,
                                                                       float temperature, float top_p,
@@ -394,70 +354,184 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* x = logits + static_cast<size_t>(row) * V;
   __shared__ uint32_t s_key[kNlMaxV + kNlMaxV / 32];
-  __shared__ u64 s_hist[kNucBuckets];
-  __shared__ u64 s_u64[kNlWaves];
-  __shared__ int s_int[2 * kNlWaves];
-  __shared__ float s_max[kNlWaves];
-  __shared__ int s_sample;
+  __shared__ uint32_t s_list[kNlList];
+  __shared__ u64 s_hist[kNlBuckets];
+  __shared__ float s_red[2][kNlWaves];
+  __shared__ u64 s_wm[kNlWaves];
+  __shared__ int s_wc[kNlWaves];
+  __shared__ u64 s_lm[kNlSmall];
+  __shared__ int s_digit, s_count, s_sample, s_owner, s_kbefore;
+  __shared__ uint32_t s_kappa;
+  __shared__ u64 s_above, s_hd, s_base;
 
-  // load: order keys into LDS, and the row maximum
-  float mx = -__builtin_huge_valf();
+  // load: order keys into LDS, the row's maximum and minimum
+  float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
 #pragma unroll 8
   for (int v = tid; v < V; v += kNlThreads) {
     const float xv = x[v];
     mx = fmaxf(mx, xv);
+    mn = fminf(mn, xv);
     s_key[nl_pad(v)] = nuc_key(xv);
   }
-  for (int i = tid; i < kNucBuckets; i += kNlThreads) s_hist[i] = 0;
+  static_assert(kNlBuckets <= kNlThreads, "one thread per bucket clears the histogram");
+  if (tid < kNlBuckets) s_hist[tid] = 0;
+  if (tid == 0) {
+    s_count = 0;
+    s_sample = -1;
+    s_owner = 0;
+    s_base = 0;
+    s_kbefore = 0;
+    s_kappa = 0;
+  }
   mx = wave_max(mx);
-  if (lane == 0) s_max[wave] = mx;
+  mn = -wave_max(-mn);
+  if (lane == 0) {
+    s_red[0][wave] = mx;
+    s_red[1][wave] = mn;
+  }
   __syncthreads();
-  mx = s_max[0];
-  for (int w = 1; w < kNlWaves; ++w) mx = fmaxf(mx, s_max[w]);
+  mx = s_red[0][0];
+  mn = s_red[1][0];
+  for (int w = 1; w < kNlWaves; ++w) {
+    mx = fmaxf(mx, s_red[0][w]);
+    mn = fminf(mn, s_red[1][w]);
+  }
   const float sc = (1.f / temperature) * 1.44269504088896341f;   // log2(e) / temperature
   auto mass = [&](uint32_t k) -> u64 { return static_cast<u64>(exp2f((nuc_value(k) - mx) * sc) * 0x1p40f); };
+  // walk A's bucket as a digit (higher digit: larger values): linear in
+  // d = (max - x) * log2(e) / temperature over [0, min(span, 40)]; every
+  // step is monotone in x, so equal values share a digit
+  const float span = fminf((mx - mn) * sc, 40.f);
+  const float bscale = span > 1e-20f ? static_cast<float>(kNlBuckets - 1) / span : 0.f;
+  auto digit_a = [&](uint32_t k) -> int {
+    const float d = (mx - nuc_value(k)) * sc;
+    return kNlBuckets - 1 - static_cast<int>(fminf(d * bscale, static_cast<float>(kNlBuckets - 1)));
+  };
 
-  // radix select by mass: digits [31:21], [20:10], [9:0]; MA collects the
-  // mass of the buckets above each chosen digit (= the keys above kappa)
-  uint32_t prefix = 0;
-  u64 need = 0, MA = 0, h_kappa = 0;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    const int hi_shift = pass == 1 ? 21 : 10;
-    u64 S = 0;
-#pragma unroll 8
-    for (int v = tid; v < V; v += kNlThreads) {
-      const uint32_t k = s_key[nl_pad(v)];
-      if (pass == 0 || (k >> hi_shift) == (prefix >> hi_shift)) {
-        const u64 m = mass(k);
-        if (m) atomicAdd(&s_hist[(k >> shift) & (nb - 1)], m);
-        S += m;
+  // (A) masses by value bucket, and the row's total mass.  Thread tid walks
+  // its own chunk [kNlChunk tid, + kNlChunk) in id order and keeps each
+  // token's mass (as the float it converts from) and bucket in registers
+  // for the gather and the draw.
+  const int v0 = kNlChunk * tid;
+  float fm[kNlChunk];          // exp2((x - max) / T) * 2^40; u64(fm) is the mass
+  uint32_t dg[kNlChunk / 4];   // walk A's digits, four per word
+  u64 S = 0;
+#pragma unroll
+  for (int j = 0; j < kNlChunk; ++j) {
+    const int v = v0 + j;
+    const uint32_t k = v < V ? s_key[nl_pad(v)] : 0x007fffffu;   // past V: -inf, mass zero
+    fm[j] = exp2f((nuc_value(k) - mx) * sc) * 0x1p40f;
+    const int d = digit_a(k);
+    if ((j & 3) == 0) dg[j >> 2] = 0;
+    dg[j >> 2] |= static_cast<uint32_t>(d) << (8 * (j & 3));
+    const u64 m = static_cast<u64>(fm[j]);
+    if (m) atomicAdd(&s_hist[d], m);
+    S += m;
+  }
+  S = wave_sum_u64(S);
+  if (lane == 0) s_wm[wave] = S;
+  __syncthreads();
+  u64 total = 0;
+  for (int w = 0; w < kNlWaves; ++w) total += s_wm[w];
+  u64 need = static_cast<u64>(ceil(static_cast<double>(top_p) * static_cast<double>(total)));
+
+  // pick on one wave, then every thread takes the digit; the histogram is
+  // cleared for the next walk
+  u64 MA = 0, h_kappa = 0;
+  auto pick = [&]() -> int {
+    if (wave == 0) {
+      u64 above;
+      const int d = nuc_pick(s_hist, kNlBuckets, need, lane, above);
+      if (lane == 0) {
+        s_digit = d;
+        s_above = above;
+        s_hd = s_hist[min(max(d, 0), kNlBuckets - 1)];
       }
     }
-    if (pass == 0) {
-      S = wave_sum_u64(S);
-      if (lane == 0) s_u64[wave] = S;
-    }
     __syncthreads();
-    if (pass == 0) {
-      u64 total = 0;
-      for (int w = 0; w < kNlWaves; ++w) total += s_u64[w];
-      need = static_cast<u64>(ceil(static_cast<double>(top_p) * static_cast<double>(total)));
-      __syncthreads();   // s_u64 is reused by the pick
-    }
-    u64 above;
-    const int d = nl_pick(s_hist, nb, need, tid, lane, wave, s_u64, s_int, above);
-    prefix |= static_cast<uint32_t>(d) << shift;
-    need = need > above ? need - above : 0;
+    const int d = min(max(s_digit, 0), kNlBuckets - 1);   // always in range: some bucket holds mass
+    const u64 above = s_above;
+    h_kappa = s_hd;
     MA += above;
-    h_kappa = s_hist[d];
+    need = need > above ? need - above : 0;
+    if (tid < kNlBuckets) s_hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < kNucBuckets; i += kNlThreads) s_hist[i] = 0;
-    __syncthreads();
+    return d;
+  };
+  const int da = pick();
+
+  // bucket da's keys gathered into s_list (any order: the walks below only
+  // build histograms); past kNlList of them the walks read the whole row
+#pragma unroll
+  for (int j = 0; j < kNlChunk; ++j) {
+    const int v = v0 + j;
+    const bool in = v < V && static_cast<int>((dg[j >> 2] >> (8 * (j & 3))) & 0xffu) == da;
+    const uint64_t bal = ballot(in);
+    if (bal) {
+      const int leader = __builtin_ctzll(bal);
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&s_count, __popcll(bal));
+      base = __shfl(base, leader);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1));
+      if (in && pos < kNlList) s_list[pos] = s_key[nl_pad(v)];
+      if (in && pos < kNlSmall) s_lm[pos] = static_cast<u64>(fm[j]);
+    }
   }
-  const uint32_t kappa = prefix;
+  __syncthreads();
+  const int nb = s_count;
+  const bool listed = nb <= kNlList;
+
+  uint32_t kappa;
+  if (nb <= kNlSmall) {
+    // a small bucket: each of its tokens (thread i, entry i) sums the masses
+    // above its key and at its key over the bucket; the key whose interval
+    // of cumulative mass holds what is still needed is kappa
+    if (tid < nb) {
+      const uint32_t ki = s_list[tid];
+      u64 above = 0, at = 0;
+      for (int j = 0; j < nb; ++j) {
+        const uint32_t kj = s_list[j];
+        const u64 mj = s_lm[j];
+        above += kj > ki ? mj : 0;
+        at += kj == ki ? mj : 0;
+      }
+      if (above < need && need <= above + at) {   // every entry with key ki agrees
+        s_kappa = ki;
+        s_above = above;
+        s_hd = at;
+      }
+    }
+    __syncthreads();
+    kappa = s_kappa;
+    const u64 above = s_above;
+    h_kappa = s_hd;
+    MA += above;
+    need = need > above ? need - above : 0;
+  } else {
+    // (B-E) radix digits of the key over bucket da
+    uint32_t prefix = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      auto add = [&](uint32_t k) {
+        if (pass == 0 || (k >> (shift + 8)) == (prefix >> (shift + 8))) {
+          const u64 m = mass(k);
+          if (m) atomicAdd(&s_hist[(k >> shift) & (kNlBuckets - 1)], m);
+        }
+      };
+      if (listed) {
+        for (int i = tid; i < nb; i += kNlThreads) add(s_list[i]);
+      } else {
+        for (int v = tid; v < V; v += kNlThreads) {
+          const uint32_t k = s_key[nl_pad(v)];
+          if (digit_a(k) == da) add(k);
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(pick()) << shift;
+    }
+    kappa = prefix;
+  }
   const u64 m_kappa = mass(kappa);
   // the last histogram's bucket is exactly key kappa: count x m_kappa
   const int count_kappa = m_kappa > 0 ? static_cast<int>(h_kappa / m_kappa) : 1;
@@ -468,8 +542,9 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
   u64 target = static_cast<u64>(floor(static_cast<double>(u) * static_cast<double>(Z)));
   if (target >= Z) target = Z - 1;   // u = 1: the nucleus's highest id
 
-  // the draw: thread tid owns tokens [kNlChunk tid, + kNlChunk) in id order
-  const int v0 = kNlChunk * tid;
+  // the draw, over each thread's chunk in id order: one scan of (mass above
+  // kappa, kappa count), since the kappa tokens taken before a thread's
+  // chunk are the first c of them
   u64 ma = 0;
   int cnt = 0;
 #pragma unroll
@@ -477,38 +552,65 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
     const int v = v0 + j;
     if (v < V) {
       const uint32_t k = s_key[nl_pad(v)];
-      if (k > kappa) ma += mass(k);
+      if (k > kappa) ma += static_cast<u64>(fm[j]);
       cnt += k == kappa ? 1 : 0;
     }
   }
-  int cnt_all;
-  const int ord = nl_block_excl_scan(cnt, s_int, lane, wave, cnt_all);
-  const int take = min(max(c - ord, 0), cnt);
-  const u64 w = ma + static_cast<u64>(take) * m_kappa;
-  u64 w_all;
-  const u64 run0 = nl_block_excl_scan(w, s_u64, lane, wave, w_all);
-  if (tid == 0) s_sample = -1;
-  __syncthreads();
-  if (w > 0 && run0 <= target && target < run0 + w) {
-    u64 run = run0;
-    int kord = ord, found = -1;
+  u64 ma_inc = ma;
+  int cnt_inc = cnt;
 #pragma unroll
-    for (int j = 0; j < kNlChunk; ++j) {
-      const int v = v0 + j;
-      if (v < V && found < 0) {
-        const uint32_t k = s_key[nl_pad(v)];
-        bool inc = k > kappa;
-        if (k == kappa) {
-          inc = kord < c;
-          ++kord;
-        }
-        if (inc) {
-          run += mass(k);
-          if (run > target) found = v;
-        }
-      }
+  for (int o = 1; o < kWave; o <<= 1) {
+    const u64 ym = __shfl_up(ma_inc, o);
+    const int yc = __shfl_up(cnt_inc, o);
+    if (lane >= o) {
+      ma_inc += ym;
+      cnt_inc += yc;
     }
-    s_sample = found;
+  }
+  if (lane == kWave - 1) {
+    s_wm[wave] = ma_inc;
+    s_wc[wave] = cnt_inc;
+  }
+  __syncthreads();
+  u64 off_m = 0;
+  int off_c = 0;
+  for (int w = 0; w < wave; ++w) {
+    off_m += s_wm[w];
+    off_c += s_wc[w];
+  }
+  const u64 ma_before = off_m + ma_inc - ma;
+  const int cnt_before = off_c + cnt_inc - cnt;
+  const int take = min(max(c - cnt_before, 0), cnt);
+  const u64 w = ma + static_cast<u64>(take) * m_kappa;
+  const u64 run0 = ma_before + static_cast<u64>(min(cnt_before, c)) * m_kappa;
+  // exactly one thread's interval holds the target (the sums are exact); it
+  // hands its chunk to wave 0, whose lane j takes token j of the chunk
+  if (w > 0 && run0 <= target && target < run0 + w) {
+    s_owner = tid;
+    s_base = run0;
+    s_kbefore = cnt_before;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int owner = s_owner;
+    const u64 base = s_base;
+    const int kbefore = s_kbefore;
+    const int v = kNlChunk * owner + lane;
+    const bool live = lane < kNlChunk && v < V;
+    const uint32_t k = live ? s_key[nl_pad(v)] : 0u;
+    // kappa tokens of the chunk up to and including this lane
+    const uint64_t kap = ballot(live && k == kappa);
+    const int kord = kbefore + __popcll(kap & ((2ull << lane) - 1)) - 1;   // this token's ordinal if k == kappa
+    const bool in = live && (k > kappa || (k == kappa && kord < c));
+    u64 m = in ? mass(k) : 0;
+    // inclusive prefix of the masses over the lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const u64 y = __shfl_up(m, o);
+      if (lane >= o) m += y;
+    }
+    const uint64_t hit = ballot(in && base + m > target);
+    if (lane == 0) s_sample = hit ? kNlChunk * owner + __builtin_ctzll(hit) : -1;
   }
   __syncthreads();
   if (tid == 0) {
