@@ -448,17 +448,27 @@ def base_head_timing(step, seed, steps):
     ws_f = torch.zeros(md.medusa_base_posterior_workspace(1, T, H, V), dtype=torch.uint8, device=dev)
     temp, eps, delta = w["temperature"], w["eps"], w["delta"]
 
+    # every call through the C entry points with pre-marshalled pointers (as
+    # the verify step's stages), so the host's per-call cost in the binding
+    # cannot leave the GPU idle between calls
+    L, sp = md.lib, torch.cuda.current_stream().cuda_stream
+    p_max, D = tr["retrieve"].shape
+    hp, op = h3.data_ptr(), out.data_ptr()
+    pp = [pk.data_ptr() for pk in packs]
+    cand, ret, npth = tr["tree_candidates"].data_ptr(), tr["retrieve"].data_ptr(), tr["num_paths"].data_ptr()
+    bp, ap, np_ = post["best_path"].data_ptr(), post["accept_len"].data_ptr(), post["next_token"].data_ptr()
+
     def gemm(i):
-        md.medusa_base_lm_head(h3, packs[i % 2], out, V=V)
+        assert L.medusa_base_lm_head(md.MEDUSA_BF16, T, H, V, hp, pp[i % 2], 1, op, sp) == 0
 
     def unfused(i):
-        md.medusa_base_lm_head(h3, packs[i % 2], out, V=V)
-        md.medusa_evaluate_posterior(out, tr["tree_candidates"], tr["retrieve"], tr["num_paths"], temp, eps, delta,
-                                     out=post, ws=ws_p)
+        gemm(i)
+        assert L.medusa_evaluate_posterior(1, T, V, p_max, D, op, cand, ret, npth, temp, eps, delta, bp, ap, np_,
+                                           ws_p.data_ptr(), ws_p.numel(), sp) == 0
 
     def fused(i):
-        md.medusa_base_posterior(h3, packs[i % 2], tr["tree_candidates"], tr["retrieve"], tr["num_paths"], temp,
-                                 eps, delta, V=V, out=post, ws=ws_f)
+        assert L.medusa_base_posterior(1, T, H, V, p_max, D, hp, pp[i % 2], 1, cand, ret, npth, temp, eps, delta,
+                                       bp, ap, np_, ws_f.data_ptr(), ws_f.numel(), sp) == 0
 
     def timed(fn):
         for i in range(4):
@@ -502,6 +512,25 @@ def _time_calls(fn, n, warm=3):
     return start.elapsed_time(end) * 1000.0 / n
 
 
+def _attention_caller(md, q, kcs, vcs, plen, mask, out, ws):
+    """fn(i): one medusa_tree_attention call on layer i % len(kcs), through
+    the C entry point with pre-marshalled pointers (no binding overhead
+    between the timed calls)."""
+    import torch
+    B, T, Hq, d = q.shape
+    S = kcs[0].shape[2]
+    sp = torch.cuda.current_stream().cuda_stream
+    kp, vp = [k.data_ptr() for k in kcs], [v.data_ptr() for v in vcs]
+    args = (q.data_ptr(), plen.data_ptr(), mask.data_ptr(), float(d) ** -0.5, out.data_ptr(), ws.data_ptr(),
+            ws.numel())
+
+    def fn(i):
+        j = i % len(kp)
+        assert md.lib.medusa_tree_attention(md.MEDUSA_BF16, B, T, Hq, d, S, args[0], kp[j], vp[j], args[1], args[2],
+                                            args[3], args[4], args[5], args[6], sp) == 0
+    return fn
+
+
 def nucleus_timing(step, seed, steps):
     """Nucleus (top-p 0.8, temperature 0.7) acceptance over the step's
     [64][32000] logits and tree: the whole call (one draw per node, then the
@@ -518,9 +547,17 @@ def nucleus_timing(step, seed, steps):
     u = torch.from_numpy(synth.node_uniforms(w, T, seed=seed)).to(step.dev)
     out = {n: torch.empty(B, dtype=torch.int32, device=step.dev) for n in ("best_path", "accept_len", "next_token")}
     ws = torch.zeros(md.medusa_posterior_nucleus_workspace(B, T), dtype=torch.uint8, device=step.dev)
-    us = _time_calls(lambda i: md.medusa_evaluate_posterior_nucleus(step.logits, t["tree_candidates"], t["retrieve"],
-                                                                    t["num_paths"], 0.7, 0.8, u, out=out, ws=ws),
-                     steps)
+    p_max, D = t["retrieve"].shape
+    sp = torch.cuda.current_stream().cuda_stream
+    ptrs = (step.logits.data_ptr(), t["tree_candidates"].data_ptr(), t["retrieve"].data_ptr(),
+            t["num_paths"].data_ptr(), u.data_ptr(), out["best_path"].data_ptr(), out["accept_len"].data_ptr(),
+            out["next_token"].data_ptr())
+
+    def call(i):
+        assert md.lib.medusa_evaluate_posterior_nucleus(B, T, V, p_max, D, ptrs[0], ptrs[1], ptrs[2], ptrs[3], 0.7,
+                                                        0.8, ptrs[4], ptrs[5], ptrs[6], ptrs[7], None,
+                                                        ws.data_ptr(), ws.numel(), sp) == 0
+    us = _time_calls(call, steps)
     byt = B * T * V * 4
     return {"us": round(us, 2), "top_p": 0.8, "temperature": 0.7, "bytes": byt,
             "achieved": round(byt / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -552,8 +589,7 @@ def attention_prefix_sweep(step, steps):
         plen = torch.full((1,), L, dtype=torch.int32, device=dev)
         ws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, 1, T, Hq, d, S), dtype=torch.uint8,
                          device=dev)
-        us = _time_calls(lambda i: md.medusa_tree_attention(q, kc[i % nl], vc[i % nl], plen, step.tree["tree_mask"],
-                                                            d ** -0.5, out=out, ws=ws), steps)
+        us = _time_calls(_attention_caller(md, q, kc, vc, plen, step.tree["tree_mask"], out, ws), steps)
         nbytes = 2 * Hq * (L + T) * d * 2 + 2 * T * Hq * d * 2
         rows.append({"L": L, "us": round(us, 2), "bytes": nbytes, "achieved": round(nbytes / us / 1e3, 1),
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
@@ -587,8 +623,7 @@ def attention_only(args):
     plen = torch.full((1,), L, dtype=torch.int32, device=dev)
     ws = torch.zeros(md.medusa_tree_attention_workspace(md.MEDUSA_BF16, 1, T, Hq, d, S), dtype=torch.uint8,
                      device=dev)
-    us = _time_calls(lambda i: md.medusa_tree_attention(q, kc[i % nl], vc[i % nl], plen, tree["tree_mask"],
-                                                        d ** -0.5, out=out, ws=ws), args.steps)
+    us = _time_calls(_attention_caller(md, q, kc, vc, plen, tree["tree_mask"], out, ws), args.steps)
     nbytes = 2 * Hq * (L + T) * d * 2 + 2 * T * Hq * d * 2
     print(json.dumps({"attention": {"L": L, "T": T, "Hq": Hq, "d": d, "max_slots": S, "calls": args.steps,
                                     "us": round(us, 2), "bytes": nbytes, "achieved": round(nbytes / us / 1e3, 1),
