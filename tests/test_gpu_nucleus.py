@@ -11,8 +11,9 @@ sequences of 15 nodes over a 1000-token vocabulary (partial thread chunks);
 top_p 1 (the whole vocabulary); a tiny top_p, where the draw is the argmax
 and the result equals greedy acceptance; equal logits and a tie group at
 the nucleus boundary spread over many threads' chunks (ties go to the
-lower ids); a one-token vocabulary; a 40000-token vocabulary, past the
-LDS-resident limit (the segmented kernel).
+lower ids); rows whose boundary bucket holds hundreds to tens of thousands
+of tokens (each selection path of the kernel); a one-token vocabulary; a
+40000-token vocabulary, past the LDS-resident limit (the segmented kernel).
 """
 
 import numpy as np
@@ -145,6 +146,42 @@ def test_nucleus_tie_group_at_the_boundary(gpu_device):
     children = [group[0], hi[1], group[6], 2, group[4], group[5], hi[2], 40]
     got, ref = _star(rows, children, 1.0, top_p, us)
     assert ref["samples"][0].tolist() == [5, 5, 40, 90, 255, 256, 300, 700, 1099]
+    _compare(got, ref)
+
+
+def _crowded_rows(V, cluster, seed):
+    """Rows whose first selection bucket (linear in value over the row's
+    range) holds many tokens: one far outlier below stretches the range, so
+    a cluster of `cluster` tokens with distinct values inside a 0.01-wide
+    interval falls into one bucket; the rest sit 12 below the cluster."""
+    rng = np.random.default_rng(seed)
+    row = np.full(V, -12.0, dtype=np.float32) + rng.uniform(0, 1e-3, V).astype(np.float32)
+    ids = rng.choice(np.arange(1, V), size=cluster, replace=False)
+    row[ids] = (1.0 + rng.uniform(0, 1e-2, cluster)).astype(np.float32)
+    row[0] = -60.0
+    return row
+
+
+@pytest.mark.parametrize("V,cluster", [(32000, 2000), (32000, 20000), (4000, 600)])
+def test_nucleus_crowded_boundary_bucket(gpu_device, V, cluster):
+    # the boundary bucket then holds more tokens than the direct resolution
+    # takes: at most 4096 of them are gathered into a list for the radix
+    # passes, a larger bucket is walked over the whole row
+    temperature, top_p = 0.7, 0.8
+    rows, us = [], []
+    for r in range(3):
+        for attempt in range(20):
+            row = _crowded_rows(V, cluster, seed=100 * r + attempt)
+            u = float(np.float32((r + 0.37) / 3.0))
+            if nucleus_margins(row, temperature, top_p, u) > 1e-5:
+                break
+        else:
+            pytest.fail("no row cleared the margins")
+        rows.append(row)
+        us.append(u)
+    rows = np.stack(rows)
+    children = [int(np.argmax(rows[0])), 7]
+    got, ref = _star(rows, children, temperature, top_p, us)
     _compare(got, ref)
 
 
