@@ -570,6 +570,35 @@ def nucleus_timing(step, seed, steps):
                     "per node"}
 
 
+def sample_typical_timing(step, seed, steps):
+    """Typical mode's sampled next token on the step's
+    [64][32000] logits, drawn at the root (best path 0, nothing accepted):
+    the whole call, HIP events around the calls, the step key advancing per
+    call.  One 32000-token row (128 KB) is read once into one workgroup's
+    registers, so the call is bound by that compute unit's ALUs, not by
+    bandwidth."""
+    import torch
+
+    import speculative_decoding_medusa_amd as md
+    w = step.w
+    t = step.tree
+    B, T, V = w["B"], step.T, w["V"]
+    p_max, D = t["retrieve"].shape
+    best = torch.zeros(B, dtype=torch.int32, device=step.dev)
+    acc = torch.zeros(B, dtype=torch.int32, device=step.dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=step.dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    ptrs = (step.logits.data_ptr(), t["retrieve"].data_ptr(), best.data_ptr(), acc.data_ptr(), nxt.data_ptr())
+
+    def call(i):
+        assert md.lib.medusa_sample_typical(B, T, V, p_max, D, ptrs[0], ptrs[1], ptrs[2], ptrs[3], w["temperature"],
+                                            w["eps"], w["delta"], seed, i, ptrs[4], sp) == 0
+    us = _time_calls(call, steps)
+    return {"us": round(us, 2), "temperature": w["temperature"], "bytes": B * V * 4,
+            "note": "one workgroup per sequence; the row is read once into registers; bound by that "
+                    "compute unit's vector ALUs"}
+
+
 def attention_prefix_sweep(step, steps):
     """Tree attention (64-node tree, 32 heads x 128) at prefixes 512, 1024,
     2048 and 4096, eight layers of KV rotated so no layer sits in the
@@ -1164,6 +1193,7 @@ def main():
         result["base_lm_head"] = base_head_timing(step, args.seed, args.steps)
     if not args.no_extra:
         result["nucleus"] = nucleus_timing(step, args.seed, args.steps)
+        result["sample_typical"] = sample_typical_timing(step, args.seed, args.steps)
         result["attention_prefix_sweep"] = attention_prefix_sweep(step, args.steps)
         result["vicuna13b"] = vicuna13b(step, args.seed, args.steps)
         result["batch8_33b"] = batch8_33b(step, args.seed, args.steps)

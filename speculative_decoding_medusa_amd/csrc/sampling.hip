@@ -11,16 +11,24 @@
 // on any machine.
 //
 // Typical-mode next token: one workgroup per sequence reads the base logits
-// at its last accepted node (retrieve[best_path][accept_len]) in three
-// passes -- maximum; S = sum e^(z - m) and A = sum (z - m) e^(z - m) with
+// at its last accepted node (retrieve[best_path][accept_len]) and computes
+// the maximum; S = sum e^(z - m) and A = sum (z - m) e^(z - m) with
 // z = logit / temperature, hence H and the threshold min(eps, delta e^-H);
 // then the mass e^(z - m) of every token with e^(z - m) / S above the
 // threshold (the acceptance rule's own test), as an integer with 40
-// fraction bits so that sums are exact and independent of order.  Thread t
-// owns a contiguous block of token ids; a workgroup scan of the blocks'
-// masses finds the one block whose interval holds floor(u * Z), and its
-// thread walks its tokens in id order to the first whose running mass
-// exceeds it.
+// fraction bits so that sums are exact and independent of order.  The draw
+// is the first token in id order whose running mass exceeds floor(u * Z),
+// Z the total.
+//
+// Rows of up to 32768 tokens stay in registers: the row is cut into chunks
+// of 4096 ids, thread t holds ids 4t .. 4t + 3 of every chunk (one 16-byte
+// load per chunk, coalesced across the wave), so id order is (chunk,
+// thread, element).  Per chunk a 64-bit wave scan of the threads' masses
+// and one scan over the 8 x 16 (chunk, wave) totals give every thread the
+// mass before each of its four-token runs; the one run whose interval holds
+// floor(u * Z) is walked element by element.  Longer rows take a streaming
+// kernel in which thread t owns a contiguous block of ids and re-reads it
+// for each pass.
 #include "common.hpp"
 
 namespace medusa {
@@ -62,8 +70,233 @@ __global__ __launch_bounds__(256) void philox_uniforms_kernel(uint64_t seed, uin
 
 constexpr int kSampleThreads = 1024;
 constexpr int kPurposeNextToken = 1;
+constexpr int kStWaves = kSampleThreads / kWave;
+constexpr int kStChunk = kSampleThreads * 4;     // ids per chunk: four per thread
+constexpr int kStChunks = 8;
+constexpr int kStRegMaxV = kStChunk * kStChunks;  // rows the register kernel takes
 
-__global__ __launch_bounds__(kSampleThreads) void sample_typical_kernel(
+// Wave-wide scans and reductions on DPP lane moves (register to register,
+// no LDS round trip): row_shr:1, 2, 4, 8 (lane i takes lane i - n of its
+// row of 16; lanes with no source, and rows outside the row mask, take
+// `fill`), then row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2
+// and 3 carry each row's last lane into the rows above it.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t fill) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), kCtrl, kRowMask, 0xf, false));
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v) {
+  const uint64_t lo = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(v), 0u);
+  const uint64_t hi = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(v >> 32), 0u);
+  return v + ((hi << 32) | lo);
+}
+
+// inclusive prefix sum over the wave's 64 lanes in lane order
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v = dpp_add_u64<0x111, 0xf>(v);
+  v = dpp_add_u64<0x112, 0xf>(v);
+  v = dpp_add_u64<0x114, 0xf>(v);
+  v = dpp_add_u64<0x118, 0xf>(v);
+  v = dpp_add_u64<0x142, 0xa>(v);
+  return dpp_add_u64<0x143, 0xc>(v);
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  return (hi << 32) | lo;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f32(float v, float fill) {
+  return __builtin_bit_cast(float, dpp_u32<kCtrl, kRowMask>(__builtin_bit_cast(uint32_t, v),
+                                                            __builtin_bit_cast(uint32_t, fill)));
+}
+
+// the wave's maximum (kMax) or sum, in every lane
+template <bool kMax>
+__device__ __forceinline__ float wave_reduce_dpp(float v) {
+  const float id = kMax ? -__builtin_huge_valf() : 0.f;
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_f32<0x111, 0xf>(v, id));
+  v = op(v, dpp_f32<0x112, 0xf>(v, id));
+  v = op(v, dpp_f32<0x114, 0xf>(v, id));
+  v = op(v, dpp_f32<0x118, 0xf>(v, id));
+  v = op(v, dpp_f32<0x142, 0xa>(v, id));
+  v = op(v, dpp_f32<0x143, 0xc>(v, id));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+
+// kVec4: V % 4 == 0 and a 16-byte aligned logits base, so that each
+// thread's four ids of a chunk are one aligned 16-byte load.  In base 2:
+// with k = log2(e) / temperature, e^(z - m) = 2^(x k - mx k) for logit x
+// and maximum logit mx, A = ln 2 * sum (x k - mx k) 2^(x k - mx k), and a
+// token is allowed when its e^(z - m) exceeds thr * S.
+template <bool kVec4>
+__global__ __launch_bounds__(kSampleThreads) void sample_typical_reg_kernel(
+    int T, int V, int p_max, int D, const float* __restrict__ logits, const int32_t* __restrict__ retrieve,
+    const int32_t* __restrict__ best_path, const int32_t* __restrict__ accept_len, float temperature, float eps,
+    float delta, uint64_t seed, uint64_t step, int32_t* __restrict__ next_token) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ float s_red[2][kStWaves];
+  __shared__ uint64_t s_scan[kStChunks * kStWaves];   // (chunk, wave) mass totals in id order
+  __shared__ int s_tok, s_last;
+  const int best = min(max(best_path[b], 0), p_max - 1);
+  const int acc = min(max(accept_len[b], 0), D - 1);
+  int node = retrieve[best * D + acc];
+  if (node < 0 || node >= T) node = 0;
+  const float* row = logits + (static_cast<size_t>(b) * T + node) * V;
+  const float NEG = -__builtin_huge_valf();
+  if (tid == 0) {
+    s_tok = -1;
+    s_last = -1;
+  }
+
+  float z[kStChunks][4];
+#pragma unroll
+  for (int c = 0; c < kStChunks; ++c) {
+    const int v0 = c * kStChunk + 4 * tid;
+    if constexpr (kVec4) {
+      if (v0 < V) {   // V % 4 == 0: the whole run is inside the row
+        const float4 q = *reinterpret_cast<const float4*>(row + v0);
+        z[c][0] = q.x;
+        z[c][1] = q.y;
+        z[c][2] = q.z;
+        z[c][3] = q.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[c][i] = NEG;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[c][i] = v0 + i < V ? row[v0 + i] : NEG;
+    }
+  }
+
+  // maximum of the raw logits (a positive temperature keeps the order)
+  float mx = NEG;
+#pragma unroll
+  for (int c = 0; c < kStChunks; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[c][i]);
+  mx = wave_reduce_dpp<true>(mx);
+  if (lane == 0) s_red[0][wave] = mx;
+  __syncthreads();
+  mx = s_red[0][0];
+#pragma unroll
+  for (int w = 1; w < kStWaves; ++w) mx = fmaxf(mx, s_red[0][w]);
+  const float kl = 1.4426950408889634f / temperature;
+  const float m2 = mx * kl;
+  __syncthreads();
+
+  // S and A, hence the entropy and the threshold; z becomes e^(z - m)
+  float S = 0.f, A2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < kStChunks; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (c * kStChunk + 4 * tid + i < V) {
+        const float d2 = fmaf(z[c][i], kl, -m2);
+        const float e = __builtin_amdgcn_exp2f(d2);
+        S += e;
+        A2 = fmaf(d2, e, A2);
+        z[c][i] = e;
+      } else {
+        z[c][i] = 0.f;
+      }
+    }
+  S = wave_reduce_dpp<false>(S);
+  A2 = wave_reduce_dpp<false>(A2);
+  if (lane == 0) {
+    s_red[0][wave] = S;
+    s_red[1][wave] = A2;
+  }
+  __syncthreads();
+  S = 0.f;
+  A2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < kStWaves; ++w) {
+    S += s_red[0][w];
+    A2 += s_red[1][w];
+  }
+  const float H = logf(S) - 0.6931471805599453f * A2 / S;
+  const float thrS = fminf(eps, delta * expf(-H)) * S;
+
+  // allowed flags (bit 4c + i) and fixed-point masses, per four-token run;
+  // per chunk the mass of the wave's earlier lanes (excl) and the wave's
+  // total
+  uint64_t excl[kStChunks];
+  uint32_t allow = 0;
+#pragma unroll
+  for (int c = 0; c < kStChunks; ++c) {
+    uint64_t own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool a = z[c][i] > thrS;
+      allow |= static_cast<uint32_t>(a) << (4 * c + i);
+      own += a ? static_cast<uint64_t>(z[c][i] * 0x1p40f) : 0ull;
+    }
+    const uint64_t inc = wave_incl_scan_u64(own);
+    excl[c] = inc - own;
+    if (lane == kWave - 1) s_scan[c * kStWaves + wave] = inc;
+  }
+  if (allow != 0) {
+    const int j = 31 - __builtin_clz(allow);
+    atomicMax(&s_last, (j >> 2) * kStChunk + 4 * tid + (j & 3));
+  }
+  __syncthreads();
+
+  // exclusive prefix of the 128 (chunk, wave) totals: lane l holds entries
+  // 2l and 2l + 1
+  const uint64_t e0 = s_scan[2 * lane], e1 = s_scan[2 * lane + 1];
+  const uint64_t pair_inc = wave_incl_scan_u64(e0 + e1);
+  const uint64_t pair_ex = pair_inc - (e0 + e1);
+  const uint64_t Z = readlane_u64(pair_inc, kWave - 1);
+  // target = floor(u * Z), u = bits * 2^-24: the 24 bits times Z, shifted
+  const uint64_t ub = philox_bits24(seed, step, b, 0, kPurposeNextToken);
+  const uint64_t plo = ub * Z, phi = __umul64hi(ub, Z);
+  const uint64_t target = (phi << 40) | (plo >> 24);
+#pragma unroll
+  for (int c = 0; c < kStChunks; ++c) {
+    // this wave's entry k = 16c + wave sits in lane k / 2, slot wave & 1
+    const int src = (c * kStWaves + wave) >> 1;
+    const uint64_t f0 = readlane_u64(e0, src);
+    const uint64_t wbase = readlane_u64(pair_ex, src) + ((wave & 1) ? f0 : 0ull);
+    const uint64_t wtotal = (wave & 1) ? readlane_u64(e1, src) : f0;
+    if (wbase <= target && target < wbase + wtotal) {   // the crossing is in this wave's run of chunk c
+      // the last lane with a non-empty run starting at or before the target
+      const uint64_t before = wbase + excl[c];
+      const uint64_t hit = __ballot(((allow >> (4 * c)) & 0xfu) != 0 && before <= target);
+      if (lane == kWave - 1 - __builtin_clzll(hit)) {
+        uint64_t run = before;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // the same mass as above, recomputed: the empty asm hides that,
+          // so the compiler keeps 32 floats live rather than 32 64-bit masses
+          float e = z[c][i];
+          asm volatile("" : "+v"(e));
+          if ((allow >> (4 * c + i)) & 1u) run += static_cast<uint64_t>(e * 0x1p40f);
+          if (run > target) {
+            s_tok = c * kStChunk + 4 * tid + i;
+            break;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // no crossing (not reached for u < 1): the highest allowed id
+    const int tok = s_tok >= 0 ? s_tok : s_last;
+    next_token[b] = tok < 0 ? 0 : tok;
+  }
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_typical_stream_kernel(
     int T, int V, int p_max, int D, const float* __restrict__ logits, const int32_t* __restrict__ retrieve,
     const int32_t* __restrict__ best_path, const int32_t* __restrict__ accept_len, float temperature, float eps,
     float delta, uint64_t seed, uint64_t step, int32_t* __restrict__ next_token) {
@@ -208,8 +441,17 @@ extern "C" int medusa_sample_typical(int B, int T, int V, int p_max, int D, cons
   MEDUSA_REQUIRE_PTR(best_path);
   MEDUSA_REQUIRE_PTR(accept_len);
   MEDUSA_REQUIRE_PTR(next_token);
-  hipLaunchKernelGGL(sample_typical_kernel, dim3(B), dim3(kSampleThreads), 0, static_cast<hipStream_t>(stream), T, V,
-                     p_max, D, logits, retrieve, best_path, accept_len, temperature, eps, delta, seed, step,
-                     next_token);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (V <= kStRegMaxV) {
+    if (V % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0)
+      hipLaunchKernelGGL(sample_typical_reg_kernel<true>, dim3(B), dim3(kSampleThreads), 0, st, T, V, p_max, D, logits,
+                         retrieve, best_path, accept_len, temperature, eps, delta, seed, step, next_token);
+    else
+      hipLaunchKernelGGL(sample_typical_reg_kernel<false>, dim3(B), dim3(kSampleThreads), 0, st, T, V, p_max, D,
+                         logits, retrieve, best_path, accept_len, temperature, eps, delta, seed, step, next_token);
+  } else {
+    hipLaunchKernelGGL(sample_typical_stream_kernel, dim3(B), dim3(kSampleThreads), 0, st, T, V, p_max, D, logits,
+                       retrieve, best_path, accept_len, temperature, eps, delta, seed, step, next_token);
+  }
   return medusa_host::hip_check("medusa_sample_typical launch");
 }

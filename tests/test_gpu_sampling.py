@@ -8,8 +8,10 @@ inputs whose draw sits clear of float error (the draw is the same with every
 near-threshold token counted in or out, and u times the allowed mass is at
 least 1e-5 of it from every running-sum boundary; the step of the key is
 advanced until it is): planted Vicuna-7B logits (64 nodes, V 32000) at the
-best path the acceptance picks, three sequences over 1000 tokens, 40000
-tokens, a flat row (token floor(u V)) and a dominant token.  Nucleus
+best path the acceptance picks, three sequences over 1000 tokens, rows at
+the register kernel's edges (4099, 4100, 32767 and 32768 tokens), 40000
+tokens (the streaming kernel), a flat row (token floor(u V)) and a dominant
+token.  Nucleus
 acceptance run on the library's own uniforms equals the oracle's on the
 same keys.
 """
@@ -89,7 +91,18 @@ def test_sample_typical_three_sequences_small_vocab(gpu_device):
 
 
 def test_sample_typical_vocab_40000(gpu_device):
+    # past 32768 tokens: the streaming kernel
     _check_tree_case(synth.workload("vicuna-7b", V=40000), 6)
+
+
+@pytest.mark.parametrize("B,V", [
+    (2, 32768),    # the register kernel's largest row, 16-byte loads
+    (1, 32767),    # its largest row of element loads (V % 4 != 0)
+    (3, 4099),     # one id past a 4096-id chunk, element loads
+    (2, 4100),     # ragged second chunk, 16-byte loads
+])
+def test_sample_typical_register_kernel_edges(gpu_device, B, V):
+    _check_tree_case(synth.workload("vicuna-7b", B=B, V=V), V % 97)
 
 
 def test_sample_typical_flat_and_dominant_rows(gpu_device):
