@@ -56,6 +56,70 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave-wide scans and reductions on DPP lane moves (register to register,
+// no LDS round trip): row_shr:1, 2, 4, 8 (lane i takes lane i - n of its
+// row of 16; lanes with no source, and rows outside the row mask, take
+// `fill`), then row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2
+// and 3 carry each row's last lane into the rows above it.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t fill) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), kCtrl, kRowMask, 0xf, false));
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v) {
+  const uint64_t lo = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(v), 0u);
+  const uint64_t hi = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(v >> 32), 0u);
+  return v + ((hi << 32) | lo);
+}
+
+// inclusive prefix sum over the wave's 64 lanes in lane order
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v = dpp_add_u64<0x111, 0xf>(v);
+  v = dpp_add_u64<0x112, 0xf>(v);
+  v = dpp_add_u64<0x114, 0xf>(v);
+  v = dpp_add_u64<0x118, 0xf>(v);
+  v = dpp_add_u64<0x142, 0xa>(v);
+  return dpp_add_u64<0x143, 0xc>(v);
+}
+
+// inclusive prefix sum over the wave's 64 lanes in lane order
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  v += static_cast<int>(dpp_u32<0x111, 0xf>(static_cast<uint32_t>(v), 0u));
+  v += static_cast<int>(dpp_u32<0x112, 0xf>(static_cast<uint32_t>(v), 0u));
+  v += static_cast<int>(dpp_u32<0x114, 0xf>(static_cast<uint32_t>(v), 0u));
+  v += static_cast<int>(dpp_u32<0x118, 0xf>(static_cast<uint32_t>(v), 0u));
+  v += static_cast<int>(dpp_u32<0x142, 0xa>(static_cast<uint32_t>(v), 0u));
+  return v + static_cast<int>(dpp_u32<0x143, 0xc>(static_cast<uint32_t>(v), 0u));
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  return (hi << 32) | lo;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f32(float v, float fill) {
+  return __builtin_bit_cast(float, dpp_u32<kCtrl, kRowMask>(__builtin_bit_cast(uint32_t, v),
+                                                            __builtin_bit_cast(uint32_t, fill)));
+}
+
+// the wave's maximum (kMax) or sum, in every lane
+template <bool kMax>
+__device__ __forceinline__ float wave_reduce_dpp(float v) {
+  const float id = kMax ? -__builtin_huge_valf() : 0.f;
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_f32<0x111, 0xf>(v, id));
+  v = op(v, dpp_f32<0x112, 0xf>(v, id));
+  v = op(v, dpp_f32<0x114, 0xf>(v, id));
+  v = op(v, dpp_f32<0x118, 0xf>(v, id));
+  v = op(v, dpp_f32<0x142, 0xa>(v, id));
+  v = op(v, dpp_f32<0x143, 0xc>(v, id));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+
 // Total order used by every top-k and argmax here: larger value first,
 // equal values by smaller index.  NaN never wins.
 __device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {

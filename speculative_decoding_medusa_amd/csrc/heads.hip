@@ -322,14 +322,9 @@ __device__ __forceinline__ void radix_topk(const float* __restrict__ cv, const i
         c[q] = h[255 - 4 * lane - q];
         sum += c[q];
       }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
+      const int incl = wave_incl_scan_i32(sum);
       const int need = sm.need;
-      const int total = __shfl(incl, kWave - 1);
+      const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
       if (total < need) {
         // fewer candidates than k (first pass only): take them all
         if (lane == 0) {

@@ -75,60 +75,6 @@ constexpr int kStChunk = kSampleThreads * 4;     // ids per chunk: four per thre
 constexpr int kStChunks = 8;
 constexpr int kStRegMaxV = kStChunk * kStChunks;  // rows the register kernel takes
 
-// Wave-wide scans and reductions on DPP lane moves (register to register,
-// no LDS round trip): row_shr:1, 2, 4, 8 (lane i takes lane i - n of its
-// row of 16; lanes with no source, and rows outside the row mask, take
-// `fill`), then row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2
-// and 3 carry each row's last lane into the rows above it.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t fill) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), kCtrl, kRowMask, 0xf, false));
-}
-
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v) {
-  const uint64_t lo = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(v), 0u);
-  const uint64_t hi = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(v >> 32), 0u);
-  return v + ((hi << 32) | lo);
-}
-
-// inclusive prefix sum over the wave's 64 lanes in lane order
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
-  v = dpp_add_u64<0x111, 0xf>(v);
-  v = dpp_add_u64<0x112, 0xf>(v);
-  v = dpp_add_u64<0x114, 0xf>(v);
-  v = dpp_add_u64<0x118, 0xf>(v);
-  v = dpp_add_u64<0x142, 0xa>(v);
-  return dpp_add_u64<0x143, 0xc>(v);
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
-  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
-  return (hi << 32) | lo;
-}
-
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_f32(float v, float fill) {
-  return __builtin_bit_cast(float, dpp_u32<kCtrl, kRowMask>(__builtin_bit_cast(uint32_t, v),
-                                                            __builtin_bit_cast(uint32_t, fill)));
-}
-
-// the wave's maximum (kMax) or sum, in every lane
-template <bool kMax>
-__device__ __forceinline__ float wave_reduce_dpp(float v) {
-  const float id = kMax ? -__builtin_huge_valf() : 0.f;
-  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
-  v = op(v, dpp_f32<0x111, 0xf>(v, id));
-  v = op(v, dpp_f32<0x112, 0xf>(v, id));
-  v = op(v, dpp_f32<0x114, 0xf>(v, id));
-  v = op(v, dpp_f32<0x118, 0xf>(v, id));
-  v = op(v, dpp_f32<0x142, 0xa>(v, id));
-  v = op(v, dpp_f32<0x143, 0xc>(v, id));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
-}
-
 // kVec4: V % 4 == 0 and a 16-byte aligned logits base, so that each
 // thread's four ids of a chunk are one aligned 16-byte load.  In base 2:
 // with k = log2(e) / temperature, e^(z - m) = 2^(x k - mx k) for logit x
