@@ -126,6 +126,26 @@ __device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
+// The wave's (max, first index) under `beats`, in every lane.
+__device__ __forceinline__ void wave_argmax_dpp(float& v, int& i) {
+  const float fv = -__builtin_huge_valf();
+  const uint32_t fi = 0x7fffffffu;
+  auto step = [&](float ov, int oi) {
+    if (beats(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  };
+  step(dpp_f32<0x111, 0xf>(v, fv), static_cast<int>(dpp_u32<0x111, 0xf>(static_cast<uint32_t>(i), fi)));
+  step(dpp_f32<0x112, 0xf>(v, fv), static_cast<int>(dpp_u32<0x112, 0xf>(static_cast<uint32_t>(i), fi)));
+  step(dpp_f32<0x114, 0xf>(v, fv), static_cast<int>(dpp_u32<0x114, 0xf>(static_cast<uint32_t>(i), fi)));
+  step(dpp_f32<0x118, 0xf>(v, fv), static_cast<int>(dpp_u32<0x118, 0xf>(static_cast<uint32_t>(i), fi)));
+  step(dpp_f32<0x142, 0xa>(v, fv), static_cast<int>(dpp_u32<0x142, 0xa>(static_cast<uint32_t>(i), fi)));
+  step(dpp_f32<0x143, 0xc>(v, fv), static_cast<int>(dpp_u32<0x143, 0xc>(static_cast<uint32_t>(i), fi)));
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+  i = __builtin_amdgcn_readlane(i, kWave - 1);
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 // Statistics of one node's logits over a set of vocabulary entries: the raw

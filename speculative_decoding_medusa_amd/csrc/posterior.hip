@@ -4,7 +4,8 @@
 // node's logits into registers once (16-byte loads), reduces max / argmax
 // (ties: lowest token id) and, for temperature > 0, the softmax statistics
 // S = sum exp(z - m) and A = sum (z - m) exp(z - m) of z = logits / temperature
-// relative to its own chunk maximum.  Wave shuffles, then LDS across waves.
+// relative to its own chunk maximum.  Wave reductions on DPP lane moves, then
+// LDS across waves.
 //
 // Stage 2 (decide): one workgroup per sequence merges the chunk statistics
 // per node (log-sum-exp rescaling), derives H = log S - A / S and the
@@ -48,12 +49,7 @@ __global__ __launch_bounds__(kPostThreads) void posterior_rows_kernel(
       const int e = lo + (r * kPostThreads + tid) * 4 + c;
       if (e < V && beats(v[4 * r + c], e, mx, arg)) { mx = v[4 * r + c]; arg = e; }
     }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(mx, o);
-    const int oa = __shfl_xor(arg, o);
-    if (beats(om, oa, mx, arg)) { mx = om; arg = oa; }
-  }
+  wave_argmax_dpp(mx, arg);
   __shared__ float smx[kPostThreads / kWave];
   __shared__ int sarg[kPostThreads / kWave];
   __shared__ float sS[kPostThreads / kWave], sA[kPostThreads / kWave];
@@ -85,8 +81,8 @@ __global__ __launch_bounds__(kPostThreads) void posterior_rows_kernel(
           A += dz * p;
         }
       }
-    S = wave_sum(S);
-    A = wave_sum(A);
+    S = wave_reduce_dpp<false>(S);
+    A = wave_reduce_dpp<false>(A);
     if (lane == 0) { sS[wave] = S; sA[wave] = A; }
     __syncthreads();
     S = 0.f;
@@ -246,11 +242,22 @@ __global__ __launch_bounds__(kPostThreads) void posterior_decide_kernel(
     }
     if (ell > best_len || (ell == best_len && p < best_p)) { best_len = ell; best_p = p; }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int ol = __shfl_xor(best_len, o);
-    const int op = __shfl_xor(best_p, o);
-    if (ol > best_len || (ol == best_len && op < best_p)) { best_len = ol; best_p = op; }
+  {
+    // the wave's longest (lowest-index on ties) on DPP lane moves; the fill
+    // (-1, INT_MAX) never wins
+    auto take = [&](uint32_t ol, uint32_t op) {
+      const int l = static_cast<int>(ol), q = static_cast<int>(op);
+      if (l > best_len || (l == best_len && q < best_p)) { best_len = l; best_p = q; }
+    };
+    const uint32_t fl = 0xffffffffu, fp = 0x7fffffffu;
+    take(dpp_u32<0x111, 0xf>(best_len, fl), dpp_u32<0x111, 0xf>(best_p, fp));
+    take(dpp_u32<0x112, 0xf>(best_len, fl), dpp_u32<0x112, 0xf>(best_p, fp));
+    take(dpp_u32<0x114, 0xf>(best_len, fl), dpp_u32<0x114, 0xf>(best_p, fp));
+    take(dpp_u32<0x118, 0xf>(best_len, fl), dpp_u32<0x118, 0xf>(best_p, fp));
+    take(dpp_u32<0x142, 0xa>(best_len, fl), dpp_u32<0x142, 0xa>(best_p, fp));
+    take(dpp_u32<0x143, 0xc>(best_len, fl), dpp_u32<0x143, 0xc>(best_p, fp));
+    best_len = __builtin_amdgcn_readlane(best_len, kWave - 1);
+    best_p = __builtin_amdgcn_readlane(best_p, kWave - 1);
   }
   if (lane == 0) { s_len[wave] = best_len; s_path[wave] = best_p; }
   __syncthreads();
