@@ -181,11 +181,15 @@ class Step:
         assert rc == 0, rc
 
     def run_lm(self):
-        w, L = self.w, self.md.lib
-        rc = L.medusa_lm_head_topk(self.md.MEDUSA_BF16, w["B"], w["H"], w["V"], w["K"], w["topk"],
-                                   self.r.data_ptr(), self.w_lm.data_ptr(), self.topk_ids.data_ptr(),
-                                   self.topk_vals.data_ptr(), None, self.heads_ws.data_ptr(),
-                                   self.heads_ws.numel(), self.stream)
+        """The lm_head + top-k with this step's tree gather in its tail
+        (medusa_lm_head_topk_tree: one kernel at this shape)."""
+        w, L, t = self.w, self.md.lib, self.tree
+        rc = L.medusa_lm_head_topk_tree(self.md.MEDUSA_BF16, w["B"], w["H"], w["V"], w["K"], w["topk"],
+                                        self.r.data_ptr(), self.w_lm.data_ptr(), self.topk_ids.data_ptr(),
+                                        self.topk_vals.data_ptr(), None, self.T, t["tree_indices"].data_ptr(),
+                                        t["depth"].data_ptr(), self.root.data_ptr(), self.plen.data_ptr(),
+                                        t["tree_candidates"].data_ptr(), t["position_ids"].data_ptr(),
+                                        self.heads_ws.data_ptr(), self.heads_ws.numel(), self.stream)
         assert rc == 0, rc
 
     def run_heads(self):
@@ -193,8 +197,9 @@ class Step:
         self.run_lm()
 
     def run_tree(self):
-        """The per-step half of the tree: this step's top-k, root tokens and
-        prefix lengths gathered through the tree built at setup."""
+        """The per-step half of the tree as a launch of its own: this step's
+        top-k, root tokens and prefix lengths gathered through the tree built
+        at setup (the step itself gathers inside run_lm)."""
         w, L, t = self.w, self.md.lib, self.tree
         rc = L.medusa_tree_candidates(w["B"], self.T, w["K"], w["topk"], t["tree_indices"].data_ptr(),
                                       t["depth"].data_ptr(), self.topk_ids.data_ptr(), self.root.data_ptr(),
@@ -243,13 +248,13 @@ class Step:
                                 p["accept_len"].data_ptr(), self.new_plen.data_ptr(), self.stream)
         assert rc == 0, rc
 
-    STAGES = ("resblock", "lm_head_topk", "tree_candidates", "tree_attention", "posterior", "commit_kv")
+    STAGES = ("resblock", "lm_head_topk_tree", "tree_attention", "posterior", "commit_kv")
 
     def run(self, events=None, lm_events=None):
         """One verify step.  events: one per stage boundary (breakdown pass);
-        lm_events: a pair bracketing the lm_head + top-k call (timed pass)."""
-        fns = (self.run_resblock, self.run_lm, self.run_tree, self.run_attention, self.run_posterior,
-               self.run_commit)
+        lm_events: a pair bracketing the lm_head + top-k (+ tree gather) call
+        (timed pass)."""
+        fns = (self.run_resblock, self.run_lm, self.run_attention, self.run_posterior, self.run_commit)
         for i, fn in enumerate(fns):
             if events is not None:
                 events[i].record()
@@ -286,11 +291,14 @@ def measured_traffic():
         return None
 
 
-def lm_bytes(w):
-    """Algorithmic bytes of one lm_head + top-k launch: every weight once,
-    r once, the top-k ids and logits written."""
+def lm_bytes(w, T):
+    """Algorithmic bytes of one lm_head + top-k launch with the tree gather
+    in its tail: every weight once, r once, the top-k ids and logits
+    written; the gather reads tree_indices and depth (T each), root token and
+    prefix length (B each) and one top-k id per node, and writes the
+    candidates and positions ([B][T] each)."""
     B, H, V, K, k = w["B"], w["H"], w["V"], w["K"], w["topk"]
-    return K * V * H * 2 + B * K * H * 4 + B * K * k * 8
+    return K * V * H * 2 + B * K * H * 4 + B * K * k * 8 + (2 * T + 2 * B + 3 * B * T) * 4
 
 
 def _cpu_model():
@@ -1149,7 +1157,7 @@ def main():
 
     stages = {name: stats(stage_ms[i]) for i, name in enumerate(Step.STAGES)}
     lm_mean_s = sum(lm_ms) / len(lm_ms) / 1000.0
-    achieved = lm_bytes(w) / lm_mean_s / 1e9
+    achieved = lm_bytes(w, step.T) / lm_mean_s / 1e9
 
     result = {
         "metric": METRIC,
@@ -1169,17 +1177,19 @@ def main():
         "config": {"workload": "vicuna-7b verify step, batch 1", "B": w["B"], "H": w["H"], "V": w["V"],
                    "K": w["K"], "topk": w["topk"], "T": step.T, "Hq": w["Hq"], "d": w["d"], "L": w["L"],
                    "n_layers": w["n_layers"], "temperature": w["temperature"]},
-        "roofline": {"kernel": "lm_head_topk", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "lm_head_topk_tree", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "traffic_unit": "bytes per call",
-                     "bytes_per_launch": lm_bytes(w),
+                     "bytes_per_launch": lm_bytes(w, step.T),
                      "mean_launch_us": round(lm_mean_s * 1e6, 2),
                      "launches_timed": len(lm_ms),
                      "timing": "HIP events around the call in one timed step of every %d" % LM_SAMPLE},
         "stages": stages,
         "stages_note": "per-stage means from a separate untimed pass of %d steps; the tree itself "
                        "(medusa_build_tree) is built once per tree spec, per step only its candidates "
-                       "and positions are gathered (medusa_tree_candidates)" % nb,
+                       "and positions are gathered, by the lm_head kernel's last merging workgroup "
+                       "(medusa_lm_head_topk_tree)" % nb,
+        "tree_candidates_alone_us": round(_time_calls(lambda i: step.run_tree(), 50), 2),
         "build_tree_us": round(_time_calls(lambda i: step.run_build_tree(), 50), 2),
         "tokens_per_step": round(1.0 + sum(a * c for a, c in enumerate(hist)) / sum(hist), 4),
         "accept_len_histogram": hist,

@@ -9,6 +9,8 @@
  *   medusa_build_tree          candidate tree from a medusa_choices spec,
  *                              once per spec; then every step
  *   medusa_tree_candidates     this step's candidates and positions
+ *                              (or medusa_heads_tree / medusa_lm_head_topk_tree:
+ *                              the heads' top-k and this gather in one call)
  *   medusa_tree_attention      tree-masked attention over the KV prefix
  *   medusa_base_lm_head        base lm_head at the tree nodes -> logits
  *                              (or medusa_base_posterior: both fused)
@@ -235,6 +237,35 @@ int medusa_build_tree(int B, int K, int topk, int n_choices,
 int medusa_tree_candidates(int B, int T, int K, int topk, const int32_t* tree_indices, const int32_t* depth,
                            const int32_t* topk_ids, const int32_t* root_token, const int32_t* prefix_len,
                            int32_t* tree_candidates, int32_t* position_ids, void* stream);
+
+/* medusa_lm_head_topk followed by medusa_tree_candidates, in one call (and
+ * medusa_heads_tree below: medusa_heads followed by it).  [API]
+ * generate_candidates: each step takes the heads' top-k and gathers the
+ * tree's candidates through tree_indices.  Arguments as in the two calls
+ * (topk_ids is both the heads' output and the gather's input; T, tree_indices,
+ * depth, root_token, prefix_len, tree_candidates and position_ids as in
+ * medusa_tree_candidates); outputs identical to the two calls in sequence.
+ * Where the lm_head's top-k merge runs inside its kernel (bf16 at batch
+ * <= 2), the merging workgroup of the last head to finish also does the
+ * gather, so the step saves the gather's launch; otherwise the gather is a
+ * launch of its own after the merge.  tree_candidates, position_ids and
+ * topk_ids must not alias (MEDUSA_ERR_ALIAS).  Workspace:
+ * medusa_heads_workspace() bytes; every call leaves its arrival counts at
+ * zero, as medusa_heads does. */
+int medusa_lm_head_topk_tree(int dtype, int B, int H, int V, int K, int topk,
+                             const float* r, const void* w_lm,
+                             int32_t* topk_ids, float* topk_logits, float* logits_or_null,
+                             int T, const int32_t* tree_indices, const int32_t* depth,
+                             const int32_t* root_token, const int32_t* prefix_len,
+                             int32_t* tree_candidates, int32_t* position_ids,
+                             void* ws, size_t ws_bytes, void* stream);
+int medusa_heads_tree(int dtype, int B, int H, int V, int K, int topk,
+                      const void* hidden, const void* w1, const void* b1, const void* w_lm,
+                      int32_t* topk_ids, float* topk_logits, float* logits_or_null,
+                      float* r_or_null, int T, const int32_t* tree_indices, const int32_t* depth,
+                      const int32_t* root_token, const int32_t* prefix_len,
+                      int32_t* tree_candidates, int32_t* position_ids,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
  * Tree attention.  [NOTES] 核心要点 (tree attention verifies every

@@ -11,7 +11,8 @@ importing the package without it raises ImportError.
 
 from ._lib import (  # noqa: F401
     MEDUSA_BF16, MEDUSA_F32, SPEC_STATUS, EXPORTED, LIB_PATH, MedusaError, lib, workspace,
-    medusa_heads_workspace, medusa_resblock, medusa_lm_head_topk, medusa_heads, medusa_heads_noalloc,
+    medusa_heads_workspace, medusa_resblock, medusa_lm_head_topk, medusa_heads, medusa_heads_noalloc, medusa_heads_tree,
+    medusa_lm_head_topk_tree,
     medusa_build_tree,
     medusa_heads_pack, medusa_lm_head_topk_packed, medusa_heads_packed, medusa_tree_candidates,
     medusa_linear_workspace, medusa_linear,
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "MEDUSA_BF16", "MEDUSA_F32", "SPEC_STATUS", "MedusaError", "workspace",
     "medusa_heads_workspace", "medusa_resblock", "medusa_lm_head_topk", "medusa_heads", "medusa_heads_noalloc",
+    "medusa_heads_tree", "medusa_lm_head_topk_tree",
     "medusa_heads_pack",
     "medusa_lm_head_topk_packed", "medusa_heads_packed", "medusa_tree_candidates", "medusa_linear_workspace",
     "medusa_linear",

@@ -46,6 +46,10 @@ _SIGS = {
     "medusa_resblock": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "medusa_lm_head_topk": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "medusa_lm_head_topk_tree": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _sz, _vp]),
+    "medusa_heads_tree": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "medusa_lm_head_topk_packed": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "medusa_heads_packed_bytes": (_sz, [_i, _i, _i]),
@@ -292,6 +296,92 @@ def medusa_heads(hidden, w1, b1, w_lm, topk, keep_logits=False, keep_r=False, ws
                           _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "medusa_heads")
     return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r)
+
+
+def medusa_heads_tree(hidden, w1, b1, w_lm, topk, tree_indices, depth, root_token, prefix_len, keep_logits=False,
+                      keep_r=False, out=None, ws=None):
+    """medusa_heads, then the tree gather of medusa_tree_candidates on its
+    top-k, in one call (the gather runs inside the lm_head kernel where its
+    top-k merge does)."""
+    dt = _dtype_code(hidden)
+    B, H = hidden.shape
+    K, V = w_lm.shape[0], w_lm.shape[1]
+    T = tree_indices.shape[0]
+    dev = hidden.device
+    o = out or {}
+    ids = o.get("topk_ids")
+    if ids is None:
+        ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    vals = o.get("topk_logits")
+    if vals is None:
+        vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    cand = o.get("tree_candidates")
+    if cand is None:
+        cand = torch.empty((B, T), dtype=torch.int32, device=dev)
+    pos = o.get("position_ids")
+    if pos is None:
+        pos = torch.empty((B, T), dtype=torch.int32, device=dev)
+    logits = torch.empty((B, K, V), dtype=torch.float32, device=dev) if keep_logits else None
+    r = torch.empty((B, K, H), dtype=torch.float32, device=dev) if keep_r else None
+    need = medusa_heads_workspace(dt, B, H, V, K, topk)
+    if ws is None:
+        ws = workspace("heads", dev, need)
+    rc = lib.medusa_heads_tree(dt, B, H, V, K, topk, _ptr(hidden, "hidden"),
+                               _ptr(w1, "w1", hidden.dtype, (K, H, H)), _ptr(b1, "b1", hidden.dtype, (K, H)),
+                               _ptr(w_lm, "w_lm", hidden.dtype, (K, V, H)),
+                               _ptr(ids, "topk_ids", torch.int32, (B, K, topk)),
+                               _ptr(vals, "topk_logits", torch.float32, (B, K, topk)), _ptr(logits, "logits"),
+                               _ptr(r, "r"), T, _ptr(tree_indices, "tree_indices", torch.int32, (T,)),
+                               _ptr(depth, "depth", torch.int32, (T,)),
+                               _ptr(root_token, "root_token", torch.int32, (B,)),
+                               _ptr(prefix_len, "prefix_len", torch.int32, (B,)),
+                               _ptr(cand, "tree_candidates", torch.int32, (B, T)),
+                               _ptr(pos, "position_ids", torch.int32, (B, T)),
+                               _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_heads_tree")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits, r=r, tree_candidates=cand, position_ids=pos)
+
+
+def medusa_lm_head_topk_tree(r, w_lm, topk, tree_indices, depth, root_token, prefix_len, keep_logits=False,
+                             out=None, ws=None):
+    """medusa_lm_head_topk on r [B][K][H], then the tree gather of
+    medusa_tree_candidates on its top-k, in one call."""
+    dt = _dtype_code(w_lm)
+    B, K, H = r.shape
+    V = w_lm.shape[1]
+    T = tree_indices.shape[0]
+    dev = r.device
+    o = out or {}
+    ids = o.get("topk_ids")
+    if ids is None:
+        ids = torch.empty((B, K, topk), dtype=torch.int32, device=dev)
+    vals = o.get("topk_logits")
+    if vals is None:
+        vals = torch.empty((B, K, topk), dtype=torch.float32, device=dev)
+    cand = o.get("tree_candidates")
+    if cand is None:
+        cand = torch.empty((B, T), dtype=torch.int32, device=dev)
+    pos = o.get("position_ids")
+    if pos is None:
+        pos = torch.empty((B, T), dtype=torch.int32, device=dev)
+    logits = torch.empty((B, K, V), dtype=torch.float32, device=dev) if keep_logits else None
+    need = medusa_heads_workspace(dt, B, H, V, K, topk)
+    if ws is None:
+        ws = workspace("heads", dev, need)
+    rc = lib.medusa_lm_head_topk_tree(dt, B, H, V, K, topk, _ptr(r, "r", torch.float32, (B, K, H)),
+                                      _ptr(w_lm, "w_lm", None, (K, V, H)),
+                                      _ptr(ids, "topk_ids", torch.int32, (B, K, topk)),
+                                      _ptr(vals, "topk_logits", torch.float32, (B, K, topk)),
+                                      _ptr(logits, "logits"), T,
+                                      _ptr(tree_indices, "tree_indices", torch.int32, (T,)),
+                                      _ptr(depth, "depth", torch.int32, (T,)),
+                                      _ptr(root_token, "root_token", torch.int32, (B,)),
+                                      _ptr(prefix_len, "prefix_len", torch.int32, (B,)),
+                                      _ptr(cand, "tree_candidates", torch.int32, (B, T)),
+                                      _ptr(pos, "position_ids", torch.int32, (B, T)),
+                                      _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "medusa_lm_head_topk_tree")
+    return dict(topk_ids=ids, topk_logits=vals, logits=logits, tree_candidates=cand, position_ids=pos)
 
 
 PURPOSE_NUCLEUS = 0

@@ -160,6 +160,19 @@ struct RowStat {
   float A;      // sum (z - m) exp(z - m)
 };
 
+// The per-step tree gather of medusa_tree_candidates as kernel arguments:
+// tree_candidates[b][t] = [root_token[b], topk_ids[b][0][..], ...][tree_indices[t]]
+// and position_ids[b][t] = prefix_len[b] + depth[t].  T = 0: no gather.
+struct TreeGather {
+  int T;
+  const int32_t* tree_indices;
+  const int32_t* depth;
+  const int32_t* root_token;
+  const int32_t* prefix_len;
+  int32_t* tree_candidates;
+  int32_t* position_ids;
+};
+
 // a <- statistics of the union of two disjoint sets (log-sum-exp rescaling;
 // an empty side contributes nothing).
 __device__ __forceinline__ void rowstat_merge(RowStat& a, const RowStat& b, bool typical) {
@@ -223,6 +236,10 @@ constexpr int kHeadsResMaxSplits = 8;
 int heads_res_splits(int H, int K);
 int heads_res_gemm(int B, int H, int K, const uint16_t* hidden, const void* w1_packed, const uint16_t* b1,
                    float* r_or_null, float* part, uint16_t* planes, hipStream_t st);
+
+// The tree gather as its own launch (tree.hip), topk_ids [B][K][topk].
+int launch_tree_candidates(int B, int K, int topk, const int32_t* topk_ids, const medusa::TreeGather& tg,
+                           hipStream_t st);
 
 // Acceptance from one drawn token per node (posterior.hip; nucleus mode).
 int decide_on_draws(int B, int T, int V, int p_max, int D, const medusa::RowStat* draws,

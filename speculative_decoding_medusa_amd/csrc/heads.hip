@@ -246,6 +246,7 @@ __device__ void block_best(float& v, int& id, float* sv, int* si) {
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeMaxKeys = 32;  // keys per thread: lists * k <= 32768
 constexpr int kFusedMergeKeys = 8;  // in-kernel merge: lists * k <= 256 * 8
+constexpr int kGatherCounter = 32;  // arrival count of merged heads, after the per-head counts
 
 __device__ __forceinline__ uint64_t merge_key(float v, int id) {
   if (id < 0 || v != v) return 0;
@@ -270,6 +271,9 @@ struct MergeSmem {
 // Top-k of the n candidates (cv, ci) by radix selection with NT threads
 // (E keys each, n <= NT * E); writes k entries of oid / oval (-1 / -inf
 // past the candidates).  Every thread of the workgroup calls it.
+// COHERENT: the candidates are read, and the results written, with
+// device-scope accesses (other workgroups of the running kernel wrote the
+// lists, and may read the results).
 template <int NT, int E, bool COHERENT>
 __device__ __forceinline__ void radix_topk(const float* __restrict__ cv, const int* __restrict__ ci, int n, int k,
                                            int32_t* __restrict__ oid, float* __restrict__ oval, MergeSmem& sm) {
@@ -358,15 +362,26 @@ __device__ __forceinline__ void radix_topk(const float* __restrict__ cv, const i
   }
   __syncthreads();
   const int S = sm.nsel;  // <= k
+  int slot = -1, oi = -1;
+  float ov = -__builtin_huge_valf();
   if (tid < S) {
     const uint64_t x = sm.keys[tid];
     int rank = 0;
     for (int t = 0; t < S; ++t) rank += sm.keys[t] > x ? 1 : 0;
-    oid[rank] = static_cast<int32_t>(~static_cast<uint32_t>(x));
-    oval[rank] = merge_key_value(x);
+    slot = rank;
+    oi = static_cast<int32_t>(~static_cast<uint32_t>(x));
+    ov = merge_key_value(x);
   } else if (tid < k) {
-    oid[tid] = -1;
-    oval[tid] = -__builtin_huge_valf();
+    slot = tid;
+  }
+  if (slot >= 0) {
+    if (COHERENT) {   // write-through: read back by another workgroup of the running kernel
+      __hip_atomic_store(oid + slot, oi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(oval + slot, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      oid[slot] = oi;
+      oval[slot] = ov;
+    }
   }
 }
 
@@ -728,7 +743,7 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     int B, int H, int V, int K, int k, int rows_per_wave, int row_stride, int G, const float* __restrict__ r,
     const uint16_t* __restrict__ wlm, float* __restrict__ logits_out, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_vals, float* __restrict__ cand_v, int32_t* __restrict__ cand_i,
-    int* __restrict__ counters, int fuse) {
+    int* __restrict__ counters, int fuse, TreeGather tg) {
   const int j = blockIdx.y, wg = blockIdx.x;
   // the wave index made uniform: rows, addresses and gather slots in scalars
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -892,6 +907,30 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     __syncthreads();
   }
   if (threadIdx.x == 0) __hip_atomic_store(counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tg.T == 0) return;
+  // The tree gather, by the merging workgroup of the last head to finish:
+  // this head's top-k is written through; count it, and the workgroup that
+  // completes the count reads every head's (device scope) and gathers.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counters + kGatherCounter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     K - 1
+                 ? 1
+                 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  for (int x = threadIdx.x; x < B * tg.T; x += kHeadsThreads) {
+    const int b = x / tg.T, t = x - b * tg.T;
+    const int ti = tg.tree_indices[t];
+    const bool in = ti >= 1 && ti <= K * k;
+    const int tok = in ? __hip_atomic_load(topk_ids + static_cast<size_t>(b) * K * k + (ti - 1), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : tg.root_token[b];
+    tg.tree_candidates[x] = tok;
+    tg.position_ids[x] = tg.prefix_len[b] + tg.depth[t];
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counters + kGatherCounter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace medusa
@@ -1083,8 +1122,12 @@ int launch_topk_merge(int B, int K, int topk, int lists, const float* cand_v, co
   return medusa_host::hip_check("medusa_lm_head_topk merge launch");
 }
 
+// tg (optional): the tree gather after the top-k, inside the lm_head kernel
+// where its merge runs there, else as a launch of its own.
 int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float* r, const void* w_lm,
-                   int32_t* ids, float* vals, float* logits, void* ws, hipStream_t st) {
+                   int32_t* ids, float* vals, float* logits, void* ws, hipStream_t st,
+                   const TreeGather* tg = nullptr) {
+  const TreeGather none{};
   LmGrid lg = lm_grid(dtype, B, H, V, K, topk, kMaxWavesPerSimd);
   char* base = static_cast<char*>(ws);
   const size_t cb = cand_bytes(dtype, B, H, V, K, topk);
@@ -1105,13 +1148,11 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
     if (H == (NS) * 512)                                                                                      \
       hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, true>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H,  \
                          V, K, topk, lg.rows_per_wave, lm_row_stride(lg.G), lg.G, r, w, logits, ids, vals,    \
-                         cand_v, cand_i,                                                                        \
-                         counters, fused ? 1 : 0);                                                              \
+                         cand_v, cand_i, counters, fused ? 1 : 0, fused && tg != nullptr ? *tg : none);         \
     else                                                                                                      \
       hipLaunchKernelGGL((lm_topk_diag_kernel<NS, NB, false>), dim3(lg.G, K), dim3(kHeadsThreads), 0, st, B, H, \
                          V, K, topk, lg.rows_per_wave, lm_row_stride(lg.G), lg.G, r, w, logits, ids, vals,    \
-                         cand_v, cand_i,                                                                        \
-                         counters, fused ? 1 : 0);                                                              \
+                         cand_v, cand_i, counters, fused ? 1 : 0, fused && tg != nullptr ? *tg : none);         \
   } while (0)
     const int ns = diag_nstmax(lg.nst);
     if (ns == 4) {
@@ -1129,8 +1170,13 @@ int launch_lm_topk(int dtype, int B, int H, int V, int K, int topk, const float*
                        lg.rows_per_wg, lg.G, r, static_cast<const float*>(w_lm), logits, ids, vals, cand_v, cand_i);
   }
   int rc = medusa_host::hip_check("medusa_lm_head_topk launch");
-  if (rc != MEDUSA_OK || fused) return rc;
-  return launch_topk_merge(B, K, topk, lg.lists, cand_v, cand_i, ids, vals, st);
+  if (rc != MEDUSA_OK) return rc;
+  if (!fused) {
+    rc = launch_topk_merge(B, K, topk, lg.lists, cand_v, cand_i, ids, vals, st);
+    if (rc != MEDUSA_OK) return rc;
+  }
+  if (tg != nullptr && !fused) return medusa_host::launch_tree_candidates(B, K, topk, ids, *tg, st);
+  return MEDUSA_OK;
 }
 
 // the GEMM path's hi/lo planes of r, [K][2B][H] bf16
@@ -1187,6 +1233,32 @@ extern "C" int medusa_resblock(int dtype, int B, int H, int K, const void* hidde
   return launch_resblock(dtype, B, H, K, hidden, w1, b1, r, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+
+// Arguments of the tree gather shared by the *_tree calls.
+int check_tree_gather(const char* fn, int T, const int32_t* tree_indices, const int32_t* depth,
+                      const int32_t* root_token, const int32_t* prefix_len, const int32_t* tree_candidates,
+                      const int32_t* position_ids, const int32_t* topk_ids) {
+  MEDUSA_REQUIRE(T >= 1 && T <= kMaxNodes, MEDUSA_ERR_SHAPE, "%s: T=%d", fn, T);
+#define MEDUSA_ARG_PTR(p)                                                                   \
+  do {                                                                                     \
+    MEDUSA_REQUIRE((p) != nullptr, MEDUSA_ERR_NULL, "%s: %s is NULL", fn, #p);             \
+    MEDUSA_REQUIRE(medusa_host::aligned16(p), MEDUSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+  MEDUSA_ARG_PTR(tree_indices);
+  MEDUSA_ARG_PTR(depth);
+  MEDUSA_ARG_PTR(root_token);
+  MEDUSA_ARG_PTR(prefix_len);
+  MEDUSA_ARG_PTR(tree_candidates);
+  MEDUSA_ARG_PTR(position_ids);
+#undef MEDUSA_ARG_PTR
+  MEDUSA_REQUIRE(tree_candidates != position_ids && tree_candidates != topk_ids && position_ids != topk_ids,
+                 MEDUSA_ERR_ALIAS, "%s: tree_candidates, position_ids and topk_ids must not alias", fn);
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
 extern "C" int medusa_lm_head_topk(int dtype, int B, int H, int V, int K, int topk, const float* r,
                                    const void* w_lm, int32_t* topk_ids, float* topk_logits,
                                    float* logits_or_null, void* ws, size_t ws_bytes, void* stream) {
@@ -1202,6 +1274,30 @@ extern "C" int medusa_lm_head_topk(int dtype, int B, int H, int V, int K, int to
                  "%s: workspace %zu < %zu bytes", __func__, ws_bytes, lm_ws_bytes(dtype, B, H, V, K, topk));
   return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws,
                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int medusa_lm_head_topk_tree(int dtype, int B, int H, int V, int K, int topk, const float* r,
+                                        const void* w_lm, int32_t* topk_ids, float* topk_logits,
+                                        float* logits_or_null, int T, const int32_t* tree_indices,
+                                        const int32_t* depth, const int32_t* root_token, const int32_t* prefix_len,
+                                        int32_t* tree_candidates, int32_t* position_ids, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  int rc = check_heads_shape(__func__, dtype, B, H, V, K, topk);
+  if (rc != MEDUSA_OK) return rc;
+  MEDUSA_REQUIRE_PTR(r);
+  MEDUSA_REQUIRE_PTR(w_lm);
+  MEDUSA_REQUIRE_PTR(topk_ids);
+  MEDUSA_REQUIRE_PTR(topk_logits);
+  if (logits_or_null != nullptr) MEDUSA_REQUIRE_PTR(logits_or_null);
+  rc = check_tree_gather(__func__, T, tree_indices, depth, root_token, prefix_len, tree_candidates, position_ids,
+                         topk_ids);
+  if (rc != MEDUSA_OK) return rc;
+  MEDUSA_REQUIRE_PTR(ws);
+  MEDUSA_REQUIRE(ws_bytes >= lm_ws_bytes(dtype, B, H, V, K, topk), MEDUSA_ERR_WORKSPACE,
+                 "%s: workspace %zu < %zu bytes", __func__, ws_bytes, lm_ws_bytes(dtype, B, H, V, K, topk));
+  const TreeGather tg{T, tree_indices, depth, root_token, prefix_len, tree_candidates, position_ids};
+  return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws,
+                        static_cast<hipStream_t>(stream), &tg);
 }
 
 extern "C" int medusa_lm_head_topk_packed(int dtype, int B, int H, int V, int K, int topk, const float* r,
@@ -1236,13 +1332,13 @@ namespace {
 // lm_ws_bytes + tail_bytes bytes.
 int run_heads(int dtype, int B, int H, int V, int K, int topk, const void* hidden, const void* w1, const void* b1,
               const void* w_lm, int32_t* topk_ids, float* topk_logits, float* logits_or_null, float* r_or_null,
-              void* ws, hipStream_t st) {
+              void* ws, hipStream_t st, const TreeGather* tg = nullptr) {
   float* r = r_or_null != nullptr
                  ? r_or_null
                  : reinterpret_cast<float*>(static_cast<char*>(ws) + lm_ws_bytes(dtype, B, H, V, K, topk));
   int rc = launch_resblock(dtype, B, H, K, hidden, w1, b1, r, st);
   if (rc != MEDUSA_OK) return rc;
-  return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws, st);
+  return launch_lm_topk(dtype, B, H, V, K, topk, r, w_lm, topk_ids, topk_logits, logits_or_null, ws, st, tg);
 }
 
 int check_heads_args(const char* fn, int dtype, int B, int H, int V, int K, int topk, const void* hidden,
@@ -1282,6 +1378,27 @@ extern "C" int medusa_heads(int dtype, int B, int H, int V, int K, int topk, con
                  ws_bytes, need);
   return run_heads(dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits, logits_or_null, r_or_null,
                    ws, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int medusa_heads_tree(int dtype, int B, int H, int V, int K, int topk, const void* hidden,
+                                 const void* w1, const void* b1, const void* w_lm, int32_t* topk_ids,
+                                 float* topk_logits, float* logits_or_null, float* r_or_null, int T,
+                                 const int32_t* tree_indices, const int32_t* depth, const int32_t* root_token,
+                                 const int32_t* prefix_len, int32_t* tree_candidates, int32_t* position_ids,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_heads_args(__func__, dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits,
+                            logits_or_null, r_or_null);
+  if (rc != MEDUSA_OK) return rc;
+  rc = check_tree_gather(__func__, T, tree_indices, depth, root_token, prefix_len, tree_candidates, position_ids,
+                         topk_ids);
+  if (rc != MEDUSA_OK) return rc;
+  MEDUSA_REQUIRE_PTR(ws);
+  const size_t need = lm_ws_bytes(dtype, B, H, V, K, topk) + tail_bytes(dtype, B, H, K);
+  MEDUSA_REQUIRE(ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__,
+                 ws_bytes, need);
+  const TreeGather tg{T, tree_indices, depth, root_token, prefix_len, tree_candidates, position_ids};
+  return run_heads(dtype, B, H, V, K, topk, hidden, w1, b1, w_lm, topk_ids, topk_logits, logits_or_null, r_or_null,
+                   ws, static_cast<hipStream_t>(stream), &tg);
 }
 
 extern "C" int medusa_heads_packed(int dtype, int B, int H, int V, int K, int topk, const void* hidden,

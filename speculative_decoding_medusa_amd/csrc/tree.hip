@@ -337,9 +337,16 @@ extern "C" int medusa_tree_candidates(int B, int T, int K, int topk, const int32
   MEDUSA_REQUIRE_PTR(tree_candidates);
   MEDUSA_REQUIRE_PTR(position_ids);
   MEDUSA_REQUIRE(tree_candidates != position_ids, MEDUSA_ERR_ALIAS, "%s: outputs must not alias", __func__);
-  hipLaunchKernelGGL(tree_candidates_kernel, dim3(static_cast<unsigned>((B * T + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), B, T, K, topk, tree_indices, depth, topk_ids, root_token,
-                     prefix_len, tree_candidates, position_ids);
+  const TreeGather tg{T, tree_indices, depth, root_token, prefix_len, tree_candidates, position_ids};
+  return medusa_host::launch_tree_candidates(B, K, topk, topk_ids, tg, static_cast<hipStream_t>(stream));
+}
+
+int medusa_host::launch_tree_candidates(int B, int K, int topk, const int32_t* topk_ids,
+                                        const medusa::TreeGather& tg, hipStream_t st) {
+  using namespace medusa;
+  hipLaunchKernelGGL(tree_candidates_kernel, dim3(static_cast<unsigned>((B * tg.T + 255) / 256)), dim3(256), 0, st,
+                     B, tg.T, K, topk, tg.tree_indices, tg.depth, topk_ids, tg.root_token, tg.prefix_len,
+                     tg.tree_candidates, tg.position_ids);
   return medusa_host::hip_check("medusa_tree_candidates launch");
 }
 

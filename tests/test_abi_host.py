@@ -33,7 +33,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_strings():
-    assert L.medusa_abi_version() == 108
+    assert L.medusa_abi_version() == 109
     for code in (OK, NULL, SHAPE, DTYPE, VALUE, WS, HIP, ALIGN, ALIAS):
         assert L.medusa_status_string(code).decode() not in ("", "unknown status")
     assert L.medusa_status_string(-99).decode() == "unknown status"
@@ -53,6 +53,40 @@ def heads(dt=1, B=1, H=64, V=100, K=2, k=4, hidden=A, w1=A, b1=A, wlm=A, ids=A, 
 def test_heads_validation(kw, code):
     assert heads(**kw) == code
     assert L.medusa_last_error().decode() != ""
+
+
+def heads_tree(dt=1, B=1, H=64, V=100, K=2, k=4, hidden=A, w1=A, b1=A, wlm=A, ids=A, vals=A, T=7, tidx=A, dep=A,
+               root=A, plen=A, cand=A + 256, pos=A + 512, ws=A, wsb=1 << 30):
+    return L.medusa_heads_tree(dt, B, H, V, K, k, hidden, w1, b1, wlm, ids, vals, None, None, T, tidx, dep, root,
+                               plen, cand, pos, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE), (dict(B=17), SHAPE), (dict(K=9), SHAPE), (dict(T=0), SHAPE), (dict(T=257), SHAPE),
+    (dict(tidx=None), NULL), (dict(root=None), NULL), (dict(pos=None), NULL), (dict(dep=MIS), ALIGN),
+    (dict(cand=A + 512), ALIAS), (dict(cand=A), ALIAS), (dict(pos=A), ALIAS), (dict(ws=None), NULL),
+    (dict(wsb=16), WS),
+])
+def test_heads_tree_validation(kw, code):
+    assert heads_tree(**kw) == code
+    assert L.medusa_last_error().decode() != ""
+
+
+def test_lm_head_topk_tree_validation():
+    f = L.medusa_lm_head_topk_tree
+    args = [1, 1, 64, 100, 2, 4, A, A, A, A, None, 7, A, A, A, A, A + 256, A + 512, A, 1 << 30, None]
+    bad = list(args)
+    bad[11] = 0
+    assert f(*bad) == SHAPE
+    bad = list(args)
+    bad[12] = None
+    assert f(*bad) == NULL
+    bad = list(args)
+    bad[16] = A
+    assert f(*bad) == ALIAS
+    bad = list(args)
+    bad[19] = 8
+    assert f(*bad) == WS
 
 
 def heads_noalloc(dt=1, B=1, H=64, V=100, K=2, k=4, hidden=A, w1=A, b1=A, wlm=A, ids=A, vals=A, logits=None,

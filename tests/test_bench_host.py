@@ -19,8 +19,11 @@ import synth  # noqa: E402
 
 def test_lm_bytes_is_weights_inputs_and_outputs():
     w = synth.workload("vicuna-7b")
-    # 5 heads x 32000 x 4096 bf16 weights, r in float32, top-10 (id, logit) pairs out
-    assert bench.lm_bytes(w) == 5 * 32000 * 4096 * 2 + 5 * 4096 * 4 + 5 * 10 * 8 == 1310802320
+    # 5 heads x 32000 x 4096 bf16 weights, r in float32, top-10 (id, logit) pairs out;
+    # the 64-node tree gather: tree_indices and depth, root and prefix length,
+    # one top-k id per node in, candidates and positions out (int32)
+    gather = (2 * 64 + 2 * 1 + 3 * 64) * 4
+    assert bench.lm_bytes(w, 64) == 5 * 32000 * 4096 * 2 + 5 * 4096 * 4 + 5 * 10 * 8 + gather == 1310803608
 
 
 def test_measured_traffic_follows_the_heads_source(tmp_path, monkeypatch):

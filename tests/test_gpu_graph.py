@@ -6,10 +6,12 @@ one attention layer, posterior, commit) captures into a single graph.  The
 graph is replayed several times; between replays eager work poisons every
 output and restores the in-place KV caches, with synchronisations around
 each replay, and every output of every replay must equal the eager step's
-bit for bit (the kernels are deterministic).  Two steps: batch 1 with
-row-major heads and a full tree build, and batch 4 with packed heads (the
+bit for bit (the kernels are deterministic).  Three steps: batch 1 with
+row-major heads and a full tree build, batch 4 with packed heads (the
 sliced ResBlock GEMM, its finisher, the lm_head GEMM and the merge) and the
-per-step tree gather on a tree built before capture.
+per-step tree gather on a tree built before capture, and batch 1 with the
+gather inside the lm_head kernel (medusa_lm_head_topk_tree, whose arrival
+counts every replay must find at zero and leave at zero).
 """
 
 import pytest
@@ -67,9 +69,14 @@ def _setup(dev, B=1):
     return x, o, k, d
 
 
-def _step(x, o, k, d, packed=False):
+def _step(x, o, k, d, packed=False, fused=False):
     t = o["tree"]
-    if packed:
+    if fused:   # the bench's step: the gather in the lm_head kernel's tail
+        md.medusa_resblock(x["hidden"], x["w1"], x["b1"], r=o["r"])
+        md.medusa_lm_head_topk_tree(o["r"], x["w_lm"], k, t["tree_indices"], t["depth"], x["root"], x["plen"],
+                                    out=dict(o["heads"], tree_candidates=t["tree_candidates"],
+                                             position_ids=t["position_ids"]), ws=o["ws_h"])
+    elif packed:
         md.medusa_heads_packed(x["hidden"], x["w1_packed"], x["b1"], x["w_lm_packed"], x["w_lm"].shape[1], k,
                                keep_r=True, out=dict(o["heads"], r=o["r"]), ws=o["ws_h"])
         md.medusa_tree_candidates(t["tree_indices"], t["depth"], o["heads"]["topk_ids"], x["root"], x["plen"], out=t)
@@ -115,34 +122,35 @@ def _reset(x, o, gather=False):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("B,packed", [(1, False), (4, True)])
-def test_step_graph_replays_equal_eager(gpu_device, B, packed):
+@pytest.mark.parametrize("B,packed,fused", [(1, False, False), (4, True, False), (1, False, True)])
+def test_step_graph_replays_equal_eager(gpu_device, B, packed, fused):
     x, o, k, d = _setup(gpu_device, B)
     t = o["tree"]
-    if packed:   # the tree's buffers, once, before any step
+    gather = packed or fused
+    if gather:   # the tree's buffers, once, before any step
         md.medusa_build_tree(x["choices"], o["heads"]["topk_ids"].zero_(), x["root"], x["plen"],
                              p_max=t["retrieve"].shape[0], out=t)
         torch.cuda.synchronize()
         assert t["status"].tolist() == [0, -1]
-    _reset(x, o, packed)
+    _reset(x, o, gather)
     torch.cuda.synchronize()
-    _step(x, o, k, d, packed)
+    _step(x, o, k, d, packed, fused)
     torch.cuda.synchronize()
-    ref = {n: v.clone() for n, v in _outputs(o, packed).items()}
-    if not packed:
+    ref = {n: v.clone() for n, v in _outputs(o, gather).items()}
+    if not gather:
         assert int(ref["tree.status"][0]) == 0
 
     graph = torch.cuda.CUDAGraph()
-    _reset(x, o, packed)
+    _reset(x, o, gather)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        _step(x, o, k, d, packed)
+        _step(x, o, k, d, packed, fused)
     torch.cuda.synchronize()
 
     for rep in range(4):
-        _reset(x, o, packed)
+        _reset(x, o, gather)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for n, v in _outputs(o, packed).items():
+        for n, v in _outputs(o, gather).items():
             assert torch.equal(v, ref[n]), "replay %d: %s differs from the eager step" % (rep, n)
