@@ -94,6 +94,20 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
   return v + static_cast<int>(dpp_u32<0x143, 0xc>(static_cast<uint32_t>(v), 0u));
 }
 
+// the wave's maximum (kMax) or minimum of signed ints, in every lane
+template <bool kMax>
+__device__ __forceinline__ int wave_reduce_i32_dpp(int v) {
+  const uint32_t id = kMax ? 0x80000000u : 0x7fffffffu;
+  auto op = [](int a, int b) { return kMax ? max(a, b) : min(a, b); };
+  v = op(v, static_cast<int>(dpp_u32<0x111, 0xf>(static_cast<uint32_t>(v), id)));
+  v = op(v, static_cast<int>(dpp_u32<0x112, 0xf>(static_cast<uint32_t>(v), id)));
+  v = op(v, static_cast<int>(dpp_u32<0x114, 0xf>(static_cast<uint32_t>(v), id)));
+  v = op(v, static_cast<int>(dpp_u32<0x118, 0xf>(static_cast<uint32_t>(v), id)));
+  v = op(v, static_cast<int>(dpp_u32<0x142, 0xa>(static_cast<uint32_t>(v), id)));
+  v = op(v, static_cast<int>(dpp_u32<0x143, 0xc>(static_cast<uint32_t>(v), id)));
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
   const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
   const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));

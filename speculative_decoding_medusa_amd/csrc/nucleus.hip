@@ -49,33 +49,21 @@ __device__ __forceinline__ float nuc_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
+// Wave reductions and scans on DPP lane moves (common.hpp).
+__device__ __forceinline__ int wave_min_i(int v) { return wave_reduce_i32_dpp<false>(v); }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
+__device__ __forceinline__ int wave_max_i(int v) { return wave_reduce_i32_dpp<true>(v); }
 
-__device__ __forceinline__ u64 wave_sum_u64(u64 v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+__device__ __forceinline__ u64 wave_sum_u64(u64 v) { return readlane_u64(wave_incl_scan_u64(v), kWave - 1); }
 
 // Inclusive scan across the wave's lanes in lane order.
 template <typename X>
-__device__ __forceinline__ X wave_incl_scan(X v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const X y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  return v;
+__device__ __forceinline__ X wave_incl_scan(X v, int) {
+  static_assert(sizeof(X) == 8 || sizeof(X) == 4, "64- or 32-bit sums");
+  if constexpr (sizeof(X) == 8)
+    return static_cast<X>(wave_incl_scan_u64(static_cast<uint64_t>(v)));
+  else
+    return static_cast<X>(wave_incl_scan_i32(static_cast<int>(v)));
 }
 
 // Bucket choice for one digit (called by one whole wave): among buckets
@@ -87,14 +75,10 @@ __device__ __forceinline__ int nuc_pick(const u64* h, int nb, u64 need, int lane
   const int lo = lane * per;
   u64 local = 0;
   for (int i = 0; i < per; ++i) local += h[lo + i];
-  // mass of the lanes above this one
-  u64 suf = local;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const u64 y = __shfl_down(suf, o);
-    if (lane + o < kWave) suf += y;
-  }
-  u64 run = suf - local;
+  // mass of the lanes above this one: the wave's total less the lanes up to
+  // and including this one
+  const u64 incl = wave_incl_scan(local, lane);
+  u64 run = readlane_u64(incl, kWave - 1) - incl;
   int cand = -1, low = 0x7fffffff;
   u64 cand_above = 0, low_above = 0;
   for (int i = per - 1; i >= 0; --i) {
@@ -117,7 +101,7 @@ __device__ __forceinline__ int nuc_pick(const u64* h, int nb, u64 need, int lane
   }
   // the owning lane's value to every lane
   const uint64_t owner = ballot(lo <= d && d < lo + per);
-  above = __shfl(a, owner ? __builtin_ctzll(owner) : 0);
+  above = readlane_u64(a, owner ? __builtin_ctzll(owner) : 0);
   return d;
 }
 
@@ -383,8 +367,8 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
     s_kbefore = 0;
     s_kappa = 0;
   }
-  mx = wave_max(mx);
-  mn = -wave_max(-mn);
+  mx = wave_reduce_dpp<true>(mx);
+  mn = -wave_reduce_dpp<true>(-mn);
   if (lane == 0) {
     s_red[0][wave] = mx;
     s_red[1][wave] = mn;
@@ -471,7 +455,7 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
       const int leader = __builtin_ctzll(bal);
       int base = 0;
       if (lane == leader) base = atomicAdd(&s_count, __popcll(bal));
-      base = __shfl(base, leader);
+      base = __builtin_amdgcn_readlane(base, leader);
       const int pos = base + __popcll(bal & ((1ull << lane) - 1));
       if (in && pos < kNlList) s_list[pos] = s_key[nl_pad(v)];
       if (in && pos < kNlSmall) s_lm[pos] = static_cast<u64>(fm[j]);
@@ -556,17 +540,8 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
       cnt += k == kappa ? 1 : 0;
     }
   }
-  u64 ma_inc = ma;
-  int cnt_inc = cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const u64 ym = __shfl_up(ma_inc, o);
-    const int yc = __shfl_up(cnt_inc, o);
-    if (lane >= o) {
-      ma_inc += ym;
-      cnt_inc += yc;
-    }
-  }
+  const u64 ma_inc = wave_incl_scan(ma, lane);
+  const int cnt_inc = wave_incl_scan(cnt, lane);
   if (lane == kWave - 1) {
     s_wm[wave] = ma_inc;
     s_wc[wave] = cnt_inc;
@@ -602,13 +577,8 @@ __global__ __launch_bounds__(kNlThreads) void nucleus_sample_lds_kernel(int V, c
     const uint64_t kap = ballot(live && k == kappa);
     const int kord = kbefore + __popcll(kap & ((2ull << lane) - 1)) - 1;   // this token's ordinal if k == kappa
     const bool in = live && (k > kappa || (k == kappa && kord < c));
-    u64 m = in ? mass(k) : 0;
     // inclusive prefix of the masses over the lanes
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const u64 y = __shfl_up(m, o);
-      if (lane >= o) m += y;
-    }
+    const u64 m = wave_incl_scan(in ? mass(k) : u64{0}, lane);
     const uint64_t hit = ballot(in && base + m > target);
     if (lane == 0) s_sample = hit ? kNlChunk * owner + __builtin_ctzll(hit) : -1;
   }
