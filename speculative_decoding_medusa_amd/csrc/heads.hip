@@ -12,7 +12,11 @@
 //    holds the activations at the same positions.  lm_head logits go into
 //    per-wave top-k lists in registers; the last workgroup of each head to
 //    finish (a device-scope arrival count; lists published with
-//    write-through stores) merges them, so the call is one kernel.
+//    write-through stores) merges them, so the call is one kernel.  With
+//    that in-kernel merge the last seventh of each head's rows is a pool
+//    handed out in blocks of four rows from a device-scope counter, so that
+//    compute units whose loads return faster (some XCDs stream about 10%
+//    faster than others) take more rows and all finish together.
 //  * bf16 otherwise: the ResBlock on a split-K MFMA kernel (four waves split
 //    each 16-row tile's K range and reduce through LDS), and the lm_head on
 //    the skinny-GEMM kernel of base_head.hip, the batch's hi/lo planes as
@@ -247,6 +251,17 @@ constexpr int kMergeThreads = 1024;
 constexpr int kMergeMaxKeys = 32;  // keys per thread: lists * k <= 32768
 constexpr int kFusedMergeKeys = 8;  // in-kernel merge: lists * k <= 256 * 8
 constexpr int kGatherCounter = 32;  // arrival count of merged heads, after the per-head counts
+// Dynamic row pool of the row-diagonal lm_head: per head a counter of handed
+// out blocks, each counter in a 256-byte line of its own (heads do not
+// contend for one atomic unit), after the 256 bytes of arrival counts.  The
+// pool is about the last seventh of each head's rows, in blocks of four
+// (measured at the Vicuna-7B shape against a static split: pools of 1/16,
+// 1/10, 1/8, 1/7 and 1/5 with blocks of four: +1.1, -3.0, -3.0, -4.0, -3.9
+// us; 1/10 with blocks of eight: -0.3 to +1.4 us).
+constexpr int kDynCounterBase = 64;      // ints
+constexpr int kDynCounterStride = 64;    // ints
+constexpr int kDynBlock = 4;             // rows per block
+constexpr int kDynPoolDiv = 7;           // pool: the last V / kDynPoolDiv rows, rounded down to whole strides
 
 __device__ __forceinline__ uint64_t merge_key(float v, int id) {
   if (id < 0 || v != v) return 0;
@@ -756,6 +771,16 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   // a wave with no rows (n == 0) still loads a valid row (dr.row clamps)
   const DiagRows dr = diag_rows(wg * kHeadsWaves + wave, rows_per_wave, row_stride, V);
   const uint16_t* wbase = wlm + static_cast<size_t>(j) * V * H;
+  // With the in-kernel merge the head's rows split into a static part, rows
+  // [0, pool0) interleaved over its waves as above, and a pool [pool0, V)
+  // handed out in blocks of kDynBlock rows, in order, from a device-scope
+  // counter: compute units whose loads return faster take more blocks.
+  const bool dyn = fuse != 0 && row_stride > 1;
+  const int pool0 = dyn ? ((V - V / kDynPoolDiv) / row_stride) * row_stride : V;
+  const int ns = dyn ? min(dr.n, (pool0 - dr.r0 + row_stride - 1) / row_stride) : dr.n;
+  int* const dyn_ctr = counters + kDynCounterBase + j * kDynCounterStride;
+  int graw = 0;   // lane 0: the block index of the pending grab
+  if (dyn && lane == 0) graw = __hip_atomic_fetch_add(dyn_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Prologue in one memory round trip: a round of r loads (clamped, with no
   // branch, so all are in flight together), the block's first two weight
@@ -819,29 +844,31 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
 
   // gather the logits of row i of the wave's sequence into lane i % 64;
   // flush every 64 rows
-  auto offer = [&](int i, const float (&lg)[NB]) {
+  int gid = 0;   // the row whose logit this lane's slot holds
+  auto flush = [&](int slot) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b >= B) continue;
+      const float v = gath[b];
+      bool ok = lane <= slot && (v == v);
+      if (cnt[b] == k)
+        ok = ok && beats(v, gid, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[b]), k - 1)),
+                         __builtin_amdgcn_readlane(li[b], k - 1));
+      const uint64_t m = ballot(ok);
+      if (m) topk_reg_insert(lv[b], li[b], cnt[b], k, v, gid, m, lane);
+      gath[b] = NEG;
+    }
+  };
+  // the i-th row of the wave (row id `row`) into slot i % 64; flush every 64
+  auto offer = [&](int i, int row, const float (&lg)[NB]) {
     const int slot = i & 63;
-    const int row = dr.r0 + i * dr.rs;
+    gid = lane == slot ? row : gid;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       gath[b] = put_lane(gath[b], lg[b], slot);
       if (logits_out != nullptr && lane == 0 && b < B) logits_out[(static_cast<size_t>(b) * K + j) * V + row] = lg[b];
     }
-    if (slot == 63 || i == dr.n - 1) {
-      const int myrow = dr.r0 + (i - slot + lane) * dr.rs;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b >= B) continue;
-        const float v = gath[b];
-        bool ok = lane <= slot && (v == v);
-        if (cnt[b] == k)
-          ok = ok && beats(v, myrow, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[b]), k - 1)),
-                           __builtin_amdgcn_readlane(li[b], k - 1));
-        const uint64_t m = ballot(ok);
-        if (m) topk_reg_insert(lv[b], li[b], cnt[b], k, v, myrow, m, lane);
-        gath[b] = NEG;
-      }
-    }
+    if (slot == 63) flush(63);
   };
 
   // Rotated double buffer: both buffers are in flight before the loop, and
@@ -853,18 +880,57 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   // prologue's loads cannot be sunk below its conversions.
   float lg[NB];
   int i = 0;
-  for (; i + 1 < dr.n; i += 2) {
+  for (; i + 1 < ns; i += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_logits<NSTMAX, NB, FULL, true>(wa, ahi, alo, H, e0, wbase + static_cast<size_t>(dr.row(i + 2)) * H, lg);
-    offer(i, lg);
+    diag_row_logits<NSTMAX, NB, FULL, true>(wa, ahi, alo, H, e0,
+                                            wbase + static_cast<size_t>(dr.row(min(i + 2, ns - 1))) * H, lg);
+    offer(i, dr.r0 + i * dr.rs, lg);
     __builtin_amdgcn_sched_barrier(0);
-    diag_row_logits<NSTMAX, NB, FULL, true>(wb, ahi, alo, H, e0, wbase + static_cast<size_t>(dr.row(i + 3)) * H, lg);
-    offer(i + 1, lg);
+    diag_row_logits<NSTMAX, NB, FULL, true>(wb, ahi, alo, H, e0,
+                                            wbase + static_cast<size_t>(dr.row(min(i + 3, ns - 1))) * H, lg);
+    offer(i + 1, dr.r0 + (i + 1) * dr.rs, lg);
   }
-  if (i < dr.n) {
+  if (i < ns) {
     diag_row_logits<NSTMAX, NB, FULL, false>(wa, ahi, alo, H, e0, wbase, lg);
-    offer(i, lg);
+    offer(i, dr.r0 + i * dr.rs, lg);
+    ++i;
   }
+  if (dyn) {
+    // The pool, a block at a time.  The grab for the next block goes out as
+    // a block starts and its value is first read (through an empty asm, so
+    // the read is not hoisted) when the refills reach the block's end:
+    // those loads of the next block's first rows keep the pipeline full.
+    asm volatile("" : "+v"(graw));
+    int blk = pool0 + __builtin_amdgcn_readfirstlane(graw) * kDynBlock;
+    if (blk < V) {
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(blk) * H, H, e0, wa);
+      diag_load_row<NSTMAX>(wbase + static_cast<size_t>(min(blk + 1, V - 1)) * H, H, e0, wb);
+    }
+    while (blk < V) {
+      int nraw = 0;
+      if (lane == 0) nraw = __hip_atomic_fetch_add(dyn_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int nblk = V;
+#pragma unroll
+      for (int t = 0; t < kDynBlock; t += 2) {
+        if (t + 2 == kDynBlock) {
+          asm volatile("" : "+v"(nraw));
+          nblk = pool0 + __builtin_amdgcn_readfirstlane(nraw) * kDynBlock;
+        }
+        const int ra = t + 2 < kDynBlock ? blk + t + 2 : nblk;
+        const int rb = t + 3 < kDynBlock ? blk + t + 3 : nblk + 1;
+        __builtin_amdgcn_sched_barrier(0);
+        diag_row_logits<NSTMAX, NB, FULL, true>(wa, ahi, alo, H, e0, wbase + static_cast<size_t>(min(ra, V - 1)) * H,
+                                                lg);
+        if (blk + t < V) offer(i++, blk + t, lg);
+        __builtin_amdgcn_sched_barrier(0);
+        diag_row_logits<NSTMAX, NB, FULL, true>(wb, ahi, alo, H, e0, wbase + static_cast<size_t>(min(rb, V - 1)) * H,
+                                                lg);
+        if (blk + t + 1 < V) offer(i++, blk + t + 1, lg);
+      }
+      blk = nblk;
+    }
+  }
+  if ((i & 63) != 0) flush((i - 1) & 63);
   // every wave publishes its own lists (list wg * 4 + wave of head j)
   const int nlists = G * kHeadsWaves;
 #pragma unroll
@@ -898,6 +964,7 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
     s_last = __hip_atomic_fetch_add(counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1 ? 1 : 0;
   __syncthreads();
   if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(counters + kDynCounterBase + j * kDynCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int n = nlists * k;
   for (int b = 0; b < B; ++b) {
     const size_t base = (static_cast<size_t>(j) * B + b) * n;
@@ -942,7 +1009,7 @@ using namespace medusa;
 
 // Workspace header: one arrival count per head for the in-kernel merge
 // (zero before the first call; every call leaves it zero).
-constexpr size_t kCounterBytes = 256;
+constexpr size_t kCounterBytes = 256 + kMaxHeads * kDynCounterStride * 4;
 
 struct LmGrid {
   bool diag;       // row-diagonal kernel (B <= 2)
@@ -1456,7 +1523,7 @@ namespace {
 
 // The arrival counts at the head of the scratch start at zero.
 __global__ __launch_bounds__(64) void scratch_clear_kernel(uint32_t* p, int n) {
-  if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0u;
+  for (int x = static_cast<int>(threadIdx.x); x < n; x += 64) p[x] = 0u;
 }
 
 std::mutex g_scratch_mu;
