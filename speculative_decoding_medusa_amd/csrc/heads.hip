@@ -13,10 +13,11 @@
 //    per-wave top-k lists in registers; the last workgroup of each head to
 //    finish (a device-scope arrival count; lists published with
 //    write-through stores) merges them, so the call is one kernel.  With
-//    that in-kernel merge the last seventh of each head's rows is a pool
-//    handed out in blocks of four rows from a device-scope counter, so that
-//    compute units whose loads return faster (some XCDs stream about 10%
-//    faster than others) take more rows and all finish together.
+//    that in-kernel merge, and H > 2048, the last seventh of each head's
+//    rows is a pool handed out in blocks of four rows from a device-scope
+//    counter, so that compute units whose loads return faster (some XCDs
+//    stream about 10% faster than others) take more rows and all finish
+//    together.
 //  * bf16 otherwise: the ResBlock on a split-K MFMA kernel (four waves split
 //    each 16-row tile's K range and reduce through LDS), and the lm_head on
 //    the skinny-GEMM kernel of base_head.hip, the batch's hi/lo planes as
@@ -775,7 +776,9 @@ __global__ __launch_bounds__(kHeadsThreads) void lm_topk_diag_kernel(
   // [0, pool0) interleaved over its waves as above, and a pool [pool0, V)
   // handed out in blocks of kDynBlock rows, in order, from a device-scope
   // counter: compute units whose loads return faster take more blocks.
-  const bool dyn = fuse != 0 && row_stride > 1;
+  // (rows of H > 2048 only: shorter rows make a block too short to hide its
+  // grab, and at H 1024 the pool cost 10 us a call, 47.8 against 58.2 us)
+  const bool dyn = NSTMAX >= 8 && fuse != 0 && row_stride > 1;
   const int pool0 = dyn ? ((V - V / kDynPoolDiv) / row_stride) * row_stride : V;
   const int ns = dyn ? min(dr.n, (pool0 - dr.r0 + row_stride - 1) / row_stride) : dr.n;
   int* const dyn_ctr = counters + kDynCounterBase + j * kDynCounterStride;
