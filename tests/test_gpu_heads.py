@@ -222,3 +222,35 @@ def test_heads_logit_error_from_r_planes(gpu_device, H):
     print("H %d logits max rel err %.3e, max abs err %.3e (logit std %.3f)" % (H, err, abs_err, float(z.std())),
           flush=True)
     assert err < 1e-4
+
+
+# The row-diagonal lm_head with its in-kernel merge (bf16, batch <= 2, lists
+# x top-k <= 2048) and rows of H > 2048 hands the last seventh of each head's
+# rows out in blocks of four from a device-scope counter.  Cases: a pool of a
+# few blocks after one static row per wave, a row count below the number of
+# waves (every row from the pool, a partial last block), a ragged V at batch
+# 2, eight heads at top-16, and H 2560 (the smallest row length that takes
+# the pool).
+@pytest.mark.parametrize("B,H,V,K,k", [
+    (1, 4096, 300, 5, 10),
+    (1, 2560, 150, 5, 10),
+    (2, 4096, 5003, 5, 10),
+    (1, 3072, 4001, 8, 16),
+    (1, 2560, 7000, 4, 8),
+])
+def test_heads_dynamic_row_pool(gpu_device, B, H, V, K, k):
+    w = synth.workload("vicuna-7b", B=B, H=H, V=V, K=K, topk=k)
+    case = heads_case(w, seed=H + V + K, margin=1e-5, max_retries=400)
+    _check(case, _run(case, w, split=(B == 1)), w)
+
+
+def test_heads_dynamic_row_pool_calls_in_turn(gpu_device):
+    # inputs A, B, A, B through one workspace at a pool shape: each call's
+    # counters start at zero (the merging workgroups reset them) and every
+    # row is taken exactly once
+    w = synth.workload("vicuna-7b", B=1, H=4096, V=3000, K=5, topk=10)
+    a = heads_case(w, seed=41, margin=1e-5, max_retries=400)
+    b = heads_case(w, seed=42, margin=1e-5, max_retries=400)
+    assert not np.array_equal(a["topk_ids"], b["topk_ids"])
+    for case in (a, b, a, b):
+        _check(case, _run(case, w, keep_logits=True), w)
