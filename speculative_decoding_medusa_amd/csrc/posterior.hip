@@ -335,8 +335,22 @@ namespace medusa {
 
 // Per-row statistics from `nparts` partial ones (disjoint vocabulary
 // blocks): one workgroup per row, every part requested in one round trip,
-// merged in registers, across the wave by shuffles, then across waves.
+// merged in registers, across the wave on DPP lane moves, then across waves.
 constexpr int kMergeParts = 4;   // parts per thread: nparts <= 1024
+
+// `a` of the lane that DPP control C (row mask M) selects; the empty set
+// where there is none
+template <int C, int M>
+__device__ __forceinline__ RowStat rowstat_dpp(const RowStat& a) {
+  const float NEG = -__builtin_huge_valf();
+  RowStat y;
+  y.mx = dpp_f32<C, M>(a.mx, NEG);
+  y.arg = static_cast<int>(dpp_u32<C, M>(static_cast<uint32_t>(a.arg), 0x7fffffffu));
+  y.m = dpp_f32<C, M>(a.m, NEG);
+  y.S = dpp_f32<C, M>(a.S, 0.f);
+  y.A = dpp_f32<C, M>(a.A, 0.f);
+  return y;
+}
 
 __global__ __launch_bounds__(kPostThreads) void posterior_merge_kernel(int nparts, int typical,
                                                                      const RowStat* __restrict__ parts,
@@ -351,20 +365,19 @@ __global__ __launch_bounds__(kPostThreads) void posterior_merge_kernel(int npart
 #pragma unroll
   for (int u = 0; u < kMergeParts; ++u)
     if (u * kPostThreads + tid < nparts) rowstat_merge(acc, x[u], typical != 0);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    RowStat y;
-    y.mx = __shfl_xor(acc.mx, o);
-    y.arg = __shfl_xor(acc.arg, o);
-    y.m = __shfl_xor(acc.m, o);
-    y.S = __shfl_xor(acc.S, o);
-    y.A = __shfl_xor(acc.A, o);
-    rowstat_merge(acc, y, typical != 0);
-  }
+  // across the wave on DPP lane moves (lanes with no source bring the empty
+  // set); lane 63 ends with the wave's statistics
+  rowstat_merge(acc, rowstat_dpp<0x111, 0xf>(acc), typical != 0);
+  rowstat_merge(acc, rowstat_dpp<0x112, 0xf>(acc), typical != 0);
+  rowstat_merge(acc, rowstat_dpp<0x114, 0xf>(acc), typical != 0);
+  rowstat_merge(acc, rowstat_dpp<0x118, 0xf>(acc), typical != 0);
+  rowstat_merge(acc, rowstat_dpp<0x142, 0xa>(acc), typical != 0);
+  rowstat_merge(acc, rowstat_dpp<0x143, 0xc>(acc), typical != 0);
   __shared__ RowStat s_part[kPostThreads / kWave];
-  if (lane == 0) s_part[wave] = acc;
+  if (lane == kWave - 1) s_part[wave] = acc;
   __syncthreads();
   if (tid == 0) {
+    acc = s_part[0];
     for (int w = 1; w < kPostThreads / kWave; ++w) rowstat_merge(acc, s_part[w], typical != 0);
     out[row] = acc;
   }
