@@ -103,15 +103,17 @@ enum {
  * H % 8 == 0, f32 needs H % 4 == 0; 1 <= topk <= min(64, V).
  *
  * Workspace: medusa_heads_workspace() bytes of device memory (per-wave
- * candidate lists, one arrival count per head and, in medusa_heads, r).
- * Its first 256 bytes must be zero before the first call that uses it
- * (allocate it zeroed once); every call leaves them zero again.  The rest
- * needs no initialisation.  medusa_lm_head_topk streams the weights in one
- * kernel on `stream`; each wave leaves a sorted top-k list, and the merge
- * of a head's lists (radix selection on unique value/id keys) runs in the
- * last workgroup of that head to finish when they fit its 2048-key budget,
- * in a second kernel otherwise.  Calls that share a workspace must not run
- * concurrently.
+ * candidate lists, one arrival count per head, one row-pool counter per
+ * head and, in medusa_heads, r).  Its first 2304 bytes (the counts) must be
+ * zero before the first call that uses it (allocate it zeroed once); every
+ * call leaves them zero again.  The rest needs no initialisation.
+ * medusa_lm_head_topk streams the weights in one kernel on `stream`; each
+ * wave leaves a sorted top-k list, and the merge of a head's lists (radix
+ * selection on unique value/id keys) runs in the last workgroup of that
+ * head to finish when they fit its 2048-key budget, in a second kernel
+ * otherwise.  With that in-kernel merge and H > 2048 the last seventh of
+ * each head's rows is handed out at run time in blocks of four rows.  Calls
+ * that share a workspace must not run concurrently.
  * ------------------------------------------------------------------- */
 size_t medusa_heads_workspace(int dtype, int B, int H, int V, int K, int topk);
 
