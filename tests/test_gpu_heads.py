@@ -254,3 +254,29 @@ def test_heads_dynamic_row_pool_calls_in_turn(gpu_device):
     assert not np.array_equal(a["topk_ids"], b["topk_ids"])
     for case in (a, b, a, b):
         _check(case, _run(case, w, keep_logits=True), w)
+
+
+def _pool_shapes(n, seed=2024):
+    """Seeded random shapes that take the lm_head's dynamic row pool (bf16,
+    batch <= 2, H > 2048, lists x top-k within the in-kernel merge)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(2056, 6145)) // 8 * 8
+        K = int(rng.integers(3, 9))
+        V = int(rng.integers(64, 8001))
+        lists = 4 * max(1, min(256 // K, -(-V // 4)))
+        kmax = min(2048 // lists, 64, V)
+        if kmax < 1:
+            continue
+        k = int(rng.integers(1, kmax + 1))
+        out.append((B, H, V, K, k))
+    return out
+
+
+@pytest.mark.parametrize("B,H,V,K,k", _pool_shapes(12))
+def test_heads_dynamic_row_pool_random_shapes(gpu_device, B, H, V, K, k):
+    w = synth.workload("vicuna-7b", B=B, H=H, V=V, K=K, topk=k)
+    case = heads_case(w, seed=B + H + V + K + k, margin=1e-5, max_retries=400)
+    _check(case, _run(case, w, keep_logits=True), w)
