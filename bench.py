@@ -34,6 +34,7 @@ METRIC = "Medusa verify steps/sec at Vicuna-7B shape (batch 1); achieved HBM GB/
 HBM_PEAK_GBS = 8000.0
 LM_SAMPLE = 10   # the roofline call is bracketed by events in one timed step of every LM_SAMPLE
 SETTLE_MS = 30.0 # GPU time of untimed steps before the warm-up
+STAGE_STEPS = 200  # steps of the untimed per-stage breakdown pass
 
 
 def parse():
@@ -1144,9 +1145,9 @@ def main():
     ms_per_step = total_ms / args.steps
     lm_ms = [lm_ev[s][0].elapsed_time(lm_ev[s][1]) for s in sampled]
 
-    # per-stage breakdown: a separate, untimed pass with an event at every
-    # stage boundary
-    nb = min(args.steps, 50)
+    # per-stage breakdown: a separate, untimed pass of STAGE_STEPS steps with
+    # an event at every stage boundary (median, p10 and p90 per stage)
+    nb = STAGE_STEPS
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(nb)]
     for s in range(nb):
         step.run(ev[s])
@@ -1164,6 +1165,7 @@ def main():
                 "p10_us": round(1000 * xs[len(xs) // 10], 2), "p90_us": round(1000 * xs[(9 * len(xs)) // 10], 2)}
 
     stages = {name: stats(stage_ms[i]) for i, name in enumerate(Step.STAGES)}
+    median_sum_us = sum(v["median_us"] for v in stages.values())
     lm_mean_s = sum(lm_ms) / len(lm_ms) / 1000.0
     achieved = lm_bytes(w, step.T) / lm_mean_s / 1e9
 
@@ -1193,7 +1195,9 @@ def main():
                      "launches_timed": len(lm_ms),
                      "timing": "HIP events around the call in one timed step of every %d" % LM_SAMPLE},
         "stages": stages,
-        "stages_note": "per-stage means from a separate untimed pass of %d steps; the tree itself "
+        "steps_per_s_stage_medians": round(1e6 / median_sum_us, 2),
+        "stages_note": "per-stage statistics from a separate untimed pass of %d steps "
+                       "(steps_per_s_stage_medians = 1e6 / the sum of the stage medians, by HIP events); the tree itself "
                        "(medusa_build_tree) is built once per tree spec, per step only its candidates "
                        "and positions are gathered, by the lm_head kernel's last merging workgroup "
                        "(medusa_lm_head_topk_tree)" % nb,
