@@ -516,6 +516,19 @@ def base_head_timing(step, seed, steps):
                                    "temperature": temp}}
 
 
+def copy_peak_gbs(nbytes=1 << 30, n=20):
+    """A measured streaming-copy rate for the roofline: a device-to-device
+    copy of nbytes (nbytes read + nbytes written per call), GB/s by HIP
+    events over n calls."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    us = _time_calls(lambda i: dst.copy_(src), n)
+    del src, dst
+    return 2.0 * nbytes / (us * 1e-6) / 1e9
+
+
 def _time_calls(fn, n, warm=3):
     """Mean microseconds per call of fn(i) over n calls, HIP events on the
     current stream (where the library enqueues)."""
@@ -1219,6 +1232,14 @@ def main():
         result["attention_prefix_sweep"] = attention_prefix_sweep(step, args.steps)
         result["vicuna13b"] = vicuna13b(step, args.seed, args.steps)
         result["batch8_33b"] = batch8_33b(step, args.seed, args.steps)
+    # a measured streaming-copy rate beside the 8 TB/s peak, taken after
+    # every GPU leg (its 2 GiB of buffers are freed before the CPU baseline)
+    copy_gbs = copy_peak_gbs()
+    result["roofline"].update({
+        "copy_peak_gbs": round(copy_gbs, 1), "frac_of_copy_peak": round(achieved / copy_gbs, 4),
+        "copy_peak_note": "measured: a 1 GiB device-to-device copy, its read and write bytes by HIP events "
+                          "over 20 calls; a copy mixes reads and writes, so a read-only stream such as the "
+                          "lm_head's can exceed it"})
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)
     print(json.dumps(result))
